@@ -1,0 +1,427 @@
+/*
+ * CPU oracle for the fused MoE expert-FFN forward.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library. It shares no code,
+ * header, table or helper with the HIP library; it reads the same input bytes
+ * through the same strides and computes the plain definition of each step,
+ * slowly and in double precision.
+ *
+ * What is computed, and where it is defined:
+ *   route  - softmax over the router logits, top-k, renormalise
+ *            (ROCm/aiter PR "TP2 MXFP4 fused-MoE configs for Qwen3.5-397B",
+ *            Summary: the unfused 512/10 and shared-expert-fused 513/11
+ *            routing conventions; the tiny workload spells out
+ *            "softmax -> top-k, renormalised").
+ *   align  - the assignments (token t, slot j), flat index a = t*k + j,
+ *            grouped by expert in ascending a and each group padded to a
+ *            multiple of block_m (aiter PR, Details: the tuner's sorted
+ *            token routing and the block_m column of the latency table;
+ *            Liger PR #1377, Testing Done: unaligned token tails).
+ *   ffn    - for every valid (t, j) with expert e: g = G_e x_t, u = U_e x_t
+ *            with gate/up views of the packed w13 [E, 2I, H] addressed by
+ *            their real expert stride (Liger PR #1377, Problems and the
+ *            review reply on weight_expert_stride), h = SiLU(g) * u
+ *            (aiter PR, Details: ActivationType.Silu), y = W2_e h.
+ *   combine - out_t = sum_j w_tj * y_tj.
+ *   mxfp4  - e2m1 codes with one e8m0 scale per 32 elements along K
+ *            (aiter PR, Details: float4_e2m1fn_x2, QuantType.per_1x32) for
+ *            weights and activations.
+ *
+ * Readings where the pages are silent (each listed with its reason in the
+ * design notes): ties in top-k go to the lower expert index and slots are in
+ * selection order; the shared expert takes weight 1.0; the MXFP4 scale is
+ * floor(log2(amax)) - 2 clamped to [-127, 127] with round-to-nearest-even
+ * onto the e2m1 grid, saturating at 6, element 2i in the low nibble; h is
+ * rounded to bf16 (bf16 mode) or quantised to MXFP4 per 32 columns (MXFP4
+ * mode) from its fp32 value; out is rounded to bf16 once, from fp32.
+ *
+ * Numbers: products of bf16 or dequantised MXFP4 values are exact in double,
+ * sums run sequentially in ascending index order in double. Rounding points
+ * that turn a float into a code or a narrower float (h, out) first round the
+ * double to fp32, the precision the GPU takes that decision in.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_OK 0
+#define ORC_EARG (-1)
+
+/* ---------------------------------------------------------------- bf16 */
+
+static double orc_bf16_to_double(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* fp32 -> bf16, round to nearest, ties to even; NaN stays NaN. */
+static uint16_t orc_float_to_bf16(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu))
+        return (uint16_t)((u >> 16) | 0x0040u);
+    uint32_t upper = u >> 16;
+    uint32_t lower = u & 0xffffu;
+    if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u)))
+        upper += 1u;
+    return (uint16_t)upper;
+}
+
+/* --------------------------------------------------------------- mxfp4 */
+
+/* The eight magnitudes an e2m1 code can hold (code bits 0..2). */
+static const double orc_e2m1_mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+double orc_e2m1_value(int code)
+{
+    double m = orc_e2m1_mag[code & 7];
+    return (code & 8) ? -m : m;
+}
+
+/* e8m0 byte -> 2^(byte-127); 255 is NaN. */
+double orc_e8m0_value(int byte)
+{
+    if (byte == 255)
+        return NAN;
+    return ldexp(1.0, byte - 127);
+}
+
+/* Shared exponent of one group: floor(log2(amax)) - 2, clamped to
+ * [-127, 127]; a zero group gets -127. amax is an fp32 value. */
+static int orc_group_exponent(double amax)
+{
+    if (amax == 0.0)
+        return -127;
+    int ex;
+    frexp(amax, &ex);            /* amax = m * 2^ex, m in [0.5, 1) */
+    int s = (ex - 1) - 2;        /* floor(log2(amax)) - 2 */
+    if (s < -127)
+        s = -127;
+    if (s > 127)
+        s = 127;
+    return s;
+}
+
+/* Nearest e2m1 code to q (already divided by the group scale): search all
+ * eight magnitudes; on equal distance the even code wins; anything above 6
+ * lands on 6. The sign bit copies the sign of q. */
+static int orc_e2m1_nearest(double q)
+{
+    double a = fabs(q);
+    int best = 0;
+    double bestd = fabs(a - orc_e2m1_mag[0]);
+    for (int c = 1; c < 8; ++c) {
+        double d = fabs(a - orc_e2m1_mag[c]);
+        if (d < bestd || (d == bestd && (c & 1) == 0 && (best & 1) == 1)) {
+            best = c;
+            bestd = d;
+        }
+    }
+    return best | (signbit(q) ? 8 : 0);
+}
+
+/* Quantise n (a multiple of 32) fp32 values to packed codes (n/2 bytes,
+ * element 2i in the low nibble) and n/32 scale bytes. */
+void orc_mxfp4_quant(const float *v, int64_t n, uint8_t *codes, uint8_t *scales)
+{
+    for (int64_t g = 0; g < n / 32; ++g) {
+        const float *p = v + g * 32;
+        double amax = 0.0;
+        for (int i = 0; i < 32; ++i) {
+            double a = fabs((double)p[i]);
+            if (a > amax)
+                amax = a;
+        }
+        int s = orc_group_exponent(amax);
+        scales[g] = (uint8_t)(s + 127);
+        for (int i = 0; i < 32; i += 2) {
+            int lo = orc_e2m1_nearest(ldexp((double)p[i], -s));
+            int hi = orc_e2m1_nearest(ldexp((double)p[i + 1], -s));
+            codes[g * 16 + i / 2] = (uint8_t)(lo | (hi << 4));
+        }
+    }
+}
+
+/* Quantise bf16 rows: src[r*rs + c*cs] for r < rows, c < K. */
+int orc_mxfp4_quant_bf16(const uint16_t *src, int64_t rows, int64_t K, int64_t rs, int64_t cs,
+                         uint8_t *codes, uint8_t *scales)
+{
+    if (K % 32 != 0)
+        return ORC_EARG;
+    float *buf = (float *)malloc(sizeof(float) * (size_t)K);
+    if (!buf)
+        return ORC_EARG;
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t c = 0; c < K; ++c)
+            buf[c] = (float)orc_bf16_to_double(src[r * rs + c * cs]);
+        orc_mxfp4_quant(buf, K, codes + r * (K / 2), scales + r * (K / 32));
+    }
+    free(buf);
+    return ORC_OK;
+}
+
+/* Dequantise one packed row of K elements. */
+static void orc_mxfp4_dequant_row(const uint8_t *codes, const uint8_t *scales, int64_t K, double *out)
+{
+    for (int64_t c = 0; c < K; ++c) {
+        int byte = codes[c / 2];
+        int code = (c & 1) ? (byte >> 4) : (byte & 15);
+        out[c] = orc_e2m1_value(code) * orc_e8m0_value(scales[c / 32]);
+    }
+}
+
+/* --------------------------------------------------------------- route */
+
+/*
+ * For each token: p = softmax(logits[t, :]) in double; the k largest p are
+ * picked one after another (equal p: lower index first); with renorm the
+ * picked p are divided by their sum (summed in slot order); the results are
+ * rounded to fp32. With shared_id >= 0 the slot after the k routed ones gets
+ * (shared_id, shared_w).
+ */
+int orc_route(const float *logits, int64_t T, int64_t E, int64_t ls_t, int64_t ls_e, int k,
+              int renorm, int shared_id, float shared_w,
+              int32_t *ids, int64_t is_t, int64_t is_j, float *w, int64_t ws_t, int64_t ws_j)
+{
+    if (k <= 0 || k > E)
+        return ORC_EARG;
+    double *p = (double *)malloc(sizeof(double) * (size_t)E);
+    char *taken = (char *)malloc((size_t)E);
+    double *pk = (double *)malloc(sizeof(double) * (size_t)k);
+    if (!p || !taken || !pk) {
+        free(p); free(taken); free(pk);
+        return ORC_EARG;
+    }
+    for (int64_t t = 0; t < T; ++t) {
+        const float *row = logits + t * ls_t;
+        double m = -INFINITY;
+        for (int64_t e = 0; e < E; ++e)
+            if ((double)row[e * ls_e] > m)
+                m = (double)row[e * ls_e];
+        double z = 0.0;
+        for (int64_t e = 0; e < E; ++e) {
+            p[e] = exp((double)row[e * ls_e] - m);
+            z += p[e];
+        }
+        for (int64_t e = 0; e < E; ++e)
+            p[e] /= z;
+        memset(taken, 0, (size_t)E);
+        for (int j = 0; j < k; ++j) {
+            int64_t best = -1;
+            for (int64_t e = 0; e < E; ++e) {
+                if (taken[e])
+                    continue;
+                if (best < 0 || p[e] > p[best])
+                    best = e;
+            }
+            taken[best] = 1;
+            ids[t * is_t + j * is_j] = (int32_t)best;
+            pk[j] = p[best];
+        }
+        double s = 0.0;
+        for (int j = 0; j < k; ++j)
+            s += pk[j];
+        for (int j = 0; j < k; ++j)
+            w[t * ws_t + j * ws_j] = (float)(renorm ? pk[j] / s : pk[j]);
+        if (shared_id >= 0) {
+            ids[t * is_t + k * is_j] = shared_id;
+            w[t * ws_t + k * ws_j] = shared_w;
+        }
+    }
+    free(p);
+    free(taken);
+    free(pk);
+    return ORC_OK;
+}
+
+/* --------------------------------------------------------------- align */
+
+/*
+ * sorted[]: for e = 0..E-1, the flat indices a = t*k + j with ids[t, j] == e
+ * in ascending a, then the sentinel value A = T*k until the group length is a
+ * multiple of bm. block_expert[b] = expert of sorted block b. Ids outside
+ * [0, E) are left out. Returns the padded length in *n_padded; fails if it
+ * would exceed cap.
+ */
+int orc_align(const int32_t *ids, int64_t T, int k, int64_t is_t, int64_t is_j, int E, int bm,
+              int32_t *sorted, int32_t *block_expert, int64_t cap, int64_t *n_padded)
+{
+    if (bm <= 0 || k <= 0)
+        return ORC_EARG;
+    int64_t A = T * (int64_t)k;
+    int64_t pos = 0;
+    for (int e = 0; e < E; ++e) {
+        int64_t start = pos;
+        for (int64_t a = 0; a < A; ++a) {
+            int64_t t = a / k, j = a % k;
+            if (ids[t * is_t + j * is_j] == e) {
+                if (pos >= cap)
+                    return ORC_EARG;
+                sorted[pos++] = (int32_t)a;
+            }
+        }
+        while ((pos - start) % bm != 0) {
+            if (pos >= cap)
+                return ORC_EARG;
+            sorted[pos++] = (int32_t)A;
+        }
+        for (int64_t b = start / bm; b < pos / bm; ++b)
+            block_expert[b] = e;
+    }
+    *n_padded = pos;
+    return ORC_OK;
+}
+
+/* ----------------------------------------------------------------- ffn */
+
+typedef struct {
+    /* mode 0 = bf16, 1 = mxfp4 */
+    int32_t mode;
+    /* 0: h as computed (double, no rounding); 1: the method's rounding of h
+     * (bf16, or MXFP4 quantise + dequantise) */
+    int32_t round_h;
+    int64_t T, H, I, E, k;
+    /* x: bf16 [T, H] */
+    const uint16_t *x;
+    int64_t xs_t, xs_h;
+    /* bf16 weights, element strides: gate/up [E, I, H], w2 [E, H, I] */
+    const uint16_t *gate, *up, *w2;
+    int64_t gs_e, gs_r, gs_c, us_e, us_r, us_c, w2s_e, w2s_r, w2s_c;
+    /* mxfp4 weights: packed codes [E, rows, K/2] and scales [E, rows, K/32],
+     * byte strides (expert, row); the last dim is contiguous */
+    const uint8_t *gate_q, *up_q, *w2_q, *gate_sc, *up_sc, *w2_sc;
+    int64_t gqs_e, gqs_r, uqs_e, uqs_r, w2qs_e, w2qs_r;
+    int64_t gss_e, gss_r, uss_e, uss_r, w2ss_e, w2ss_r;
+    /* routing */
+    const int32_t *ids;
+    int64_t is_t, is_j;
+    const float *wts;
+    int64_t ws_t, ws_j;
+} orc_ffn_args;
+
+static double orc_silu_mul(double g, double u)
+{
+    return g / (1.0 + exp(-g)) * u;
+}
+
+/* One token: out_acc[H] = sum_j w_tj * y_tj, with y per the definition. */
+static int orc_ffn_token(const orc_ffn_args *a, int64_t t, double *xh, double *wrow, double *hrow,
+                         float *hf, uint8_t *hq, uint8_t *hs, double *acc)
+{
+    const int64_t H = a->H, I = a->I;
+    /* x row: exact bf16 value, or MXFP4 quantise + dequantise of it */
+    for (int64_t c = 0; c < H; ++c)
+        xh[c] = orc_bf16_to_double(a->x[t * a->xs_t + c * a->xs_h]);
+    if (a->mode == 1) {
+        float *xf = hf; /* reuse: H fp32 scratch is available in hf (size >= H) */
+        for (int64_t c = 0; c < H; ++c)
+            xf[c] = (float)xh[c];
+        uint8_t *xq = hq, *xs = hs;
+        orc_mxfp4_quant(xf, H, xq, xs);
+        orc_mxfp4_dequant_row(xq, xs, H, xh);
+    }
+    for (int64_t n = 0; n < H; ++n)
+        acc[n] = 0.0;
+    for (int64_t j = 0; j < a->k; ++j) {
+        int64_t e = a->ids[t * a->is_t + j * a->is_j];
+        if (e < 0 || e >= a->E)
+            continue;
+        double wt = (double)a->wts[t * a->ws_t + j * a->ws_j];
+        for (int64_t i = 0; i < I; ++i) {
+            double g = 0.0, u = 0.0;
+            if (a->mode == 0) {
+                const uint16_t *gr = a->gate + e * a->gs_e + i * a->gs_r;
+                const uint16_t *ur = a->up + e * a->us_e + i * a->us_r;
+                for (int64_t c = 0; c < H; ++c)
+                    g += xh[c] * orc_bf16_to_double(gr[c * a->gs_c]);
+                for (int64_t c = 0; c < H; ++c)
+                    u += xh[c] * orc_bf16_to_double(ur[c * a->us_c]);
+            } else {
+                orc_mxfp4_dequant_row(a->gate_q + e * a->gqs_e + i * a->gqs_r,
+                                      a->gate_sc + e * a->gss_e + i * a->gss_r, H, wrow);
+                for (int64_t c = 0; c < H; ++c)
+                    g += xh[c] * wrow[c];
+                orc_mxfp4_dequant_row(a->up_q + e * a->uqs_e + i * a->uqs_r,
+                                      a->up_sc + e * a->uss_e + i * a->uss_r, H, wrow);
+                for (int64_t c = 0; c < H; ++c)
+                    u += xh[c] * wrow[c];
+            }
+            hrow[i] = orc_silu_mul(g, u);
+        }
+        if (a->round_h) {
+            if (a->mode == 0) {
+                for (int64_t i = 0; i < I; ++i)
+                    hrow[i] = orc_bf16_to_double(orc_float_to_bf16((float)hrow[i]));
+            } else {
+                for (int64_t i = 0; i < I; ++i)
+                    hf[i] = (float)hrow[i];
+                orc_mxfp4_quant(hf, I, hq, hs);
+                orc_mxfp4_dequant_row(hq, hs, I, hrow);
+            }
+        }
+        for (int64_t n = 0; n < H; ++n) {
+            double y = 0.0;
+            if (a->mode == 0) {
+                const uint16_t *wr = a->w2 + e * a->w2s_e + n * a->w2s_r;
+                for (int64_t i = 0; i < I; ++i)
+                    y += hrow[i] * orc_bf16_to_double(wr[i * a->w2s_c]);
+            } else {
+                orc_mxfp4_dequant_row(a->w2_q + e * a->w2qs_e + n * a->w2qs_r,
+                                      a->w2_sc + e * a->w2ss_e + n * a->w2ss_r, I, wrow);
+                for (int64_t i = 0; i < I; ++i)
+                    y += hrow[i] * wrow[i];
+            }
+            acc[n] += wt * y;
+        }
+    }
+    return ORC_OK;
+}
+
+/*
+ * Forward for the tokens listed in toks[0..n_toks) (all tokens when toks is
+ * NULL, n_toks = T). out_acc[r, n] holds the double sum, out_bf16[r, n] its
+ * bf16 rounding through fp32. Row r of the outputs is token toks[r].
+ */
+int orc_ffn(const orc_ffn_args *a, const int64_t *toks, int64_t n_toks, double *out_acc,
+            uint16_t *out_bf16)
+{
+    if (a->mode == 1 && (a->H % 32 != 0 || a->I % 32 != 0))
+        return ORC_EARG;
+    int64_t wmax = a->H > a->I ? a->H : a->I;
+    int err = 0;
+#pragma omp parallel
+    {
+        double *xh = (double *)malloc(sizeof(double) * (size_t)a->H);
+        double *wrow = (double *)malloc(sizeof(double) * (size_t)wmax);
+        double *hrow = (double *)malloc(sizeof(double) * (size_t)a->I);
+        float *hf = (float *)malloc(sizeof(float) * (size_t)wmax);
+        uint8_t *hq = (uint8_t *)malloc((size_t)wmax);
+        uint8_t *hs = (uint8_t *)malloc((size_t)wmax);
+        double *acc = (double *)malloc(sizeof(double) * (size_t)a->H);
+        if (!xh || !wrow || !hrow || !hf || !hq || !hs || !acc) {
+#pragma omp atomic write
+            err = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t r = 0; r < n_toks; ++r) {
+                int64_t t = toks ? toks[r] : r;
+                orc_ffn_token(a, t, xh, wrow, hrow, hf, hq, hs, acc);
+                for (int64_t n = 0; n < a->H; ++n) {
+                    out_acc[r * a->H + n] = acc[n];
+                    out_bf16[r * a->H + n] = orc_float_to_bf16((float)acc[n]);
+                }
+            }
+        }
+        free(xh); free(wrow); free(hrow); free(hf); free(hq); free(hs); free(acc);
+    }
+    return err ? ORC_EARG : ORC_OK;
+}
+
+/* Size of orc_ffn_args, so the Python side can check its mirror. */
+int64_t orc_ffn_args_size(void) { return (int64_t)sizeof(orc_ffn_args); }
