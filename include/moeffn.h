@@ -1,0 +1,224 @@
+/*
+ * moeffn — fused mixture-of-experts expert-FFN forward for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The forward pass of one MoE layer, as the pages describe it:
+ *   1. route     top-k over the router's softmax, renormalised
+ *                (ROCm/aiter PR "TP2 MXFP4 fused-MoE configs for
+ *                Qwen3.5-397B", Summary: unfused 512/10 and
+ *                shared-expert-fused 513/11 routing);
+ *   2. align     the (token, slot) assignments grouped by expert, each group
+ *                padded to block_m rows (aiter PR, Details: sorted routing
+ *                and the block_m column of the tuned latency table);
+ *   3. gemm1     gathered token rows x gate_e^T and x up_e^T, where gate and
+ *                up may be views into one packed w13 [E, 2I, H] whose expert
+ *                stride is 2*I*H (Liger-Kernel PR #1377 "Support strided
+ *                Liger MoE input weights", Problems);
+ *   4. act       h = SiLU(gate) * up (aiter PR, Details: ActivationType.Silu);
+ *   5. gemm2     h x w2_e^T with w2 [E, H, I];
+ *   6. combine   out_t = sum over slots j of w_tj * y_tj.
+ * bf16 mode runs all of it in bf16 with fp32 accumulation; MXFP4 mode holds
+ * weights and activations as e2m1 codes with one e8m0 scale per 32 elements
+ * along K (aiter PR, Details: float4_e2m1fn_x2, QuantType.per_1x32).
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ * - Tensors are described by moe_tensor_t: `data` is the device address of
+ *   element [0, ..., 0] of the view (any storage offset already applied),
+ *   `size`/`stride` are per dimension, strides in elements of `dtype`
+ *   (MOE_DT_FP4X2: one element = one byte holding two e2m1 codes, element 2i
+ *   of the logical row in the low nibble). Strides may be any positive value;
+ *   a dimension of size 1 may have any stride. A packed w13 view, a per-layer
+ *   routed_experts slice with token stride L*k (prime-rl PR #2860, Problem)
+ *   and an activation with last-dim stride != 1 (LightLLM issue #1467) are all
+ *   accepted without copies and give results bit-identical to contiguous
+ *   inputs. A layout the kernels cannot read correctly is rejected with
+ *   MOE_ERR_LAYOUT, never read as if it were contiguous.
+ * - The caller owns all memory: inputs, outputs and the workspace. The
+ *   library allocates nothing, keeps no per-call state, performs no host
+ *   synchronisation and no device-to-host copy, and launches only on the
+ *   caller's stream. Calls are asynchronous and can be captured in a HIP
+ *   graph. Two calls that share a workspace must be ordered on one stream.
+ * - Every argument check runs on the host before the first launch: a call
+ *   that returns an error has enqueued nothing. MOE_ERR_HIP reports a failed
+ *   launch; moe_last_error() then holds the HIP error text.
+ * - Inputs must be finite (logits may be -inf as long as each row keeps at
+ *   least k finite entries). Outputs must not overlap inputs.
+ */
+#ifndef MOEFFN_H
+#define MOEFFN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_MAX_DIMS 4
+/* Number of timed stages of moe_fused_fwd (see moe_fused_args_t). */
+#define MOE_NUM_STAGES 5
+
+typedef enum {
+    MOE_DT_BF16 = 1,   /* bfloat16 */
+    MOE_DT_F32 = 2,    /* float32 */
+    MOE_DT_I32 = 3,    /* int32 */
+    MOE_DT_FP4X2 = 4,  /* two e2m1 codes per byte, element 2i in the low nibble */
+    MOE_DT_E8M0 = 5    /* one unsigned byte b per 32 elements, scale 2^(b-127) */
+} moe_dtype_t;
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_NULL = -1,        /* a required pointer is NULL */
+    MOE_ERR_SHAPE = -2,       /* sizes disagree (e.g. gate H != x H) */
+    MOE_ERR_DTYPE = -3,       /* wrong element type for this argument */
+    MOE_ERR_LAYOUT = -4,      /* strides or alignment the kernels cannot honour */
+    MOE_ERR_WORKSPACE = -5,   /* workspace NULL, misaligned or too small */
+    MOE_ERR_UNSUPPORTED = -6, /* sizes outside what this build handles */
+    MOE_ERR_HIP = -7,         /* a HIP launch failed */
+    MOE_ERR_ARG = -8          /* any other invalid scalar argument */
+} moe_status_t;
+
+typedef enum { MOE_MODE_BF16 = 0, MOE_MODE_MXFP4 = 1 } moe_mode_t;
+typedef enum { MOE_ACT_SILU = 0 } moe_activation_t;
+
+typedef struct {
+    void *data;
+    int32_t dtype;                 /* moe_dtype_t */
+    int32_t ndim;
+    int64_t size[MOE_MAX_DIMS];
+    int64_t stride[MOE_MAX_DIMS];  /* in elements */
+} moe_tensor_t;
+
+/* A HIP stream (hipStream_t); NULL is the default stream. */
+typedef void *moe_stream_t;
+
+/* -------------------------------------------------------------- route --
+ * moe_topk_softmax: router, step 1.
+ *   logits   [T, E_r] float32, any strides.
+ *   k        routed slots, 1 <= k <= min(E_r, 32).
+ *   renorm   1: w_j = softmax_j / sum over the k picked (the pages' "top-k,
+ *            renormalised"); 0: plain softmax values of the picked experts.
+ *   shared_id, shared_w   if shared_id >= 0, slot k is (shared_id, shared_w)
+ *            (the 513/11 convention: expert 512 in every token's 11th slot).
+ *   ids      [T, k (+1 if shared)] int32 out, any strides.
+ *   weights  [T, k (+1)] float32 out, any strides.
+ * Picks the k largest logits, ties to the lower expert index, slots in that
+ * order. Weights are computed in double precision and rounded once to fp32.
+ * T = 0 is a no-op.
+ */
+int moe_topk_softmax(const moe_tensor_t *logits, int32_t k, int32_t renorm, int32_t shared_id,
+                     float shared_w, const moe_tensor_t *ids, const moe_tensor_t *weights,
+                     moe_stream_t stream);
+
+/* -------------------------------------------------------------- align --
+ * moe_align: step 2, standalone.
+ *   ids           [T, k] int32, any strides. Ids outside [0, E) are skipped.
+ *   num_experts   E >= 1.
+ *   block_m       16, 32, 64, 128 or 256.
+ *   sorted_ids    [cap] int32 out, contiguous: for e = 0..E-1 the flat
+ *                 indices a = t*k + j with ids[t, j] == e in ascending a, then
+ *                 the sentinel T*k until the group is a multiple of block_m.
+ *                 cap must be >= moe_align_capacity(T*k, E, block_m).
+ *   block_expert  [cap / block_m] int32 out: expert of each sorted block.
+ *   n_padded      [1] int32 out: used length of sorted_ids.
+ *   ws, ws_bytes  scratch of at least moe_align_workspace_size() bytes,
+ *                 256-byte aligned.
+ * Entries of sorted_ids and block_expert past n_padded are left unspecified.
+ */
+int moe_align(const moe_tensor_t *ids, int32_t num_experts, int32_t block_m,
+              const moe_tensor_t *sorted_ids, const moe_tensor_t *block_expert,
+              const moe_tensor_t *n_padded, void *ws, size_t ws_bytes, moe_stream_t stream);
+/* Upper bound on n_padded for A assignments. Host only. */
+int64_t moe_align_capacity(int64_t assignments, int32_t num_experts, int32_t block_m);
+/* Scratch bytes moe_align needs. Host only, no device calls. */
+int moe_align_workspace_size(int64_t tokens, int32_t k, int32_t num_experts, int32_t block_m,
+                             size_t *bytes);
+
+/* -------------------------------------------------------------- quant --
+ * moe_quant_mxfp4: bf16 -> MXFP4, the activation quantisation of step 3 in
+ * MXFP4 mode and the offline weight quantisation.
+ *   src     [R, K] or [E, R, K] bf16, any strides; K a multiple of 32.
+ *   codes   same leading shape, [.., K/2] FP4X2 out; last stride 1.
+ *   scales  same leading shape, [.., K/32] E8M0 out; last stride 1.
+ * Per group of 32 along K: s = floor(log2(max|v|)) - 2 clamped to
+ * [-127, 127] (s = -127 for an all-zero group), scale byte s + 127, each
+ * element the e2m1 code nearest to v / 2^s, ties to the even code, saturating
+ * at +-6, sign kept (including -0).
+ */
+int moe_quant_mxfp4(const moe_tensor_t *src, const moe_tensor_t *codes,
+                    const moe_tensor_t *scales, moe_stream_t stream);
+
+/* -------------------------------------------------------------- fused --
+ * Arguments of the fused forward (steps 2-6).
+ *   mode        MOE_MODE_BF16 or MOE_MODE_MXFP4.
+ *   activation  MOE_ACT_SILU.
+ *   x           [T, H] bf16, any strides (quantised inside in MXFP4 mode).
+ *   gate, up    bf16 [E, I, H] | FP4X2 [E, I, H/2]; last stride 1; expert
+ *               and row strides free (64-bit), so views into a packed
+ *               w13 [E, 2I, H] work as they are.
+ *   gate_scale, up_scale   MXFP4 only: E8M0 [E, I, H/32], last stride 1.
+ *   w2          bf16 [E, H, I] | FP4X2 [E, H, I/2]; last stride 1.
+ *   w2_scale    MXFP4 only: E8M0 [E, H, I/32], last stride 1.
+ *   topk_ids    [T, k] int32, any strides; ids outside [0, E) are skipped.
+ *   topk_weights [T, k] float32, any strides.
+ *   out         [T, H] bf16 out, any strides.
+ *   stage_events NULL, or 2*MOE_NUM_STAGES hipEvent_t handles created by the
+ *               caller; event 2s is recorded before stage s and 2s+1 after
+ *               it, on the call's stream. Stages: 0 align, 1 prepare
+ *               (activation quantise or re-layout; may be empty), 2 gemm1 +
+ *               act, 3 gemm2, 4 combine.
+ *   force_config  -1 for the built-in choice, else an index into the
+ *               library's config list (tests of tile invariance).
+ * Numerics: fp32 accumulation; h rounded to bf16 (bf16 mode) or quantised to
+ * MXFP4 per 32 columns (MXFP4 mode); per-slot results y in fp32; combine
+ * acc = fmaf(w_tj, y_tj, acc) over j = 0..k-1 in slot order from +0, then one
+ * round to bf16. The tile configuration depends only on (mode, T, H, I, E, k),
+ * never on strides, so every layout runs the same arithmetic.
+ */
+typedef struct {
+    int32_t mode;
+    int32_t activation;
+    moe_tensor_t x;
+    moe_tensor_t gate, up;
+    moe_tensor_t gate_scale, up_scale;
+    moe_tensor_t w2, w2_scale;
+    moe_tensor_t topk_ids;
+    moe_tensor_t topk_weights;
+    moe_tensor_t out;
+    void *const *stage_events;
+    int32_t force_config;
+    int32_t reserved;
+} moe_fused_args_t;
+
+/* The tile configuration a call would use. */
+typedef struct {
+    int32_t bucket;        /* smallest power of two >= T, capped at 32768 */
+    int32_t block_m;       /* rows per sorted block */
+    int32_t gemm1_kernel;  /* kernel family id of gemm1 */
+    int32_t gemm2_kernel;  /* kernel family id of gemm2 */
+    int32_t gemm1_split_k; /* waves splitting K inside a workgroup */
+    int32_t gemm2_split_k;
+    int32_t config_index;  /* index into the library's config list */
+    int32_t num_configs;   /* size of that list */
+} moe_config_t;
+
+/* Validate args and report the configuration. Host only. */
+int moe_query_config(const moe_fused_args_t *args, moe_config_t *cfg);
+/* Validate args and report the workspace bytes moe_fused_fwd needs. Host only. */
+int moe_fused_workspace_size(const moe_fused_args_t *args, size_t *bytes);
+/* The fused forward: align, (prepare), gemm1 + act, gemm2, combine.
+ * ws: caller-owned device scratch, 256-byte aligned, >= the reported size;
+ * its contents on entry do not matter. T = 0 returns MOE_OK with no launch. */
+int moe_fused_fwd(const moe_fused_args_t *args, void *ws, size_t ws_bytes, moe_stream_t stream);
+
+/* ------------------------------------------------------------- errors --
+ * Static text for a status code; never NULL. */
+const char *moe_strerror(int status);
+/* Thread-local detail of the last failing call on this thread ("" if none). */
+const char *moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOEFFN_H */

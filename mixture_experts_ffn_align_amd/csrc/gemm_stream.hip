@@ -1,0 +1,334 @@
+// Grouped expert GEMMs of the fused MoE forward, weight-streaming variant.
+//
+// Stage 1 (gemm1 + act): for one sorted block of BM rows, all routed to
+// expert e, the rows of x they came from (t = a / k) times gate_e^T and
+// up_e^T, then h = SiLU(g) * u (ROCm/aiter PR "TP2 MXFP4 fused-MoE configs
+// for Qwen3.5-397B", Details: ActivationType.Silu). gate and up are addressed
+// through their own expert and row strides, so views into one packed
+// w13 [E, 2I, H] are read in place (Liger-Kernel PR #1377, Problems: each
+// expert's first weight tile must come from the real expert stride, not from
+// I / TileN).
+// Stage 2 (gemm2): h rows times w2_e^T, each fp32 result row written to its
+// flat assignment index a = t*k + j, ready for the slot-ordered combine.
+//
+// Work split. A workgroup is four wave64s. Each wave owns 4 MFMA column
+// blocks of 16 (stage 1: 32 gate + 32 up rows -> 32 h columns; stage 2: 64
+// output columns) for all BM rows; WK waves split K and reduce through LDS
+// in a fixed order. Both operands are K-contiguous, which is exactly the
+// per-lane layout of v_mfma_f32_16x16x32_bf16 / v_mfma_scale_f32_16x16x128
+// (lane l: row l % 16, a run of consecutive k chosen by l / 16), so every lane
+// loads its 16-byte operand straight from memory into registers: weights
+// stream HBM -> VGPR once per block with no LDS round trip, and the loads of
+// the next K step are issued before the MFMAs of the current one.
+//
+// In MXFP4 mode one lane's 32 e2m1 codes are exactly one scale block, so the
+// per-1x32 e8m0 scales feed the block-scaled MFMA directly, and the stage 1
+// epilogue quantises h per 32 columns in registers (max over 16 lanes).
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+template <int MODE>
+struct Frag;
+template <>
+struct Frag<0> {          // bf16: 8 values per lane per step
+    bf16x8_t v;
+};
+template <>
+struct Frag<1> {          // fp4: 32 codes (16 bytes) per lane per step + one scale byte
+    i32x4_t v;
+    int sc;
+};
+
+__device__ __forceinline__ float silu_mul(float g, float u) {
+    // g / (1 + e^-g): for very negative g, e^-g overflows to +inf and the
+    // reciprocal gives 0, so the result is a signed zero, never NaN.
+    float e = __expf(-g);
+    return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
+}
+
+template <int MODE, int STAGE, int BM, int WK, int U>
+__global__ __launch_bounds__(256) void gemm_stream(GemmParams p) {
+    constexpr int MB = BM / 16;
+    constexpr int NB = 4;
+    constexpr int WN = 4 / WK;
+    constexpr int KSTEP = MODE == 0 ? 32 : 128;
+    constexpr int WCOLS = STAGE == 1 ? 32 : 64;
+    constexpr int TILE_N = WN * WCOLS;
+
+    const int lane = lane_id();
+    const int w = threadIdx.x >> 6;
+    const int wn = w / WK, wk = w % WK;
+    const int r16 = lane & 15, kg = lane >> 4;
+
+    // ---- tile mapping: ((n-group, m-block), n-tile in group), XCD-aware
+    const int n_tiles = p.N / TILE_N;
+    const uint32_t L = xcd_remap(blockIdx.x, gridDim.x);
+    const int G = p.n_tile_groups;
+    const int ji = (int)(L % (uint32_t)G);
+    const uint32_t rest = L / (uint32_t)G;
+    const int mb = (int)(rest % (uint32_t)p.max_mblocks);
+    const int jg = (int)(rest / (uint32_t)p.max_mblocks);
+    const int nt = jg * G + ji;
+    if (nt >= n_tiles) return;
+    const int n_blocks = __builtin_nontemporal_load(p.n_padded) / BM;
+    if (mb >= n_blocks) return;
+    const int e = p.block_expert[mb];
+    const int row0 = mb * BM;
+    const int n0 = nt * TILE_N + wn * WCOLS;
+
+    // ---- operand row addresses (per lane)
+    const char* a_ptr[MB];
+    const uint8_t* a_sc[MB];
+#pragma unroll
+    for (int mi = 0; mi < MB; ++mi) {
+        const int row = row0 + mi * 16 + r16;
+        int64_t arow = row;
+        if (STAGE == 1) {
+            const int a = p.sorted[row];
+            arow = a < p.A ? (int64_t)((unsigned)a / (unsigned)p.k) : 0;
+        }
+        if (MODE == 0) {
+            a_ptr[mi] = reinterpret_cast<const char*>(p.a) + arow * p.a_row * 2;
+            a_sc[mi] = nullptr;
+        } else {
+            a_ptr[mi] = reinterpret_cast<const char*>(p.a) + arow * p.a_row;
+            a_sc[mi] = p.a_sc + arow * p.a_sc_row;
+        }
+    }
+    const char* b_ptr[NB];
+    const uint8_t* b_sc[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const bool second = STAGE == 1 && nb >= 2;
+        const int wrow = STAGE == 1 ? n0 + (nb & 1) * 16 + r16 : n0 + nb * 16 + r16;
+        const char* base = reinterpret_cast<const char*>(second ? p.b1 : p.b0);
+        const int64_t se = second ? p.b1_e : p.b0_e;
+        const int64_t sr = second ? p.b1_r : p.b0_r;
+        if (MODE == 0) {
+            b_ptr[nb] = base + ((int64_t)e * se + (int64_t)wrow * sr) * 2;
+            b_sc[nb] = nullptr;
+        } else {
+            b_ptr[nb] = base + (int64_t)e * se + (int64_t)wrow * sr;
+            const uint8_t* sb = second ? p.b1_sc : p.b0_sc;
+            const int64_t sse = second ? p.b1sc_e : p.b0sc_e;
+            const int64_t ssr = second ? p.b1sc_r : p.b0sc_r;
+            b_sc[nb] = sb + (int64_t)e * sse + (int64_t)wrow * ssr;
+        }
+    }
+
+    // ---- K loop over this wave's share
+    const int kw = p.K / WK;
+    const int kbeg = wk * kw;
+    const int steps = kw / KSTEP;
+    // byte offset of this lane's operand run for step s
+    auto koff = [&](int s) -> int64_t {
+        const int k = kbeg + s * KSTEP;
+        return MODE == 0 ? (int64_t)(k + kg * 8) * 2 : (int64_t)(k / 2 + kg * 16);
+    };
+    auto sidx = [&](int s) -> int { return (kbeg + s * KSTEP) / 32 + kg; };
+
+    Frag<MODE> fa[2][U][MB];
+    Frag<MODE> fb[2][U][NB];
+    f32x4_t acc[MB][NB];
+#pragma unroll
+    for (int mi = 0; mi < MB; ++mi)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[mi][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    auto load_chunk = [&](int buf, int s0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int s = s0 + u;
+            if (s < steps) {
+                const int64_t off = koff(s);
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    using V = decltype(fb[buf][u][nb].v);
+                    fb[buf][u][nb].v = *reinterpret_cast<const V*>(b_ptr[nb] + off);
+                }
+#pragma unroll
+                for (int mi = 0; mi < MB; ++mi) {
+                    using V = decltype(fa[buf][u][mi].v);
+                    fa[buf][u][mi].v = *reinterpret_cast<const V*>(a_ptr[mi] + off);
+                }
+                if constexpr (MODE == 1) {
+                    const int si = sidx(s);
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) fb[buf][u][nb].sc = b_sc[nb][si];
+#pragma unroll
+                    for (int mi = 0; mi < MB; ++mi) fa[buf][u][mi].sc = a_sc[mi][si];
+                }
+            }
+        }
+    };
+    auto compute_chunk = [&](int buf, int s0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (s0 + u < steps) {
+#pragma unroll
+                for (int mi = 0; mi < MB; ++mi)
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) {
+                        if constexpr (MODE == 0) {
+                            acc[mi][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                fa[buf][u][mi].v, fb[buf][u][nb].v, acc[mi][nb], 0, 0, 0);
+                        } else {
+                            const i32x4_t av = fa[buf][u][mi].v, bv = fb[buf][u][nb].v;
+                            const i32x8_t a8 = {av[0], av[1], av[2], av[3], 0, 0, 0, 0};
+                            const i32x8_t b8 = {bv[0], bv[1], bv[2], bv[3], 0, 0, 0, 0};
+                            acc[mi][nb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                                a8, b8, acc[mi][nb], 4, 4, 0, fa[buf][u][mi].sc, 0,
+                                fb[buf][u][nb].sc);
+                        }
+                    }
+            }
+        }
+    };
+
+    load_chunk(0, 0);
+    for (int s0 = 0; s0 < steps; s0 += 2 * U) {
+        if (s0 + U < steps) load_chunk(1, s0 + U);
+        compute_chunk(0, s0);
+        if (s0 + U >= steps) break;
+        if (s0 + 2 * U < steps) load_chunk(0, s0 + 2 * U);
+        compute_chunk(1, s0 + U);
+    }
+
+    // ---- split-K reduction through LDS (fixed order wk = 0..WK-1)
+    constexpr int RED_FLOATS = WK > 1 ? 4 * MB * NB * 4 * 64 : 1;
+    __shared__ float red[RED_FLOATS];
+    if constexpr (WK > 1) {
+#pragma unroll
+        for (int mi = 0; mi < MB; ++mi)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    red[(((w * MB + mi) * NB + nb) * 4 + i) * 64 + lane] = acc[mi][nb][i];
+        __syncthreads();
+    }
+    auto tile = [&](int mi, int nb) -> f32x4_t {
+        if constexpr (WK == 1) {
+            return acc[mi][nb];
+        } else {
+            f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int q = 0; q < WK; ++q) {
+                const int src = wn * WK + q;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) s[i] += red[(((src * MB + mi) * NB + nb) * 4 + i) * 64 + lane];
+            }
+            return s;
+        }
+    };
+
+    // ---- epilogues
+    if constexpr (STAGE == 1 && MODE == 0) {
+        uint16_t* h = reinterpret_cast<uint16_t*>(p.out);
+#pragma unroll
+        for (int unit = 0; unit < MB * 2; ++unit) {
+            if (unit % WK != wk) continue;
+            const int mi = unit / 2, np = unit % 2;
+            const f32x4_t g = tile(mi, np), u = tile(mi, np + 2);
+            const int col = n0 + np * 16 + r16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t row = row0 + mi * 16 + kg * 4 + i;
+                h[row * p.N + col] = f32_to_bf16_bits(silu_mul(g[i], u[i]));
+            }
+        }
+    } else if constexpr (STAGE == 1 && MODE == 1) {
+        uint8_t* hq = reinterpret_cast<uint8_t*>(p.out);
+#pragma unroll
+        for (int mi = 0; mi < MB; ++mi) {
+            if (mi % WK != wk) continue;
+            const f32x4_t g0 = tile(mi, 0), g1 = tile(mi, 1), u0 = tile(mi, 2), u1 = tile(mi, 3);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float h0 = silu_mul(g0[i], u0[i]);
+                const float h1 = silu_mul(g1[i], u1[i]);
+                const uint32_t b0 = __float_as_uint(h0), b1 = __float_as_uint(h1);
+                uint32_t amax = max(b0 & 0x7fffffffu, b1 & 0x7fffffffu);
+#pragma unroll
+                for (int off = 1; off < 16; off <<= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, off));
+                const int s = group_exponent(amax);
+                const E2m1Thresholds th = e2m1_thresholds(s);
+                const uint32_t c0 = e2m1_code(b0, th), c1 = e2m1_code(b1, th);
+                const uint32_t o0 = (uint32_t)__shfl_xor((int)c0, 1), o1 = (uint32_t)__shfl_xor((int)c1, 1);
+                const int64_t row = row0 + mi * 16 + kg * 4 + i;
+                uint8_t* rp = hq + row * (p.N / 2);
+                if ((r16 & 1) == 0) {
+                    rp[(n0 + r16) / 2] = (uint8_t)(c0 | (o0 << 4));
+                    rp[(n0 + 16 + r16) / 2] = (uint8_t)(c1 | (o1 << 4));
+                }
+                if (r16 == 0) p.out_sc[row * (p.N / 32) + n0 / 32] = (uint8_t)(s + 127);
+            }
+        }
+    } else {
+        float* y = reinterpret_cast<float*>(p.out);
+#pragma unroll
+        for (int unit = 0; unit < MB * NB; ++unit) {
+            if (unit % WK != wk) continue;
+            const int mi = unit / NB, nb = unit % NB;
+            const f32x4_t t = tile(mi, nb);
+            const int col = n0 + nb * 16 + r16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int a = p.sorted[row0 + mi * 16 + kg * 4 + i];
+                if (a < p.A) y[(int64_t)a * p.N + col] = t[i];
+            }
+        }
+    }
+}
+
+typedef void (*GemmFn)(GemmParams);
+
+template <int MODE, int STAGE, int BM, int WK>
+constexpr GemmFn pick() {
+    return gemm_stream<MODE, STAGE, BM, WK, (MODE == 0 ? 2 : 1)>;
+}
+
+template <int MODE, int STAGE>
+GemmFn table(int bm, int wk) {
+#define MOE_CASE(B, W) \
+    if (bm == B && wk == W) return pick<MODE, STAGE, B, W>();
+    MOE_CASE(16, 1) MOE_CASE(16, 2) MOE_CASE(16, 4)
+    MOE_CASE(32, 1) MOE_CASE(32, 2) MOE_CASE(32, 4)
+    MOE_CASE(64, 1) MOE_CASE(64, 2) MOE_CASE(64, 4)
+#undef MOE_CASE
+    return nullptr;
+}
+
+GemmFn lookup(const GemmKernelId& id) {
+    if (id.mode == 0 && id.stage == 1) return table<0, 1>(id.bm, id.wk);
+    if (id.mode == 0 && id.stage == 2) return table<0, 2>(id.bm, id.wk);
+    if (id.mode == 1 && id.stage == 1) return table<1, 1>(id.bm, id.wk);
+    if (id.mode == 1 && id.stage == 2) return table<1, 2>(id.bm, id.wk);
+    return nullptr;
+}
+
+}  // namespace
+
+int gemm_tile_n(const GemmKernelId& id) {
+    const int wn = 4 / id.wk;
+    return wn * (id.stage == 1 ? 32 : 64);
+}
+
+bool gemm_supported(const GemmKernelId& id) { return lookup(id) != nullptr; }
+
+hipError_t launch_gemm(const GemmKernelId& id, const GemmParams& p, hipStream_t s) {
+    GemmFn fn = lookup(id);
+    if (!fn) return hipErrorInvalidValue;
+    const int tile_n = gemm_tile_n(id);
+    const int n_tiles = p.N / tile_n;
+    const int G = p.n_tile_groups;
+    const int64_t groups = (n_tiles + G - 1) / G;
+    const int64_t grid = groups * (int64_t)p.max_mblocks * G;
+    if (grid == 0) return hipSuccess;
+    hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,666 @@
+// Host side of libmoeffn: argument checks, configuration choice, workspace
+// layout and the launch sequence behind the C ABI declared in moeffn.h.
+//
+// Every check runs before the first launch, so a call that fails has
+// enqueued nothing (Liger-Kernel PR #1377, Testing Done: mismatched gate
+// hidden dims fail before any descriptor is built; strided grad inputs are
+// rejected before any native allocation). A layout the kernels cannot read
+// is rejected, never read as if contiguous (LightLLM issue #1467).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "moe_internal.h"
+#include "moeffn.h"
+
+using namespace moe;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+int ok() {
+    g_last_error.clear();
+    return MOE_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+    return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+const char* dtype_name(int d) {
+    switch (d) {
+        case MOE_DT_BF16: return "bf16";
+        case MOE_DT_F32: return "f32";
+        case MOE_DT_I32: return "i32";
+        case MOE_DT_FP4X2: return "fp4x2";
+        case MOE_DT_E8M0: return "e8m0";
+        default: return "?";
+    }
+}
+
+int elem_bytes(int d) {
+    switch (d) {
+        case MOE_DT_BF16: return 2;
+        case MOE_DT_F32: case MOE_DT_I32: return 4;
+        case MOE_DT_FP4X2: case MOE_DT_E8M0: return 1;
+        default: return 0;
+    }
+}
+
+int64_t numel(const moe_tensor_t& t) {
+    int64_t n = 1;
+    for (int i = 0; i < t.ndim; ++i) n *= t.size[i];
+    return n;
+}
+
+// Basic descriptor sanity: dtype, rank, non-negative sizes, positive strides
+// on dimensions longer than 1, and data present when the tensor is not empty.
+int check_desc(const moe_tensor_t* t, const char* name, int dtype, int ndim) {
+    if (!t) return fail(MOE_ERR_NULL, "%s: descriptor is NULL", name);
+    if (t->dtype != dtype)
+        return fail(MOE_ERR_DTYPE, "%s: dtype %s, expected %s", name, dtype_name(t->dtype), dtype_name(dtype));
+    if (t->ndim != ndim) return fail(MOE_ERR_SHAPE, "%s: %d dims, expected %d", name, t->ndim, ndim);
+    for (int i = 0; i < ndim; ++i) {
+        if (t->size[i] < 0) return fail(MOE_ERR_SHAPE, "%s: negative size in dim %d", name, i);
+        if (t->size[i] > 1 && t->stride[i] <= 0)
+            return fail(MOE_ERR_LAYOUT, "%s: stride %lld in dim %d must be positive", name,
+                        (long long)t->stride[i], i);
+    }
+    if (numel(*t) > 0 && !t->data) return fail(MOE_ERR_NULL, "%s: data is NULL", name);
+    return MOE_OK;
+}
+
+int check_shape(const moe_tensor_t& t, const char* name, std::initializer_list<int64_t> want) {
+    int i = 0;
+    for (int64_t w : want) {
+        if (t.size[i] != w) {
+            return fail(MOE_ERR_SHAPE, "%s: size[%d] = %lld, expected %lld", name, i, (long long)t.size[i],
+                        (long long)w);
+        }
+        ++i;
+    }
+    return MOE_OK;
+}
+
+// Byte range [lo, hi) a strided tensor can touch.
+void extent(const moe_tensor_t& t, uintptr_t* lo, uintptr_t* hi) {
+    int64_t span = 0;
+    for (int i = 0; i < t.ndim; ++i)
+        if (t.size[i] > 0) span += (t.size[i] - 1) * t.stride[i];
+    *lo = (uintptr_t)t.data;
+    *hi = *lo + (uintptr_t)((span + 1) * elem_bytes(t.dtype));
+}
+
+bool overlaps(const moe_tensor_t& a, const moe_tensor_t& b) {
+    if (numel(a) == 0 || numel(b) == 0 || !a.data || !b.data) return false;
+    uintptr_t al, ah, bl, bh;
+    extent(a, &al, &ah);
+    extent(b, &bl, &bh);
+    return al < bh && bl < ah;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int64_t align_capacity(int64_t A, int64_t E, int64_t bm) {
+    if (A <= 0) return 0;
+    int64_t cap = A + std::min(E, A) * (bm - 1);
+    return (cap + bm - 1) / bm * bm;
+}
+
+bool valid_bm(int bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128 || bm == 256; }
+
+// -------------------------------------------------------- configurations
+//
+// The list of tile configurations the fused forward can run. The choice
+// depends only on (mode, T, H, I, E, k), never on strides or addresses, so
+// strided and contiguous calls execute the same arithmetic.
+struct Cfg {
+    int bm, wk1, wk2;
+};
+const Cfg kConfigs[] = {
+    {16, 4, 4}, {32, 4, 4}, {64, 4, 4},
+    {16, 2, 2}, {32, 2, 2}, {64, 2, 2},
+    {16, 1, 1}, {32, 1, 1}, {64, 1, 1},
+};
+constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
+
+int bucket_of(int64_t T) {
+    int b = 1;
+    while (b < T && b < 32768) b <<= 1;
+    return b;
+}
+
+int default_config(int mode, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k) {
+    (void)mode;
+    (void)H;
+    (void)I;
+    const int64_t bucket = bucket_of(T);
+    const double rows = (double)bucket * (double)k / (double)E;   // expected rows per expert
+    if (rows <= 16.0) return 0;
+    if (rows <= 32.0) return 1;
+    return 2;
+}
+
+struct Plan {
+    int mode;
+    int64_t T, H, I, E, k, A;
+    Cfg cfg;
+    int cfg_index;
+    int64_t cap;
+    bool pack_x;
+    // workspace offsets
+    size_t off_counts, off_sorted, off_bexp, off_npad, off_x, off_xs, off_h, off_hs, off_y, total;
+};
+
+int kstep(int mode) { return mode == MOE_MODE_MXFP4 ? 128 : 32; }
+
+// Validate a fused call and build its plan. No device calls.
+int plan_fused(const moe_fused_args_t* a, Plan* pl) {
+    if (!a) return fail(MOE_ERR_NULL, "args is NULL");
+    if (a->mode != MOE_MODE_BF16 && a->mode != MOE_MODE_MXFP4)
+        return fail(MOE_ERR_ARG, "mode %d is not MOE_MODE_BF16 or MOE_MODE_MXFP4", a->mode);
+    if (a->activation != MOE_ACT_SILU) return fail(MOE_ERR_ARG, "activation %d unsupported", a->activation);
+    const bool fp4 = a->mode == MOE_MODE_MXFP4;
+    int rc;
+    if ((rc = check_desc(&a->x, "x", MOE_DT_BF16, 2))) return rc;
+    const int64_t T = a->x.size[0], H = a->x.size[1];
+    const int wdt = fp4 ? MOE_DT_FP4X2 : MOE_DT_BF16;
+    if ((rc = check_desc(&a->gate, "gate", wdt, 3))) return rc;
+    if ((rc = check_desc(&a->up, "up", wdt, 3))) return rc;
+    if ((rc = check_desc(&a->w2, "w2", wdt, 3))) return rc;
+    const int64_t E = a->gate.size[0], I = a->gate.size[1];
+    const int64_t Hw = fp4 ? H / 2 : H, Iw = fp4 ? I / 2 : I;
+    if (fp4 && (H % 2 != 0)) return fail(MOE_ERR_SHAPE, "x: H = %lld must be even in MXFP4 mode", (long long)H);
+    if (a->gate.size[2] != Hw)
+        return fail(MOE_ERR_SHAPE, "gate: hidden size %lld does not match x (H = %lld)", (long long)a->gate.size[2],
+                    (long long)H);
+    if ((rc = check_shape(a->up, "up", {E, I, Hw}))) return rc;
+    if ((rc = check_shape(a->w2, "w2", {E, H, Iw}))) return rc;
+    if (fp4) {
+        if ((rc = check_desc(&a->gate_scale, "gate_scale", MOE_DT_E8M0, 3))) return rc;
+        if ((rc = check_desc(&a->up_scale, "up_scale", MOE_DT_E8M0, 3))) return rc;
+        if ((rc = check_desc(&a->w2_scale, "w2_scale", MOE_DT_E8M0, 3))) return rc;
+        if ((rc = check_shape(a->gate_scale, "gate_scale", {E, I, H / 32}))) return rc;
+        if ((rc = check_shape(a->up_scale, "up_scale", {E, I, H / 32}))) return rc;
+        if ((rc = check_shape(a->w2_scale, "w2_scale", {E, H, I / 32}))) return rc;
+    }
+    if ((rc = check_desc(&a->topk_ids, "topk_ids", MOE_DT_I32, 2))) return rc;
+    if ((rc = check_desc(&a->topk_weights, "topk_weights", MOE_DT_F32, 2))) return rc;
+    const int64_t k = a->topk_ids.size[1];
+    if ((rc = check_shape(a->topk_ids, "topk_ids", {T, k}))) return rc;
+    if ((rc = check_shape(a->topk_weights, "topk_weights", {T, k}))) return rc;
+    if ((rc = check_desc(&a->out, "out", MOE_DT_BF16, 2))) return rc;
+    if ((rc = check_shape(a->out, "out", {T, H}))) return rc;
+
+    // sizes this build handles
+    if (E < 1 || E > 1024) return fail(MOE_ERR_UNSUPPORTED, "E = %lld outside [1, 1024]", (long long)E);
+    if (k < 1 || k > 64) return fail(MOE_ERR_UNSUPPORTED, "k = %lld outside [1, 64]", (long long)k);
+    const int ks = kstep(a->mode);
+    if (H < ks || I < ks || H % 64 != 0 || H % ks != 0 || I % ks != 0 || I % 32 != 0)
+        return fail(MOE_ERR_UNSUPPORTED, "H = %lld and I = %lld must be multiples of %d (and H of 64)",
+                    (long long)H, (long long)I, std::max(ks, 32));
+    if (T > (int64_t)1 << 24 || T * k > ((int64_t)1 << 30))
+        return fail(MOE_ERR_UNSUPPORTED, "T*k = %lld too large", (long long)(T * k));
+
+    // weight layouts: last dim contiguous, 16-byte aligned rows and experts
+    const moe_tensor_t* ws[3] = {&a->gate, &a->up, &a->w2};
+    const char* wn[3] = {"gate", "up", "w2"};
+    const int eb = elem_bytes(wdt);
+    for (int i = 0; i < 3; ++i) {
+        const moe_tensor_t& w = *ws[i];
+        if (w.stride[2] != 1) return fail(MOE_ERR_LAYOUT, "%s: last-dim stride must be 1", wn[i]);
+        if (!aligned16(w.data) || ((w.stride[1] * eb) % 16) != 0 || ((w.stride[0] * eb) % 16) != 0)
+            return fail(MOE_ERR_LAYOUT, "%s: rows and experts must start on 16-byte boundaries", wn[i]);
+    }
+    if (fp4) {
+        const moe_tensor_t* ss[3] = {&a->gate_scale, &a->up_scale, &a->w2_scale};
+        const char* sn[3] = {"gate_scale", "up_scale", "w2_scale"};
+        for (int i = 0; i < 3; ++i)
+            if (ss[i]->stride[2] != 1) return fail(MOE_ERR_LAYOUT, "%s: last-dim stride must be 1", sn[i]);
+    }
+    // outputs must not alias inputs
+    const moe_tensor_t* ins[6] = {&a->x, &a->gate, &a->up, &a->w2, &a->topk_ids, &a->topk_weights};
+    for (auto* t : ins)
+        if (overlaps(a->out, *t)) return fail(MOE_ERR_LAYOUT, "out overlaps an input");
+
+    // configuration
+    int ci = a->force_config;
+    if (ci < 0) ci = default_config(a->mode, T, H, I, E, k);
+    if (ci >= kNumConfigs) return fail(MOE_ERR_ARG, "force_config %d out of range", ci);
+    Cfg c = kConfigs[ci];
+    // the split of K is a preference: halve it until it divides K into whole steps
+    auto fit = [&](int pref, int64_t K) {
+        int w = pref;
+        while (w > 1 && K % (ks * w) != 0) w >>= 1;
+        return w;
+    };
+    c.wk1 = fit(c.wk1, H);
+    c.wk2 = fit(c.wk2, I);
+    GemmKernelId g1{fp4 ? 1 : 0, 1, c.bm, c.wk1}, g2{fp4 ? 1 : 0, 2, c.bm, c.wk2};
+    if (!gemm_supported(g1) || !gemm_supported(g2)) return fail(MOE_ERR_UNSUPPORTED, "config %d not built", ci);
+    if (I % gemm_tile_n(g1) != 0 || H % gemm_tile_n(g2) != 0)
+        return fail(MOE_ERR_UNSUPPORTED, "config %d: I or H not a multiple of the tile width", ci);
+
+    pl->mode = a->mode;
+    pl->T = T;
+    pl->H = H;
+    pl->I = I;
+    pl->E = E;
+    pl->k = k;
+    pl->A = T * k;
+    pl->cfg = c;
+    pl->cfg_index = ci;
+    pl->cap = align_capacity(pl->A, E, c.bm);
+    const bool x_direct = a->x.stride[1] == 1 && aligned16(a->x.data) &&
+                          (T <= 1 || (a->x.stride[0] * 2) % 16 == 0);
+    pl->pack_x = !fp4 && !x_direct;
+
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t o = off;
+        off = round_up(off + bytes, 256);
+        return o;
+    };
+    pl->off_counts = take(align_scratch_bytes(pl->A, (int32_t)E));
+    pl->off_sorted = take((size_t)pl->cap * 4);
+    pl->off_bexp = take((size_t)(pl->cap / c.bm) * 4);
+    pl->off_npad = take(4);
+    pl->off_x = pl->off_xs = 0;
+    if (fp4) {
+        pl->off_x = take((size_t)T * (size_t)(H / 2));
+        pl->off_xs = take((size_t)T * (size_t)(H / 32));
+    } else if (pl->pack_x) {
+        pl->off_x = take((size_t)T * (size_t)H * 2);
+    }
+    if (fp4) {
+        pl->off_h = take((size_t)pl->cap * (size_t)(I / 2));
+        pl->off_hs = take((size_t)pl->cap * (size_t)(I / 32));
+    } else {
+        pl->off_h = take((size_t)pl->cap * (size_t)I * 2);
+        pl->off_hs = 0;
+    }
+    pl->off_y = take((size_t)pl->A * (size_t)H * 4);
+    pl->total = off;
+    return MOE_OK;
+}
+
+struct StageTimer {
+    void* const* ev;
+    hipStream_t s;
+    void begin(int st) const {
+        if (ev) (void)hipEventRecord((hipEvent_t)ev[2 * st], s);
+    }
+    void end(int st) const {
+        if (ev) (void)hipEventRecord((hipEvent_t)ev[2 * st + 1], s);
+    }
+};
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_strerror(int status) {
+    switch (status) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_NULL: return "a required pointer is NULL";
+        case MOE_ERR_SHAPE: return "tensor sizes do not match";
+        case MOE_ERR_DTYPE: return "wrong element type";
+        case MOE_ERR_LAYOUT: return "unsupported strides or alignment";
+        case MOE_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+        case MOE_ERR_UNSUPPORTED: return "sizes outside what this build supports";
+        case MOE_ERR_HIP: return "HIP launch failed";
+        case MOE_ERR_ARG: return "invalid argument";
+        default: return "unknown status";
+    }
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+int moe_topk_softmax(const moe_tensor_t* logits, int32_t k, int32_t renorm, int32_t shared_id, float shared_w,
+                     const moe_tensor_t* ids, const moe_tensor_t* weights, moe_stream_t stream) {
+    int rc;
+    if ((rc = check_desc(logits, "logits", MOE_DT_F32, 2))) return rc;
+    const int64_t T = logits->size[0], E = logits->size[1];
+    if (E < 1 || E > 1024) return fail(MOE_ERR_UNSUPPORTED, "logits: %lld experts outside [1, 1024]", (long long)E);
+    if (k < 1 || k > 32 || k > E) return fail(MOE_ERR_ARG, "k = %d outside [1, min(E, 32)]", k);
+    if (renorm != 0 && renorm != 1) return fail(MOE_ERR_ARG, "renorm must be 0 or 1");
+    const int64_t kt = k + (shared_id >= 0 ? 1 : 0);
+    if ((rc = check_desc(ids, "ids", MOE_DT_I32, 2))) return rc;
+    if ((rc = check_desc(weights, "weights", MOE_DT_F32, 2))) return rc;
+    if ((rc = check_shape(*ids, "ids", {T, kt}))) return rc;
+    if ((rc = check_shape(*weights, "weights", {T, kt}))) return rc;
+    if (T > ((int64_t)1 << 31) - 4) return fail(MOE_ERR_UNSUPPORTED, "T too large");
+    if (overlaps(*ids, *logits) || overlaps(*weights, *logits) || overlaps(*ids, *weights))
+        return fail(MOE_ERR_LAYOUT, "outputs overlap inputs or each other");
+    if (T == 0) return ok();
+    RouteParams p{};
+    p.logits = (const float*)logits->data;
+    p.T = T;
+    p.ls_t = logits->stride[0];
+    p.ls_e = logits->stride[1];
+    p.E = (int32_t)E;
+    p.k = k;
+    p.renorm = renorm;
+    p.shared_id = shared_id;
+    p.shared_w = shared_w;
+    p.ids = (int32_t*)ids->data;
+    p.is_t = ids->stride[0];
+    p.is_j = ids->stride[1];
+    p.w = (float*)weights->data;
+    p.ws_t = weights->stride[0];
+    p.ws_j = weights->stride[1];
+    hipError_t e = launch_route(p, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "route");
+    return ok();
+}
+
+int64_t moe_align_capacity(int64_t assignments, int32_t num_experts, int32_t block_m) {
+    if (assignments < 0 || num_experts < 1 || !valid_bm(block_m)) return -1;
+    return align_capacity(assignments, num_experts, block_m);
+}
+
+int moe_align_workspace_size(int64_t tokens, int32_t k, int32_t num_experts, int32_t block_m, size_t* bytes) {
+    if (!bytes) return fail(MOE_ERR_NULL, "bytes is NULL");
+    if (tokens < 0 || k < 1 || num_experts < 1 || num_experts > 1024 || !valid_bm(block_m))
+        return fail(MOE_ERR_ARG, "invalid sizes");
+    *bytes = round_up(align_scratch_bytes(tokens * k, num_experts), 256);
+    return ok();
+}
+
+int moe_align(const moe_tensor_t* ids, int32_t num_experts, int32_t block_m, const moe_tensor_t* sorted_ids,
+              const moe_tensor_t* block_expert, const moe_tensor_t* n_padded, void* ws, size_t ws_bytes,
+              moe_stream_t stream) {
+    int rc;
+    if ((rc = check_desc(ids, "ids", MOE_DT_I32, 2))) return rc;
+    if (num_experts < 1 || num_experts > 1024)
+        return fail(MOE_ERR_UNSUPPORTED, "num_experts = %d outside [1, 1024]", num_experts);
+    if (!valid_bm(block_m)) return fail(MOE_ERR_ARG, "block_m = %d not in {16, 32, 64, 128, 256}", block_m);
+    const int64_t T = ids->size[0], k = ids->size[1];
+    if (k < 1) return fail(MOE_ERR_SHAPE, "ids: k must be >= 1");
+    const int64_t A = T * k;
+    if (A > ((int64_t)1 << 30)) return fail(MOE_ERR_UNSUPPORTED, "T*k too large");
+    const int64_t cap = align_capacity(A, num_experts, block_m);
+    if ((rc = check_desc(sorted_ids, "sorted_ids", MOE_DT_I32, 1))) return rc;
+    if ((rc = check_desc(block_expert, "block_expert", MOE_DT_I32, 1))) return rc;
+    if ((rc = check_desc(n_padded, "n_padded", MOE_DT_I32, 1))) return rc;
+    if (sorted_ids->size[0] < cap || (sorted_ids->size[0] > 1 && sorted_ids->stride[0] != 1))
+        return fail(MOE_ERR_SHAPE, "sorted_ids needs %lld contiguous entries", (long long)cap);
+    if (block_expert->size[0] < cap / block_m || (block_expert->size[0] > 1 && block_expert->stride[0] != 1))
+        return fail(MOE_ERR_SHAPE, "block_expert needs %lld contiguous entries", (long long)(cap / block_m));
+    if (n_padded->size[0] < 1) return fail(MOE_ERR_SHAPE, "n_padded needs one entry");
+    if (!n_padded->data) return fail(MOE_ERR_NULL, "n_padded: data is NULL");
+    const size_t need = align_scratch_bytes(A, num_experts);
+    if (need > 0 && (!ws || ((uintptr_t)ws & 255u) || ws_bytes < need))
+        return fail(MOE_ERR_WORKSPACE, "align needs %zu bytes of 256-byte aligned scratch", need);
+    if (overlaps(*sorted_ids, *ids) || overlaps(*block_expert, *ids) || overlaps(*n_padded, *ids))
+        return fail(MOE_ERR_LAYOUT, "outputs overlap ids");
+    AlignParams p{};
+    p.ids = (const int32_t*)ids->data;
+    p.is_t = ids->stride[0];
+    p.is_j = ids->stride[1];
+    p.T = (int32_t)T;
+    p.k = (int32_t)k;
+    p.A = (int32_t)A;
+    p.E = num_experts;
+    p.bm = block_m;
+    p.sorted = (int32_t*)sorted_ids->data;
+    p.block_expert = (int32_t*)block_expert->data;
+    p.n_padded = (int32_t*)n_padded->data;
+    p.counts = (int32_t*)ws;
+    hipError_t e = launch_align(p, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "align");
+    return ok();
+}
+
+int moe_quant_mxfp4(const moe_tensor_t* src, const moe_tensor_t* codes, const moe_tensor_t* scales,
+                    moe_stream_t stream) {
+    if (!src || !codes || !scales) return fail(MOE_ERR_NULL, "NULL descriptor");
+    const int nd = src->ndim;
+    if (nd != 2 && nd != 3) return fail(MOE_ERR_SHAPE, "src must have 2 or 3 dims");
+    int rc;
+    if ((rc = check_desc(src, "src", MOE_DT_BF16, nd))) return rc;
+    if ((rc = check_desc(codes, "codes", MOE_DT_FP4X2, nd))) return rc;
+    if ((rc = check_desc(scales, "scales", MOE_DT_E8M0, nd))) return rc;
+    const int64_t K = src->size[nd - 1];
+    if (K % 32 != 0) return fail(MOE_ERR_UNSUPPORTED, "K = %lld must be a multiple of 32", (long long)K);
+    for (int i = 0; i < nd - 1; ++i)
+        if (codes->size[i] != src->size[i] || scales->size[i] != src->size[i])
+            return fail(MOE_ERR_SHAPE, "codes/scales leading dims must match src");
+    if (codes->size[nd - 1] != K / 2 || scales->size[nd - 1] != K / 32)
+        return fail(MOE_ERR_SHAPE, "codes must be [.., K/2] and scales [.., K/32]");
+    if (codes->stride[nd - 1] != 1 || scales->stride[nd - 1] != 1)
+        return fail(MOE_ERR_LAYOUT, "codes and scales need last-dim stride 1");
+    if (overlaps(*codes, *src) || overlaps(*scales, *src) || overlaps(*codes, *scales))
+        return fail(MOE_ERR_LAYOUT, "outputs overlap");
+    QuantParams p{};
+    p.src = (const uint16_t*)src->data;
+    p.codes = (uint8_t*)codes->data;
+    p.scales = (uint8_t*)scales->data;
+    p.K = K;
+    if (nd == 3) {
+        p.E = src->size[0];
+        p.R = src->size[1];
+        p.ss_e = src->stride[0];
+        p.ss_r = src->stride[1];
+        p.ss_k = src->stride[2];
+        p.cs_e = codes->stride[0];
+        p.cs_r = codes->stride[1];
+        p.xs_e = scales->stride[0];
+        p.xs_r = scales->stride[1];
+    } else {
+        p.E = 1;
+        p.R = src->size[0];
+        p.ss_e = 0;
+        p.ss_r = src->stride[0];
+        p.ss_k = src->stride[1];
+        p.cs_e = 0;
+        p.cs_r = codes->stride[0];
+        p.xs_e = 0;
+        p.xs_r = scales->stride[0];
+    }
+    hipError_t e = launch_quant_mxfp4(p, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "quant_mxfp4");
+    return ok();
+}
+
+int moe_query_config(const moe_fused_args_t* args, moe_config_t* cfg) {
+    if (!cfg) return fail(MOE_ERR_NULL, "cfg is NULL");
+    Plan pl;
+    int rc = plan_fused(args, &pl);
+    if (rc) return rc;
+    cfg->bucket = bucket_of(pl.T);
+    cfg->block_m = pl.cfg.bm;
+    cfg->gemm1_kernel = args->mode == MOE_MODE_MXFP4 ? 11 : 1;
+    cfg->gemm2_kernel = args->mode == MOE_MODE_MXFP4 ? 12 : 2;
+    cfg->gemm1_split_k = pl.cfg.wk1;
+    cfg->gemm2_split_k = pl.cfg.wk2;
+    cfg->config_index = pl.cfg_index;
+    cfg->num_configs = kNumConfigs;
+    return ok();
+}
+
+int moe_fused_workspace_size(const moe_fused_args_t* args, size_t* bytes) {
+    if (!bytes) return fail(MOE_ERR_NULL, "bytes is NULL");
+    Plan pl;
+    int rc = plan_fused(args, &pl);
+    if (rc) return rc;
+    *bytes = pl.total;
+    return ok();
+}
+
+int moe_fused_fwd(const moe_fused_args_t* args, void* ws, size_t ws_bytes, moe_stream_t stream) {
+    Plan pl;
+    int rc = plan_fused(args, &pl);
+    if (rc) return rc;
+    if (pl.T == 0) return ok();
+    if (!ws || ((uintptr_t)ws & 255u) || ws_bytes < pl.total)
+        return fail(MOE_ERR_WORKSPACE, "fused forward needs %zu bytes of 256-byte aligned workspace", pl.total);
+    const moe_fused_args_t& a = *args;
+    hipStream_t s = (hipStream_t)stream;
+    char* base = (char*)ws;
+    const StageTimer tm{a.stage_events, s};
+    const bool fp4 = pl.mode == MOE_MODE_MXFP4;
+    int32_t* sorted = (int32_t*)(base + pl.off_sorted);
+    int32_t* bexp = (int32_t*)(base + pl.off_bexp);
+    int32_t* npad = (int32_t*)(base + pl.off_npad);
+    hipError_t e;
+
+    // stage 0: align
+    tm.begin(0);
+    AlignParams ap{};
+    ap.ids = (const int32_t*)a.topk_ids.data;
+    ap.is_t = a.topk_ids.stride[0];
+    ap.is_j = a.topk_ids.stride[1];
+    ap.T = (int32_t)pl.T;
+    ap.k = (int32_t)pl.k;
+    ap.A = (int32_t)pl.A;
+    ap.E = (int32_t)pl.E;
+    ap.bm = pl.cfg.bm;
+    ap.sorted = sorted;
+    ap.block_expert = bexp;
+    ap.n_padded = npad;
+    ap.counts = (int32_t*)(base + pl.off_counts);
+    if ((e = launch_align(ap, s)) != hipSuccess) return hip_fail(e, "align");
+    tm.end(0);
+
+    // stage 1: prepare the activation operand
+    tm.begin(1);
+    const void* a_op = a.x.data;
+    int64_t a_row = a.x.stride[0];
+    if (fp4) {
+        QuantParams qp{};
+        qp.src = (const uint16_t*)a.x.data;
+        qp.E = 1;
+        qp.R = pl.T;
+        qp.K = pl.H;
+        qp.ss_r = a.x.stride[0];
+        qp.ss_k = a.x.stride[1];
+        qp.codes = (uint8_t*)(base + pl.off_x);
+        qp.cs_r = pl.H / 2;
+        qp.scales = (uint8_t*)(base + pl.off_xs);
+        qp.xs_r = pl.H / 32;
+        if ((e = launch_quant_mxfp4(qp, s)) != hipSuccess) return hip_fail(e, "quant x");
+        a_op = base + pl.off_x;
+        a_row = pl.H / 2;
+    } else if (pl.pack_x) {
+        PackParams pp{};
+        pp.src = (const uint16_t*)a.x.data;
+        pp.s_t = a.x.stride[0];
+        pp.s_h = a.x.stride[1];
+        pp.dst = (uint16_t*)(base + pl.off_x);
+        pp.T = pl.T;
+        pp.H = pl.H;
+        if ((e = launch_pack_bf16(pp, s)) != hipSuccess) return hip_fail(e, "pack x");
+        a_op = base + pl.off_x;
+        a_row = pl.H;
+    }
+    tm.end(1);
+
+    const int32_t max_mblocks = (int32_t)(pl.cap / pl.cfg.bm);
+    // stage 2: gemm1 + SiLU(gate) * up
+    tm.begin(2);
+    GemmParams g1{};
+    g1.sorted = sorted;
+    g1.block_expert = bexp;
+    g1.n_padded = npad;
+    g1.A = (int32_t)pl.A;
+    g1.k = (int32_t)pl.k;
+    g1.E = (int32_t)pl.E;
+    g1.a = a_op;
+    g1.a_row = a_row;
+    g1.a_sc = fp4 ? (const uint8_t*)(base + pl.off_xs) : nullptr;
+    g1.a_sc_row = pl.H / 32;
+    g1.b0 = a.gate.data;
+    g1.b1 = a.up.data;
+    g1.b0_e = a.gate.stride[0];
+    g1.b0_r = a.gate.stride[1];
+    g1.b1_e = a.up.stride[0];
+    g1.b1_r = a.up.stride[1];
+    if (fp4) {
+        g1.b0_sc = (const uint8_t*)a.gate_scale.data;
+        g1.b1_sc = (const uint8_t*)a.up_scale.data;
+        g1.b0sc_e = a.gate_scale.stride[0];
+        g1.b0sc_r = a.gate_scale.stride[1];
+        g1.b1sc_e = a.up_scale.stride[0];
+        g1.b1sc_r = a.up_scale.stride[1];
+    }
+    g1.K = (int32_t)pl.H;
+    g1.N = (int32_t)pl.I;
+    g1.out = base + pl.off_h;
+    g1.out_sc = fp4 ? (uint8_t*)(base + pl.off_hs) : nullptr;
+    g1.n_tile_groups = 8;
+    g1.max_mblocks = max_mblocks;
+    GemmKernelId k1{fp4 ? 1 : 0, 1, pl.cfg.bm, pl.cfg.wk1};
+    if ((e = launch_gemm(k1, g1, s)) != hipSuccess) return hip_fail(e, "gemm1");
+    tm.end(2);
+
+    // stage 3: gemm2
+    tm.begin(3);
+    GemmParams g2{};
+    g2.sorted = sorted;
+    g2.block_expert = bexp;
+    g2.n_padded = npad;
+    g2.A = (int32_t)pl.A;
+    g2.k = (int32_t)pl.k;
+    g2.E = (int32_t)pl.E;
+    g2.a = base + pl.off_h;
+    g2.a_row = fp4 ? pl.I / 2 : pl.I;
+    g2.a_sc = fp4 ? (const uint8_t*)(base + pl.off_hs) : nullptr;
+    g2.a_sc_row = pl.I / 32;
+    g2.b0 = a.w2.data;
+    g2.b0_e = a.w2.stride[0];
+    g2.b0_r = a.w2.stride[1];
+    if (fp4) {
+        g2.b0_sc = (const uint8_t*)a.w2_scale.data;
+        g2.b0sc_e = a.w2_scale.stride[0];
+        g2.b0sc_r = a.w2_scale.stride[1];
+    }
+    g2.K = (int32_t)pl.I;
+    g2.N = (int32_t)pl.H;
+    g2.out = base + pl.off_y;
+    g2.n_tile_groups = 8;
+    g2.max_mblocks = max_mblocks;
+    GemmKernelId k2{fp4 ? 1 : 0, 2, pl.cfg.bm, pl.cfg.wk2};
+    if ((e = launch_gemm(k2, g2, s)) != hipSuccess) return hip_fail(e, "gemm2");
+    tm.end(3);
+
+    // stage 4: combine
+    tm.begin(4);
+    CombineParams cp{};
+    cp.y = (const float*)(base + pl.off_y);
+    cp.ids = (const int32_t*)a.topk_ids.data;
+    cp.is_t = a.topk_ids.stride[0];
+    cp.is_j = a.topk_ids.stride[1];
+    cp.w = (const float*)a.topk_weights.data;
+    cp.ws_t = a.topk_weights.stride[0];
+    cp.ws_j = a.topk_weights.stride[1];
+    cp.out = (uint16_t*)a.out.data;
+    cp.os_t = a.out.stride[0];
+    cp.os_h = a.out.stride[1];
+    cp.T = (int32_t)pl.T;
+    cp.k = (int32_t)pl.k;
+    cp.E = (int32_t)pl.E;
+    cp.H = (int32_t)pl.H;
+    if ((e = launch_combine(cp, s)) != hipSuccess) return hip_fail(e, "combine");
+    tm.end(4);
+    return ok();
+}
+
+}  // extern "C"

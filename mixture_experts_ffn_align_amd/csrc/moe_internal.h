@@ -1,0 +1,204 @@
+// Internal declarations shared by the HIP translation units of libmoeffn:
+// device helpers (bf16 rounding, e2m1 coding, wave primitives) and the
+// parameter blocks / launchers each kernel file exports to the host planner.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---------------------------------------------------------------- types
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------- bf16 helpers
+
+// fp32 -> bf16 bits, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return (uint16_t)((u >> 16) | 0x40u);
+    uint32_t r = u + 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(r >> 16);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+    return __uint_as_float((uint32_t)b << 16);
+}
+
+// ---------------------------------------------------------- e2m1 coding
+//
+// One group of 32 values shares the exponent s = floor(log2(amax)) - 2,
+// clamped to [-127, 127] (s = -127 when amax is zero or subnormal). An
+// element's code is the e2m1 magnitude nearest to |v| / 2^s, ties to the even
+// code, saturating at 6. The decision is taken on the fp32 bit pattern of
+// |v| against the seven midpoints scaled by 2^s, all integers, so it is exact
+// whatever the denormal mode of the ALU.
+
+// Shared exponent from the fp32 bits of amax (sign already cleared).
+__device__ __forceinline__ int group_exponent(uint32_t amax_bits) {
+    int ef = (int)(amax_bits >> 23);
+    if (ef == 0) return -127;            // zero or subnormal: floor(log2) - 2 < -127
+    int s = ef - 127 - 2;
+    return s < -127 ? -127 : (s > 127 ? 127 : s);
+}
+
+// fp32 bit pattern of mant * 2^e for mant in {1, 1.25, 1.5, 1.75} given as the
+// 23-bit fraction; exact for every e >= -129 used here.
+__device__ __forceinline__ uint32_t scaled_bits(uint32_t frac, int e) {
+    if (e >= -126) return ((uint32_t)(e + 127) << 23) | frac;
+    uint32_t full = (1u << 23) | frac;   // subnormal: value = full * 2^(e - 23)
+    return full >> (-126 - e);
+}
+
+struct E2m1Thresholds {
+    uint32_t t[7];
+};
+
+// Midpoints between neighbouring e2m1 magnitudes, scaled by 2^s:
+// 0.25 0.75 1.25 1.75 2.5 3.5 5.
+__device__ __forceinline__ E2m1Thresholds e2m1_thresholds(int s) {
+    E2m1Thresholds th;
+    th.t[0] = scaled_bits(0x000000u, s - 2);   // 1.0  * 2^-2
+    th.t[1] = scaled_bits(0x400000u, s - 1);   // 1.5  * 2^-1
+    th.t[2] = scaled_bits(0x200000u, s);       // 1.25 * 2^0
+    th.t[3] = scaled_bits(0x600000u, s);       // 1.75 * 2^0
+    th.t[4] = scaled_bits(0x200000u, s + 1);   // 1.25 * 2^1
+    th.t[5] = scaled_bits(0x600000u, s + 1);   // 1.75 * 2^1
+    th.t[6] = scaled_bits(0x200000u, s + 2);   // 1.25 * 2^2
+    return th;
+}
+
+// Code of one value from its fp32 bits. At a midpoint whose lower neighbour
+// has an odd code (0.75, 1.75, 3.5) the tie goes up to the even code.
+__device__ __forceinline__ uint32_t e2m1_code(uint32_t vbits, const E2m1Thresholds& th) {
+    uint32_t a = vbits & 0x7fffffffu;
+    uint32_t c = (a > th.t[0]) + (a >= th.t[1]) + (a > th.t[2]) + (a >= th.t[3]) +
+                 (a > th.t[4]) + (a >= th.t[5]) + (a > th.t[6]);
+    return c | ((vbits >> 28) & 8u);
+}
+
+// ------------------------------------------------------- wave primitives
+
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+    int l = lane_id();
+    return l == 0 ? 0ull : (~0ull >> (64 - l));
+}
+
+// Workgroup index remapped so that consecutive logical tiles land on the same
+// XCD: the hardware deals workgroups round-robin over the 8 XCDs, so block b
+// runs on XCD b % 8. Logical index = (b % 8) * (G / 8) + b / 8 for the part of
+// the grid that fills whole rounds; the tail keeps its index.
+__device__ __forceinline__ uint32_t xcd_remap(uint32_t b, uint32_t G) {
+    uint32_t full = G & ~7u;
+    if (b >= full) return b;
+    return (b & 7u) * (full >> 3) + (b >> 3);
+}
+
+// ------------------------------------------------------------ launchers
+
+struct RouteParams {
+    const float* logits;
+    int64_t T, ls_t, ls_e;
+    int32_t E, k, renorm, shared_id;
+    float shared_w;
+    int32_t* ids;
+    int64_t is_t, is_j;
+    float* w;
+    int64_t ws_t, ws_j;
+};
+hipError_t launch_route(const RouteParams& p, hipStream_t s);
+
+struct AlignParams {
+    const int32_t* ids;
+    int64_t is_t, is_j;
+    int32_t T, k, A, E, bm;
+    int32_t* sorted;        // [cap]
+    int32_t* block_expert;  // [cap / bm]
+    int32_t* n_padded;      // [1]
+    int32_t* counts;        // [nchunks * E] scratch (multi-block path)
+};
+// Scratch bytes the multi-block path needs for A assignments over E experts.
+size_t align_scratch_bytes(int64_t A, int32_t E);
+hipError_t launch_align(const AlignParams& p, hipStream_t s);
+
+struct QuantParams {
+    const uint16_t* src;
+    int64_t ss_e, ss_r, ss_k;   // element strides
+    uint8_t* codes;
+    int64_t cs_e, cs_r;         // byte strides (last = 1)
+    uint8_t* scales;
+    int64_t xs_e, xs_r;
+    int64_t E, R, K;            // leading count (1 for 2-D), rows, K
+};
+hipError_t launch_quant_mxfp4(const QuantParams& p, hipStream_t s);
+
+struct PackParams {
+    const uint16_t* src;
+    int64_t s_t, s_h;
+    uint16_t* dst;   // [T, H] contiguous
+    int64_t T, H;
+};
+hipError_t launch_pack_bf16(const PackParams& p, hipStream_t s);
+
+// One grouped GEMM launch. Stage 1: A = gathered x rows, B = gate/up rows,
+// epilogue SiLU(g)*u -> h. Stage 2: A = h rows, B = w2 rows, epilogue scatter
+// of fp32 y rows to their flat assignment index.
+struct GemmParams {
+    // routing / align
+    const int32_t* sorted;
+    const int32_t* block_expert;
+    const int32_t* n_padded;
+    int32_t A, k, E;
+    // A operand
+    const void* a;          // bf16 [rows, K] or fp4x2 [rows, K/2]
+    int64_t a_row;          // row stride in elements (bf16) or bytes (fp4)
+    const uint8_t* a_sc;    // fp4 scales [rows, K/32]
+    int64_t a_sc_row;
+    // B operands (weights); for stage 1 b0 = gate, b1 = up, for stage 2 b0 = w2
+    const void* b0;
+    const void* b1;
+    int64_t b0_e, b0_r, b1_e, b1_r;          // strides: elements (bf16) / bytes (fp4)
+    const uint8_t* b0_sc;
+    const uint8_t* b1_sc;
+    int64_t b0sc_e, b0sc_r, b1sc_e, b1sc_r;  // scale strides in bytes
+    int32_t K;              // contraction length
+    int32_t N;              // output columns (stage 1: I, stage 2: H)
+    // outputs
+    void* out;              // stage 1: h (bf16 [P, I] or fp4 [P, I/2]); stage 2: y fp32 [A, H]
+    uint8_t* out_sc;        // stage 1 MXFP4: h scales [P, I/32]
+    int32_t n_tile_groups;  // tiles along N are walked in groups of this size
+    int32_t max_mblocks;
+};
+
+struct GemmKernelId {
+    int mode;    // 0 bf16, 1 mxfp4
+    int stage;   // 1 or 2
+    int bm;      // 16, 32, 64
+    int wk;      // waves splitting K: 1, 2 or 4
+};
+// Output columns one workgroup covers.
+int gemm_tile_n(const GemmKernelId& id);
+bool gemm_supported(const GemmKernelId& id);
+hipError_t launch_gemm(const GemmKernelId& id, const GemmParams& p, hipStream_t s);
+
+struct CombineParams {
+    const float* y;         // [A, H]
+    const int32_t* ids;
+    int64_t is_t, is_j;
+    const float* w;
+    int64_t ws_t, ws_j;
+    uint16_t* out;
+    int64_t os_t, os_h;
+    int32_t T, k, E, H;
+};
+hipError_t launch_combine(const CombineParams& p, hipStream_t s);
+
+}  // namespace moe

@@ -154,16 +154,25 @@ int orc_mxfp4_quant_bf16(const uint16_t *src, int64_t rows, int64_t K, int64_t r
 {
     if (K % 32 != 0)
         return ORC_EARG;
-    float *buf = (float *)malloc(sizeof(float) * (size_t)K);
-    if (!buf)
-        return ORC_EARG;
-    for (int64_t r = 0; r < rows; ++r) {
-        for (int64_t c = 0; c < K; ++c)
-            buf[c] = (float)orc_bf16_to_double(src[r * rs + c * cs]);
-        orc_mxfp4_quant(buf, K, codes + r * (K / 2), scales + r * (K / 32));
+    int err = 0;
+    /* rows are independent; threads only split the row loop */
+#pragma omp parallel
+    {
+        float *buf = (float *)malloc(sizeof(float) * (size_t)K);
+        if (!buf) {
+#pragma omp atomic write
+            err = 1;
+        } else {
+#pragma omp for schedule(static)
+            for (int64_t r = 0; r < rows; ++r) {
+                for (int64_t c = 0; c < K; ++c)
+                    buf[c] = (float)orc_bf16_to_double(src[r * rs + c * cs]);
+                orc_mxfp4_quant(buf, K, codes + r * (K / 2), scales + r * (K / 32));
+            }
+        }
+        free(buf);
     }
-    free(buf);
-    return ORC_OK;
+    return err ? ORC_EARG : ORC_OK;
 }
 
 /* Dequantise one packed row of K elements. */

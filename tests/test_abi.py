@@ -1,0 +1,168 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol the header
+declares, and its host-side checks reject bad arguments before any launch
+(no call here reaches a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import mixture_experts_ffn_align_amd as moe
+from mixture_experts_ffn_align_amd import _abi
+from mixture_experts_ffn_align_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moeffn.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    L = _abi.load()
+    names = _declared()
+    assert set(names) == set(_abi.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_strerror_covers_all_codes():
+    L = _abi.load()
+    for code in _abi.STATUS:
+        assert L.moe_strerror(code)
+    assert L.moe_strerror(12345) == b"unknown status"
+
+
+def _bf16_case(T=8, H=256, I=128, E=8, k=2):
+    x = torch.zeros(T, H, dtype=torch.bfloat16)
+    w13 = torch.zeros(E, 2 * I, H, dtype=torch.bfloat16)
+    w2 = torch.zeros(E, H, I, dtype=torch.bfloat16)
+    ids = torch.zeros(T, k, dtype=torch.int32)
+    w = torch.zeros(T, k, dtype=torch.float32)
+    gate, up = W.packed_views(w13, I)
+    return x, gate, up, w2, ids, w
+
+
+def _status(fn):
+    with pytest.raises(moe.MoEError) as ei:
+        fn()
+    return _abi.STATUS[ei.value.status]
+
+
+def test_shape_errors_name_the_argument():
+    x, gate, up, w2, ids, w = _bf16_case()
+    bad_gate = torch.zeros(8, 128, 128, dtype=torch.bfloat16)          # hidden 128 != 256
+    st = _status(lambda: moe.moe_fused_workspace_size(x, bad_gate, up, w2, ids, w))
+    assert st == "MOE_ERR_SHAPE"
+    assert "gate" in _abi.load().moe_last_error().decode()
+    assert _status(lambda: moe.moe_fused_workspace_size(x, gate, up[:4], w2, ids, w)) == "MOE_ERR_SHAPE"
+    assert _status(lambda: moe.moe_fused_workspace_size(x, gate, up, w2, ids[:, :1], w)) == "MOE_ERR_SHAPE"
+
+
+def test_dtype_and_layout_errors():
+    x, gate, up, w2, ids, w = _bf16_case()
+    assert _status(lambda: moe.moe_fused_workspace_size(x.float(), gate, up, w2, ids, w)) == "MOE_ERR_DTYPE"
+    assert _status(lambda: moe.moe_fused_workspace_size(x, gate, up, w2, ids.float(), w)) == "MOE_ERR_DTYPE"
+    # weight last-dim stride must be 1
+    gt = torch.zeros(8, 256, 128, dtype=torch.bfloat16).transpose(1, 2)   # [8, 128, 256], stride (.., 1, 128)
+    assert _status(lambda: moe.moe_fused_workspace_size(x, gt, up, w2, ids, w)) == "MOE_ERR_LAYOUT"
+    # rows not on 16-byte boundaries
+    buf = torch.zeros(8, 128, 260, dtype=torch.bfloat16)
+    assert _status(lambda: moe.moe_fused_workspace_size(x, buf[:, :, :256], up, w2, ids, w)) == "MOE_ERR_LAYOUT"
+    # output overlapping an input
+    st = _status(lambda: moe.moe_query_config(x, gate, up, w2, ids, w, out=x))
+    assert st == "MOE_ERR_LAYOUT"
+
+
+def test_unsupported_sizes():
+    x, gate, up, w2, ids, w = _bf16_case(E=2000)
+    assert _status(lambda: moe.moe_fused_workspace_size(x, gate, up, w2, ids, w)) == "MOE_ERR_UNSUPPORTED"
+    x, gate, up, w2, ids, w = _bf16_case(I=48)
+    assert _status(lambda: moe.moe_fused_workspace_size(x, gate, up, w2, ids, w)) == "MOE_ERR_UNSUPPORTED"
+
+
+def test_workspace_too_small_is_rejected_before_launch():
+    x, gate, up, w2, ids, w = _bf16_case()
+    ws = torch.zeros(256, dtype=torch.uint8)
+    st = _status(lambda: moe.moe_fused_fwd(x, gate, up, w2, ids, w, workspace=ws, stream=0))
+    assert st == "MOE_ERR_WORKSPACE"
+
+
+def test_empty_batch_returns_ok_without_launch():
+    x, gate, up, w2, ids, w = _bf16_case(T=0)
+    out = moe.moe_fused_fwd(x, gate, up, w2, ids, w, workspace=torch.zeros(256, dtype=torch.uint8),
+                            stream=0)
+    assert out.shape == (0, 256)
+
+
+def test_mxfp4_shapes_and_k_multiple():
+    T, H, I, E = 4, 256, 128, 4
+    x = torch.zeros(T, H, dtype=torch.bfloat16)
+    gq = torch.zeros(E, I, H // 2, dtype=torch.uint8)
+    gs = torch.zeros(E, I, H // 32, dtype=torch.uint8)
+    wq = torch.zeros(E, H, I // 2, dtype=torch.uint8)
+    ws_ = torch.zeros(E, H, I // 32, dtype=torch.uint8)
+    ids = torch.zeros(T, 2, dtype=torch.int32)
+    w = torch.zeros(T, 2, dtype=torch.float32)
+    n = moe.moe_fused_workspace_size(x, gq, gq.clone(), wq, ids, w, gate_scale=gs, up_scale=gs.clone(),
+                                     w2_scale=ws_, mode=moe.MODE_MXFP4)
+    assert n > 0
+    st = _status(lambda: moe.moe_fused_workspace_size(x, gq, gq.clone(), wq, ids, w, gate_scale=gs[:, :, :4],
+                                                      up_scale=gs.clone(), w2_scale=ws_, mode=moe.MODE_MXFP4))
+    assert st == "MOE_ERR_SHAPE"
+    x2 = torch.zeros(T, 192, dtype=torch.bfloat16)                 # 192 is not a multiple of 128
+    g2 = torch.zeros(E, I, 96, dtype=torch.uint8)
+    s2 = torch.zeros(E, I, 6, dtype=torch.uint8)
+    w22 = torch.zeros(E, 192, I // 2, dtype=torch.uint8)
+    s22 = torch.zeros(E, 192, I // 32, dtype=torch.uint8)
+    st = _status(lambda: moe.moe_fused_workspace_size(x2, g2, g2.clone(), w22, ids, w, gate_scale=s2,
+                                                      up_scale=s2.clone(), w2_scale=s22, mode=moe.MODE_MXFP4))
+    assert st == "MOE_ERR_UNSUPPORTED"
+
+
+def test_workspace_does_not_depend_on_weight_strides():
+    """No weight copy is ever made: packed views and contiguous copies need the
+    same workspace and get the same configuration (the copies the Liger PR
+    measured at 0.375 GiB per layer do not exist here)."""
+    x, gate, up, w2, ids, w = _bf16_case(T=64)
+    a = moe.moe_fused_workspace_size(x, gate, up, w2, ids, w)
+    b = moe.moe_fused_workspace_size(x, gate.contiguous(), up.contiguous(), w2, ids, w)
+    assert a == b
+    assert moe.moe_query_config(x, gate, up, w2, ids, w) == moe.moe_query_config(
+        x, gate.contiguous(), up.contiguous(), w2, ids, w)
+    # x stored transposed needs one re-layout buffer of T*H bf16 and nothing else
+    xt = x.t().contiguous().t()
+    c = moe.moe_fused_workspace_size(xt, gate, up, w2, ids, w)
+    assert a < c <= a + 64 * 256 * 2 + 256
+
+
+def test_config_depends_on_bucket_only():
+    cfgs = []
+    for T in (1, 2, 16, 17, 32, 512):
+        x, gate, up, w2, ids, w = _bf16_case(T=T)
+        cfgs.append(moe.moe_query_config(x, gate, up, w2, ids, w))
+    assert cfgs[0]["bucket"] == 1 and cfgs[3]["bucket"] == 32 and cfgs[-1]["bucket"] == 512
+    assert cfgs[3] == cfgs[4]
+
+
+def test_align_and_route_argument_checks():
+    ids = torch.zeros(4, 2, dtype=torch.int32)
+    L = _abi.load()
+    assert L.moe_align_capacity(8, 8, 16) == 128
+    assert L.moe_align_capacity(0, 8, 16) == 0
+    assert L.moe_align_capacity(8, 8, 24) == -1
+    st = _status(lambda: moe.moe_align(ids, 8, 24))
+    assert st == "MOE_ERR_ARG"
+    logits = torch.zeros(4, 8)
+    st = _status(lambda: moe.moe_topk_softmax(logits, 9, stream=0))
+    assert st == "MOE_ERR_ARG"
+    st = _status(lambda: moe.moe_topk_softmax(logits, 2, ids=torch.zeros(4, 3, dtype=torch.int32),
+                                              stream=0))
+    assert st == "MOE_ERR_SHAPE"
+    nb = ctypes.c_size_t(0)
+    assert L.moe_align_workspace_size(4, 2, 8, 16, ctypes.byref(nb)) == 0 and nb.value == 0
+    assert L.moe_align_workspace_size(40000, 8, 128, 16, ctypes.byref(nb)) == 0 and nb.value > 0

@@ -1,0 +1,118 @@
+"""GPU parity of the single steps against the oracle, bit-exact:
+router ids (weights within 1 ulp), align, and MXFP4 quantisation."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import mixture_experts_ffn_align_amd as moe
+from mixture_experts_ffn_align_amd import workloads as W
+from harness import assert_routing_equal, np_, np_bits, route_both
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.mark.parametrize("shape,T,kind", [
+    (W.TINY_BF16, 64, "uniform"),
+    (W.QWEN3_235B_BF16, 512, "uniform"),
+    (W.QWEN3_235B_BF16, 4099, "zipf"),
+    (W.QWEN35_397B_TP2_FP4_512, 333, "uniform"),
+    (W.QWEN35_397B_TP2_FP4_513, 1024, "uniform"),
+])
+def test_router_matches_oracle(shape, T, kind):
+    g = torch.Generator(device=DEV).manual_seed(T)
+    if kind == "zipf":
+        logits = W.zipf_logits(T, shape.routed_experts, g, DEV)
+    else:
+        logits = W.uniform_logits(T, shape.routed_experts, g, DEV)
+    inp = {"shape": shape, "logits": logits}
+    gpu, orc = route_both(inp)
+    assert_routing_equal(gpu, orc)
+    exact = (np_(gpu[1]) == orc[1]).mean()
+    assert exact > 0.999
+
+
+def test_router_strided_logits_and_outputs():
+    g = torch.Generator(device=DEV).manual_seed(3)
+    buf = torch.randn(128, 300, generator=g, device=DEV)
+    logits = buf.t()                                        # [300, 128], strides (1, 300)
+    ids_all = torch.full((300, 3, 8), -7, dtype=torch.int32, device=DEV)
+    w_all = torch.full((300, 3, 8), float("nan"), device=DEV)
+    moe.moe_topk_softmax(logits, 8, ids=ids_all[:, 1, :], weights=w_all[:, 1, :])
+    oi, ow = oracle.route(np_(logits.contiguous()), 8)
+    assert (np_(ids_all[:, 1, :]) == oi).all()
+    assert (np_(ids_all[:, 0, :]) == -7).all() and (np_(ids_all[:, 2, :]) == -7).all()
+    d = np.abs(np_(w_all[:, 1, :]).view(np.int32).astype(np.int64) - ow.view(np.int32))
+    assert d.max() <= 1
+
+
+def test_router_without_renorm():
+    g = torch.Generator(device=DEV).manual_seed(4)
+    logits = torch.randn(77, 64, generator=g, device=DEV)
+    gi, gw = moe.moe_topk_softmax(logits, 6, renorm=False)
+    oi, ow = oracle.route(np_(logits), 6, renorm=False)
+    assert (np_(gi) == oi).all()
+    d = np.abs(np_(gw).view(np.int32).astype(np.int64) - ow.view(np.int32))
+    assert d.max() <= 1
+
+
+def _align_case(ids: torch.Tensor, E: int, bm: int):
+    s, be, n = moe.moe_align(ids, E, bm)
+    torch.cuda.synchronize()
+    os_, obe, on = oracle.align(np_(ids.contiguous()), E, bm)
+    n = int(n.item())
+    assert n == on
+    assert (np_(s[:n]) == os_).all()
+    assert (np_(be[:n // bm]) == obe).all()
+
+
+@pytest.mark.parametrize("T,k,E,bm", [
+    (64, 2, 8, 16), (1, 8, 128, 16), (7, 8, 128, 32), (333, 8, 128, 32), (512, 8, 128, 64),
+    (2048, 8, 128, 64),            # A = 16384: single workgroup, exactly one chunk
+    (2049, 8, 128, 64),            # one past: multi-block path
+    (4099, 8, 128, 32), (16384, 8, 128, 64), (32768, 11, 513, 128), (777, 10, 512, 16),
+])
+def test_align_matches_oracle(T, k, E, bm):
+    g = torch.Generator(device=DEV).manual_seed(T * 7 + k)
+    ids = torch.randint(0, E, (T, k), generator=g, device=DEV, dtype=torch.int32)
+    _align_case(ids, E, bm)
+
+
+def test_align_skewed_invalid_and_strided():
+    g = torch.Generator(device=DEV).manual_seed(11)
+    T, k, E = 5000, 8, 128
+    full = torch.randint(-2, E + 2, (1, T, 46, k), generator=g, device=DEV, dtype=torch.int32)
+    full[0, : T // 2, 7, 0] = 5                              # one hot expert
+    ids = full[0, :, 7, :]
+    assert ids.stride() == (368, 1)
+    _align_case(ids, E, 32)
+    _align_case(torch.full((3, 4), -1, dtype=torch.int32, device=DEV), 16, 16)
+
+
+def test_quant_matches_oracle_exhaustive_bf16():
+    b = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    v = (b.astype(np.uint32) << 16).view(np.float32)
+    b = b[np.isfinite(v)]
+    rng = np.random.default_rng(0)
+    b = np.concatenate([b, rng.permutation(b)])
+    n = b.size // 256 * 256
+    rows = np.ascontiguousarray(b[:n].reshape(-1, 256))
+    src = torch.from_numpy(rows.view(np.int16)).view(torch.bfloat16).to(DEV)
+    c, s = moe.moe_quant_mxfp4(src)
+    oc, os_ = oracle.mxfp4_quant(rows)
+    assert (np_(c) == oc).all() and (np_(s) == os_).all()
+
+
+def test_quant_strided_and_3d():
+    g = torch.Generator(device=DEV).manual_seed(5)
+    buf = (torch.randn(512, 40, generator=g, device=DEV) * 3).to(torch.bfloat16)
+    x = buf.t()                                              # [40, 512], stride (1, 40)
+    c, s = moe.moe_quant_mxfp4(x)
+    oc, os_ = oracle.mxfp4_quant(np_bits(x.contiguous()))
+    assert (np_(c) == oc).all() and (np_(s) == os_).all()
+    w = (torch.randn(3, 64, 256, generator=g, device=DEV)).to(torch.bfloat16)
+    view = w[:, 16:48, :]
+    c3, s3 = moe.moe_quant_mxfp4(view)
+    oc3, os3 = oracle.mxfp4_quant(np_bits(view.contiguous()))
+    assert (np_(c3) == oc3).all() and (np_(s3) == os3).all()
