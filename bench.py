@@ -1,0 +1,337 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused MoE expert-FFN forward on one MI355X.
+
+One step = the whole hot path on one batch: router (top-k softmax) and the
+fused forward (align, gemm1 + SiLU*up, gemm2, combine) for the
+Qwen3-235B-shaped bf16 layer (H=4096, I=1536, E=128, top-8) at T=512 tokens,
+gate/up passed as views into the packed w13. Inputs are seeded synthetic
+tensors already resident in HBM. The JSON line also carries the same layer at
+T=4096 and T=16384 with router-replay id slices (the other token counts the
+metric names), the per-stage times from HIP events, the roofline of the
+dominant kernel (gemm1) and the oracle timed on the host cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+METRIC = "fused-MoE fwd µs/call + TFLOP/s & %roofline at T=512/4096/16384 tokens"
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "gemm1_bf16_qwen3_235b_t512_counters.md")
+KERNEL_SOURCES = ("mixture_experts_ffn_align_amd/csrc/gemm_stream.hip",
+                  "mixture_experts_ffn_align_amd/csrc/moe_internal.h")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """Raw hipEvent_t handles from the HIP runtime torch already loaded."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            out.append(e.value)
+        return out
+
+    def record(self, ev, stream):
+        if self.hip.hipEventRecord(ctypes.c_void_p(ev), ctypes.c_void_p(stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float(0)
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.hip.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per gemm1 launch from the committed rocprofv3 counter runs,
+    or None when the kernel source changed since they were taken."""
+    if not os.path.exists(PROFILE_COUNTERS):
+        return None
+    text = open(PROFILE_COUNTERS).read()
+    m = re.search(r"```json\n(.*?)\n```", text, re.S)
+    if not m:
+        return None
+    d = json.loads(m.group(1))
+    if d.get("source_hash") != source_hash():
+        return None
+    return d.get("traffic_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="budget for the oracle's CPU baseline sample (0 to skip)")
+    ap.add_argument("--no-extra", action="store_true", help="skip the T=4096/16384 lines")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy three times (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
+              "(multi-GPU expert/tensor parallel sharding is a design note, not built).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import mixture_experts_ffn_align_amd as moe
+    from mixture_experts_ffn_align_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.calibrate_copy:
+        src = torch.ones(2 ** 28, dtype=torch.float32, device=dev)     # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] copied 1 GiB three times")
+        return
+    sh = W.QWEN3_235B_BF16
+    T, H, I, E, k = 512, sh.hidden, sh.inter, sh.experts, sh.top_k
+    log(f"[bench] drawing weights {sh.name}")
+    g = torch.Generator(device=dev).manual_seed(0)
+    w13, w2 = W.draw_weights(sh, g, dev)
+    inp = W.make_inputs(sh, T, seed=0, device=dev, weights=(w13, w2))
+    gate, up = W.packed_views(w13, I)
+    x, logits = inp["x"], inp["logits"]
+    ids = torch.empty(T, k, dtype=torch.int32, device=dev)
+    wts = torch.empty(T, k, dtype=torch.float32, device=dev)
+    out = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(moe.moe_fused_workspace_size(x, gate, up, w2, ids, wts), dtype=torch.uint8,
+                     device=dev)
+    cfg = moe.moe_query_config(x, gate, up, w2, ids, wts)
+    stream = torch.cuda.current_stream().cuda_stream
+    hip = HipEvents()
+    nst = len(moe.STAGES)
+
+    def step(evs=None):
+        if evs is not None:
+            hip.record(evs[0], stream)
+        moe.moe_topk_softmax(logits, k, ids=ids, weights=wts, stream=stream)
+        if evs is not None:
+            hip.record(evs[1], stream)
+        moe.moe_fused_fwd(x, gate, up, w2, ids, wts, out=out, workspace=ws,
+                          stage_events=None if evs is None else evs[2:], stream=stream)
+
+    log(f"[bench] warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evsets = [hip.create(2 + 2 * nst) for _ in range(args.steps)]
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evsets[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    stage_ms = {"route": 0.0}
+    stage_ms.update({s: 0.0 for s in moe.STAGES})
+    gpu_ms = 0.0
+    for evs in evsets:
+        stage_ms["route"] += hip.elapsed_ms(evs[0], evs[1])
+        for s, name in enumerate(moe.STAGES):
+            stage_ms[name] += hip.elapsed_ms(evs[2 + 2 * s], evs[3 + 2 * s])
+        gpu_ms += hip.elapsed_ms(evs[0], evs[-1])
+    for key in stage_ms:
+        stage_ms[key] /= args.steps
+    gpu_ms /= args.steps
+    for evs in evsets:
+        hip.destroy(evs)
+
+    touched = int(torch.unique(ids).numel())
+    A = T * k
+    per_expert = 3 * I * H * 2
+    bytes_call = touched * per_expert + 2 * T * H * 2 + 8 * A + T * sh.routed_experts * 4
+    flops_call = 6 * H * I * A
+    us = ms_per_step * 1e3
+    tflops = flops_call / (us * 1e-6) / 1e12
+    roof_call = max(bytes_call / (HBM_PEAK_GBS * 1e9), flops_call / (BF16_PEAK_TFLOPS * 1e12)) / (us * 1e-6)
+    g1_bytes = touched * 2 * I * H * 2 + T * H * 2
+    g1_s = stage_ms["gemm1"] * 1e-3
+    g1_gbs = g1_bytes / g1_s / 1e9
+    traffic = read_traffic()
+
+    # flushed single calls: a 512 MB write before each call evicts L2 and MALL
+    flush = torch.empty(512 * 2 ** 20 // 4, dtype=torch.float32, device=dev)
+    flushed = []
+    e2 = hip.create(2)
+    for _ in range(10):
+        flush.fill_(1.0)
+        hip.record(e2[0], stream)
+        step()
+        hip.record(e2[1], stream)
+        torch.cuda.synchronize()
+        flushed.append(hip.elapsed_ms(e2[0], e2[1]))
+    del flush
+    flushed_us = float(np.median(flushed)) * 1e3
+
+    extra = {}
+    if not args.no_extra:
+        for TT in (4096, 16384):
+            log(f"[bench] T={TT} router-replay slices, packed views")
+            ri = W.make_inputs(sh, TT, seed=0, device=dev, routing="replay", weights=(w13, w2))
+            xo = torch.empty(TT, H, dtype=torch.bfloat16, device=dev)
+            ids_s, w_s = ri["topk_ids"], ri["topk_weights"]
+            wsx = torch.empty(moe.moe_fused_workspace_size(ri["x"], gate, up, w2, ids_s, w_s),
+                              dtype=torch.uint8, device=dev)
+            n_w, n_t = max(3, args.warmup // 2), max(5, args.steps // 4)
+            for _ in range(n_w):
+                moe.moe_fused_fwd(ri["x"], gate, up, w2, ids_s, w_s, out=xo, workspace=wsx, stream=stream)
+            ev = hip.create(2 + 2 * nst)
+            g1 = 0.0
+            torch.cuda.synchronize()
+            ta = time.perf_counter()
+            for _ in range(n_t):
+                moe.moe_fused_fwd(ri["x"], gate, up, w2, ids_s, w_s, out=xo, workspace=wsx,
+                                  stage_events=ev[2:], stream=stream)
+                torch.cuda.synchronize()
+                g1 += hip.elapsed_ms(ev[2 + 2 * 2], ev[3 + 2 * 2])
+            tb = time.perf_counter()
+            hip.destroy(ev)
+            us_t = (tb - ta) * 1e6 / n_t
+            At = TT * k
+            touched_t = int(torch.unique(ids_s).numel())
+            b_t = touched_t * per_expert + 2 * TT * H * 2 + 8 * At
+            f_t = 6 * H * I * At
+            extra[str(TT)] = {
+                "us_per_call": round(us_t, 1),
+                "tflops": round(f_t / (us_t * 1e-6) / 1e12, 1),
+                "roofline_frac": round(max(b_t / (HBM_PEAK_GBS * 1e9), f_t / (BF16_PEAK_TFLOPS * 1e12))
+                                       / (us_t * 1e-6), 3),
+                "bound": "hbm" if b_t / HBM_PEAK_GBS / 1e9 > f_t / BF16_PEAK_TFLOPS / 1e12 else "mfma",
+                "gemm1_us": round(g1 * 1e3 / n_t, 1),
+                "inputs": "packed w13 views, ids/weights [:, :, 7, :] of [1,T,46,8] (token stride 368)",
+            }
+            del ri, xo, wsx
+            torch.cuda.empty_cache()
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(inp, w13, w2, T, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": round(us, 2),
+        "unit": "us/call",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "Qwen3-235B-shaped MoE layer, bf16, T=512 tokens, H=4096, I=1536, E=128, top-8, "
+                        "router + fused forward, gate/up as packed w13 views",
+            "tokens": T, "hidden": H, "inter": I, "experts": E, "top_k": k,
+            "block_m": cfg["block_m"], "gemm1_split_k": cfg["gemm1_split_k"],
+        },
+        "tflops": round(tflops, 2),
+        "roofline_frac_call": round(roof_call, 3),
+        "touched_experts": touched,
+        "algorithmic_bytes_per_call": bytes_call,
+        "gpu_us_per_step_events": round(gpu_ms * 1e3, 1),
+        "flushed_us_per_call_median": round(flushed_us, 1),
+        "stage_us": {kk: round(v * 1e3, 1) for kk, v in stage_ms.items()},
+        "roofline": {
+            "kernel": "gemm1 (gemm_stream bf16 stage 1)",
+            "bound": "hbm",
+            "achieved": round(g1_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(g1_gbs / HBM_PEAK_GBS, 3),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": g1_bytes,
+        },
+        "per_tokens": extra,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(inp, w13, w2, T, budget_s):
+    """The oracle (router + per-token FFN + combine) on the host cores, on the
+    first tokens of the same batch until the time budget is spent, scaled to
+    one call of T tokens."""
+    import numpy as np
+    import oracle
+    from mixture_experts_ffn_align_amd import workloads as W
+
+    sh = inp["shape"]
+    log("[bench] cpu baseline: copying weights to host")
+    bits = lambda t: t.cpu().contiguous().view(__import__("torch").int16).numpy().view(np.uint16)
+    g, u = W.packed_views(w13, sh.inter)
+    G, U, D = bits(g), bits(u), bits(w2)
+    x = bits(inp["x"])
+    logits = inp["logits"].cpu().numpy()
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    oracle.lib()
+    done = 0
+    t0 = time.perf_counter()
+    batch = max(threads, 4)
+    while done < T and time.perf_counter() - t0 < budget_s:
+        n = min(batch, T - done)
+        ids, w = oracle.route(np.ascontiguousarray(logits[done:done + n]), sh.routed_k)
+        oracle.ffn(np.ascontiguousarray(x[done:done + n]), ids, w, num_experts=sh.experts, gate=G, up=U,
+                   w2=D)
+        done += n
+        log(f"[bench] cpu baseline: {done} tokens in {time.perf_counter() - t0:.1f} s")
+    el = time.perf_counter() - t0
+    return {
+        "value": round(el / done * T * 1e6, 1),
+        "unit": "us/call",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"first {done} of {T} tokens (router + FFN + combine, fp64), {el:.1f} s, scaled to {T} tokens",
+    }
+
+
+if __name__ == "__main__":
+    main()

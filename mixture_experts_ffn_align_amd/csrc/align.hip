@@ -4,20 +4,23 @@
 // Liger-Kernel PR #1377, Testing Done: unaligned token tails).
 //
 // A counting sort in three phases: histogram, scan, scatter. Each wave owns a
-// contiguous range of flat indices a = t*k + j; within a wave, lanes with the
-// same expert are ranked by a ballot over lower lanes, so the output keeps
-// ascending a inside every expert. Small problems run all three phases in one
-// workgroup (one launch); larger ones use three launches over 16384-index
-// chunks.
+// contiguous range of flat indices a = t*k + j and ranks each round of 64 by
+// a bitonic sort across the wave, so the output keeps ascending a inside every
+// expert. Up to 16384 assignments run all three phases in one workgroup of
+// 1024 threads (one launch); larger problems use three launches over
+// 4096-index chunks.
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
-constexpr int kThreads = 512;
+constexpr int kThreads = 512;                // multi-block kernels
 constexpr int kWaves = kThreads / kWave;
-constexpr int kChunk = 16384;                 // indices per workgroup (multi-block)
-constexpr int kWaveItems = kChunk / kWaves;   // 2048
+constexpr int kChunk = 4096;                  // indices per workgroup (multi-block)
+constexpr int kWaveItems = kChunk / kWaves;   // 512
+constexpr int kFusedThreads = 1024;           // single-workgroup path
+constexpr int kFusedWaves = kFusedThreads / kWave;
+constexpr int kFusedMaxA = 16384;
 
 __device__ __forceinline__ int expert_of(const AlignParams& p, int a) {
     int t = (int)((unsigned)a / (unsigned)p.k);
@@ -34,75 +37,95 @@ __device__ void wave_count(const AlignParams& p, int lo, int hi, int* cnt) {
 }
 
 // Scatter [lo, hi) using base[e] as the running output position of expert e.
+// Each round of 64 indices is ranked by sorting the keys (expert << 6 | lane)
+// across the wave with a bitonic network: equal experts end up adjacent and in
+// lane order, so an element's rank inside its expert is its distance from the
+// start of its run. The last lane of a run advances base[e] for the next round.
 __device__ void wave_scatter(const AlignParams& p, int lo, int hi, int* base) {
     const int lane = lane_id();
     for (int a0 = lo; a0 < hi; a0 += kWave) {
         const int a = a0 + lane;
-        int e = a < hi ? expert_of(p, a) : -1;
-        const bool valid = e >= 0;
-        uint64_t active = __ballot(valid);
-        while (active) {
-            const int leader = __ffsll((unsigned long long)active) - 1;
-            const int e0 = __shfl(e, leader);
-            const uint64_t m = __ballot(valid && e == e0);
-            const int b = base[e0];
-            if (valid && e == e0) p.sorted[b + __popcll(m & lanemask_lt())] = a;
-            if (lane == leader) base[e0] = b + __popcll(m);
-            active &= ~m;
+        const int e = a < hi ? expert_of(p, a) : -1;
+        uint32_t key = e >= 0 ? ((uint32_t)e << 6) | (uint32_t)lane : 0x80000000u | (uint32_t)lane;
+#pragma unroll
+        for (int k = 2; k <= kWave; k <<= 1) {
+#pragma unroll
+            for (int j = k >> 1; j > 0; j >>= 1) {
+                const uint32_t o = (uint32_t)__shfl_xor((int)key, j);
+                const bool ascending = (lane & k) == 0;
+                const bool lower = (lane & j) == 0;
+                key = (lower == ascending) ? min(key, o) : max(key, o);
+            }
+        }
+        const bool valid = (key >> 31) == 0;
+        const uint32_t ek = key >> 6;
+        const uint32_t prev = (uint32_t)__shfl_up((int)ek, 1);
+        const uint32_t next = (uint32_t)__shfl_down((int)ek, 1);
+        const uint64_t starts = __ballot(lane == 0 || prev != ek);
+        const bool is_end = lane == kWave - 1 || next != ek;
+        const uint64_t upto = lane == kWave - 1 ? ~0ull : ((2ull << lane) - 1);
+        const int start = 63 - __clzll((long long)(starts & upto));
+        const int rank = lane - start;
+        if (valid) {
+            const int b = base[ek];
+            p.sorted[b + rank] = a0 + (int)(key & 63u);
+            if (is_end) base[ek] = b + rank + 1;
         }
     }
 }
 
-// Exclusive scan of v[0..n) in place (n <= 2 * kThreads); returns the total.
+// Exclusive scan of v[0..n) in place (n <= 2 * NT); returns the total.
+template <int NT>
 __device__ int block_exclusive_scan(int* v, int n, int* wave_tot) {
+    constexpr int NW = NT / kWave;
     const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
-    // two items per thread: [2*tid, 2*tid+1]
-    int x0 = 2 * tid < n ? v[2 * tid] : 0;
-    int x1 = 2 * tid + 1 < n ? v[2 * tid + 1] : 0;
-    int s = x0 + x1;
+    const int x0 = 2 * tid < n ? v[2 * tid] : 0;
+    const int x1 = 2 * tid + 1 < n ? v[2 * tid + 1] : 0;
+    const int s = x0 + x1;
     int inc = s;
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
-        int o = __shfl_up(inc, off);
+        const int o = __shfl_up(inc, off);
         if (lane >= off) inc += o;
     }
     if (lane == kWave - 1) wave_tot[w] = inc;
     __syncthreads();
     if (tid == 0) {
         int run = 0;
-        for (int i = 0; i < kWaves; ++i) {
-            int c = wave_tot[i];
+        for (int i = 0; i < NW; ++i) {
+            const int c = wave_tot[i];
             wave_tot[i] = run;
             run += c;
         }
-        wave_tot[kWaves] = run;
+        wave_tot[NW] = run;
     }
     __syncthreads();
-    int excl = wave_tot[w] + inc - s;
+    const int excl = wave_tot[w] + inc - s;
     if (2 * tid < n) v[2 * tid] = excl;
     if (2 * tid + 1 < n) v[2 * tid + 1] = excl + x0;
-    int total = wave_tot[kWaves];
+    const int total = wave_tot[NW];
     __syncthreads();
     return total;
 }
 
-// Given tot[e] (assignments per expert) in LDS: compute the padded offsets
-// off[e], write block_expert and the sentinels, and n_padded.
+// Given tot[e] (assignments per expert) in LDS: the padded offsets off[e],
+// block_expert, the sentinels and n_padded.
+template <int NT>
 __device__ void layout_experts(const AlignParams& p, const int* tot, int* off, int* scratch) {
     const int E = p.E, bm = p.bm;
-    for (int e = threadIdx.x; e < E; e += kThreads) off[e] = (tot[e] + bm - 1) / bm * bm;
+    for (int e = threadIdx.x; e < E; e += NT) off[e] = (tot[e] + bm - 1) / bm * bm;
     __syncthreads();
-    const int npad = block_exclusive_scan(off, E, scratch);
+    const int npad = block_exclusive_scan<NT>(off, E, scratch);
     const int nblk = npad / bm;
-    // block b belongs to the last expert whose offset is <= b*bm
-    for (int b = threadIdx.x; b < nblk; b += kThreads) {
+    // block b belongs to the last expert whose offset is <= b*bm (experts
+    // without tokens share their successor's offset and own no block)
+    for (int b = threadIdx.x; b < nblk; b += NT) {
         const int pos = b * bm;
         int lo = 0, hi = E - 1;
         while (lo < hi) {
-            int mid = (lo + hi + 1) >> 1;
+            const int mid = (lo + hi + 1) >> 1;
             if (off[mid] <= pos) lo = mid; else hi = mid - 1;
         }
-        // skip experts with no blocks that share the same offset
         const int e = lo;
         p.block_expert[b] = e;
         const int fill_from = off[e] + tot[e];
@@ -113,33 +136,33 @@ __device__ void layout_experts(const AlignParams& p, const int* tot, int* off, i
 }
 
 // Whole align in one workgroup.
-__global__ __launch_bounds__(kThreads) void align_fused(AlignParams p) {
+__global__ __launch_bounds__(kFusedThreads) void align_fused(AlignParams p) {
     extern __shared__ int lds[];
     const int E = p.E;
-    int* wcnt = lds;                     // [kWaves][E]
-    int* tot = wcnt + kWaves * E;        // [E]
-    int* off = tot + E;                  // [E]
-    int* scratch = off + E;              // [kWaves + 1]
+    int* wcnt = lds;                          // [kFusedWaves][E]
+    int* tot = wcnt + kFusedWaves * E;        // [E]
+    int* off = tot + E;                       // [E]
+    int* scratch = off + E;                   // [kFusedWaves + 1]
     const int w = threadIdx.x >> 6;
-    for (int i = threadIdx.x; i < kWaves * E; i += kThreads) wcnt[i] = 0;
+    for (int i = threadIdx.x; i < kFusedWaves * E; i += kFusedThreads) wcnt[i] = 0;
     __syncthreads();
-    const int per = (p.A + kWaves - 1) / kWaves;
+    const int per = (p.A + kFusedWaves - 1) / kFusedWaves;
     const int lo = min(p.A, w * per), hi = min(p.A, lo + per);
     wave_count(p, lo, hi, wcnt + w * E);
     __syncthreads();
-    for (int e = threadIdx.x; e < E; e += kThreads) {
+    for (int e = threadIdx.x; e < E; e += kFusedThreads) {
         int run = 0;
-        for (int v = 0; v < kWaves; ++v) {
-            int c = wcnt[v * E + e];
+        for (int v = 0; v < kFusedWaves; ++v) {
+            const int c = wcnt[v * E + e];
             wcnt[v * E + e] = run;
             run += c;
         }
         tot[e] = run;
     }
     __syncthreads();
-    layout_experts(p, tot, off, scratch);
-    for (int e = threadIdx.x; e < E; e += kThreads)
-        for (int v = 0; v < kWaves; ++v) wcnt[v * E + e] += off[e];
+    layout_experts<kFusedThreads>(p, tot, off, scratch);
+    for (int e = threadIdx.x; e < E; e += kFusedThreads)
+        for (int v = 0; v < kFusedWaves; ++v) wcnt[v * E + e] += off[e];
     __syncthreads();
     wave_scatter(p, lo, hi, wcnt + w * E);
 }
@@ -150,9 +173,8 @@ __global__ __launch_bounds__(kThreads) void align_count(AlignParams p) {
     const int E = p.E;
     for (int i = threadIdx.x; i < E; i += kThreads) lds[i] = 0;
     __syncthreads();
-    const int base = blockIdx.x * kChunk;
     const int w = threadIdx.x >> 6;
-    const int lo = min(p.A, base + w * kWaveItems), hi = min(p.A, lo + kWaveItems);
+    const int lo = min(p.A, (int)blockIdx.x * kChunk + w * kWaveItems), hi = min(p.A, lo + kWaveItems);
     wave_count(p, lo, hi, lds);
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += kThreads) p.counts[(int64_t)blockIdx.x * E + e] = lds[e];
@@ -168,14 +190,14 @@ __global__ __launch_bounds__(kThreads) void align_scan(AlignParams p, int nchunk
     for (int e = threadIdx.x; e < E; e += kThreads) {
         int run = 0;
         for (int b = 0; b < nchunks; ++b) {
-            int c = p.counts[(int64_t)b * E + e];
+            const int c = p.counts[(int64_t)b * E + e];
             p.counts[(int64_t)b * E + e] = run;
             run += c;
         }
         tot[e] = run;
     }
     __syncthreads();
-    layout_experts(p, tot, off, scratch);
+    layout_experts<kThreads>(p, tot, off, scratch);
     for (int e = threadIdx.x; e < E; e += kThreads)
         for (int b = 0; b < nchunks; ++b) p.counts[(int64_t)b * E + e] += off[e];
 }
@@ -187,15 +209,14 @@ __global__ __launch_bounds__(kThreads) void align_scatter(AlignParams p) {
     int* wcnt = lds;   // [kWaves][E]
     for (int i = threadIdx.x; i < kWaves * E; i += kThreads) wcnt[i] = 0;
     __syncthreads();
-    const int base = blockIdx.x * kChunk;
     const int w = threadIdx.x >> 6;
-    const int lo = min(p.A, base + w * kWaveItems), hi = min(p.A, lo + kWaveItems);
+    const int lo = min(p.A, (int)blockIdx.x * kChunk + w * kWaveItems), hi = min(p.A, lo + kWaveItems);
     wave_count(p, lo, hi, wcnt + w * E);
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += kThreads) {
         int run = p.counts[(int64_t)blockIdx.x * E + e];
         for (int v = 0; v < kWaves; ++v) {
-            int c = wcnt[v * E + e];
+            const int c = wcnt[v * E + e];
             wcnt[v * E + e] = run;
             run += c;
         }
@@ -204,26 +225,31 @@ __global__ __launch_bounds__(kThreads) void align_scatter(AlignParams p) {
     wave_scatter(p, lo, hi, wcnt + w * E);
 }
 
+bool use_fused(int A, int E) {
+    return A <= kFusedMaxA && (size_t)(kFusedWaves + 2) * E * sizeof(int) + 256 <= 64 * 1024;
+}
+
 }  // namespace
 
 size_t align_scratch_bytes(int64_t A, int32_t E) {
-    int64_t nchunks = (A + kChunk - 1) / kChunk;
-    return (size_t)(nchunks > 1 ? nchunks : 0) * (size_t)E * sizeof(int32_t);
+    if (use_fused((int)A, E)) return 0;
+    const int64_t nchunks = (A + kChunk - 1) / kChunk;
+    return (size_t)nchunks * (size_t)E * sizeof(int32_t);
 }
 
 hipError_t launch_align(const AlignParams& p, hipStream_t s) {
     const int E = p.E;
-    const int nchunks = (p.A + kChunk - 1) / kChunk;
-    if (nchunks <= 1) {
-        size_t lds = sizeof(int) * ((size_t)kWaves * E + 2 * E + kWaves + 1);
-        hipLaunchKernelGGL(align_fused, dim3(1), dim3(kThreads), lds, s, p);
+    if (use_fused(p.A, E)) {
+        const size_t lds = sizeof(int) * ((size_t)kFusedWaves * E + 2 * E + kFusedWaves + 1);
+        hipLaunchKernelGGL(align_fused, dim3(1), dim3(kFusedThreads), lds, s, p);
         return hipGetLastError();
     }
-    size_t lds_c = sizeof(int) * (size_t)E;
+    const int nchunks = (p.A + kChunk - 1) / kChunk;
+    const size_t lds_c = sizeof(int) * (size_t)E;
     hipLaunchKernelGGL(align_count, dim3(nchunks), dim3(kThreads), lds_c, s, p);
-    size_t lds_s = sizeof(int) * (2 * (size_t)E + kWaves + 1);
+    const size_t lds_s = sizeof(int) * (2 * (size_t)E + kWaves + 1);
     hipLaunchKernelGGL(align_scan, dim3(1), dim3(kThreads), lds_s, s, p, nchunks);
-    size_t lds_x = sizeof(int) * (size_t)kWaves * E;
+    const size_t lds_x = sizeof(int) * (size_t)kWaves * E;
     hipLaunchKernelGGL(align_scatter, dim3(nchunks), dim3(kThreads), lds_x, s, p);
     return hipGetLastError();
 }

@@ -16,14 +16,24 @@
 // output columns) for all BM rows; WK waves split K and reduce through LDS
 // in a fixed order. Both operands are K-contiguous, which is exactly the
 // per-lane layout of v_mfma_f32_16x16x32_bf16 / v_mfma_scale_f32_16x16x128
-// (lane l: row l % 16, a run of consecutive k chosen by l / 16), so every lane
-// loads its 16-byte operand straight from memory into registers: weights
-// stream HBM -> VGPR once per block with no LDS round trip, and the loads of
-// the next K step are issued before the MFMAs of the current one.
+// (lane l: row l % 16, a run of consecutive k chosen by l / 16):
+//  * weights (B) are read by exactly one wave, so every lane loads its
+//    16-byte operand straight from HBM into registers, the next U steps
+//    always in flight while the current ones multiply;
+//  * token rows (A) are shared by the waves that split N, so they are staged
+//    once per workgroup in LDS, already in MFMA fragment order: lane l of
+//    the loading wave writes offset 16*l of a 1 KB fragment, and a consuming
+//    wave reads the same offset back with one ds_read_b128. Chunks of cs
+//    steps are double buffered: the next chunk is loaded into a few VGPRs
+//    at the start of a chunk and written to the idle buffer at its end, with
+//    one workgroup barrier per chunk that waits on LDS only, never on the
+//    weight loads in flight.
 //
 // In MXFP4 mode one lane's 32 e2m1 codes are exactly one scale block, so the
 // per-1x32 e8m0 scales feed the block-scaled MFMA directly, and the stage 1
 // epilogue quantises h per 32 columns in registers (max over 16 lanes).
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -48,23 +58,40 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
     return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
 }
 
+// Occupancy target per SIMD: the weight stream needs as many waves in flight
+// as the register file allows, so the allocation is capped (4 waves for 16
+// rows, 3 for 32, 2 for 64).
+template <int MODE, int BM, int WK>
+constexpr int waves_per_simd() { return BM <= 16 ? ((MODE == 1 || WK == 1) ? 4 : 3) : (BM <= 32 ? 3 : 2); }
+
 template <int MODE, int STAGE, int BM, int WK, int U>
-__global__ __launch_bounds__(256) void gemm_stream(GemmParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_per_simd<MODE, BM, WK>(), 8)))
+void gemm_stream(GemmParams p) {
     constexpr int MB = BM / 16;
     constexpr int NB = 4;
     constexpr int WN = 4 / WK;
     constexpr int KSTEP = MODE == 0 ? 32 : 128;
     constexpr int WCOLS = STAGE == 1 ? 32 : 64;
     constexpr int TILE_N = WN * WCOLS;
+    // 1 KB A fragments per LDS buffer: room for a chunk of at least 2U steps
+    constexpr int FRAGS = (U * WK * MB > 16) ? U * WK * MB : 16;
+    static_assert(FRAGS % 4 == 0 && 2 * FRAGS <= 64, "A staging must fit 64 KB of LDS");
+    constexpr int RED_FLOATS = 4 * MB * NB * 4 * 64;
+    constexpr int LDS_FLOATS = (WK > 1 && RED_FLOATS > 2 * FRAGS * 256) ? RED_FLOATS : 2 * FRAGS * 256;
+    constexpr int AREGS = FRAGS / 4;      // fragments one wave stages per chunk (at most)
+    __shared__ __attribute__((aligned(16))) float lds[LDS_FLOATS];
 
     const int lane = lane_id();
     const int w = threadIdx.x >> 6;
     const int wn = w / WK, wk = w % WK;
     const int r16 = lane & 15, kg = lane >> 4;
 
-    // ---- tile mapping: ((n-group, m-block), n-tile in group), XCD-aware
+    // ---- tile mapping: ((n-group, m-block), n-tile in group). Consecutive
+    // workgroups go to different XCDs, which spreads the weight stream of
+    // neighbouring tiles over all of them; pinning a contiguous tile range to
+    // one XCD measured slower for this stream.
     const int n_tiles = p.N / TILE_N;
-    const uint32_t L = xcd_remap(blockIdx.x, gridDim.x);
+    const uint32_t L = blockIdx.x;
     const int G = p.n_tile_groups;
     const int ji = (int)(L % (uint32_t)G);
     const uint32_t rest = L / (uint32_t)G;
@@ -72,7 +99,7 @@ __global__ __launch_bounds__(256) void gemm_stream(GemmParams p) {
     const int jg = (int)(rest / (uint32_t)p.max_mblocks);
     const int nt = jg * G + ji;
     if (nt >= n_tiles) return;
-    const int n_blocks = __builtin_nontemporal_load(p.n_padded) / BM;
+    const int n_blocks = *p.n_padded / BM;
     if (mb >= n_blocks) return;
     const int e = p.block_expert[mb];
     const int row0 = mb * BM;
@@ -118,88 +145,138 @@ __global__ __launch_bounds__(256) void gemm_stream(GemmParams p) {
         }
     }
 
-    // ---- K loop over this wave's share
+    // ---- K loop
     const int kw = p.K / WK;
-    const int kbeg = wk * kw;
-    const int steps = kw / KSTEP;
-    // byte offset of this lane's operand run for step s
-    auto koff = [&](int s) -> int64_t {
-        const int k = kbeg + s * KSTEP;
+    const int steps = kw / KSTEP;                 // steps per wave; the host keeps it a multiple of 2U
+    // byte offset of a lane's operand run for step s of K share q
+    auto koff = [&](int q, int s) -> int64_t {
+        const int k = q * kw + s * KSTEP;
         return MODE == 0 ? (int64_t)(k + kg * 8) * 2 : (int64_t)(k / 2 + kg * 16);
     };
-    auto sidx = [&](int s) -> int { return (kbeg + s * KSTEP) / 32 + kg; };
+    // A chunks of cs steps: a multiple of U that divides steps, at most
+    // FRAGS fragments per buffer
+    int cs = FRAGS / (WK * MB);
+    cs = cs < steps ? cs : steps;
+    cs = cs < U ? U : cs - cs % U;
+    while (steps % cs != 0) cs -= U;
+    const int nac = steps / cs;
+    const int nfrag = WK * MB * cs;              // fragments per chunk (<= FRAGS)
+    char* const lds_bytes = reinterpret_cast<char*>(lds);
+    // fragment f = (q * MB + mi) * cs + st of buffer b sits at (b * FRAGS + f) KB;
+    // wave w stages fragments f = w, w + 4, ...
+    i32x4_t areg[AREGS];
+    // Both are branch-free (slots past nfrag load a valid fragment again and
+    // fill unused LDS), so the compiler's wait counts stay exact.
+    auto load_A = [&](int ac) {
+#pragma unroll
+        for (int i = 0; i < AREGS; ++i) {
+            int f = w + 4 * i;
+            f = f < nfrag ? f : nfrag - 1;
+            const int st = f % cs, qm = f / cs;
+            const int q = qm / MB, mi = qm % MB;
+            const char* src = a_ptr[0];
+#pragma unroll
+            for (int m = 1; m < MB; ++m) src = m == mi ? a_ptr[m] : src;
+            areg[i] = *reinterpret_cast<const i32x4_t*>(src + koff(q, ac * cs + st));
+        }
+    };
+    auto store_A = [&](int b) {
+#pragma unroll
+        for (int i = 0; i < AREGS; ++i)
+            *reinterpret_cast<i32x4_t*>(lds_bytes + ((size_t)(b * FRAGS + w + 4 * i) << 10) + lane * 16) = areg[i];
+    };
 
-    Frag<MODE> fa[2][U][MB];
-    Frag<MODE> fb[2][U][NB];
+    // Weights: a ring of U step-slots per wave. Slot u holds step s+u; right
+    // after its MFMAs consume it, it is refilled with step s+u+U, so U-1
+    // steps of weight loads are always in flight.
+    Frag<MODE> fb[U][NB];
+    int fasc[U][MB];
     f32x4_t acc[MB][NB];
 #pragma unroll
     for (int mi = 0; mi < MB; ++mi)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[mi][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    auto load_chunk = [&](int buf, int s0) {
+    auto load_B = [&](int slot, int st) {
+        st = st < steps ? st : steps - 1;       // past the end: re-read the last step (L2 hit)
+        const int64_t off = koff(wk, st);
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int s = s0 + u;
-            if (s < steps) {
-                const int64_t off = koff(s);
+        for (int nb = 0; nb < NB; ++nb) {
+            using V = decltype(fb[slot][nb].v);
+            fb[slot][nb].v = *reinterpret_cast<const V*>(b_ptr[nb] + off);
+        }
+        if constexpr (MODE == 1) {
+            const int si = (wk * kw + st * KSTEP) / 32 + kg;
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb) {
-                    using V = decltype(fb[buf][u][nb].v);
-                    fb[buf][u][nb].v = *reinterpret_cast<const V*>(b_ptr[nb] + off);
-                }
+            for (int nb = 0; nb < NB; ++nb) fb[slot][nb].sc = b_sc[nb][si];
 #pragma unroll
-                for (int mi = 0; mi < MB; ++mi) {
-                    using V = decltype(fa[buf][u][mi].v);
-                    fa[buf][u][mi].v = *reinterpret_cast<const V*>(a_ptr[mi] + off);
-                }
-                if constexpr (MODE == 1) {
-                    const int si = sidx(s);
+            for (int mi = 0; mi < MB; ++mi) fasc[slot][mi] = a_sc[mi][si];
+        }
+    };
+    auto compute = [&](int slot, const char* abuf, int sl) {
 #pragma unroll
-                    for (int nb = 0; nb < NB; ++nb) fb[buf][u][nb].sc = b_sc[nb][si];
+        for (int mi = 0; mi < MB; ++mi) {
+            const char* src = abuf + (size_t)(((wk * MB + mi) * cs + sl) << 10) + lane * 16;
+            const i32x4_t araw = *reinterpret_cast<const i32x4_t*>(src);
 #pragma unroll
-                    for (int mi = 0; mi < MB; ++mi) fa[buf][u][mi].sc = a_sc[mi][si];
+            for (int nb = 0; nb < NB; ++nb) {
+                if constexpr (MODE == 0) {
+                    acc[mi][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8_t, araw), fb[slot][nb].v, acc[mi][nb], 0, 0, 0);
+                } else {
+                    const i32x4_t bv = fb[slot][nb].v;
+                    const i32x8_t a8 = {araw[0], araw[1], araw[2], araw[3], 0, 0, 0, 0};
+                    const i32x8_t b8 = {bv[0], bv[1], bv[2], bv[3], 0, 0, 0, 0};
+                    acc[mi][nb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        a8, b8, acc[mi][nb], 4, 4, 0, fasc[slot][mi], 0, fb[slot][nb].sc);
                 }
             }
         }
     };
-    auto compute_chunk = [&](int buf, int s0) {
+    // U steps starting at s0 (a multiple of U) of A chunk ac; every slot is
+    // refilled right after use, unconditionally, so wait counts stay exact
+    auto ring = [&](const char* abuf, int ac, int s0) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            if (s0 + u < steps) {
-#pragma unroll
-                for (int mi = 0; mi < MB; ++mi)
-#pragma unroll
-                    for (int nb = 0; nb < NB; ++nb) {
-                        if constexpr (MODE == 0) {
-                            acc[mi][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                fa[buf][u][mi].v, fb[buf][u][nb].v, acc[mi][nb], 0, 0, 0);
-                        } else {
-                            const i32x4_t av = fa[buf][u][mi].v, bv = fb[buf][u][nb].v;
-                            const i32x8_t a8 = {av[0], av[1], av[2], av[3], 0, 0, 0, 0};
-                            const i32x8_t b8 = {bv[0], bv[1], bv[2], bv[3], 0, 0, 0, 0};
-                            acc[mi][nb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                                a8, b8, acc[mi][nb], 4, 4, 0, fa[buf][u][mi].sc, 0,
-                                fb[buf][u][nb].sc);
-                        }
-                    }
-            }
+            compute(u, abuf, s0 + u - ac * cs);
+            __builtin_amdgcn_sched_barrier(0);
+            load_B(u, s0 + u + U);
+            __builtin_amdgcn_sched_barrier(0);
         }
+    };
+    // LDS-only workgroup barrier: waits for this wave's LDS writes, not for
+    // the weight loads in flight
+    auto lds_barrier = [&]() {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt((15 << 0) | (3 << 14) | (7 << 4) | (0 << 8));   // lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        __asm__ volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
     };
 
-    load_chunk(0, 0);
-    for (int s0 = 0; s0 < steps; s0 += 2 * U) {
-        if (s0 + U < steps) load_chunk(1, s0 + U);
-        compute_chunk(0, s0);
-        if (s0 + U >= steps) break;
-        if (s0 + 2 * U < steps) load_chunk(0, s0 + 2 * U);
-        compute_chunk(1, s0 + U);
+#pragma unroll
+    for (int u = 0; u < U; ++u) load_B(u, u);
+    load_A(0);
+    store_A(0);
+    for (int ac = 0; ac < nac; ++ac) {
+        lds_barrier();                             // chunk ac visible; buffer (ac+1)&1 idle
+        const char* abuf = lds_bytes + ((size_t)((ac & 1) * FRAGS) << 10);
+        load_A(ac + 1 < nac ? ac + 1 : ac);        // next chunk into registers
+        __builtin_amdgcn_sched_barrier(0);
+        // the first U steps are peeled so that the next chunk goes to LDS at a
+        // point where its loads are known to be older than the weight loads in
+        // flight (no drain of the weight stream)
+        ring(abuf, ac, ac * cs);
+        store_A((ac + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        for (int s0 = ac * cs + U; s0 < (ac + 1) * cs; s0 += U) ring(abuf, ac, s0);
     }
 
-    // ---- split-K reduction through LDS (fixed order wk = 0..WK-1)
-    constexpr int RED_FLOATS = WK > 1 ? 4 * MB * NB * 4 * 64 : 1;
-    __shared__ float red[RED_FLOATS];
+    // ---- split-K reduction through LDS (fixed order wk = 0..WK-1); the
+    // buffer reuses the A chunks, so every wave must be done reading them
+    float* red = lds;
     if constexpr (WK > 1) {
+        __syncthreads();
 #pragma unroll
         for (int mi = 0; mi < MB; ++mi)
 #pragma unroll
@@ -285,31 +362,39 @@ __global__ __launch_bounds__(256) void gemm_stream(GemmParams p) {
 
 typedef void (*GemmFn)(GemmParams);
 
-template <int MODE, int STAGE, int BM, int WK>
+template <int MODE, int STAGE, int BM, int WK, int U>
 constexpr GemmFn pick() {
-    return gemm_stream<MODE, STAGE, BM, WK, (MODE == 0 ? 2 : 1)>;
+    return gemm_stream<MODE, STAGE, BM, WK, U>;
 }
 
-template <int MODE, int STAGE>
+template <int MODE, int STAGE, int U>
 GemmFn table(int bm, int wk) {
 #define MOE_CASE(B, W) \
-    if (bm == B && wk == W) return pick<MODE, STAGE, B, W>();
+    if (bm == B && wk == W) return pick<MODE, STAGE, B, W, U>();
     MOE_CASE(16, 1) MOE_CASE(16, 2) MOE_CASE(16, 4)
     MOE_CASE(32, 1) MOE_CASE(32, 2) MOE_CASE(32, 4)
-    MOE_CASE(64, 1) MOE_CASE(64, 2) MOE_CASE(64, 4)
+    MOE_CASE(64, 1) MOE_CASE(64, 2)
 #undef MOE_CASE
     return nullptr;
 }
 
+// bf16 runs a ring of 4 steps (32 k each); MXFP4 a ring of 4 steps (128 k
+// each) where a wave's share of K allows it, else 2.
 GemmFn lookup(const GemmKernelId& id) {
-    if (id.mode == 0 && id.stage == 1) return table<0, 1>(id.bm, id.wk);
-    if (id.mode == 0 && id.stage == 2) return table<0, 2>(id.bm, id.wk);
-    if (id.mode == 1 && id.stage == 1) return table<1, 1>(id.bm, id.wk);
-    if (id.mode == 1 && id.stage == 2) return table<1, 2>(id.bm, id.wk);
+    if (id.mode == 0 && id.u == 4) return id.stage == 1 ? table<0, 1, 4>(id.bm, id.wk) : table<0, 2, 4>(id.bm, id.wk);
+    if (id.mode == 1 && id.u == 4) return id.stage == 1 ? table<1, 1, 4>(id.bm, id.wk) : table<1, 2, 4>(id.bm, id.wk);
+    if (id.mode == 1 && id.u == 2) return id.stage == 1 ? table<1, 1, 2>(id.bm, id.wk) : table<1, 2, 2>(id.bm, id.wk);
     return nullptr;
 }
 
 }  // namespace
+
+int gemm_ring_steps(int mode, int64_t k_per_wave) {
+    if (mode == 0) return 4;
+    return k_per_wave % (128 * 4) == 0 ? 4 : 2;
+}
+
+int gemm_k_granule(const GemmKernelId& id) { return id.mode == 0 ? 32 * 4 : 128 * 2; }
 
 int gemm_tile_n(const GemmKernelId& id) {
     const int wn = 4 / id.wk;

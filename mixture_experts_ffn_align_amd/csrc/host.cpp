@@ -135,8 +135,8 @@ struct Cfg {
     int bm, wk1, wk2;
 };
 const Cfg kConfigs[] = {
-    {16, 4, 4}, {32, 4, 4}, {64, 4, 4},
-    {16, 2, 2}, {32, 2, 2}, {64, 2, 2},
+    {16, 4, 4}, {32, 4, 4}, {64, 2, 2},
+    {16, 2, 2}, {32, 2, 2}, {64, 1, 1},
     {16, 1, 1}, {32, 1, 1}, {64, 1, 1},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
@@ -147,15 +147,23 @@ int bucket_of(int64_t T) {
     return b;
 }
 
+// Block rows cover the typical busiest expert of the bucket in one block (so
+// each expert's weights stream from HBM once); the K split grows only while
+// the grid would not fill the chip.
 int default_config(int mode, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k) {
     (void)mode;
     (void)H;
-    (void)I;
     const int64_t bucket = bucket_of(T);
     const double rows = (double)bucket * (double)k / (double)E;   // expected rows per expert
-    if (rows <= 16.0) return 0;
-    if (rows <= 32.0) return 1;
-    return 2;
+    const double busy = rows + 3.0 * __builtin_sqrt(rows);          // typical maximum
+    const int bm = busy <= 16.0 ? 16 : (busy <= 32.0 ? 32 : 64);
+    const int64_t blocks = std::min<int64_t>(bucket * k, E) *
+                           std::max<int64_t>(1, (int64_t)(rows / bm + 0.999));
+    int wk = 1;
+    while (wk < 4 && (bm < 64 || wk < 2) && blocks * (I / (32 * (4 / wk))) < 1024) wk <<= 1;
+    for (int c = 0; c < kNumConfigs; ++c)
+        if (kConfigs[c].bm == bm && kConfigs[c].wk1 == wk) return c;
+    return 0;
 }
 
 struct Plan {
@@ -245,15 +253,22 @@ int plan_fused(const moe_fused_args_t* a, Plan* pl) {
     if (ci < 0) ci = default_config(a->mode, T, H, I, E, k);
     if (ci >= kNumConfigs) return fail(MOE_ERR_ARG, "force_config %d out of range", ci);
     Cfg c = kConfigs[ci];
-    // the split of K is a preference: halve it until it divides K into whole steps
-    auto fit = [&](int pref, int64_t K) {
+    // the split of K is a preference: halve it until every wave's share of K
+    // is a whole number of pipelined chunks
+    auto fit = [&](int pref, int stage, int64_t K) {
         int w = pref;
-        while (w > 1 && K % (ks * w) != 0) w >>= 1;
+        while (w > 1 && K % ((int64_t)gemm_k_granule(GemmKernelId{fp4 ? 1 : 0, stage, c.bm, w, 0}) * w) != 0)
+            w >>= 1;
         return w;
     };
-    c.wk1 = fit(c.wk1, H);
-    c.wk2 = fit(c.wk2, I);
-    GemmKernelId g1{fp4 ? 1 : 0, 1, c.bm, c.wk1}, g2{fp4 ? 1 : 0, 2, c.bm, c.wk2};
+    c.wk1 = fit(c.wk1, 1, H);
+    c.wk2 = fit(c.wk2, 2, I);
+    const int gran = gemm_k_granule(GemmKernelId{fp4 ? 1 : 0, 1, c.bm, 1, 0});
+    if (H % gran != 0 || I % gran != 0)
+        return fail(MOE_ERR_UNSUPPORTED, "H = %lld and I = %lld must be multiples of %d", (long long)H,
+                    (long long)I, gran);
+    GemmKernelId g1{fp4 ? 1 : 0, 1, c.bm, c.wk1, gemm_ring_steps(a->mode, H / c.wk1)};
+    GemmKernelId g2{fp4 ? 1 : 0, 2, c.bm, c.wk2, gemm_ring_steps(a->mode, I / c.wk2)};
     if (!gemm_supported(g1) || !gemm_supported(g2)) return fail(MOE_ERR_UNSUPPORTED, "config %d not built", ci);
     if (I % gemm_tile_n(g1) != 0 || H % gemm_tile_n(g2) != 0)
         return fail(MOE_ERR_UNSUPPORTED, "config %d: I or H not a multiple of the tile width", ci);
@@ -605,9 +620,9 @@ int moe_fused_fwd(const moe_fused_args_t* args, void* ws, size_t ws_bytes, moe_s
     g1.N = (int32_t)pl.I;
     g1.out = base + pl.off_h;
     g1.out_sc = fp4 ? (uint8_t*)(base + pl.off_hs) : nullptr;
-    g1.n_tile_groups = 8;
+    g1.n_tile_groups = 2;
     g1.max_mblocks = max_mblocks;
-    GemmKernelId k1{fp4 ? 1 : 0, 1, pl.cfg.bm, pl.cfg.wk1};
+    GemmKernelId k1{fp4 ? 1 : 0, 1, pl.cfg.bm, pl.cfg.wk1, gemm_ring_steps(pl.mode, pl.H / pl.cfg.wk1)};
     if ((e = launch_gemm(k1, g1, s)) != hipSuccess) return hip_fail(e, "gemm1");
     tm.end(2);
 
@@ -635,9 +650,9 @@ int moe_fused_fwd(const moe_fused_args_t* args, void* ws, size_t ws_bytes, moe_s
     g2.K = (int32_t)pl.I;
     g2.N = (int32_t)pl.H;
     g2.out = base + pl.off_y;
-    g2.n_tile_groups = 8;
+    g2.n_tile_groups = 2;
     g2.max_mblocks = max_mblocks;
-    GemmKernelId k2{fp4 ? 1 : 0, 2, pl.cfg.bm, pl.cfg.wk2};
+    GemmKernelId k2{fp4 ? 1 : 0, 2, pl.cfg.bm, pl.cfg.wk2, gemm_ring_steps(pl.mode, pl.I / pl.cfg.wk2)};
     if ((e = launch_gemm(k2, g2, s)) != hipSuccess) return hip_fail(e, "gemm2");
     tm.end(3);
 

@@ -183,9 +183,14 @@ struct GemmKernelId {
     int stage;   // 1 or 2
     int bm;      // 16, 32, 64
     int wk;      // waves splitting K: 1, 2 or 4
+    int u;       // weight steps in each wave's load ring (from gemm_ring_steps)
 };
+// Ring depth for a wave's share of K.
+int gemm_ring_steps(int mode, int64_t k_per_wave);
 // Output columns one workgroup covers.
 int gemm_tile_n(const GemmKernelId& id);
+// Smallest unit of K a wave's share must be a multiple of.
+int gemm_k_granule(const GemmKernelId& id);
 bool gemm_supported(const GemmKernelId& id);
 hipError_t launch_gemm(const GemmKernelId& id, const GemmParams& p, hipStream_t s);
 

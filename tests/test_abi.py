@@ -100,7 +100,7 @@ def test_empty_batch_returns_ok_without_launch():
 
 
 def test_mxfp4_shapes_and_k_multiple():
-    T, H, I, E = 4, 256, 128, 4
+    T, H, I, E = 4, 256, 256, 4
     x = torch.zeros(T, H, dtype=torch.bfloat16)
     gq = torch.zeros(E, I, H // 2, dtype=torch.uint8)
     gs = torch.zeros(E, I, H // 32, dtype=torch.uint8)
@@ -114,7 +114,7 @@ def test_mxfp4_shapes_and_k_multiple():
     st = _status(lambda: moe.moe_fused_workspace_size(x, gq, gq.clone(), wq, ids, w, gate_scale=gs[:, :, :4],
                                                       up_scale=gs.clone(), w2_scale=ws_, mode=moe.MODE_MXFP4))
     assert st == "MOE_ERR_SHAPE"
-    x2 = torch.zeros(T, 192, dtype=torch.bfloat16)                 # 192 is not a multiple of 128
+    x2 = torch.zeros(T, 192, dtype=torch.bfloat16)                 # 192 is not a multiple of 256
     g2 = torch.zeros(E, I, 96, dtype=torch.uint8)
     s2 = torch.zeros(E, I, 6, dtype=torch.uint8)
     w22 = torch.zeros(E, 192, I // 2, dtype=torch.uint8)
