@@ -60,9 +60,11 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
 
 // Occupancy target per SIMD: the weight stream needs as many waves in flight
 // as the register file allows, so the allocation is capped (4 waves for 16
-// rows, 3 for 32, 2 for 64).
+// rows, 3 for 32, 2 for 64 and 128).
 template <int MODE, int BM, int WK>
-constexpr int waves_per_simd() { return BM <= 16 ? ((MODE == 1 || WK == 1) ? 4 : 3) : (BM <= 32 ? 3 : 2); }
+constexpr int waves_per_simd() {
+    return BM <= 16 ? ((MODE == 1 || WK == 1) ? 4 : 3) : (BM <= 32 ? 3 : 2);
+}
 
 template <int MODE, int STAGE, int BM, int WK, int U>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_per_simd<MODE, BM, WK>(), 8)))
@@ -378,18 +380,31 @@ GemmFn table(int bm, int wk) {
     return nullptr;
 }
 
-// bf16 runs a ring of 4 steps (32 k each); MXFP4 a ring of 4 steps (128 k
-// each) where a wave's share of K allows it, else 2.
+template <int MODE, int STAGE>
+GemmFn table_u(int bm, int wk, int u) {
+    if (bm == 128 && wk == 1) {
+        return u == 2 ? pick<MODE, STAGE, 128, 1, 2>() : nullptr;
+    }
+    if (u == 4) return table<MODE, STAGE, 4>(bm, wk);
+    if constexpr (MODE == 1) {
+        if (u == 2) return table<MODE, STAGE, 2>(bm, wk);
+    }
+    return nullptr;
+}
+
+// The weight ring holds 4 steps (bf16: 32 k each; MXFP4: 128 k each, where a
+// wave's share of K allows it, else 2); with 128 rows the accumulators leave
+// room for 2.
 GemmFn lookup(const GemmKernelId& id) {
-    if (id.mode == 0 && id.u == 4) return id.stage == 1 ? table<0, 1, 4>(id.bm, id.wk) : table<0, 2, 4>(id.bm, id.wk);
-    if (id.mode == 1 && id.u == 4) return id.stage == 1 ? table<1, 1, 4>(id.bm, id.wk) : table<1, 2, 4>(id.bm, id.wk);
-    if (id.mode == 1 && id.u == 2) return id.stage == 1 ? table<1, 1, 2>(id.bm, id.wk) : table<1, 2, 2>(id.bm, id.wk);
+    if (id.mode == 0) return id.stage == 1 ? table_u<0, 1>(id.bm, id.wk, id.u) : table_u<0, 2>(id.bm, id.wk, id.u);
+    if (id.mode == 1) return id.stage == 1 ? table_u<1, 1>(id.bm, id.wk, id.u) : table_u<1, 2>(id.bm, id.wk, id.u);
     return nullptr;
 }
 
 }  // namespace
 
-int gemm_ring_steps(int mode, int64_t k_per_wave) {
+int gemm_ring_steps(int mode, int bm, int64_t k_per_wave) {
+    if (bm >= 128) return 2;
     if (mode == 0) return 4;
     return k_per_wave % (128 * 4) == 0 ? 4 : 2;
 }

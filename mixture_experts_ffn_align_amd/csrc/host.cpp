@@ -137,7 +137,7 @@ struct Cfg {
 const Cfg kConfigs[] = {
     {16, 4, 4}, {32, 4, 4}, {64, 2, 2},
     {16, 2, 2}, {32, 2, 2}, {64, 1, 1},
-    {16, 1, 1}, {32, 1, 1}, {64, 1, 1},
+    {16, 1, 1}, {32, 1, 1}, {128, 1, 1},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -156,7 +156,7 @@ int default_config(int mode, int64_t T, int64_t H, int64_t I, int64_t E, int64_t
     const int64_t bucket = bucket_of(T);
     const double rows = (double)bucket * (double)k / (double)E;   // expected rows per expert
     const double busy = rows + 3.0 * __builtin_sqrt(rows);          // typical maximum
-    const int bm = busy <= 16.0 ? 16 : (busy <= 32.0 ? 32 : 64);
+    const int bm = busy <= 16.0 ? 16 : (busy <= 32.0 ? 32 : (rows < 192.0 ? 64 : 128));
     const int64_t blocks = std::min<int64_t>(bucket * k, E) *
                            std::max<int64_t>(1, (int64_t)(rows / bm + 0.999));
     int wk = 1;
@@ -267,8 +267,8 @@ int plan_fused(const moe_fused_args_t* a, Plan* pl) {
     if (H % gran != 0 || I % gran != 0)
         return fail(MOE_ERR_UNSUPPORTED, "H = %lld and I = %lld must be multiples of %d", (long long)H,
                     (long long)I, gran);
-    GemmKernelId g1{fp4 ? 1 : 0, 1, c.bm, c.wk1, gemm_ring_steps(a->mode, H / c.wk1)};
-    GemmKernelId g2{fp4 ? 1 : 0, 2, c.bm, c.wk2, gemm_ring_steps(a->mode, I / c.wk2)};
+    GemmKernelId g1{fp4 ? 1 : 0, 1, c.bm, c.wk1, gemm_ring_steps(a->mode, c.bm, H / c.wk1)};
+    GemmKernelId g2{fp4 ? 1 : 0, 2, c.bm, c.wk2, gemm_ring_steps(a->mode, c.bm, I / c.wk2)};
     if (!gemm_supported(g1) || !gemm_supported(g2)) return fail(MOE_ERR_UNSUPPORTED, "config %d not built", ci);
     if (I % gemm_tile_n(g1) != 0 || H % gemm_tile_n(g2) != 0)
         return fail(MOE_ERR_UNSUPPORTED, "config %d: I or H not a multiple of the tile width", ci);
@@ -622,7 +622,7 @@ int moe_fused_fwd(const moe_fused_args_t* args, void* ws, size_t ws_bytes, moe_s
     g1.out_sc = fp4 ? (uint8_t*)(base + pl.off_hs) : nullptr;
     g1.n_tile_groups = 2;
     g1.max_mblocks = max_mblocks;
-    GemmKernelId k1{fp4 ? 1 : 0, 1, pl.cfg.bm, pl.cfg.wk1, gemm_ring_steps(pl.mode, pl.H / pl.cfg.wk1)};
+    GemmKernelId k1{fp4 ? 1 : 0, 1, pl.cfg.bm, pl.cfg.wk1, gemm_ring_steps(pl.mode, pl.cfg.bm, pl.H / pl.cfg.wk1)};
     if ((e = launch_gemm(k1, g1, s)) != hipSuccess) return hip_fail(e, "gemm1");
     tm.end(2);
 
@@ -652,7 +652,7 @@ int moe_fused_fwd(const moe_fused_args_t* args, void* ws, size_t ws_bytes, moe_s
     g2.out = base + pl.off_y;
     g2.n_tile_groups = 2;
     g2.max_mblocks = max_mblocks;
-    GemmKernelId k2{fp4 ? 1 : 0, 2, pl.cfg.bm, pl.cfg.wk2, gemm_ring_steps(pl.mode, pl.I / pl.cfg.wk2)};
+    GemmKernelId k2{fp4 ? 1 : 0, 2, pl.cfg.bm, pl.cfg.wk2, gemm_ring_steps(pl.mode, pl.cfg.bm, pl.I / pl.cfg.wk2)};
     if ((e = launch_gemm(k2, g2, s)) != hipSuccess) return hip_fail(e, "gemm2");
     tm.end(3);
 

@@ -186,7 +186,7 @@ struct GemmKernelId {
     int u;       // weight steps in each wave's load ring (from gemm_ring_steps)
 };
 // Ring depth for a wave's share of K.
-int gemm_ring_steps(int mode, int64_t k_per_wave);
+int gemm_ring_steps(int mode, int bm, int64_t k_per_wave);
 // Output columns one workgroup covers.
 int gemm_tile_n(const GemmKernelId& id);
 // Smallest unit of K a wave's share must be a multiple of.
