@@ -46,9 +46,8 @@ struct Frag<0> {          // bf16: 8 values per lane per step
     bf16x8_t v;
 };
 template <>
-struct Frag<1> {          // fp4: 32 codes (16 bytes) per lane per step + one scale byte
+struct Frag<1> {          // fp4: 32 codes (16 bytes) per lane per step
     i32x4_t v;
-    int sc;
 };
 
 __device__ __forceinline__ float silu_mul(float g, float u) {
@@ -59,21 +58,24 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
 }
 
 // Occupancy target per SIMD: the weight stream needs as many waves in flight
-// as the register file allows, so the allocation is capped (4 waves for 16
-// rows, 3 for 32, 2 for 64 and 128).
-template <int MODE, int BM, int WK>
+// as the register file allows, so the allocation is capped (bf16: 4 waves
+// for 16 rows, 3 for 32, 2 for 64 and 128; MXFP4, whose ring also carries
+// scale windows: 3 for 16 rows, else 2).
+template <int MODE, int BM, int WK, int NB>
 constexpr int waves_per_simd() {
-    return BM <= 16 ? ((MODE == 1 || WK == 1) ? 4 : 3) : (BM <= 32 ? 3 : 2);
+    if (MODE == 1) return BM <= 16 ? 3 : 2;
+    return NB == 2 ? (BM <= 32 ? 4 : 3) : (BM <= 16 ? (WK == 1 ? 4 : 3) : (BM <= 32 ? 3 : 2));
 }
 
-template <int MODE, int STAGE, int BM, int WK, int U>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_per_simd<MODE, BM, WK>(), 8)))
+template <int MODE, int STAGE, int BM, int WK, int U, int NB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_per_simd<MODE, BM, WK, NB>(), 8)))
 void gemm_stream(GemmParams p) {
+    static_assert(NB == 2 || NB == 4, "a wave owns 2 or 4 column blocks of 16");
+    static_assert(MODE == 0 || STAGE == 2 || NB == 4, "MXFP4 h quantisation needs 32 h columns per wave");
     constexpr int MB = BM / 16;
-    constexpr int NB = 4;
     constexpr int WN = 4 / WK;
     constexpr int KSTEP = MODE == 0 ? 32 : 128;
-    constexpr int WCOLS = STAGE == 1 ? 32 : 64;
+    constexpr int WCOLS = STAGE == 1 ? NB * 8 : NB * 16;
     constexpr int TILE_N = WN * WCOLS;
     // 1 KB A fragments per LDS buffer: room for a chunk of at least 2U steps
     constexpr int FRAGS = (U * WK * MB > 16) ? U * WK * MB : 16;
@@ -114,6 +116,9 @@ void gemm_stream(GemmParams p) {
     for (int mi = 0; mi < MB; ++mi) {
         const int row = row0 + mi * 16 + r16;
         int64_t arow = row;
+        // a padding row of stage 2 re-reads the block's first row (a cache
+        // hit) instead of streaming an h row nobody wrote
+        if (STAGE == 2 && p.sorted[row] >= p.A) arow = row0;
         if (STAGE == 1) {
             const int a = p.sorted[row];
             arow = a < p.A ? (int64_t)((unsigned)a / (unsigned)p.k) : 0;
@@ -130,8 +135,8 @@ void gemm_stream(GemmParams p) {
     const uint8_t* b_sc[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-        const bool second = STAGE == 1 && nb >= 2;
-        const int wrow = STAGE == 1 ? n0 + (nb & 1) * 16 + r16 : n0 + nb * 16 + r16;
+        const bool second = STAGE == 1 && nb >= NB / 2;
+        const int wrow = STAGE == 1 ? n0 + (nb % (NB / 2)) * 16 + r16 : n0 + nb * 16 + r16;
         const char* base = reinterpret_cast<const char*>(second ? p.b1 : p.b0);
         const int64_t se = second ? p.b1_e : p.b0_e;
         const int64_t sr = second ? p.b1_r : p.b0_r;
@@ -192,7 +197,13 @@ void gemm_stream(GemmParams p) {
     // after its MFMAs consume it, it is refilled with step s+u+U, so U-1
     // steps of weight loads are always in flight.
     Frag<MODE> fb[U][NB];
-    int fasc[U][MB];
+    // MXFP4 scales: per ring round, one window of 4*U bytes per row (all four
+    // k-groups of the U steps) in one load per row; byte 4u+kg of the window is
+    // this lane's scale for step u. The next round's window loads with the
+    // round's first refill.
+    // After a window lands, byte u of the packed word is this lane's scale for
+    // step u of the round.
+    uint32_t bsc[NB], asc[MB], bsc_n[NB][U], asc_n[MB][U];
     f32x4_t acc[MB][NB];
 #pragma unroll
     for (int mi = 0; mi < MB; ++mi)
@@ -207,12 +218,40 @@ void gemm_stream(GemmParams p) {
             using V = decltype(fb[slot][nb].v);
             fb[slot][nb].v = *reinterpret_cast<const V*>(b_ptr[nb] + off);
         }
+    };
+    using SW = typename std::conditional<U == 4, i32x4_t, int __attribute__((ext_vector_type(2)))>::type;
+    auto pack_scales = [&]() {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            uint32_t v = 0;
+#pragma unroll
+            for (int u = 0; u < U; ++u) v |= ((bsc_n[nb][u] >> (8 * kg)) & 0xffu) << (8 * u);
+            bsc[nb] = v;
+        }
+#pragma unroll
+        for (int mi = 0; mi < MB; ++mi) {
+            uint32_t v = 0;
+#pragma unroll
+            for (int u = 0; u < U; ++u) v |= ((asc_n[mi][u] >> (8 * kg)) & 0xffu) << (8 * u);
+            asc[mi] = v;
+        }
+    };
+    auto load_scales = [&](uint32_t (&bdst)[NB][U], uint32_t (&adst)[MB][U], int s0) {
         if constexpr (MODE == 1) {
-            const int si = (wk * kw + st * KSTEP) / 32 + kg;
+            s0 = s0 < steps - U ? s0 : steps - U;
+            const int kb0 = (wk * kw + s0 * KSTEP) / 32;     // a multiple of 4*U
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) fb[slot][nb].sc = b_sc[nb][si];
+            for (int nb = 0; nb < NB; ++nb) {
+                const SW v = *reinterpret_cast<const SW*>(b_sc[nb] + kb0);
 #pragma unroll
-            for (int mi = 0; mi < MB; ++mi) fasc[slot][mi] = a_sc[mi][si];
+                for (int u = 0; u < U; ++u) bdst[nb][u] = (uint32_t)v[u];
+            }
+#pragma unroll
+            for (int mi = 0; mi < MB; ++mi) {
+                const SW v = *reinterpret_cast<const SW*>(a_sc[mi] + kb0);
+#pragma unroll
+                for (int u = 0; u < U; ++u) adst[mi][u] = (uint32_t)v[u];
+            }
         }
     };
     auto compute = [&](int slot, const char* abuf, int sl) {
@@ -230,7 +269,8 @@ void gemm_stream(GemmParams p) {
                     const i32x8_t a8 = {araw[0], araw[1], araw[2], araw[3], 0, 0, 0, 0};
                     const i32x8_t b8 = {bv[0], bv[1], bv[2], bv[3], 0, 0, 0, 0};
                     acc[mi][nb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        a8, b8, acc[mi][nb], 4, 4, 0, fasc[slot][mi], 0, fb[slot][nb].sc);
+                        a8, b8, acc[mi][nb], 4, 4, 0, (int)(asc[mi] >> (8 * slot)), 0,
+                        (int)(bsc[nb] >> (8 * slot)));
                 }
             }
         }
@@ -243,8 +283,10 @@ void gemm_stream(GemmParams p) {
             compute(u, abuf, s0 + u - ac * cs);
             __builtin_amdgcn_sched_barrier(0);
             load_B(u, s0 + u + U);
+            if (u == 0) load_scales(bsc_n, asc_n, s0 + U);
             __builtin_amdgcn_sched_barrier(0);
         }
+        if constexpr (MODE == 1) pack_scales();
     };
     // LDS-only workgroup barrier: waits for this wave's LDS writes, not for
     // the weight loads in flight
@@ -258,6 +300,8 @@ void gemm_stream(GemmParams p) {
 
 #pragma unroll
     for (int u = 0; u < U; ++u) load_B(u, u);
+    load_scales(bsc_n, asc_n, 0);
+    if constexpr (MODE == 1) pack_scales();
     load_A(0);
     store_A(0);
     for (int ac = 0; ac < nac; ++ac) {
@@ -307,10 +351,10 @@ void gemm_stream(GemmParams p) {
     if constexpr (STAGE == 1 && MODE == 0) {
         uint16_t* h = reinterpret_cast<uint16_t*>(p.out);
 #pragma unroll
-        for (int unit = 0; unit < MB * 2; ++unit) {
+        for (int unit = 0; unit < MB * (NB / 2); ++unit) {
             if (unit % WK != wk) continue;
-            const int mi = unit / 2, np = unit % 2;
-            const f32x4_t g = tile(mi, np), u = tile(mi, np + 2);
+            const int mi = unit / (NB / 2), np = unit % (NB / 2);
+            const f32x4_t g = tile(mi, np), u = tile(mi, np + NB / 2);
             const int col = n0 + np * 16 + r16;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -364,9 +408,9 @@ void gemm_stream(GemmParams p) {
 
 typedef void (*GemmFn)(GemmParams);
 
-template <int MODE, int STAGE, int BM, int WK, int U>
+template <int MODE, int STAGE, int BM, int WK, int U, int NB = 4>
 constexpr GemmFn pick() {
-    return gemm_stream<MODE, STAGE, BM, WK, U>;
+    return gemm_stream<MODE, STAGE, BM, WK, U, NB>;
 }
 
 template <int MODE, int STAGE, int U>
@@ -381,10 +425,18 @@ GemmFn table(int bm, int wk) {
 }
 
 template <int MODE, int STAGE>
-GemmFn table_u(int bm, int wk, int u) {
-    if (bm == 128 && wk == 1) {
-        return u == 2 ? pick<MODE, STAGE, 128, 1, 2>() : nullptr;
+GemmFn table_u(int bm, int wk, int u, int nb) {
+    if constexpr (MODE == 0) {
+        // narrow waves (2 column blocks, a ring of 8) for the weight stream
+        if (nb == 2) {
+            if (wk != 1 || u != 8) return nullptr;
+            if (bm == 32) return pick<MODE, STAGE, 32, 1, 8, 2>();
+            if (bm == 64) return pick<MODE, STAGE, 64, 1, 8, 2>();
+            return nullptr;
+        }
     }
+    if (nb != 4) return nullptr;
+    if (bm == 128 && wk == 1) return u == 2 ? pick<MODE, STAGE, 128, 1, 2>() : nullptr;
     if (u == 4) return table<MODE, STAGE, 4>(bm, wk);
     if constexpr (MODE == 1) {
         if (u == 2) return table<MODE, STAGE, 2>(bm, wk);
@@ -394,26 +446,31 @@ GemmFn table_u(int bm, int wk, int u) {
 
 // The weight ring holds 4 steps (bf16: 32 k each; MXFP4: 128 k each, where a
 // wave's share of K allows it, else 2); with 128 rows the accumulators leave
-// room for 2.
+// room for 2; narrow bf16 waves hold 8.
 GemmFn lookup(const GemmKernelId& id) {
-    if (id.mode == 0) return id.stage == 1 ? table_u<0, 1>(id.bm, id.wk, id.u) : table_u<0, 2>(id.bm, id.wk, id.u);
-    if (id.mode == 1) return id.stage == 1 ? table_u<1, 1>(id.bm, id.wk, id.u) : table_u<1, 2>(id.bm, id.wk, id.u);
+    if (id.mode == 0)
+        return id.stage == 1 ? table_u<0, 1>(id.bm, id.wk, id.u, id.nb) : table_u<0, 2>(id.bm, id.wk, id.u, id.nb);
+    if (id.mode == 1)
+        return id.stage == 1 ? table_u<1, 1>(id.bm, id.wk, id.u, id.nb) : table_u<1, 2>(id.bm, id.wk, id.u, id.nb);
     return nullptr;
 }
 
 }  // namespace
 
-int gemm_ring_steps(int mode, int bm, int64_t k_per_wave) {
+int gemm_ring_steps(int mode, int bm, int nb, int64_t k_per_wave) {
+    if (mode == 0 && nb == 2) return 8;
     if (bm >= 128) return 2;
     if (mode == 0) return 4;
     return k_per_wave % (128 * 4) == 0 ? 4 : 2;
 }
 
-int gemm_k_granule(const GemmKernelId& id) { return id.mode == 0 ? 32 * 4 : 128 * 2; }
+int gemm_k_granule(const GemmKernelId& id) {
+    return id.mode == 0 ? 32 * (id.nb == 2 ? 8 : 4) : 128 * 2;
+}
 
 int gemm_tile_n(const GemmKernelId& id) {
     const int wn = 4 / id.wk;
-    return wn * (id.stage == 1 ? 32 : 64);
+    return wn * (id.stage == 1 ? id.nb * 8 : id.nb * 16);
 }
 
 bool gemm_supported(const GemmKernelId& id) { return lookup(id) != nullptr; }

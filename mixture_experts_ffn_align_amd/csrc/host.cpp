@@ -132,12 +132,13 @@ bool valid_bm(int bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128 || 
 // depends only on (mode, T, H, I, E, k), never on strides or addresses, so
 // strided and contiguous calls execute the same arithmetic.
 struct Cfg {
-    int bm, wk1, wk2;
+    int bm, wk1, wk2, nb;
 };
 const Cfg kConfigs[] = {
-    {16, 4, 4}, {32, 4, 4}, {64, 2, 2},
-    {16, 2, 2}, {32, 2, 2}, {64, 1, 1},
-    {16, 1, 1}, {32, 1, 1}, {128, 1, 1},
+    {16, 4, 4, 4}, {32, 4, 4, 4}, {64, 2, 2, 4},
+    {16, 2, 2, 4}, {32, 2, 2, 4}, {64, 1, 1, 4},
+    {16, 1, 1, 4}, {32, 1, 1, 4}, {128, 1, 1, 4},
+    {32, 1, 1, 2}, {64, 1, 1, 2},    // bf16 only: narrow waves, deep weight ring
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -151,18 +152,21 @@ int bucket_of(int64_t T) {
 // each expert's weights stream from HBM once); the K split grows only while
 // the grid would not fill the chip.
 int default_config(int mode, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k) {
-    (void)mode;
     (void)H;
     const int64_t bucket = bucket_of(T);
     const double rows = (double)bucket * (double)k / (double)E;   // expected rows per expert
     const double busy = rows + 3.0 * __builtin_sqrt(rows);          // typical maximum
-    const int bm = busy <= 16.0 ? 16 : (busy <= 32.0 ? 32 : (rows < 192.0 ? 64 : 128));
+    int bm;
+    if (mode == MOE_MODE_MXFP4)    // the fp4 stream prefers short blocks; 128 rows spill
+        bm = busy <= 32.0 ? 16 : 64;
+    else
+        bm = busy <= 16.0 ? 16 : (busy <= 32.0 ? 32 : (rows < 192.0 ? 64 : 128));
     const int64_t blocks = std::min<int64_t>(bucket * k, E) *
                            std::max<int64_t>(1, (int64_t)(rows / bm + 0.999));
     int wk = 1;
     while (wk < 4 && (bm < 64 || wk < 2) && blocks * (I / (32 * (4 / wk))) < 1024) wk <<= 1;
     for (int c = 0; c < kNumConfigs; ++c)
-        if (kConfigs[c].bm == bm && kConfigs[c].wk1 == wk) return c;
+        if (kConfigs[c].bm == bm && kConfigs[c].wk1 == wk && kConfigs[c].nb == 4) return c;
     return 0;
 }
 
@@ -238,10 +242,18 @@ int plan_fused(const moe_fused_args_t* a, Plan* pl) {
             return fail(MOE_ERR_LAYOUT, "%s: rows and experts must start on 16-byte boundaries", wn[i]);
     }
     if (fp4) {
+        // each lane reads a window of 4 * ring-steps scale bytes per row at once
         const moe_tensor_t* ss[3] = {&a->gate_scale, &a->up_scale, &a->w2_scale};
         const char* sn[3] = {"gate_scale", "up_scale", "w2_scale"};
-        for (int i = 0; i < 3; ++i)
-            if (ss[i]->stride[2] != 1) return fail(MOE_ERR_LAYOUT, "%s: last-dim stride must be 1", sn[i]);
+        for (int i = 0; i < 3; ++i) {
+            const moe_tensor_t& t = *ss[i];
+            const int64_t K = t.size[2] * 32;
+            const int64_t al = (K % 512 == 0) ? 16 : 8;
+            if (t.stride[2] != 1) return fail(MOE_ERR_LAYOUT, "%s: last-dim stride must be 1", sn[i]);
+            if (((uintptr_t)t.data % al) != 0 || (t.stride[1] % al) != 0 || (t.stride[0] % al) != 0)
+                return fail(MOE_ERR_LAYOUT, "%s: rows and experts must start on %lld-byte boundaries", sn[i],
+                            (long long)al);
+        }
     }
     // outputs must not alias inputs
     const moe_tensor_t* ins[6] = {&a->x, &a->gate, &a->up, &a->w2, &a->topk_ids, &a->topk_weights};
@@ -257,18 +269,18 @@ int plan_fused(const moe_fused_args_t* a, Plan* pl) {
     // is a whole number of pipelined chunks
     auto fit = [&](int pref, int stage, int64_t K) {
         int w = pref;
-        while (w > 1 && K % ((int64_t)gemm_k_granule(GemmKernelId{fp4 ? 1 : 0, stage, c.bm, w, 0}) * w) != 0)
+        while (w > 1 && K % ((int64_t)gemm_k_granule(GemmKernelId{fp4 ? 1 : 0, stage, c.bm, w, 0, c.nb}) * w) != 0)
             w >>= 1;
         return w;
     };
     c.wk1 = fit(c.wk1, 1, H);
     c.wk2 = fit(c.wk2, 2, I);
-    const int gran = gemm_k_granule(GemmKernelId{fp4 ? 1 : 0, 1, c.bm, 1, 0});
+    const int gran = gemm_k_granule(GemmKernelId{fp4 ? 1 : 0, 1, c.bm, 1, 0, c.nb});
     if (H % gran != 0 || I % gran != 0)
         return fail(MOE_ERR_UNSUPPORTED, "H = %lld and I = %lld must be multiples of %d", (long long)H,
                     (long long)I, gran);
-    GemmKernelId g1{fp4 ? 1 : 0, 1, c.bm, c.wk1, gemm_ring_steps(a->mode, c.bm, H / c.wk1)};
-    GemmKernelId g2{fp4 ? 1 : 0, 2, c.bm, c.wk2, gemm_ring_steps(a->mode, c.bm, I / c.wk2)};
+    GemmKernelId g1{fp4 ? 1 : 0, 1, c.bm, c.wk1, gemm_ring_steps(a->mode, c.bm, c.nb, H / c.wk1), c.nb};
+    GemmKernelId g2{fp4 ? 1 : 0, 2, c.bm, c.wk2, gemm_ring_steps(a->mode, c.bm, c.nb, I / c.wk2), c.nb};
     if (!gemm_supported(g1) || !gemm_supported(g2)) return fail(MOE_ERR_UNSUPPORTED, "config %d not built", ci);
     if (I % gemm_tile_n(g1) != 0 || H % gemm_tile_n(g2) != 0)
         return fail(MOE_ERR_UNSUPPORTED, "config %d: I or H not a multiple of the tile width", ci);
@@ -622,7 +634,8 @@ int moe_fused_fwd(const moe_fused_args_t* args, void* ws, size_t ws_bytes, moe_s
     g1.out_sc = fp4 ? (uint8_t*)(base + pl.off_hs) : nullptr;
     g1.n_tile_groups = 2;
     g1.max_mblocks = max_mblocks;
-    GemmKernelId k1{fp4 ? 1 : 0, 1, pl.cfg.bm, pl.cfg.wk1, gemm_ring_steps(pl.mode, pl.cfg.bm, pl.H / pl.cfg.wk1)};
+    GemmKernelId k1{fp4 ? 1 : 0, 1, pl.cfg.bm, pl.cfg.wk1,
+                    gemm_ring_steps(pl.mode, pl.cfg.bm, pl.cfg.nb, pl.H / pl.cfg.wk1), pl.cfg.nb};
     if ((e = launch_gemm(k1, g1, s)) != hipSuccess) return hip_fail(e, "gemm1");
     tm.end(2);
 
@@ -652,7 +665,8 @@ int moe_fused_fwd(const moe_fused_args_t* args, void* ws, size_t ws_bytes, moe_s
     g2.out = base + pl.off_y;
     g2.n_tile_groups = 2;
     g2.max_mblocks = max_mblocks;
-    GemmKernelId k2{fp4 ? 1 : 0, 2, pl.cfg.bm, pl.cfg.wk2, gemm_ring_steps(pl.mode, pl.cfg.bm, pl.I / pl.cfg.wk2)};
+    GemmKernelId k2{fp4 ? 1 : 0, 2, pl.cfg.bm, pl.cfg.wk2,
+                    gemm_ring_steps(pl.mode, pl.cfg.bm, pl.cfg.nb, pl.I / pl.cfg.wk2), pl.cfg.nb};
     if ((e = launch_gemm(k2, g2, s)) != hipSuccess) return hip_fail(e, "gemm2");
     tm.end(3);
 

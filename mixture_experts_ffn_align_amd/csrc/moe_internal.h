@@ -184,9 +184,10 @@ struct GemmKernelId {
     int bm;      // 16, 32, 64
     int wk;      // waves splitting K: 1, 2 or 4
     int u;       // weight steps in each wave's load ring (from gemm_ring_steps)
+    int nb;      // 16-column MFMA blocks per wave: 4, or 2 (bf16 weight stream)
 };
 // Ring depth for a wave's share of K.
-int gemm_ring_steps(int mode, int bm, int64_t k_per_wave);
+int gemm_ring_steps(int mode, int bm, int nb, int64_t k_per_wave);
 // Output columns one workgroup covers.
 int gemm_tile_n(const GemmKernelId& id);
 // Smallest unit of K a wave's share must be a multiple of.

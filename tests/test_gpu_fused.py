@@ -70,9 +70,13 @@ def test_tiny_bf16_tile_configs():
     outs = {}
     info = moe.moe_query_config(inp["x"], *W.packed_views(inp["w13"], 128), inp["w2"], *gpu)
     for c in range(info["num_configs"]):
-        outs[c] = _fused_bf16(inp, *gpu, force_config=c).clone()
+        try:
+            outs[c] = _fused_bf16(inp, *gpu, force_config=c).clone()
+        except moe.MoEError as err:          # a config this shape cannot use
+            assert err.status == -6, err
+    assert len(outs) >= 6
     groups = {}
-    for c in range(info["num_configs"]):
+    for c in outs:
         _check_bf16(inp, outs[c], *orc, np.arange(64))
         q = moe.moe_query_config(inp["x"], *W.packed_views(inp["w13"], 128), inp["w2"], *gpu,
                                  force_config=c)
