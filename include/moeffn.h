@@ -195,8 +195,9 @@ typedef struct {
 typedef struct {
     int32_t bucket;        /* smallest power of two >= T, capped at 32768 */
     int32_t block_m;       /* rows per sorted block */
-    int32_t gemm1_kernel;  /* kernel family id of gemm1 */
-    int32_t gemm2_kernel;  /* kernel family id of gemm2 */
+    int32_t gemm1_kernel;  /* kernel family of gemm1: 1 bf16 weight-streaming, 3 bf16 LDS-tiled,
+                              11 and 13 the same two in MXFP4 mode */
+    int32_t gemm2_kernel;  /* kernel family of gemm2: gemm1's plus one */
     int32_t gemm1_split_k; /* waves splitting K inside a workgroup */
     int32_t gemm2_split_k;
     int32_t config_index;  /* index into the library's config list */

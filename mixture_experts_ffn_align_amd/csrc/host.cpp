@@ -133,12 +133,14 @@ bool valid_bm(int bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128 || 
 // strided and contiguous calls execute the same arithmetic.
 struct Cfg {
     int bm, wk1, wk2, nb;
+    int tile;    // 0: weight-streaming GEMMs; 1 + shape: LDS-tiled GEMMs of that tile shape
 };
 const Cfg kConfigs[] = {
-    {16, 4, 4, 4}, {32, 4, 4, 4}, {64, 2, 2, 4},
-    {16, 2, 2, 4}, {32, 2, 2, 4}, {64, 1, 1, 4},
-    {16, 1, 1, 4}, {32, 1, 1, 4}, {128, 1, 1, 4},
-    {32, 1, 1, 2}, {64, 1, 1, 2},    // bf16 only: narrow waves, deep weight ring
+    {16, 4, 4, 4, 0}, {32, 4, 4, 4, 0}, {64, 2, 2, 4, 0},
+    {16, 2, 2, 4, 0}, {32, 2, 2, 4, 0}, {64, 1, 1, 4, 0},
+    {16, 1, 1, 4, 0}, {32, 1, 1, 4, 0}, {128, 1, 1, 4, 0},
+    {32, 1, 1, 2, 0}, {64, 1, 1, 2, 0},    // bf16 only: narrow waves, deep weight ring
+    {256, 1, 1, 4, 1}, {128, 1, 1, 4, 2},   // many rows per expert: weight reuse
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -152,10 +154,21 @@ int bucket_of(int64_t T) {
 // each expert's weights stream from HBM once); the K split grows only while
 // the grid would not fill the chip.
 int default_config(int mode, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k) {
-    (void)H;
     const int64_t bucket = bucket_of(T);
     const double rows = (double)bucket * (double)k / (double)E;   // expected rows per expert
     const double busy = rows + 3.0 * __builtin_sqrt(rows);          // typical maximum
+    // enough rows per expert to reuse each weight tile several times: tiled
+    const int md = mode == MOE_MODE_MXFP4 ? 1 : 0;
+    if (rows >= 192.0)
+        for (int c = 0; c < kNumConfigs; ++c) {
+            const int shape = kConfigs[c].tile - 1;
+            if (shape < 0 || !gemm_tile_supported(md, shape)) continue;
+            if (md == 0 && shape != 1) continue;   // bf16: 128 x 512 tiles measured fastest
+            const int gran = gemm_tile_k_granule(md);
+            if (H % gran == 0 && I % gran == 0 && I % gemm_tile_cols(shape, 1) == 0 &&
+                H % gemm_tile_cols(shape, 2) == 0)
+                return c;
+        }
     int bm;
     if (mode == MOE_MODE_MXFP4)    // the fp4 stream prefers short blocks; 128 rows spill
         bm = busy <= 32.0 ? 16 : 64;
@@ -273,17 +286,31 @@ int plan_fused(const moe_fused_args_t* a, Plan* pl) {
             w >>= 1;
         return w;
     };
-    c.wk1 = fit(c.wk1, 1, H);
-    c.wk2 = fit(c.wk2, 2, I);
-    const int gran = gemm_k_granule(GemmKernelId{fp4 ? 1 : 0, 1, c.bm, 1, 0, c.nb});
-    if (H % gran != 0 || I % gran != 0)
-        return fail(MOE_ERR_UNSUPPORTED, "H = %lld and I = %lld must be multiples of %d", (long long)H,
-                    (long long)I, gran);
-    GemmKernelId g1{fp4 ? 1 : 0, 1, c.bm, c.wk1, gemm_ring_steps(a->mode, c.bm, c.nb, H / c.wk1), c.nb};
-    GemmKernelId g2{fp4 ? 1 : 0, 2, c.bm, c.wk2, gemm_ring_steps(a->mode, c.bm, c.nb, I / c.wk2), c.nb};
-    if (!gemm_supported(g1) || !gemm_supported(g2)) return fail(MOE_ERR_UNSUPPORTED, "config %d not built", ci);
-    if (I % gemm_tile_n(g1) != 0 || H % gemm_tile_n(g2) != 0)
-        return fail(MOE_ERR_UNSUPPORTED, "config %d: I or H not a multiple of the tile width", ci);
+    if (c.tile) {
+        const int shape = c.tile - 1, md = fp4 ? 1 : 0;
+        const int gran = gemm_tile_k_granule(md);
+        if (!gemm_tile_supported(md, shape))
+            return fail(MOE_ERR_UNSUPPORTED, "config %d: tile shape not built for this mode", ci);
+        c.bm = gemm_tile_rows(md, shape);
+        if (H % gran != 0 || I % gran != 0 || I % gemm_tile_cols(shape, 1) != 0 ||
+            H % gemm_tile_cols(shape, 2) != 0)
+            return fail(MOE_ERR_UNSUPPORTED,
+                        "config %d: H = %lld and I = %lld must be multiples of %d, I of %d and H of %d", ci,
+                        (long long)H, (long long)I, gran, gemm_tile_cols(shape, 1), gemm_tile_cols(shape, 2));
+    } else {
+        c.wk1 = fit(c.wk1, 1, H);
+        c.wk2 = fit(c.wk2, 2, I);
+        const int gran = gemm_k_granule(GemmKernelId{fp4 ? 1 : 0, 1, c.bm, 1, 0, c.nb});
+        if (H % gran != 0 || I % gran != 0)
+            return fail(MOE_ERR_UNSUPPORTED, "H = %lld and I = %lld must be multiples of %d", (long long)H,
+                        (long long)I, gran);
+        GemmKernelId g1{fp4 ? 1 : 0, 1, c.bm, c.wk1, gemm_ring_steps(a->mode, c.bm, c.nb, H / c.wk1), c.nb};
+        GemmKernelId g2{fp4 ? 1 : 0, 2, c.bm, c.wk2, gemm_ring_steps(a->mode, c.bm, c.nb, I / c.wk2), c.nb};
+        if (!gemm_supported(g1) || !gemm_supported(g2))
+            return fail(MOE_ERR_UNSUPPORTED, "config %d not built", ci);
+        if (I % gemm_tile_n(g1) != 0 || H % gemm_tile_n(g2) != 0)
+            return fail(MOE_ERR_UNSUPPORTED, "config %d: I or H not a multiple of the tile width", ci);
+    }
 
     pl->mode = a->mode;
     pl->T = T;
@@ -298,6 +325,15 @@ int plan_fused(const moe_fused_args_t* a, Plan* pl) {
     const bool x_direct = a->x.stride[1] == 1 && aligned16(a->x.data) &&
                           (T <= 1 || (a->x.stride[0] * 2) % 16 == 0);
     pl->pack_x = !fp4 && !x_direct;
+    if (c.tile) {
+        // the tiled kernels address every operand row with a 32-bit offset
+        const int64_t eb = fp4 ? 1 : 2;
+        const int64_t x_row = fp4 ? H / 2 : (pl->pack_x ? H * 2 : a->x.stride[0] * 2);
+        const int64_t lim = (int64_t)1 << 31;
+        if (T * x_row >= lim || pl->cap * I * eb >= lim || I * a->gate.stride[1] * eb >= lim ||
+            I * a->up.stride[1] * eb >= lim || H * a->w2.stride[1] * eb >= lim)
+            return fail(MOE_ERR_UNSUPPORTED, "config %d: operands too large for the tiled kernels", ci);
+    }
 
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -514,8 +550,9 @@ int moe_query_config(const moe_fused_args_t* args, moe_config_t* cfg) {
     if (rc) return rc;
     cfg->bucket = bucket_of(pl.T);
     cfg->block_m = pl.cfg.bm;
-    cfg->gemm1_kernel = args->mode == MOE_MODE_MXFP4 ? 11 : 1;
-    cfg->gemm2_kernel = args->mode == MOE_MODE_MXFP4 ? 12 : 2;
+    const int fam = (args->mode == MOE_MODE_MXFP4 ? 10 : 0) + (pl.cfg.tile ? 2 : 0);
+    cfg->gemm1_kernel = fam + 1;
+    cfg->gemm2_kernel = fam + 2;
     cfg->gemm1_split_k = pl.cfg.wk1;
     cfg->gemm2_split_k = pl.cfg.wk2;
     cfg->config_index = pl.cfg_index;
@@ -634,9 +671,14 @@ int moe_fused_fwd(const moe_fused_args_t* args, void* ws, size_t ws_bytes, moe_s
     g1.out_sc = fp4 ? (uint8_t*)(base + pl.off_hs) : nullptr;
     g1.n_tile_groups = 2;
     g1.max_mblocks = max_mblocks;
-    GemmKernelId k1{fp4 ? 1 : 0, 1, pl.cfg.bm, pl.cfg.wk1,
-                    gemm_ring_steps(pl.mode, pl.cfg.bm, pl.cfg.nb, pl.H / pl.cfg.wk1), pl.cfg.nb};
-    if ((e = launch_gemm(k1, g1, s)) != hipSuccess) return hip_fail(e, "gemm1");
+    if (pl.cfg.tile) {
+        e = launch_gemm_tile(fp4 ? 1 : 0, pl.cfg.tile - 1, 1, g1, s);
+    } else {
+        GemmKernelId k1{fp4 ? 1 : 0, 1, pl.cfg.bm, pl.cfg.wk1,
+                        gemm_ring_steps(pl.mode, pl.cfg.bm, pl.cfg.nb, pl.H / pl.cfg.wk1), pl.cfg.nb};
+        e = launch_gemm(k1, g1, s);
+    }
+    if (e != hipSuccess) return hip_fail(e, "gemm1");
     tm.end(2);
 
     // stage 3: gemm2
@@ -665,9 +707,14 @@ int moe_fused_fwd(const moe_fused_args_t* args, void* ws, size_t ws_bytes, moe_s
     g2.out = base + pl.off_y;
     g2.n_tile_groups = 2;
     g2.max_mblocks = max_mblocks;
-    GemmKernelId k2{fp4 ? 1 : 0, 2, pl.cfg.bm, pl.cfg.wk2,
-                    gemm_ring_steps(pl.mode, pl.cfg.bm, pl.cfg.nb, pl.I / pl.cfg.wk2), pl.cfg.nb};
-    if ((e = launch_gemm(k2, g2, s)) != hipSuccess) return hip_fail(e, "gemm2");
+    if (pl.cfg.tile) {
+        e = launch_gemm_tile(fp4 ? 1 : 0, pl.cfg.tile - 1, 2, g2, s);
+    } else {
+        GemmKernelId k2{fp4 ? 1 : 0, 2, pl.cfg.bm, pl.cfg.wk2,
+                        gemm_ring_steps(pl.mode, pl.cfg.bm, pl.cfg.nb, pl.I / pl.cfg.wk2), pl.cfg.nb};
+        e = launch_gemm(k2, g2, s);
+    }
+    if (e != hipSuccess) return hip_fail(e, "gemm2");
     tm.end(3);
 
     // stage 4: combine

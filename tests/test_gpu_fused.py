@@ -172,6 +172,63 @@ def test_mxfp4_tp2_shard(fp4_weights, shape, T):
     assert r <= FP4_TOL and er <= FP4_ERR_RATIO
 
 
+def _configs_by_family(query):
+    """config index of each GEMM kernel family the library lists"""
+    n = query(-1)["num_configs"]
+    fam = {}
+    for c in range(n):
+        try:
+            q = query(c)
+        except moe.MoEError as err:
+            assert err.status == -6, err
+            continue
+        fam.setdefault((q["gemm1_kernel"], q["gemm1_split_k"], q["gemm2_split_k"]), []).append(c)
+    return fam
+
+
+def test_tiled_and_streaming_gemms_same_bits_bf16(w235):
+    """Both GEMM families sum K in the same order: identical outputs."""
+    inp = W.make_inputs(W.QWEN3_235B_BF16, 4096, seed=3, device=DEV, weights=w235)
+    gpu, orc = route_both(inp)
+    gate, up = W.packed_views(inp["w13"], 1536)
+    fam = _configs_by_family(lambda c: moe.moe_query_config(inp["x"], gate, up, inp["w2"], *gpu,
+                                                            force_config=c))
+    assert len(fam[(3, 1, 1)]) == 2          # every tile shape
+    assert moe.moe_query_config(inp["x"], gate, up, inp["w2"], *gpu)["gemm1_kernel"] == 3
+    out_s = _fused_bf16(inp, *gpu, force_config=fam[(1, 1, 1)][-1]).clone()
+    for c in fam[(3, 1, 1)]:
+        out_t = _fused_bf16(inp, *gpu, force_config=c)
+        assert torch.equal(out_t, out_s), f"config {c}"
+    _check_bf16(inp, out_s, *orc, sample_tokens(4096, 6))
+
+
+@pytest.mark.parametrize("T", [64, 2048])
+def test_tiled_and_streaming_gemms_same_bits_mxfp4(fp4_weights, T):
+    shape = W.QWEN35_397B_TP2_FP4_513
+    w13, w2, ((gq, gs), (uq, us), (wq, wsc)) = fp4_weights(shape)
+    inp = W.make_inputs(shape, T, seed=5, device=DEV, weights=(w13, w2))
+    gpu, orc = route_both(inp)
+
+    def run(c):
+        return moe.moe_fused_fwd(inp["x"], gq, uq, wq, *gpu, gate_scale=gs, up_scale=us, w2_scale=wsc,
+                                 mode=moe.MODE_MXFP4, force_config=c).clone()
+
+    def query(c):
+        return moe.moe_query_config(inp["x"], gq, uq, wq, *gpu, gate_scale=gs, up_scale=us,
+                                    w2_scale=wsc, mode=moe.MODE_MXFP4, force_config=c)
+
+    fam = _configs_by_family(query)
+    out_t = run(fam[(13, 1, 1)][0])
+    for c in fam[(11, 1, 1)]:
+        assert torch.equal(run(c), out_t), f"config {c}"
+    toks = sample_tokens(T, 4)
+    oi, ow = orc
+    used = sorted({int(e) for e in oi[toks].ravel()})
+    acc, _ = oracle_ffn_tokens(inp, oi, ow, toks, mx=oracle_quant_experts(w13, w2, shape.inter, used))
+    got = bf16_to_f64(out_t[torch.from_numpy(toks).to(DEV)])
+    assert rel_l2(got, acc) <= FP4_TOL and err_ratio(got, acc) <= FP4_ERR_RATIO
+
+
 def test_nan_canaries_in_unread_memory():
     """Unused half of the packed w13, padding columns of x and the other
     layers of the routing tensors hold NaN / out-of-range values; any read of
