@@ -10,27 +10,30 @@
 // configs for Qwen3.5-397B", Details: larger block_m for the large token
 // buckets).
 //
-// A workgroup is eight wave64s (two per SIMD; four waves, one per SIMD, in
-// MXFP4 mode) and owns BM rows of one expert
-// times BW weight rows (stage 1: BW/2 gate + BW/2 up rows -> BW/2 h columns;
-// stage 2: BW output columns); each wave multiplies 64 rows by 128 weight
-// rows (4 x 8 MFMA blocks of 16 x 16, accumulators in 128 VGPRs), so one
-// k-step reads 12 fragments from LDS for 32 MFMAs. K advances in stages of
-// 128 bytes per row (64 bf16 or 256 e2m1 values), i.e. two MFMA k-steps; the
-// LDS holds two stages.
+// A workgroup of NW wave64s owns BM rows of one expert times BW weight rows
+// (stage 1: BW/2 gate + BW/2 up rows -> BW/2 h columns; stage 2: BW output
+// columns); each wave multiplies 64 rows by 128 weight rows (4 x 8 MFMA
+// blocks of 16 x 16, accumulators in 128 registers), so one k-step reads 12
+// fragments from LDS for 32 MFMAs. K advances in stages of 64 bytes per row
+// (32 bf16 or 128 e2m1 values), SUBS = 1 or 2 MFMA k-steps per stage of
+// 64 SUBS bytes per row.
 //
-// Loads. One wave instruction reads 8 rows x 128 contiguous bytes (lanes
-// 8q .. 8q+7 read row q), a whole cache line per 8 lanes: on gfx950 this
-// streams from L2 at about three times the rate of the 16 rows x 64 bytes
-// that an MFMA fragment spans. The stage goes global -> registers -> LDS, one
-// stage ahead of the one being multiplied.
+// Loads go straight from global memory to LDS (global_load_lds_dwordx4, no
+// registers, no LDS write instructions): one wave instruction fills 1 KB of
+// LDS, 8 tile rows x 128 bytes (SUBS = 2: a whole cache line per 8 lanes) or
+// 16 rows x 64 bytes (SUBS = 1: each quad of lanes reads one row's 64
+// contiguous bytes). 4 / SUBS stage buffers rotate, the loads of the stage
+// 4 / SUBS - 1 ahead are issued while a stage is multiplied, and one
+// workgroup barrier per stage publishes a landed stage and retires a consumed
+// one.
 //
-// LDS layout. Row-major, 128 bytes per tile row per stage, the 16-byte
-// chunk c of row r stored at chunk position c ^ f(r), f(r) = (r/2) ^ 4 (r%2)
-// (mod 8). An MFMA fragment (lane l: row l % 16, chunk 4 s + l / 16 for
-// k-step s of the stage) and a load instruction (8 rows x 8 chunks) then
-// both touch 8 distinct 16-byte bank groups in every 8 lanes and 16 in every
-// 16, so neither the writes nor the fragment reads conflict.
+// LDS layout. Rows are stored row-major, the 16-byte chunk c of tile row r at
+// chunk position c ^ g(r): g(r) = r / 4 (mod 4) for 64-byte rows and
+// (r / 2) ^ 4 (r % 2) (mod 8) for 128-byte rows (r mod 16). An MFMA fragment
+// (lane l: row l % 16, chunk l / 16 of its k-step) then reads 16 distinct
+// 16-byte bank groups in every 16 lanes; the loads choose which chunk each
+// lane fetches so that the lane order of the LDS write is the swizzled
+// order.
 //
 // Consecutive workgroups are kept on one XCD and cover groups of row blocks x
 // weight tiles, so the row blocks of an expert share its weight tiles through
@@ -40,26 +43,34 @@
 namespace moe {
 namespace {
 
-constexpr int kRowBytes = 128;     // bytes of one row per stage
-constexpr int kScRow = 8;          // e8m0 bytes of one row per stage
+constexpr int kBlock = 1024;       // bytes one load instruction writes
+constexpr int kScStep = 4;         // e8m0 bytes of one row per k-step
 
-constexpr int WMI = 4;             // row blocks of 16 per wave
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// BM rows x BW weight rows per workgroup of NW waves; each wave multiplies
-// 64 rows by 128 weight rows
-template <int MODE, int BM, int BW, int NW>
+// BM rows x BW weight rows per workgroup of NW waves, SUBS k-steps of
+// 64 bytes per row per stage; a wave multiplies 16 WMI rows by 128 weight
+// rows
+template <int MODE, int BM, int BW, int NW, int SUBS>
 struct TileShape {
-    static constexpr int kWaves = NW;
     static constexpr int kThreads = 64 * NW;
-    static constexpr int kWM = BM / (16 * WMI);            // waves along rows
-    static constexpr int kWN = NW / kWM;                   // waves along weight rows
-    static_assert(kWM * kWN == NW && BW == kWN * 128, "waves of 64 x 128");
+    static constexpr int kRowBytes = 64 * SUBS;
+    static constexpr int kRowsPerLoad = kBlock / kRowBytes;
+    static constexpr int kNBuf = 4 / SUBS;
+    static constexpr int kWN = BW / 128;                   // waves along weight rows
+    static constexpr int kWM = NW / kWN;                   // waves along rows
+    static constexpr int kWMI = BM / (16 * kWM);           // row blocks per wave
+    static_assert(kWM * kWN == NW && kWMI * 16 * kWM == BM && kWMI >= 1 && kWMI <= 4, "wave grid");
     static constexpr int kRows = BM + BW;
-    static constexpr int kLoads = kRows / (8 * NW);        // 8-row loads per wave per stage
-    static constexpr int kScBytes = MODE == 1 ? kRows * kScRow : 0;
-    static constexpr int kBuf = kRows * kRowBytes + kScBytes;
+    static constexpr int kLoads = kRows / (kRowsPerLoad * NW);   // 1 KB loads per wave per stage
+    static_assert(kLoads * kRowsPerLoad * NW == kRows, "whole loads");
+    // 4-byte scale loads per thread per k-step (MXFP4)
+    static constexpr int kScLoads = MODE == 1 ? (kRows + kThreads - 1) / kThreads : 0;
+    static constexpr int kScOff = kRows * kRowBytes;
+    static constexpr int kScPlane = kScLoads * kThreads * kScStep;   // one k-step's scales
+    static constexpr int kBuf = kScOff + SUBS * kScPlane;
     static constexpr int kGroupM = BM == 256 ? 4 : 8;      // row blocks per tile group
-    static constexpr int kGroupN = 32 / kGroupM;           // weight tiles per tile group
+    static constexpr int kGroupN = (NW == 8 ? 32 : 64) / kGroupM;   // weight tiles per tile group
 };
 
 __device__ __forceinline__ float silu_mul(float g, float u) {
@@ -69,30 +80,34 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
     return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
 }
 
-// byte offset of 16-byte chunk c of tile row r inside a stage buffer
-__device__ __forceinline__ int lds_chunk(int r, int c) {
-    const int f = ((r >> 1) ^ ((r & 1) << 2)) & 7;
-    return r * kRowBytes + ((c ^ f) & 7) * 16;
+// 16-byte chunk position of chunk c in tile row r (rows of 64 or 128 bytes;
+// see the LDS layout above)
+template <int CPR>
+__device__ __forceinline__ int swz_t(int r, int c) {
+    if (CPR == 4) return (c ^ (r >> 2)) & 3;
+    return (c ^ ((r >> 1) ^ ((r & 1) << 2))) & 7;
 }
 
-// Workgroup barrier that waits for this wave's LDS accesses only, not for
-// the global loads of the next stage in flight.
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt((15 << 0) | (3 << 14) | (7 << 4) | (0 << 8));   // lgkmcnt(0)
-    __builtin_amdgcn_s_barrier();
-    __asm__ volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
+// s_waitcnt vmcnt(n) lgkmcnt(0) (gfx9 encoding; expcnt not waited)
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
 }
 
-template <int MODE, int STAGE, int BM, int BW, int NW>
+template <int MODE, int STAGE, int BM, int BW, int NW, int SUBS>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void gemm_tile(GemmParams p) {
-    using TS = TileShape<MODE, BM, BW, NW>;
-    constexpr int kWaves = TS::kWaves, kThreads = TS::kThreads;
-    constexpr int kLoads = TS::kLoads, BUF = TS::kBuf;
-    constexpr int kWN = TS::kWN;
-    __shared__ __attribute__((aligned(16))) char lds[2 * BUF];
+    using TS = TileShape<MODE, BM, BW, NW, SUBS>;
+    constexpr int kLoads = TS::kLoads, kScLoads = TS::kScLoads, BUF = TS::kBuf, kWN = TS::kWN;
+    constexpr int kRowBytes = TS::kRowBytes, RPL = TS::kRowsPerLoad, WMI = TS::kWMI;
+    auto swz = [](int r, int c) { return swz_t<kRowBytes / 16>(r & 15, c); };
+    // one array per stage buffer, so the compiler sees that reading one
+    // buffer does not depend on the loads still landing in another
+    __shared__ __attribute__((aligned(16))) char lds0[BUF];
+    __shared__ __attribute__((aligned(16))) char lds1[BUF];
+    __shared__ __attribute__((aligned(16))) char lds2[SUBS == 1 ? BUF : 16];
+    __shared__ __attribute__((aligned(16))) char lds3[SUBS == 1 ? BUF : 16];
 
     const int lane = lane_id();
     const int w = threadIdx.x >> 6;
@@ -105,9 +120,9 @@ void gemm_tile(GemmParams p) {
     const uint32_t Lg = xcd_remap(blockIdx.x, gridDim.x);
     const uint32_t per_group = TS::kGroupM * TS::kGroupN;
     const uint32_t m_groups = (uint32_t)(p.max_mblocks + TS::kGroupM - 1) / TS::kGroupM;
-    const uint32_t grp = Lg / per_group, r = Lg % per_group;
-    const int mb = (int)((grp % m_groups) * TS::kGroupM + r % TS::kGroupM);
-    const int nt = (int)((grp / m_groups) * TS::kGroupN + r / TS::kGroupM);
+    const uint32_t grp = Lg / per_group, rr = Lg % per_group;
+    const int mb = (int)((grp % m_groups) * TS::kGroupM + rr % TS::kGroupM);
+    const int nt = (int)((grp / m_groups) * TS::kGroupN + rr / TS::kGroupM);
     if (nt >= n_tiles || mb >= p.max_mblocks) return;
     const int n_blocks = *p.n_padded / BM;
     if (mb >= n_blocks) return;
@@ -115,10 +130,6 @@ void gemm_tile(GemmParams p) {
     const int row0 = mb * BM;
     const int n0 = nt * tile_cols;
 
-    // ---- source rows: load i of wave w covers tile rows 8 (w + 8 i) .. +8;
-    // this lane reads row 8 (w + 4 i) + lane / 8, bytes 16 (lane % 8) .. +16
-    // of the stage. Tile rows [0, BM) are A rows, [BM, BM + BW) weight rows.
-    const int lrow = lane >> 3, lchunk = lane & 7;
     auto a_row_of = [&](int row) -> int64_t {
         if (STAGE == 1) {
             const int a = p.sorted[row];
@@ -129,89 +140,85 @@ void gemm_tile(GemmParams p) {
         return p.sorted[row] < p.A ? row : row0;
     };
     constexpr int EB = MODE == 0 ? 2 : 1;   // bytes per stride unit
-    // Whether load i reads A or gate/up rows is the same for the whole wave,
-    // so each load has a wave-uniform base and a 32-bit per-lane offset (the
-    // host keeps every operand offset below 2^31 bytes). Its LDS destination
-    // is dst + 8 KB * i: 64 tile rows further, same swizzle.
+
+    // ---- load i of wave w fills LDS block j = w + NW i (tile rows RPL j ..
+    // +RPL; [0, BM) are A rows, [BM, BM + BW) weight rows). Lane l writes
+    // position l of the block: local row l / (64 / RPL), chunk position
+    // p = l % (64 / RPL), so it fetches the chunk that the swizzle stores
+    // there. A or weight, gate or up, is the same for the whole wave, so each
+    // load has a wave-uniform base and a 32-bit per-lane offset (the host
+    // keeps every operand offset below 2^31 bytes).
+    constexpr int CPR = kRowBytes / 16;   // 16-byte chunks per row
+    const int lr = lane / CPR;
+    const int lchunk = swz(RPL * (w % (16 / RPL)) + lr, lane % CPR);
     const char* ld_base[kLoads];
     uint32_t ld_off[kLoads];
-    const int dst = lds_chunk(8 * w + lrow, lchunk);
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-        const int t = 8 * (w + kWaves * i) + lrow;   // tile row
-        if (8 * (w + kWaves * i) < BM) {
+        const int j = w + NW * i;
+        const int t = RPL * j + lr;   // tile row
+        if (RPL * j < BM) {
             ld_base[i] = reinterpret_cast<const char*>(p.a);
             ld_off[i] = (uint32_t)(a_row_of(row0 + t) * p.a_row * EB);
         } else {
             const int R = t - BM;
-            const bool second = STAGE == 1 && 8 * (w + kWaves * i) - BM >= BW / 2;
+            const bool second = STAGE == 1 && RPL * j - BM >= BW / 2;
             const int wrow = n0 + (STAGE == 1 ? R % (BW / 2) : R);
-            ld_base[i] = reinterpret_cast<const char*>(second ? p.b1 : p.b0) + (int64_t)e * (second ? p.b1_e : p.b0_e) * EB;
+            ld_base[i] =
+                reinterpret_cast<const char*>(second ? p.b1 : p.b0) + (int64_t)e * (second ? p.b1_e : p.b0_e) * EB;
             ld_off[i] = (uint32_t)((int64_t)wrow * (second ? p.b1_r : p.b0_r) * EB);
         }
         ld_off[i] += lchunk * 16;
     }
-    // MXFP4: thread t stages the 8 scale bytes per stage of tile rows t,
-    // t + 512, ...; a thread past the last tile row re-reads that row and
-    // does not store it
-    constexpr int kScLoads = MODE == 1 ? (TS::kRows + kThreads - 1) / kThreads : 0;
-    const uint8_t* sc_src[kScLoads > 0 ? kScLoads : 1];
+    // MXFP4: 4-byte scale loads, thread t of load j covers tile row
+    // t + kThreads j (LDS position = that row; past the last row it re-reads
+    // the last row into a slot nobody reads)
+    const uint8_t* sc_base[kScLoads > 0 ? kScLoads : 1];
+    uint32_t sc_off[kScLoads > 0 ? kScLoads : 1];
     if constexpr (MODE == 1) {
 #pragma unroll
         for (int j = 0; j < kScLoads; ++j) {
-            const int t = min((int)threadIdx.x + kThreads * j, TS::kRows - 1);
-            if (t < BM) {
-                sc_src[j] = p.a_sc + a_row_of(row0 + t) * p.a_sc_row;
+            const int t = min((int)threadIdx.x + TS::kThreads * j, TS::kRows - 1);
+            const int t0 = TS::kThreads * j + 64 * w;   // first row of this wave: A or B, gate or up for all
+            if (t0 < BM) {
+                sc_base[j] = p.a_sc;
+                sc_off[j] = (uint32_t)(a_row_of(row0 + t) * p.a_sc_row);
             } else {
                 const int R = t - BM;
-                const bool second = STAGE == 1 && R >= BW / 2;
+                const bool second = STAGE == 1 && t0 - BM >= BW / 2;
                 const int wrow = n0 + (STAGE == 1 ? R % (BW / 2) : R);
-                const uint8_t* sb = second ? p.b1_sc : p.b0_sc;
-                sc_src[j] =
-                    sb + (int64_t)e * (second ? p.b1sc_e : p.b0sc_e) + (int64_t)wrow * (second ? p.b1sc_r : p.b0sc_r);
+                sc_base[j] = (second ? p.b1_sc : p.b0_sc) + (int64_t)e * (second ? p.b1sc_e : p.b0sc_e);
+                sc_off[j] = (uint32_t)((int64_t)wrow * (second ? p.b1sc_r : p.b0sc_r));
             }
         }
     }
 
-    const int S = p.K / (MODE == 0 ? 64 : 256);   // stages; the host keeps it even
+    const int S = p.K / (MODE == 0 ? 32 : 128) / SUBS;   // stages; the host keeps it a multiple of kNBuf
 
-    // ---- global -> registers -> LDS
-    i32x4_t st[kLoads];
-    uint2 sc[kScLoads > 0 ? kScLoads : 1];
-    auto issue = [&](int s) {
-        s = s < S ? s : S - 1;    // past the end: re-read the last stage (L2 hit)
+    // issue the loads of stage s (clamped: past the end the last stage is
+    // loaded again, into a buffer nobody reads) into buffer buf
+    auto issue = [&](char* buf, int s) {
+        s = s < S ? s : S - 1;
 #pragma unroll
         for (int i = 0; i < kLoads; ++i)
-            st[i] = *reinterpret_cast<const i32x4_t*>(ld_base[i] + (ld_off[i] + (uint32_t)(s * kRowBytes)));
+            __builtin_amdgcn_global_load_lds(
+                reinterpret_cast<const void*>(ld_base[i] + (ld_off[i] + (uint32_t)(s * kRowBytes))),
+                (lds_ptr_t)(buf + (w + NW * i) * kBlock), 16, 0, 0);
         if constexpr (MODE == 1) {
 #pragma unroll
-            for (int j = 0; j < kScLoads; ++j) sc[j] = *reinterpret_cast<const uint2*>(sc_src[j] + s * kScRow);
+            for (int u = 0; u < SUBS; ++u)
+#pragma unroll
+                for (int j = 0; j < kScLoads; ++j)
+                    __builtin_amdgcn_global_load_lds(
+                        reinterpret_cast<const void*>(sc_base[j] + (sc_off[j] + (uint32_t)((s * SUBS + u) * kScStep))),
+                        (lds_ptr_t)(buf + TS::kScOff + u * TS::kScPlane + (TS::kThreads * j + 64 * w) * kScStep), 4,
+                        0, 0);
         }
     };
-    // scales go to LDS as [row][k-group][k-step] so that a lane's two bytes
-    // of a stage are adjacent
-    auto interleave = [](uint32_t d0, uint32_t d1, int hi) -> uint32_t {
-        const uint32_t x = hi ? d0 >> 16 : d0, y = hi ? d1 >> 16 : d1;
-        return (x & 0xffu) | ((y & 0xffu) << 8) | ((x & 0xff00u) << 8) | ((y & 0xff00u) << 16);
-    };
-    auto commit = [&](int b) {
-        char* buf = lds + b * BUF;
-#pragma unroll
-        for (int i = 0; i < kLoads; ++i) *reinterpret_cast<i32x4_t*>(buf + dst + i * 8 * kWaves * kRowBytes) = st[i];
-        if constexpr (MODE == 1) {
-            char* scb = buf + TS::kRows * kRowBytes;
-#pragma unroll
-            for (int j = 0; j < kScLoads; ++j) {
-                const int t = threadIdx.x + kThreads * j;
-                if (t < TS::kRows)
-                    *reinterpret_cast<uint2*>(scb + t * kScRow) =
-                        make_uint2(interleave(sc[j].x, sc[j].y, 0), interleave(sc[j].x, sc[j].y, 1));
-            }
-        }
-    };
+    constexpr int kPerStage = kLoads + SUBS * kScLoads;   // vector memory instructions per stage
 
-    // ---- MFMA over one LDS stage: wave (wm, wn) multiplies tile rows
-    // wm*16*WMI .. +16*WMI by its 8 weight row blocks
+    // ---- MFMA over one stage: wave (wm, wn) multiplies tile rows
+    // wm*64 .. +64 by its 8 weight row blocks
     f32x4_t acc[WMI][8];
 #pragma unroll
     for (int mi = 0; mi < WMI; ++mi)
@@ -222,30 +229,26 @@ void gemm_tile(GemmParams p) {
         if (STAGE == 1) return ni < 4 ? wn * 4 + ni : BW / 32 + wn * 4 + (ni - 4);
         return wn * 8 + ni;
     };
-    // fragment row block rb of a k-step: row 16 rb + r16, chunk 4 sub + kg
-    const int rd0 = lds_chunk(r16, kg), rd1 = lds_chunk(r16, 4 + kg);
-    auto compute = [&](int b) {
-        const char* buf = lds + b * BUF;
-        uint32_t as[WMI], bs[8];
-        if constexpr (MODE == 1) {
-            const char* scb = buf + TS::kRows * kRowBytes;
+    auto compute = [&](const char* buf) {
 #pragma unroll
-            for (int mi = 0; mi < WMI; ++mi)
-                as[mi] = *reinterpret_cast<const uint16_t*>(scb + ((wm * WMI + mi) * 16 + r16) * kScRow + kg * 2);
-#pragma unroll
-            for (int ni = 0; ni < 8; ++ni)
-                bs[ni] = *reinterpret_cast<const uint16_t*>(scb + (BM + b_rb(ni) * 16 + r16) * kScRow + kg * 2);
-        }
-#pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
-            const int rd = sub ? rd1 : rd0;
+        for (int u = 0; u < SUBS; ++u) {
+            // fragment row block rb: row 16 rb + r16, chunk 4 u + kg
+            const int rd = r16 * kRowBytes + swz(r16, 4 * u + kg) * 16;
             i32x4_t af[WMI], bf[8];
+            uint32_t as[WMI], bs[8];
 #pragma unroll
             for (int mi = 0; mi < WMI; ++mi)
                 af[mi] = *reinterpret_cast<const i32x4_t*>(buf + (wm * WMI + mi) * 16 * kRowBytes + rd);
 #pragma unroll
             for (int ni = 0; ni < 8; ++ni)
                 bf[ni] = *reinterpret_cast<const i32x4_t*>(buf + (BM + b_rb(ni) * 16) * kRowBytes + rd);
+            if constexpr (MODE == 1) {
+                const uint8_t* sb = reinterpret_cast<const uint8_t*>(buf + TS::kScOff + u * TS::kScPlane);
+#pragma unroll
+                for (int mi = 0; mi < WMI; ++mi) as[mi] = sb[((wm * WMI + mi) * 16 + r16) * kScStep + kg];
+#pragma unroll
+                for (int ni = 0; ni < 8; ++ni) bs[ni] = sb[(BM + b_rb(ni) * 16 + r16) * kScStep + kg];
+            }
 #pragma unroll
             for (int mi = 0; mi < WMI; ++mi)
 #pragma unroll
@@ -257,37 +260,58 @@ void gemm_tile(GemmParams p) {
                     } else {
                         const i32x8_t a8 = {af[mi][0], af[mi][1], af[mi][2], af[mi][3], 0, 0, 0, 0};
                         const i32x8_t b8 = {bf[ni][0], bf[ni][1], bf[ni][2], bf[ni][3], 0, 0, 0, 0};
-                        // the byte of the scale words for this k-step: op_sel
-                        if (sub == 0)
-                            acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                                a8, b8, acc[mi][ni], 4, 4, 0, (int)as[mi], 0, (int)bs[ni]);
-                        else
-                            acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                                a8, b8, acc[mi][ni], 4, 4, 1, (int)as[mi], 1, (int)bs[ni]);
+                        acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            a8, b8, acc[mi][ni], 4, 4, 0, (int)as[mi], 0, (int)bs[ni]);
                     }
                 }
-            // MXFP4 holds one k-step of fragments at a time (register budget)
-            if constexpr (MODE == 1) __builtin_amdgcn_sched_barrier(0);
         }
     };
+    // stage s's loads have landed for every wave and every wave is done with
+    // stage s - 1: wait for this wave's loads up to stage s (the later
+    // stages stay in flight) and its LDS reads, then meet
+    auto publish = [&]() {
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vm_lgkm<(TS::kNBuf - 2) * kPerStage>();
+        __builtin_amdgcn_s_barrier();
+        __asm__ volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    };
 
-    // ---- pipeline: stage s is multiplied from buffer s % 2 while the loads
-    // of stage s + 1 are in flight
-    issue(0);
-    commit(0);
-    lds_barrier();
-    for (int s = 0; s < S; s += 2) {
-        issue(s + 1);
-        compute(0);
-        commit(1);
-        lds_barrier();
-        issue(s + 2);
-        compute(1);
-        commit(0);
-        lds_barrier();
+    // ---- pipeline over kNBuf rotating buffers: stage s in buffer s % kNBuf,
+    // stage s + kNBuf - 1 loading into the buffer stage s - 1 used
+    if constexpr (SUBS == 1) {
+        issue(lds0, 0);
+        issue(lds1, 1);
+        issue(lds2, 2);
+        for (int s = 0; s < S; s += 4) {
+            publish();
+            issue(lds3, s + 3);
+            compute(lds0);
+            publish();
+            issue(lds0, s + 4);
+            compute(lds1);
+            publish();
+            issue(lds1, s + 5);
+            compute(lds2);
+            publish();
+            issue(lds2, s + 6);
+            compute(lds3);
+        }
+    } else {
+        issue(lds0, 0);
+        for (int s = 0; s < S; s += 2) {
+            publish();
+            issue(lds1, s + 1);
+            compute(lds0);
+            publish();
+            issue(lds0, s + 2);
+            compute(lds1);
+        }
     }
+    // drain the loads past the end before the workgroup's LDS is released
+    wait_vm_lgkm<0>();
 
-    // ---- epilogues: acc[mi][ni][i] is row wm*16*WMI + mi*16 + kg*4 + i,
+    // ---- epilogues: acc[mi][ni][i] is row wm*64 + mi*16 + kg*4 + i,
     // column r16 of the ni-th column block
     if constexpr (STAGE == 1 && MODE == 0) {
         uint16_t* h = reinterpret_cast<uint16_t*>(p.out);
@@ -345,41 +369,58 @@ void gemm_tile(GemmParams p) {
     }
 }
 
-template <int MODE, int STAGE, int BM, int BW, int NW>
+// bf16 stages of 128 bytes per row (8 rows x 128 bytes per load, two
+// buffers); MXFP4 stages of 64 bytes (four buffers: the e2m1 k-step is four
+// times deeper, so a stage is already long)
+template <int MODE, int STAGE, int BM, int BW, int NW, int SUBS = (MODE == 0 ? 2 : 1)>
 hipError_t launch_one(const GemmParams& p, hipStream_t s) {
-    using TS = TileShape<MODE, BM, BW, NW>;
+    using TS = TileShape<MODE, BM, BW, NW, SUBS>;
     const int64_t n_tiles = p.N / (STAGE == 1 ? BW / 2 : BW);
     const int64_t m_groups = (p.max_mblocks + TS::kGroupM - 1) / TS::kGroupM;
     const int64_t n_groups = (n_tiles + TS::kGroupN - 1) / TS::kGroupN;
     const int64_t grid = m_groups * n_groups * TS::kGroupM * TS::kGroupN;
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL((gemm_tile<MODE, STAGE, BM, BW, NW>), dim3((unsigned)grid), dim3(TS::kThreads), 0, s, p);
+    hipLaunchKernelGGL((gemm_tile<MODE, STAGE, BM, BW, NW, SUBS>), dim3((unsigned)grid), dim3(TS::kThreads), 0, s, p);
     return hipGetLastError();
 }
 
 }  // namespace
 
-// Tile shapes: 0 = 256 x 256 (eight waves; MXFP4: 128 x 256, four waves of
-// one per SIMD, whose accumulators fit only in the larger register budget),
-// 1 = 128 x 512 (bf16, eight waves).
-int gemm_tile_rows(int mode, int shape) { return shape == 0 && mode == 0 ? 256 : 128; }
+// Tile shapes (rows x weight rows, waves): 0 = 256 x 256 x 8, 1 = 128 x 512 x
+// 8, 2 = 64 x 512 x 4, 3 = 32 x 512 x 4.
+int gemm_tile_rows(int mode, int shape) {
+    (void)mode;
+    static const int rows[4] = {256, 128, 64, 32};
+    return rows[shape];
+}
 
 int gemm_tile_cols(int shape, int stage) {
-    const int bw = shape == 1 ? 512 : 256;
+    const int bw = shape == 0 ? 256 : 512;
     return stage == 1 ? bw / 2 : bw;
 }
 
-int gemm_tile_k_granule(int mode) { return mode == 0 ? 2 * 64 : 2 * 256; }
+// K of four stages
+int gemm_tile_k_granule(int mode) { return mode == 0 ? 4 * 32 : 4 * 128; }
 
-bool gemm_tile_supported(int mode, int shape) { return shape == 0 || (shape == 1 && mode == 0); }
+// MXFP4: 128 x 512 stages do not fit the LDS with their scales, and 32 + 512
+// rows are not whole 16-row loads of four waves
+bool gemm_tile_supported(int mode, int shape) { return mode == 0 ? shape >= 0 && shape <= 3 : shape == 0 || shape == 2; }
 
 hipError_t launch_gemm_tile(int mode, int shape, int stage, const GemmParams& p, hipStream_t s) {
     if (!gemm_tile_supported(mode, shape) || p.N % gemm_tile_cols(shape, stage) != 0 ||
         p.K % gemm_tile_k_granule(mode) != 0)
         return hipErrorInvalidValue;
-    if (mode == 1) return stage == 1 ? launch_one<1, 1, 128, 256, 4>(p, s) : launch_one<1, 2, 128, 256, 4>(p, s);
-    if (shape == 0) return stage == 1 ? launch_one<0, 1, 256, 256, 8>(p, s) : launch_one<0, 2, 256, 256, 8>(p, s);
-    return stage == 1 ? launch_one<0, 1, 128, 512, 8>(p, s) : launch_one<0, 2, 128, 512, 8>(p, s);
+#define MOE_TILE(MD, BM, BW, NW) \
+    return stage == 1 ? launch_one<MD, 1, BM, BW, NW>(p, s) : launch_one<MD, 2, BM, BW, NW>(p, s)
+    if (mode == 1) {
+        if (shape == 0) MOE_TILE(1, 256, 256, 8);
+        MOE_TILE(1, 64, 512, 4);
+    }
+    if (shape == 0) MOE_TILE(0, 256, 256, 8);
+    if (shape == 1) MOE_TILE(0, 128, 512, 8);
+    if (shape == 2) MOE_TILE(0, 64, 512, 4);
+    MOE_TILE(0, 32, 512, 4);
+#undef MOE_TILE
 }
 
 }  // namespace moe

@@ -141,6 +141,7 @@ const Cfg kConfigs[] = {
     {16, 1, 1, 4, 0}, {32, 1, 1, 4, 0}, {128, 1, 1, 4, 0},
     {32, 1, 1, 2, 0}, {64, 1, 1, 2, 0},    // bf16 only: narrow waves, deep weight ring
     {256, 1, 1, 4, 1}, {128, 1, 1, 4, 2},   // many rows per expert: weight reuse
+    {64, 1, 1, 4, 3}, {32, 1, 1, 4, 4},     // LDS-staged weight stream
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -150,36 +151,54 @@ int bucket_of(int64_t T) {
     return b;
 }
 
-// Block rows cover the typical busiest expert of the bucket in one block (so
-// each expert's weights stream from HBM once); the K split grows only while
-// the grid would not fill the chip.
+// Index of the tiled config of a tile shape, or -1 when it cannot run
+// these sizes.
+int tile_config(int md, int shape, int64_t H, int64_t I) {
+    if (!gemm_tile_supported(md, shape)) return -1;
+    const int gran = gemm_tile_k_granule(md);
+    if (H % gran != 0 || I % gran != 0 || I % gemm_tile_cols(shape, 1) != 0 || H % gemm_tile_cols(shape, 2) != 0)
+        return -1;
+    for (int c = 0; c < kNumConfigs; ++c)
+        if (kConfigs[c].tile == shape + 1) return c;
+    return -1;
+}
+
+// Default configuration per token bucket, from measurements on MI355X
+// (Qwen3-235B-shaped bf16 and the TP2 MXFP4 shard):
+//  * many rows per expert: LDS-tiled GEMMs (bf16 128 x 512 tiles from 64
+//    expected rows per expert; MXFP4 64 x 512 from 64 rows, 256 x 256 from
+//    128);
+//  * bf16 with 4 to 16 rows per expert spread over many experts: the 32-row
+//    LDS-staged weight stream;
+//  * otherwise the register weight stream, whose block rows cover the
+//    typical busiest expert of the bucket in one block (each expert's
+//    weights stream from HBM once) and whose K split grows only while the
+//    grid would not fill the chip.
 int default_config(int mode, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k) {
     const int64_t bucket = bucket_of(T);
     const double rows = (double)bucket * (double)k / (double)E;   // expected rows per expert
     const double busy = rows + 3.0 * __builtin_sqrt(rows);          // typical maximum
-    // enough rows per expert to reuse each weight tile several times: tiled
     const int md = mode == MOE_MODE_MXFP4 ? 1 : 0;
-    if (rows >= 192.0)
-        for (int c = 0; c < kNumConfigs; ++c) {
-            const int shape = kConfigs[c].tile - 1;
-            if (shape < 0 || !gemm_tile_supported(md, shape)) continue;
-            if (md == 0 && shape != 1) continue;   // bf16: 128 x 512 tiles measured fastest
-            const int gran = gemm_tile_k_granule(md);
-            if (H % gran == 0 && I % gran == 0 && I % gemm_tile_cols(shape, 1) == 0 &&
-                H % gemm_tile_cols(shape, 2) == 0)
-                return c;
-        }
+    const int64_t experts = std::min<int64_t>(bucket * k, E);      // touched at most
+    int c = -1;
+    if (md == 0) {
+        if (rows >= 64.0) c = tile_config(0, 1, H, I);
+        else if (rows >= 4.0 && rows <= 16.0 && experts * (I / 256) >= 512) c = tile_config(0, 3, H, I);
+    } else {
+        if (rows >= 128.0) c = tile_config(1, 0, H, I);
+        else if (rows >= 64.0) c = tile_config(1, 2, H, I);
+    }
+    if (c >= 0) return c;
     int bm;
-    if (mode == MOE_MODE_MXFP4)    // the fp4 stream prefers short blocks; 128 rows spill
+    if (md == 1)    // the fp4 stream prefers short blocks; 128 rows spill
         bm = busy <= 32.0 ? 16 : 64;
     else
         bm = busy <= 16.0 ? 16 : (busy <= 32.0 ? 32 : (rows < 192.0 ? 64 : 128));
-    const int64_t blocks = std::min<int64_t>(bucket * k, E) *
-                           std::max<int64_t>(1, (int64_t)(rows / bm + 0.999));
+    const int64_t blocks = experts * std::max<int64_t>(1, (int64_t)(rows / bm + 0.999));
     int wk = 1;
     while (wk < 4 && (bm < 64 || wk < 2) && blocks * (I / (32 * (4 / wk))) < 1024) wk <<= 1;
-    for (int c = 0; c < kNumConfigs; ++c)
-        if (kConfigs[c].bm == bm && kConfigs[c].wk1 == wk && kConfigs[c].nb == 4) return c;
+    for (c = 0; c < kNumConfigs; ++c)
+        if (kConfigs[c].bm == bm && kConfigs[c].wk1 == wk && kConfigs[c].nb == 4 && !kConfigs[c].tile) return c;
     return 0;
 }
 

@@ -195,9 +195,8 @@ int gemm_k_granule(const GemmKernelId& id);
 bool gemm_supported(const GemmKernelId& id);
 hipError_t launch_gemm(const GemmKernelId& id, const GemmParams& p, hipStream_t s);
 
-// LDS-tiled grouped GEMM for many rows per expert. Tile shapes (rows x
-// weight rows per workgroup): 0 = 256 x 256 (MXFP4: 128 x 256), 1 = 128 x
-// 512 (bf16 only).
+// LDS-tiled grouped GEMM. Tile shapes (rows x weight rows per workgroup):
+// 0 = 256 x 256, 1 = 128 x 512 (bf16 only), 2 = 64 x 512, 3 = 32 x 512.
 // Row blocks of gemm_tile_rows(mode, shape), gemm_tile_cols(shape, stage) output
 // columns per workgroup, K a multiple of gemm_tile_k_granule(mode). Same
 // parameter block and epilogues as above.
