@@ -29,11 +29,24 @@ __device__ __forceinline__ int expert_of(const AlignParams& p, int a) {
     return (e >= 0 && e < p.E) ? e : -1;
 }
 
-__device__ void wave_count(const AlignParams& p, int lo, int hi, int* cnt) {
-    for (int a = lo + lane_id(); a < hi; a += kWave) {
-        int e = expert_of(p, a);
-        if (e >= 0) atomicAdd(&cnt[e], 1);
+// Experts of a wave's indices [lo, hi), lane-strided: eid[r] is the expert
+// of index lo + 64 r + lane (-1 past hi or when invalid). All loads are
+// issued before any is used.
+template <int R>
+__device__ void wave_load(const AlignParams& p, int lo, int hi, int (&eid)[R]) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int a = lo + r * kWave + lane;
+        eid[r] = a < hi ? expert_of(p, a) : -1;
     }
+}
+
+template <int R>
+__device__ void wave_count(const int (&eid)[R], int* cnt) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        if (eid[r] >= 0) atomicAdd(&cnt[eid[r]], 1);
 }
 
 // Scatter [lo, hi) using base[e] as the running output position of expert e.
@@ -41,11 +54,14 @@ __device__ void wave_count(const AlignParams& p, int lo, int hi, int* cnt) {
 // across the wave with a bitonic network: equal experts end up adjacent and in
 // lane order, so an element's rank inside its expert is its distance from the
 // start of its run. The last lane of a run advances base[e] for the next round.
-__device__ void wave_scatter(const AlignParams& p, int lo, int hi, int* base) {
+template <int R>
+__device__ void wave_scatter(const AlignParams& p, int lo, int hi, const int (&eid)[R], int* base) {
     const int lane = lane_id();
-    for (int a0 = lo; a0 < hi; a0 += kWave) {
-        const int a = a0 + lane;
-        const int e = a < hi ? expert_of(p, a) : -1;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int a0 = lo + r * kWave;
+        if (a0 >= hi) break;
+        const int e = eid[r];
         uint32_t key = e >= 0 ? ((uint32_t)e << 6) | (uint32_t)lane : 0x80000000u | (uint32_t)lane;
 #pragma unroll
         for (int k = 2; k <= kWave; k <<= 1) {
@@ -148,7 +164,9 @@ __global__ __launch_bounds__(kFusedThreads) void align_fused(AlignParams p) {
     __syncthreads();
     const int per = (p.A + kFusedWaves - 1) / kFusedWaves;
     const int lo = min(p.A, w * per), hi = min(p.A, lo + per);
-    wave_count(p, lo, hi, wcnt + w * E);
+    int eid[kFusedMaxA / kFusedThreads];
+    wave_load(p, lo, hi, eid);
+    wave_count(eid, wcnt + w * E);
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += kFusedThreads) {
         int run = 0;
@@ -164,7 +182,7 @@ __global__ __launch_bounds__(kFusedThreads) void align_fused(AlignParams p) {
     for (int e = threadIdx.x; e < E; e += kFusedThreads)
         for (int v = 0; v < kFusedWaves; ++v) wcnt[v * E + e] += off[e];
     __syncthreads();
-    wave_scatter(p, lo, hi, wcnt + w * E);
+    wave_scatter(p, lo, hi, eid, wcnt + w * E);
 }
 
 // Multi-block phase 1: counts[b][e] for chunk b.
@@ -175,7 +193,9 @@ __global__ __launch_bounds__(kThreads) void align_count(AlignParams p) {
     __syncthreads();
     const int w = threadIdx.x >> 6;
     const int lo = min(p.A, (int)blockIdx.x * kChunk + w * kWaveItems), hi = min(p.A, lo + kWaveItems);
-    wave_count(p, lo, hi, lds);
+    int eid[kWaveItems / kWave];
+    wave_load(p, lo, hi, eid);
+    wave_count(eid, lds);
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += kThreads) p.counts[(int64_t)blockIdx.x * E + e] = lds[e];
 }
@@ -187,19 +207,33 @@ __global__ __launch_bounds__(kThreads) void align_scan(AlignParams p, int nchunk
     int* tot = lds;
     int* off = tot + E;
     int* scratch = off + E;
+    // counts of one expert are read 16 chunks at a time, all loads in flight
+    constexpr int kBatch = 16;
     for (int e = threadIdx.x; e < E; e += kThreads) {
         int run = 0;
-        for (int b = 0; b < nchunks; ++b) {
-            const int c = p.counts[(int64_t)b * E + e];
-            p.counts[(int64_t)b * E + e] = run;
-            run += c;
+        for (int b0 = 0; b0 < nchunks; b0 += kBatch) {
+            int c[kBatch];
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i) c[i] = b0 + i < nchunks ? p.counts[(int64_t)(b0 + i) * E + e] : 0;
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i) {
+                if (b0 + i < nchunks) p.counts[(int64_t)(b0 + i) * E + e] = run;
+                run += c[i];
+            }
         }
         tot[e] = run;
     }
     __syncthreads();
     layout_experts<kThreads>(p, tot, off, scratch);
     for (int e = threadIdx.x; e < E; e += kThreads)
-        for (int b = 0; b < nchunks; ++b) p.counts[(int64_t)b * E + e] += off[e];
+        for (int b0 = 0; b0 < nchunks; b0 += kBatch) {
+            int c[kBatch];
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i) c[i] = b0 + i < nchunks ? p.counts[(int64_t)(b0 + i) * E + e] : 0;
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i)
+                if (b0 + i < nchunks) p.counts[(int64_t)(b0 + i) * E + e] = c[i] + off[e];
+        }
 }
 
 // Multi-block phase 3: stable scatter of chunk b.
@@ -211,7 +245,9 @@ __global__ __launch_bounds__(kThreads) void align_scatter(AlignParams p) {
     __syncthreads();
     const int w = threadIdx.x >> 6;
     const int lo = min(p.A, (int)blockIdx.x * kChunk + w * kWaveItems), hi = min(p.A, lo + kWaveItems);
-    wave_count(p, lo, hi, wcnt + w * E);
+    int eid[kWaveItems / kWave];
+    wave_load(p, lo, hi, eid);
+    wave_count(eid, wcnt + w * E);
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += kThreads) {
         int run = p.counts[(int64_t)blockIdx.x * E + e];
@@ -222,7 +258,7 @@ __global__ __launch_bounds__(kThreads) void align_scatter(AlignParams p) {
         }
     }
     __syncthreads();
-    wave_scatter(p, lo, hi, wcnt + w * E);
+    wave_scatter(p, lo, hi, eid, wcnt + w * E);
 }
 
 bool use_fused(int A, int E) {

@@ -1,4 +1,5 @@
 // Combine: out[t, n] = bf16(sum over slots j = 0..k-1 of w[t, j] * y[t*k + j, n]),
+// y read as fp32 (bf16 mode) or as bf16 widened exactly to fp32 (MXFP4 mode),
 // accumulated with fmaf in slot order from +0 and rounded once. Slots whose
 // id lies outside [0, E) contribute nothing. No atomics, so the result is the
 // same on every run and for every input layout.
@@ -7,7 +8,8 @@
 namespace moe {
 namespace {
 
-// Each thread produces 4 consecutive columns of one token.
+// Each thread produces 4 consecutive columns of one token; y is fp32 or bf16.
+template <bool Y16>
 __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
     const int nqb = (p.H / 4 + 255) / 256;            // workgroups per token
     const int t = blockIdx.x / nqb;
@@ -19,7 +21,15 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
         const int e = p.ids[(int64_t)t * p.is_t + (int64_t)j * p.is_j];
         if (e < 0 || e >= p.E) continue;
         const float wt = p.w[(int64_t)t * p.ws_t + (int64_t)j * p.ws_j];
-        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(p.y + ((int64_t)t * p.k + j) * p.H + n);
+        const int64_t off = ((int64_t)t * p.k + j) * p.H + n;
+        f32x4_t v;
+        if constexpr (Y16) {
+            const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(p.y) + off);
+            v = f32x4_t{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                        __uint_as_float(u.y & 0xffff0000u)};
+        } else {
+            v = *reinterpret_cast<const f32x4_t*>(reinterpret_cast<const float*>(p.y) + off);
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(wt, v[i], acc[i]);
     }
@@ -42,7 +52,8 @@ hipError_t launch_combine(const CombineParams& p, hipStream_t s) {
     if (p.T == 0) return hipSuccess;
     const int quads = p.H / 4;
     dim3 grid((unsigned)(((quads + 255) / 256) * (int64_t)p.T));
-    hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, s, p);
+    if (p.y_bf16) hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL(combine_kernel<false>, grid, dim3(256), 0, s, p);
     return hipGetLastError();
 }
 

@@ -355,16 +355,23 @@ void gemm_tile(GemmParams p) {
                 }
             }
     } else {
-        float* y = reinterpret_cast<float*>(p.out);
+        // y rows: fp32, or bf16 (RNE) in MXFP4 mode
 #pragma unroll
         for (int mi = 0; mi < WMI; ++mi)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int a = p.sorted[row0 + wm * 16 * WMI + mi * 16 + kg * 4 + i];
                 if (a >= p.A) continue;
-                float* yr = y + (int64_t)a * p.N + n0 + wn * 128 + r16;
+                const int64_t off = (int64_t)a * p.N + n0 + wn * 128 + r16;
+                if constexpr (MODE == 1) {
+                    uint16_t* yr = reinterpret_cast<uint16_t*>(p.out) + off;
 #pragma unroll
-                for (int ni = 0; ni < 8; ++ni) yr[ni * 16] = acc[mi][ni][i];
+                    for (int ni = 0; ni < 8; ++ni) yr[ni * 16] = f32_to_bf16_bits(acc[mi][ni][i]);
+                } else {
+                    float* yr = reinterpret_cast<float*>(p.out) + off;
+#pragma unroll
+                    for (int ni = 0; ni < 8; ++ni) yr[ni * 16] = acc[mi][ni][i];
+                }
             }
     }
 }

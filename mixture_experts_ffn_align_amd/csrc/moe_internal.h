@@ -150,7 +150,7 @@ hipError_t launch_pack_bf16(const PackParams& p, hipStream_t s);
 
 // One grouped GEMM launch. Stage 1: A = gathered x rows, B = gate/up rows,
 // epilogue SiLU(g)*u -> h. Stage 2: A = h rows, B = w2 rows, epilogue scatter
-// of fp32 y rows to their flat assignment index.
+// of y rows (fp32; bf16 in MXFP4 mode) to their flat assignment index.
 struct GemmParams {
     // routing / align
     const int32_t* sorted;
@@ -172,7 +172,7 @@ struct GemmParams {
     int32_t K;              // contraction length
     int32_t N;              // output columns (stage 1: I, stage 2: H)
     // outputs
-    void* out;              // stage 1: h (bf16 [P, I] or fp4 [P, I/2]); stage 2: y fp32 [A, H]
+    void* out;              // stage 1: h (bf16 [P, I] or fp4 [P, I/2]); stage 2: y [A, H] (fp32 / MXFP4: bf16)
     uint8_t* out_sc;        // stage 1 MXFP4: h scales [P, I/32]
     int32_t n_tile_groups;  // tiles along N are walked in groups of this size
     int32_t max_mblocks;
@@ -207,7 +207,8 @@ bool gemm_tile_supported(int mode, int shape);
 hipError_t launch_gemm_tile(int mode, int shape, int stage, const GemmParams& p, hipStream_t s);
 
 struct CombineParams {
-    const float* y;         // [A, H]
+    const void* y;          // [A, H] fp32, or bf16 when y_bf16
+    int32_t y_bf16;
     const int32_t* ids;
     int64_t is_t, is_j;
     const float* w;
