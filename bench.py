@@ -32,7 +32,9 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 METRIC = "fused-MoE fwd µs/call + TFLOP/s & %roofline at T=512/4096/16384 tokens"
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "gemm1_bf16_qwen3_235b_t512_counters.md")
 KERNEL_SOURCES = ("mixture_experts_ffn_align_amd/csrc/gemm_stream.hip",
+                  "mixture_experts_ffn_align_amd/csrc/gemm_tile.hip",
                   "mixture_experts_ffn_align_amd/csrc/moe_internal.h")
+KERNEL_FAMILY = {1: "gemm_stream", 3: "gemm_tile", 11: "gemm_stream", 13: "gemm_tile"}
 
 
 def log(*a):
@@ -223,7 +225,7 @@ def main():
             for _ in range(n_w):
                 moe.moe_fused_fwd(ri["x"], gate, up, w2, ids_s, w_s, out=xo, workspace=wsx, stream=stream)
             ev = hip.create(2 + 2 * nst)
-            g1 = 0.0
+            g1 = g2 = 0.0
             torch.cuda.synchronize()
             ta = time.perf_counter()
             for _ in range(n_t):
@@ -231,8 +233,10 @@ def main():
                                   stage_events=ev[2:], stream=stream)
                 torch.cuda.synchronize()
                 g1 += hip.elapsed_ms(ev[2 + 2 * 2], ev[3 + 2 * 2])
+                g2 += hip.elapsed_ms(ev[2 + 2 * 3], ev[3 + 2 * 3])
             tb = time.perf_counter()
             hip.destroy(ev)
+            qt = moe.moe_query_config(ri["x"], gate, up, w2, ids_s, w_s)
             us_t = (tb - ta) * 1e6 / n_t
             At = TT * k
             touched_t = int(torch.unique(ids_s).numel())
@@ -245,6 +249,11 @@ def main():
                                        / (us_t * 1e-6), 3),
                 "bound": "hbm" if b_t / HBM_PEAK_GBS / 1e9 > f_t / BF16_PEAK_TFLOPS / 1e12 else "mfma",
                 "gemm1_us": round(g1 * 1e3 / n_t, 1),
+                "gemm2_us": round(g2 * 1e3 / n_t, 1),
+                # MFMA utilisation of the GEMMs alone (algorithmic flops over their time)
+                "gemm1_mfma_frac": round(4 * H * I * At / (g1 * 1e-3 / n_t) / (BF16_PEAK_TFLOPS * 1e12), 3),
+                "gemm2_mfma_frac": round(2 * H * I * At / (g2 * 1e-3 / n_t) / (BF16_PEAK_TFLOPS * 1e12), 3),
+                "kernel": f"{KERNEL_FAMILY.get(qt['gemm1_kernel'], '?')} block_m={qt['block_m']}",
                 "inputs": "packed w13 views, ids/weights [:, :, 7, :] of [1,T,46,8] (token stride 368)",
             }
             del ri, xo, wsx
@@ -281,7 +290,8 @@ def main():
         "flushed_us_per_call_median": round(flushed_us, 1),
         "stage_us": {kk: round(v * 1e3, 1) for kk, v in stage_ms.items()},
         "roofline": {
-            "kernel": "gemm1 (gemm_stream bf16 stage 1)",
+            "kernel": f"gemm1 ({KERNEL_FAMILY.get(cfg['gemm1_kernel'], '?')} bf16 stage 1, "
+                      f"block_m={cfg['block_m']})",
             "bound": "hbm",
             "achieved": round(g1_gbs, 1),
             "peak": HBM_PEAK_GBS,

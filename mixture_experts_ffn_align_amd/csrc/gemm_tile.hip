@@ -35,9 +35,10 @@
 // lane fetches so that the lane order of the LDS write is the swizzled
 // order.
 //
-// Consecutive workgroups are kept on one XCD and cover groups of row blocks x
-// weight tiles, so the row blocks of an expert share its weight tiles through
-// that XCD's L2 and the weight tiles share the rows.
+// Consecutive workgroups are kept on one XCD and walk 32 consecutive row
+// blocks of one weight tile, so the row blocks of an expert stream its weight
+// tile through that XCD's L2 together (the token rows, a few MB, are re-read
+// once per weight tile from the L2 / MALL).
 #include "moe_internal.h"
 
 namespace moe {
@@ -69,8 +70,10 @@ struct TileShape {
     static constexpr int kScOff = kRows * kRowBytes;
     static constexpr int kScPlane = kScLoads * kThreads * kScStep;   // one k-step's scales
     static constexpr int kBuf = kScOff + SUBS * kScPlane;
-    static constexpr int kGroupM = BM == 256 ? 4 : 8;      // row blocks per tile group
-    static constexpr int kGroupN = (NW == 8 ? 32 : 64) / kGroupM;   // weight tiles per tile group
+    // 32 consecutive row blocks (a few experts) share one weight tile at a
+    // time on one XCD; a group never holds empty slots
+    static constexpr int kGroupM = 32;
+    static constexpr int kGroupN = 1;
 };
 
 __device__ __forceinline__ float silu_mul(float g, float u) {

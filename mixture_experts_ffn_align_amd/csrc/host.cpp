@@ -165,11 +165,9 @@ int tile_config(int md, int shape, int64_t H, int64_t I) {
 
 // Default configuration per token bucket, from measurements on MI355X
 // (Qwen3-235B-shaped bf16 and the TP2 MXFP4 shard):
-//  * many rows per expert: LDS-tiled GEMMs (bf16 128 x 512 tiles from 64
-//    expected rows per expert; MXFP4 64 x 512 from 64 rows, 256 x 256 from
-//    128);
-//  * bf16 with 4 to 16 rows per expert spread over many experts: the 32-row
-//    LDS-staged weight stream;
+//  * enough rows per expert: LDS-tiled GEMMs (bf16: 64 x 512 tiles from 24
+//    expected rows per expert, 128 x 512 from 64, 256 x 256 from 512;
+//    MXFP4: 64 x 512 from 64 rows, 256 x 256 from 128);
 //  * otherwise the register weight stream, whose block rows cover the
 //    typical busiest expert of the bucket in one block (each expert's
 //    weights stream from HBM once) and whose K split grows only while the
@@ -182,8 +180,9 @@ int default_config(int mode, int64_t T, int64_t H, int64_t I, int64_t E, int64_t
     const int64_t experts = std::min<int64_t>(bucket * k, E);      // touched at most
     int c = -1;
     if (md == 0) {
-        if (rows >= 64.0) c = tile_config(0, 1, H, I);
-        else if (rows >= 4.0 && rows <= 16.0 && experts * (I / 256) >= 512) c = tile_config(0, 3, H, I);
+        if (rows >= 512.0) c = tile_config(0, 0, H, I);
+        else if (rows >= 64.0) c = tile_config(0, 1, H, I);
+        else if (rows >= 24.0) c = tile_config(0, 2, H, I);
     } else {
         if (rows >= 128.0) c = tile_config(1, 0, H, I);
         else if (rows >= 64.0) c = tile_config(1, 2, H, I);
