@@ -50,14 +50,15 @@ constexpr int kScStep = 4;         // e8m0 bytes of one row per k-step
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // BM rows x BW weight rows per workgroup of NW waves, SUBS k-steps of
-// 64 bytes per row per stage; a wave multiplies 16 WMI rows by 128 weight
-// rows
-template <int MODE, int BM, int BW, int NW, int SUBS>
+// 64 bytes per row per stage, NBUF stage buffers; a wave multiplies 16 WMI
+// rows by 128 weight rows
+template <int MODE, int BM, int BW, int NW, int SUBS, int NBUF>
 struct TileShape {
     static constexpr int kThreads = 64 * NW;
     static constexpr int kRowBytes = 64 * SUBS;
     static constexpr int kRowsPerLoad = kBlock / kRowBytes;
-    static constexpr int kNBuf = 4 / SUBS;
+    static constexpr int kNBuf = NBUF;
+    static_assert(NBUF == 2 || NBUF == 4, "two or four stage buffers");
     static constexpr int kWN = BW / 128;                   // waves along weight rows
     static constexpr int kWM = NW / kWN;                   // waves along rows
     static constexpr int kWMI = BM / (16 * kWM);           // row blocks per wave
@@ -98,10 +99,10 @@ __device__ __forceinline__ void wait_vm_lgkm() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
 }
 
-template <int MODE, int STAGE, int BM, int BW, int NW, int SUBS>
+template <int MODE, int STAGE, int BM, int BW, int NW, int SUBS, int NBUF>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void gemm_tile(GemmParams p) {
-    using TS = TileShape<MODE, BM, BW, NW, SUBS>;
+    using TS = TileShape<MODE, BM, BW, NW, SUBS, NBUF>;
     constexpr int kLoads = TS::kLoads, kScLoads = TS::kScLoads, BUF = TS::kBuf, kWN = TS::kWN;
     constexpr int kRowBytes = TS::kRowBytes, RPL = TS::kRowsPerLoad, WMI = TS::kWMI;
     auto swz = [](int r, int c) { return swz_t<kRowBytes / 16>(r & 15, c); };
@@ -109,8 +110,8 @@ void gemm_tile(GemmParams p) {
     // buffer does not depend on the loads still landing in another
     __shared__ __attribute__((aligned(16))) char lds0[BUF];
     __shared__ __attribute__((aligned(16))) char lds1[BUF];
-    __shared__ __attribute__((aligned(16))) char lds2[SUBS == 1 ? BUF : 16];
-    __shared__ __attribute__((aligned(16))) char lds3[SUBS == 1 ? BUF : 16];
+    __shared__ __attribute__((aligned(16))) char lds2[NBUF == 4 ? BUF : 16];
+    __shared__ __attribute__((aligned(16))) char lds3[NBUF == 4 ? BUF : 16];
 
     const int lane = lane_id();
     const int w = threadIdx.x >> 6;
@@ -175,23 +176,21 @@ void gemm_tile(GemmParams p) {
     }
     // MXFP4: 4-byte scale loads, thread t of load j covers tile row
     // t + kThreads j (LDS position = that row; past the last row it re-reads
-    // the last row into a slot nobody reads)
-    const uint8_t* sc_base[kScLoads > 0 ? kScLoads : 1];
-    uint32_t sc_off[kScLoads > 0 ? kScLoads : 1];
+    // the last row into a slot nobody reads). A wave's 64 rows can straddle
+    // the A / weight boundary, so each lane forms its own address.
+    const uint8_t* sc_src[kScLoads > 0 ? kScLoads : 1];
     if constexpr (MODE == 1) {
 #pragma unroll
         for (int j = 0; j < kScLoads; ++j) {
             const int t = min((int)threadIdx.x + TS::kThreads * j, TS::kRows - 1);
-            const int t0 = TS::kThreads * j + 64 * w;   // first row of this wave: A or B, gate or up for all
-            if (t0 < BM) {
-                sc_base[j] = p.a_sc;
-                sc_off[j] = (uint32_t)(a_row_of(row0 + t) * p.a_sc_row);
+            if (t < BM) {
+                sc_src[j] = p.a_sc + a_row_of(row0 + t) * p.a_sc_row;
             } else {
                 const int R = t - BM;
-                const bool second = STAGE == 1 && t0 - BM >= BW / 2;
+                const bool second = STAGE == 1 && R >= BW / 2;
                 const int wrow = n0 + (STAGE == 1 ? R % (BW / 2) : R);
-                sc_base[j] = (second ? p.b1_sc : p.b0_sc) + (int64_t)e * (second ? p.b1sc_e : p.b0sc_e);
-                sc_off[j] = (uint32_t)((int64_t)wrow * (second ? p.b1sc_r : p.b0sc_r));
+                sc_src[j] = (second ? p.b1_sc : p.b0_sc) + (int64_t)e * (second ? p.b1sc_e : p.b0sc_e) +
+                            (int64_t)wrow * (second ? p.b1sc_r : p.b0sc_r);
             }
         }
     }
@@ -213,7 +212,7 @@ void gemm_tile(GemmParams p) {
 #pragma unroll
                 for (int j = 0; j < kScLoads; ++j)
                     __builtin_amdgcn_global_load_lds(
-                        reinterpret_cast<const void*>(sc_base[j] + (sc_off[j] + (uint32_t)((s * SUBS + u) * kScStep))),
+                        reinterpret_cast<const void*>(sc_src[j] + (s * SUBS + u) * kScStep),
                         (lds_ptr_t)(buf + TS::kScOff + u * TS::kScPlane + (TS::kThreads * j + 64 * w) * kScStep), 4,
                         0, 0);
         }
@@ -282,7 +281,7 @@ void gemm_tile(GemmParams p) {
 
     // ---- pipeline over kNBuf rotating buffers: stage s in buffer s % kNBuf,
     // stage s + kNBuf - 1 loading into the buffer stage s - 1 used
-    if constexpr (SUBS == 1) {
+    if constexpr (NBUF == 4) {
         issue(lds0, 0);
         issue(lds1, 1);
         issue(lds2, 2);
@@ -379,58 +378,72 @@ void gemm_tile(GemmParams p) {
     }
 }
 
-// bf16 stages of 128 bytes per row (8 rows x 128 bytes per load, two
-// buffers); MXFP4 stages of 64 bytes (four buffers: the e2m1 k-step is four
-// times deeper, so a stage is already long)
-template <int MODE, int STAGE, int BM, int BW, int NW, int SUBS = (MODE == 0 ? 2 : 1)>
+// Stages of 128 bytes per row (8 rows x 128 bytes per load, two buffers),
+// except MXFP4 with 256-row blocks: 64 bytes (four buffers; the e2m1 k-step
+// is four times deeper, so a stage is already long)
+template <int MODE, int STAGE, int BM, int BW, int NW, int SUBS = (MODE == 0 || BM <= 64 ? 2 : 1),
+          int NBUF = 4 / SUBS>
 hipError_t launch_one(const GemmParams& p, hipStream_t s) {
-    using TS = TileShape<MODE, BM, BW, NW, SUBS>;
+    using TS = TileShape<MODE, BM, BW, NW, SUBS, NBUF>;
     const int64_t n_tiles = p.N / (STAGE == 1 ? BW / 2 : BW);
     const int64_t m_groups = (p.max_mblocks + TS::kGroupM - 1) / TS::kGroupM;
     const int64_t n_groups = (n_tiles + TS::kGroupN - 1) / TS::kGroupN;
     const int64_t grid = m_groups * n_groups * TS::kGroupM * TS::kGroupN;
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL((gemm_tile<MODE, STAGE, BM, BW, NW, SUBS>), dim3((unsigned)grid), dim3(TS::kThreads), 0, s, p);
+    hipLaunchKernelGGL((gemm_tile<MODE, STAGE, BM, BW, NW, SUBS, NBUF>), dim3((unsigned)grid), dim3(TS::kThreads), 0,
+                       s, p);
     return hipGetLastError();
 }
 
 }  // namespace
 
 // Tile shapes (rows x weight rows, waves): 0 = 256 x 256 x 8, 1 = 128 x 512 x
-// 8, 2 = 64 x 512 x 4, 3 = 32 x 512 x 4.
+// 8, 2 = 64 x 512 x 4, 3 = 32 x 512 x 4, 4 = 64 x 256 x 4 (bf16) or 32 x 256
+// x 4 (MXFP4), with four 128-byte stage buffers (three stages in flight)
+// where K allows it.
 int gemm_tile_rows(int mode, int shape) {
-    (void)mode;
-    static const int rows[4] = {256, 128, 64, 32};
-    return rows[shape];
+    static const int rows[5] = {256, 128, 64, 32, 64};
+    return mode == 1 && shape == 4 ? 32 : rows[shape];
 }
 
 int gemm_tile_cols(int shape, int stage) {
-    const int bw = shape == 0 ? 256 : 512;
+    const int bw = (shape == 0 || shape == 4) ? 256 : 512;
     return stage == 1 ? bw / 2 : bw;
 }
 
-// K of four stages
-int gemm_tile_k_granule(int mode) { return mode == 0 ? 4 * 32 : 4 * 128; }
+// K that is a whole number of stage rotations: two 128-byte stages (four for
+// bf16 shape 4), four 64-byte MXFP4 stages
+int gemm_tile_k_granule(int mode, int shape) {
+    if (mode == 1) return 4 * 128;
+    return shape == 4 ? 4 * 64 : 2 * 64;
+}
 
-// MXFP4: 128 x 512 stages do not fit the LDS with their scales, and 32 + 512
-// rows are not whole 16-row loads of four waves
-bool gemm_tile_supported(int mode, int shape) { return mode == 0 ? shape >= 0 && shape <= 3 : shape == 0 || shape == 2; }
+// MXFP4 128 x 512 stages do not fit the LDS with their scales
+bool gemm_tile_supported(int mode, int shape) { return shape >= 0 && shape <= 4 && !(mode == 1 && shape == 1); }
 
 hipError_t launch_gemm_tile(int mode, int shape, int stage, const GemmParams& p, hipStream_t s) {
     if (!gemm_tile_supported(mode, shape) || p.N % gemm_tile_cols(shape, stage) != 0 ||
-        p.K % gemm_tile_k_granule(mode) != 0)
+        p.K % gemm_tile_k_granule(mode, shape) != 0)
         return hipErrorInvalidValue;
 #define MOE_TILE(MD, BM, BW, NW) \
     return stage == 1 ? launch_one<MD, 1, BM, BW, NW>(p, s) : launch_one<MD, 2, BM, BW, NW>(p, s)
+#define MOE_TILE4(MD, BM, BW, NW) \
+    return stage == 1 ? launch_one<MD, 1, BM, BW, NW, 2, 4>(p, s) : launch_one<MD, 2, BM, BW, NW, 2, 4>(p, s)
     if (mode == 1) {
         if (shape == 0) MOE_TILE(1, 256, 256, 8);
-        MOE_TILE(1, 64, 512, 4);
+        if (shape == 2) MOE_TILE(1, 64, 512, 4);
+        if (shape == 3) MOE_TILE(1, 32, 512, 4);
+        // four buffers need four 256-value stages per rotation
+        if (p.K % (4 * 256) == 0) MOE_TILE4(1, 32, 256, 4);
+        MOE_TILE(1, 32, 256, 4);
     }
     if (shape == 0) MOE_TILE(0, 256, 256, 8);
     if (shape == 1) MOE_TILE(0, 128, 512, 8);
     if (shape == 2) MOE_TILE(0, 64, 512, 4);
-    MOE_TILE(0, 32, 512, 4);
+    if (shape == 3) MOE_TILE(0, 32, 512, 4);
+    MOE_TILE4(0, 64, 256, 4);
 #undef MOE_TILE
+#undef MOE_TILE4
 }
 
 }  // namespace moe

@@ -142,6 +142,7 @@ const Cfg kConfigs[] = {
     {32, 1, 1, 2, 0}, {64, 1, 1, 2, 0},    // bf16 only: narrow waves, deep weight ring
     {256, 1, 1, 4, 1}, {128, 1, 1, 4, 2},   // many rows per expert: weight reuse
     {64, 1, 1, 4, 3}, {32, 1, 1, 4, 4},     // LDS-staged weight stream
+    {64, 1, 1, 4, 5},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -155,7 +156,7 @@ int bucket_of(int64_t T) {
 // these sizes.
 int tile_config(int md, int shape, int64_t H, int64_t I) {
     if (!gemm_tile_supported(md, shape)) return -1;
-    const int gran = gemm_tile_k_granule(md);
+    const int gran = gemm_tile_k_granule(md, shape);
     if (H % gran != 0 || I % gran != 0 || I % gemm_tile_cols(shape, 1) != 0 || H % gemm_tile_cols(shape, 2) != 0)
         return -1;
     for (int c = 0; c < kNumConfigs; ++c)
@@ -165,9 +166,10 @@ int tile_config(int md, int shape, int64_t H, int64_t I) {
 
 // Default configuration per token bucket, from measurements on MI355X
 // (Qwen3-235B-shaped bf16 and the TP2 MXFP4 shard):
-//  * enough rows per expert: LDS-tiled GEMMs (bf16: 64 x 512 tiles from 24
-//    expected rows per expert, 128 x 512 from 64, 256 x 256 from 512;
-//    MXFP4: 64 x 512 from 64 rows, 256 x 256 from 128);
+//  * enough rows per expert: LDS-tiled GEMMs (bf16: 64 x 256 tiles with
+//    three stages in flight from 4 expected rows per expert, 128 x 512 from
+//    192, 256 x 256 from 512; MXFP4: 64 x 512 from 64 rows, 256 x 256 from
+//    128);
 //  * otherwise the register weight stream, whose block rows cover the
 //    typical busiest expert of the bucket in one block (each expert's
 //    weights stream from HBM once) and whose K split grows only while the
@@ -181,8 +183,8 @@ int default_config(int mode, int64_t T, int64_t H, int64_t I, int64_t E, int64_t
     int c = -1;
     if (md == 0) {
         if (rows >= 512.0) c = tile_config(0, 0, H, I);
-        else if (rows >= 64.0) c = tile_config(0, 1, H, I);
-        else if (rows >= 24.0) c = tile_config(0, 2, H, I);
+        else if (rows >= 192.0) c = tile_config(0, 1, H, I);
+        else if (rows >= 4.0) c = tile_config(0, 4, H, I);
     } else {
         if (rows >= 128.0) c = tile_config(1, 0, H, I);
         else if (rows >= 64.0) c = tile_config(1, 2, H, I);
@@ -306,7 +308,7 @@ int plan_fused(const moe_fused_args_t* a, Plan* pl) {
     };
     if (c.tile) {
         const int shape = c.tile - 1, md = fp4 ? 1 : 0;
-        const int gran = gemm_tile_k_granule(md);
+        const int gran = gemm_tile_k_granule(md, shape);
         if (!gemm_tile_supported(md, shape))
             return fail(MOE_ERR_UNSUPPORTED, "config %d: tile shape not built for this mode", ci);
         c.bm = gemm_tile_rows(md, shape);

@@ -196,13 +196,14 @@ bool gemm_supported(const GemmKernelId& id);
 hipError_t launch_gemm(const GemmKernelId& id, const GemmParams& p, hipStream_t s);
 
 // LDS-tiled grouped GEMM. Tile shapes (rows x weight rows per workgroup):
-// 0 = 256 x 256, 1 = 128 x 512 (bf16 only), 2 = 64 x 512, 3 = 32 x 512.
+// 0 = 256 x 256, 1 = 128 x 512 (bf16 only), 2 = 64 x 512, 3 = 32 x 512,
+// 4 = 64 x 256 (bf16) / 32 x 256 (MXFP4).
 // Row blocks of gemm_tile_rows(mode, shape), gemm_tile_cols(shape, stage) output
-// columns per workgroup, K a multiple of gemm_tile_k_granule(mode). Same
+// columns per workgroup, K a multiple of gemm_tile_k_granule(mode, shape). Same
 // parameter block and epilogues as above.
 int gemm_tile_rows(int mode, int shape);
 int gemm_tile_cols(int shape, int stage);
-int gemm_tile_k_granule(int mode);
+int gemm_tile_k_granule(int mode, int shape);
 bool gemm_tile_supported(int mode, int shape);
 hipError_t launch_gemm_tile(int mode, int shape, int stage, const GemmParams& p, hipStream_t s);
 
