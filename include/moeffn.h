@@ -165,9 +165,9 @@ int moe_quant_mxfp4(const moe_tensor_t *src, const moe_tensor_t *codes,
  *   out         [T, H] bf16 out, any strides.
  *   stage_events NULL, or 2*MOE_NUM_STAGES hipEvent_t handles created by the
  *               caller; event 2s is recorded before stage s and 2s+1 after
- *               it, on the call's stream. Stages: 0 align, 1 prepare
- *               (activation quantise or re-layout; may be empty), 2 gemm1 +
- *               act, 3 gemm2, 4 combine.
+ *               it, on the call's stream; NULL entries are skipped. Stages:
+ *               0 align, 1 prepare (activation quantise or re-layout; may be
+ *               empty), 2 gemm1 + act, 3 gemm2, 4 combine.
  *   force_config  -1 for the built-in choice, else an index into the
  *               library's config list (tests of tile invariance).
  * Numerics: fp32 accumulation; h rounded to bf16 (bf16 mode) or quantised to

@@ -129,7 +129,7 @@ def _fused_args(x, gate, up, w2, topk_ids, topk_weights, out, gate_scale=None, u
     a.force_config = force_config
     keep = None
     if stage_events is not None:
-        keep = (ctypes.c_void_p * len(stage_events))(*stage_events)
+        keep = (ctypes.c_void_p * len(stage_events))(*[e or None for e in stage_events])
         a.stage_events = ctypes.cast(keep, ctypes.c_void_p)
     return a, keep
 
@@ -174,7 +174,7 @@ def moe_fused_fwd(x: torch.Tensor, gate: torch.Tensor, up: torch.Tensor, w2: tor
 
     bf16 mode: gate/up [E, I, H] and w2 [E, H, I] bf16 (any expert/row strides).
     MXFP4 mode: gate/up/w2 are uint8 code tensors [.., K/2] with uint8 e8m0
-    scales [.., K/32]. stage_events: 10 raw hipEvent_t handles or None.
+    scales [.., K/32]. stage_events: 10 raw hipEvent_t handles (0 skips one) or None.
     """
     L = _abi.load()
     if out is None:

@@ -388,10 +388,10 @@ struct StageTimer {
     void* const* ev;
     hipStream_t s;
     void begin(int st) const {
-        if (ev) (void)hipEventRecord((hipEvent_t)ev[2 * st], s);
+        if (ev && ev[2 * st]) (void)hipEventRecord((hipEvent_t)ev[2 * st], s);
     }
     void end(int st) const {
-        if (ev) (void)hipEventRecord((hipEvent_t)ev[2 * st + 1], s);
+        if (ev && ev[2 * st + 1]) (void)hipEventRecord((hipEvent_t)ev[2 * st + 1], s);
     }
 };
 
