@@ -194,7 +194,7 @@ typedef struct {
 /* The tile configuration a call would use. */
 typedef struct {
     int32_t bucket;        /* smallest power of two >= T, capped at 32768 */
-    int32_t block_m;       /* rows per sorted block */
+    int32_t block_m;       /* rows per sorted block of gemm1 */
     int32_t gemm1_kernel;  /* kernel family of gemm1: 1 bf16 weight-streaming, 3 bf16 LDS-tiled,
                               11 and 13 the same two in MXFP4 mode */
     int32_t gemm2_kernel;  /* kernel family of gemm2: gemm1's plus one */
@@ -202,6 +202,7 @@ typedef struct {
     int32_t gemm2_split_k;
     int32_t config_index;  /* index into the library's config list */
     int32_t num_configs;   /* size of that list */
+    int32_t block_m2;      /* rows per sorted block of gemm2 (a second align when it differs) */
 } moe_config_t;
 
 /* Validate args and report the configuration. Host only. */

@@ -43,7 +43,8 @@ class Config(ctypes.Structure):
     _fields_ = [("bucket", ctypes.c_int32), ("block_m", ctypes.c_int32),
                 ("gemm1_kernel", ctypes.c_int32), ("gemm2_kernel", ctypes.c_int32),
                 ("gemm1_split_k", ctypes.c_int32), ("gemm2_split_k", ctypes.c_int32),
-                ("config_index", ctypes.c_int32), ("num_configs", ctypes.c_int32)]
+                ("config_index", ctypes.c_int32), ("num_configs", ctypes.c_int32),
+                ("block_m2", ctypes.c_int32)]
 
 
 EXPORTS = ("moe_topk_softmax", "moe_align", "moe_align_capacity", "moe_align_workspace_size",

@@ -9,7 +9,9 @@
 // expert's first weight tile must come from the real expert stride, not from
 // I / TileN).
 // Stage 2 (gemm2): h rows times w2_e^T, each fp32 result row written to its
-// flat assignment index a = t*k + j, ready for the slot-ordered combine.
+// flat assignment index a = t*k + j, ready for the slot-ordered combine. h
+// itself is stored by flat assignment index too, so the two stages may use
+// differently padded sorted layouts.
 //
 // Work split. A workgroup is four wave64s. Each wave owns 4 MFMA column
 // blocks of 16 (stage 1: 32 gate + 32 up rows -> 32 h columns; stage 2: 64
@@ -114,15 +116,10 @@ void gemm_stream(GemmParams p) {
     const uint8_t* a_sc[MB];
 #pragma unroll
     for (int mi = 0; mi < MB; ++mi) {
-        const int row = row0 + mi * 16 + r16;
-        int64_t arow = row;
-        // a padding row of stage 2 re-reads the block's first row (a cache
-        // hit) instead of streaming an h row nobody wrote
-        if (STAGE == 2 && p.sorted[row] >= p.A) arow = row0;
-        if (STAGE == 1) {
-            const int a = p.sorted[row];
-            arow = a < p.A ? (int64_t)((unsigned)a / (unsigned)p.k) : 0;
-        }
+        // stage 1 gathers the token row t = a / k; stage 2 the h row of the
+        // flat assignment a; a padding row re-reads row 0
+        const int a = p.sorted[row0 + mi * 16 + r16];
+        const int64_t arow = a < p.A ? (STAGE == 1 ? (int64_t)((unsigned)a / (unsigned)p.k) : (int64_t)a) : 0;
         if (MODE == 0) {
             a_ptr[mi] = reinterpret_cast<const char*>(p.a) + arow * p.a_row * 2;
             a_sc[mi] = nullptr;
@@ -358,8 +355,8 @@ void gemm_stream(GemmParams p) {
             const int col = n0 + np * 16 + r16;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int64_t row = row0 + mi * 16 + kg * 4 + i;
-                h[row * p.N + col] = f32_to_bf16_bits(silu_mul(g[i], u[i]));
+                const int a = p.sorted[row0 + mi * 16 + kg * 4 + i];   // h rows by flat assignment
+                if (a < p.A) h[(int64_t)a * p.N + col] = f32_to_bf16_bits(silu_mul(g[i], u[i]));
             }
         }
     } else if constexpr (STAGE == 1 && MODE == 1) {
@@ -380,13 +377,14 @@ void gemm_stream(GemmParams p) {
                 const E2m1Thresholds th = e2m1_thresholds(s);
                 const uint32_t c0 = e2m1_code(b0, th), c1 = e2m1_code(b1, th);
                 const uint32_t o0 = (uint32_t)__shfl_xor((int)c0, 1), o1 = (uint32_t)__shfl_xor((int)c1, 1);
-                const int64_t row = row0 + mi * 16 + kg * 4 + i;
-                uint8_t* rp = hq + row * (p.N / 2);
+                const int a = p.sorted[row0 + mi * 16 + kg * 4 + i];   // h rows by flat assignment
+                if (a >= p.A) continue;
+                uint8_t* rp = hq + (int64_t)a * (p.N / 2);
                 if ((r16 & 1) == 0) {
                     rp[(n0 + r16) / 2] = (uint8_t)(c0 | (o0 << 4));
                     rp[(n0 + 16 + r16) / 2] = (uint8_t)(c1 | (o1 << 4));
                 }
-                if (r16 == 0) p.out_sc[row * (p.N / 32) + n0 / 32] = (uint8_t)(s + 127);
+                if (r16 == 0) p.out_sc[(int64_t)a * (p.N / 32) + n0 / 32] = (uint8_t)(s + 127);
             }
         }
     } else {

@@ -134,14 +134,12 @@ void gemm_tile(GemmParams p) {
     const int row0 = mb * BM;
     const int n0 = nt * tile_cols;
 
+    // stage 1 gathers the token row t = a / k, stage 2 the h row of the flat
+    // assignment a; a padding row re-reads row 0
     auto a_row_of = [&](int row) -> int64_t {
-        if (STAGE == 1) {
-            const int a = p.sorted[row];
-            return a < p.A ? (int64_t)((unsigned)a / (unsigned)p.k) : 0;
-        }
-        // a padding row re-reads the block's first row instead of an h row
-        // nobody wrote
-        return p.sorted[row] < p.A ? row : row0;
+        const int a = p.sorted[row];
+        if (a >= p.A) return 0;
+        return STAGE == 1 ? (int64_t)((unsigned)a / (unsigned)p.k) : (int64_t)a;
     };
     constexpr int EB = MODE == 0 ? 2 : 1;   // bytes per stride unit
 
@@ -324,8 +322,9 @@ void gemm_tile(GemmParams p) {
                 const int col = n0 + wn * 64 + j * 16 + r16;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int64_t row = row0 + wm * 16 * WMI + mi * 16 + kg * 4 + i;
-                    h[row * p.N + col] = f32_to_bf16_bits(silu_mul(acc[mi][j][i], acc[mi][4 + j][i]));
+                    const int a = p.sorted[row0 + wm * 16 * WMI + mi * 16 + kg * 4 + i];   // by flat assignment
+                    if (a < p.A)
+                        h[(int64_t)a * p.N + col] = f32_to_bf16_bits(silu_mul(acc[mi][j][i], acc[mi][4 + j][i]));
                 }
             }
     } else if constexpr (STAGE == 1 && MODE == 1) {
@@ -347,13 +346,14 @@ void gemm_tile(GemmParams p) {
                     const E2m1Thresholds th = e2m1_thresholds(sx);
                     const uint32_t k0 = e2m1_code(b0, th), k1 = e2m1_code(b1, th);
                     const uint32_t o0 = (uint32_t)__shfl_xor((int)k0, 1), o1 = (uint32_t)__shfl_xor((int)k1, 1);
-                    const int64_t row = row0 + wm * 16 * WMI + mi * 16 + kg * 4 + i;
-                    uint8_t* rp = hq + row * (p.N / 2);
+                    const int a = p.sorted[row0 + wm * 16 * WMI + mi * 16 + kg * 4 + i];   // by flat assignment
+                    if (a >= p.A) continue;
+                    uint8_t* rp = hq + (int64_t)a * (p.N / 2);
                     if ((r16 & 1) == 0) {
                         rp[(c0 + r16) / 2] = (uint8_t)(k0 | (o0 << 4));
                         rp[(c0 + 16 + r16) / 2] = (uint8_t)(k1 | (o1 << 4));
                     }
-                    if (r16 == 0) p.out_sc[row * (p.N / 32) + c0 / 32] = (uint8_t)(sx + 127);
+                    if (r16 == 0) p.out_sc[(int64_t)a * (p.N / 32) + c0 / 32] = (uint8_t)(sx + 127);
                 }
             }
     } else {

@@ -134,15 +134,20 @@ bool valid_bm(int bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128 || 
 struct Cfg {
     int bm, wk1, wk2, nb;
     int tile;    // 0: weight-streaming GEMMs; 1 + shape: LDS-tiled GEMMs of that tile shape
+    int g2;      // -1, or the entry whose gemm2 kernel runs gemm2 (own block size and align)
 };
 const Cfg kConfigs[] = {
-    {16, 4, 4, 4, 0}, {32, 4, 4, 4, 0}, {64, 2, 2, 4, 0},
-    {16, 2, 2, 4, 0}, {32, 2, 2, 4, 0}, {64, 1, 1, 4, 0},
-    {16, 1, 1, 4, 0}, {32, 1, 1, 4, 0}, {128, 1, 1, 4, 0},
-    {32, 1, 1, 2, 0}, {64, 1, 1, 2, 0},    // bf16 only: narrow waves, deep weight ring
-    {256, 1, 1, 4, 1}, {128, 1, 1, 4, 2},   // many rows per expert: weight reuse
-    {64, 1, 1, 4, 3}, {32, 1, 1, 4, 4},     // LDS-staged weight stream
-    {64, 1, 1, 4, 5},
+    {16, 4, 4, 4, 0, -1}, {32, 4, 4, 4, 0, -1}, {64, 2, 2, 4, 0, -1},
+    {16, 2, 2, 4, 0, -1}, {32, 2, 2, 4, 0, -1}, {64, 1, 1, 4, 0, -1},
+    {16, 1, 1, 4, 0, -1}, {32, 1, 1, 4, 0, -1}, {128, 1, 1, 4, 0, -1},
+    {32, 1, 1, 2, 0, -1}, {64, 1, 1, 2, 0, -1},    // bf16 only: narrow waves, deep weight ring
+    {256, 1, 1, 4, 1, -1}, {128, 1, 1, 4, 2, -1},  // many rows per expert: weight reuse
+    {64, 1, 1, 4, 3, -1}, {32, 1, 1, 4, 4, -1},    // LDS-staged weight stream
+    {64, 1, 1, 4, 5, -1},
+    // gemm1 on the register stream, gemm2 on an LDS-staged tile
+    {16, 1, 1, 4, 0, 15}, {16, 2, 2, 4, 0, 15}, {16, 4, 4, 4, 0, 15},
+    {16, 1, 1, 4, 0, 14}, {16, 2, 2, 4, 0, 14}, {16, 4, 4, 4, 0, 14},
+    {64, 1, 1, 4, 0, 13},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -173,7 +178,8 @@ int tile_config(int md, int shape, int64_t H, int64_t I) {
 //  * otherwise the register weight stream, whose block rows cover the
 //    typical busiest expert of the bucket in one block (each expert's
 //    weights stream from HBM once) and whose K split grows only while the
-//    grid would not fill the chip.
+//    grid would not fill the chip; its gemm2 moves to an LDS-staged tile
+//    (own block size, second align) where that measured faster.
 int default_config(int mode, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k) {
     const int64_t bucket = bucket_of(T);
     const double rows = (double)bucket * (double)k / (double)E;   // expected rows per expert
@@ -198,20 +204,40 @@ int default_config(int mode, int64_t T, int64_t H, int64_t I, int64_t E, int64_t
     const int64_t blocks = experts * std::max<int64_t>(1, (int64_t)(rows / bm + 0.999));
     int wk = 1;
     while (wk < 4 && (bm < 64 || wk < 2) && blocks * (I / (32 * (4 / wk))) < 1024) wk <<= 1;
+    // gemm2 from an LDS-staged tile once enough experts are touched to fill
+    // the chip with its wider workgroups and the gain covers the second align
+    int g2 = -1;
+    if (md == 0 && bm == 16 && rows >= 0.5 && tile_config(0, 4, H, I) >= 0) g2 = tile_config(0, 4, H, I);
+    if (md == 1 && bm == 16 && rows >= 4.0 && tile_config(1, 3, H, I) >= 0) g2 = tile_config(1, 3, H, I);
+    if (md == 1 && bm == 64 && tile_config(1, 2, H, I) >= 0) g2 = tile_config(1, 2, H, I);
     for (c = 0; c < kNumConfigs; ++c)
-        if (kConfigs[c].bm == bm && kConfigs[c].wk1 == wk && kConfigs[c].nb == 4 && !kConfigs[c].tile) return c;
+        if (kConfigs[c].bm == bm && kConfigs[c].wk1 == wk && kConfigs[c].nb == 4 && !kConfigs[c].tile &&
+            kConfigs[c].g2 == g2)
+            return c;
+    for (c = 0; c < kNumConfigs; ++c)
+        if (kConfigs[c].bm == bm && kConfigs[c].wk1 == wk && kConfigs[c].nb == 4 && !kConfigs[c].tile &&
+            kConfigs[c].g2 < 0)
+            return c;
     return 0;
 }
+
+// One GEMM's resolved kernel: rows per sorted block, K split and column
+// blocks per wave (register stream), or an LDS tile shape.
+struct KSpec {
+    int bm, wk, nb;
+    int tile;    // 0: register weight stream; 1 + shape: LDS-tiled
+};
 
 struct Plan {
     int mode;
     int64_t T, H, I, E, k, A;
-    Cfg cfg;
+    KSpec ks[2];           // gemm1, gemm2
     int cfg_index;
-    int64_t cap;
+    int64_t cap[2];        // sorted capacity of each GEMM's block size
+    bool two_aligns;       // the GEMMs use different block sizes
     bool pack_x;
     // workspace offsets
-    size_t off_counts, off_sorted, off_bexp, off_npad, off_x, off_xs, off_h, off_hs, off_y, total;
+    size_t off_counts, off_sorted[2], off_bexp[2], off_npad[2], off_x, off_xs, off_h, off_hs, off_y, total;
 };
 
 int kstep(int mode) { return mode == MOE_MODE_MXFP4 ? 128 : 32; }
@@ -297,40 +323,41 @@ int plan_fused(const moe_fused_args_t* a, Plan* pl) {
     int ci = a->force_config;
     if (ci < 0) ci = default_config(a->mode, T, H, I, E, k);
     if (ci >= kNumConfigs) return fail(MOE_ERR_ARG, "force_config %d out of range", ci);
-    Cfg c = kConfigs[ci];
-    // the split of K is a preference: halve it until every wave's share of K
-    // is a whole number of pipelined chunks
-    auto fit = [&](int pref, int stage, int64_t K) {
-        int w = pref;
-        while (w > 1 && K % ((int64_t)gemm_k_granule(GemmKernelId{fp4 ? 1 : 0, stage, c.bm, w, 0, c.nb}) * w) != 0)
-            w >>= 1;
-        return w;
+    const Cfg c1 = kConfigs[ci];
+    const Cfg c2 = c1.g2 >= 0 ? kConfigs[c1.g2] : c1;
+    const int md = fp4 ? 1 : 0;
+    // resolve and check one GEMM's kernel; the split of K is a preference:
+    // halve it until every wave's share of K is a whole number of pipelined
+    // chunks
+    auto resolve = [&](const Cfg& c, int stage, KSpec* ks) -> int {
+        const int64_t K = stage == 1 ? H : I, N = stage == 1 ? I : H;
+        *ks = KSpec{c.bm, stage == 1 ? c.wk1 : c.wk2, c.nb, c.tile};
+        if (c.tile) {
+            const int shape = c.tile - 1;
+            if (!gemm_tile_supported(md, shape))
+                return fail(MOE_ERR_UNSUPPORTED, "config %d: tile shape not built for this mode", ci);
+            ks->bm = gemm_tile_rows(md, shape);
+            const int gran = gemm_tile_k_granule(md, shape);
+            if (K % gran != 0 || N % gemm_tile_cols(shape, stage) != 0)
+                return fail(MOE_ERR_UNSUPPORTED, "config %d: gemm%d needs K %% %d == 0 and N %% %d == 0", ci, stage,
+                            gran, gemm_tile_cols(shape, stage));
+            return MOE_OK;
+        }
+        int w = ks->wk;
+        while (w > 1 && K % ((int64_t)gemm_k_granule(GemmKernelId{md, stage, c.bm, w, 0, c.nb}) * w) != 0) w >>= 1;
+        ks->wk = w;
+        const int gran = gemm_k_granule(GemmKernelId{md, stage, c.bm, 1, 0, c.nb});
+        if (K % gran != 0)
+            return fail(MOE_ERR_UNSUPPORTED, "config %d: gemm%d K = %lld must be a multiple of %d", ci, stage,
+                        (long long)K, gran);
+        GemmKernelId id{md, stage, c.bm, w, gemm_ring_steps(a->mode, c.bm, c.nb, K / w), c.nb};
+        if (!gemm_supported(id)) return fail(MOE_ERR_UNSUPPORTED, "config %d not built", ci);
+        if (N % gemm_tile_n(id) != 0)
+            return fail(MOE_ERR_UNSUPPORTED, "config %d: gemm%d N not a multiple of the tile width", ci, stage);
+        return MOE_OK;
     };
-    if (c.tile) {
-        const int shape = c.tile - 1, md = fp4 ? 1 : 0;
-        const int gran = gemm_tile_k_granule(md, shape);
-        if (!gemm_tile_supported(md, shape))
-            return fail(MOE_ERR_UNSUPPORTED, "config %d: tile shape not built for this mode", ci);
-        c.bm = gemm_tile_rows(md, shape);
-        if (H % gran != 0 || I % gran != 0 || I % gemm_tile_cols(shape, 1) != 0 ||
-            H % gemm_tile_cols(shape, 2) != 0)
-            return fail(MOE_ERR_UNSUPPORTED,
-                        "config %d: H = %lld and I = %lld must be multiples of %d, I of %d and H of %d", ci,
-                        (long long)H, (long long)I, gran, gemm_tile_cols(shape, 1), gemm_tile_cols(shape, 2));
-    } else {
-        c.wk1 = fit(c.wk1, 1, H);
-        c.wk2 = fit(c.wk2, 2, I);
-        const int gran = gemm_k_granule(GemmKernelId{fp4 ? 1 : 0, 1, c.bm, 1, 0, c.nb});
-        if (H % gran != 0 || I % gran != 0)
-            return fail(MOE_ERR_UNSUPPORTED, "H = %lld and I = %lld must be multiples of %d", (long long)H,
-                        (long long)I, gran);
-        GemmKernelId g1{fp4 ? 1 : 0, 1, c.bm, c.wk1, gemm_ring_steps(a->mode, c.bm, c.nb, H / c.wk1), c.nb};
-        GemmKernelId g2{fp4 ? 1 : 0, 2, c.bm, c.wk2, gemm_ring_steps(a->mode, c.bm, c.nb, I / c.wk2), c.nb};
-        if (!gemm_supported(g1) || !gemm_supported(g2))
-            return fail(MOE_ERR_UNSUPPORTED, "config %d not built", ci);
-        if (I % gemm_tile_n(g1) != 0 || H % gemm_tile_n(g2) != 0)
-            return fail(MOE_ERR_UNSUPPORTED, "config %d: I or H not a multiple of the tile width", ci);
-    }
+    if ((rc = resolve(c1, 1, &pl->ks[0]))) return rc;
+    if ((rc = resolve(c2, 2, &pl->ks[1]))) return rc;
 
     pl->mode = a->mode;
     pl->T = T;
@@ -339,20 +366,23 @@ int plan_fused(const moe_fused_args_t* a, Plan* pl) {
     pl->E = E;
     pl->k = k;
     pl->A = T * k;
-    pl->cfg = c;
     pl->cfg_index = ci;
-    pl->cap = align_capacity(pl->A, E, c.bm);
+    pl->cap[0] = align_capacity(pl->A, E, pl->ks[0].bm);
+    pl->cap[1] = align_capacity(pl->A, E, pl->ks[1].bm);
+    pl->two_aligns = pl->ks[0].bm != pl->ks[1].bm;
     const bool x_direct = a->x.stride[1] == 1 && aligned16(a->x.data) &&
                           (T <= 1 || (a->x.stride[0] * 2) % 16 == 0);
     pl->pack_x = !fp4 && !x_direct;
-    if (c.tile) {
+    {
         // the tiled kernels address every operand row with a 32-bit offset
         const int64_t eb = fp4 ? 1 : 2;
         const int64_t x_row = fp4 ? H / 2 : (pl->pack_x ? H * 2 : a->x.stride[0] * 2);
         const int64_t lim = (int64_t)1 << 31;
-        if (T * x_row >= lim || pl->cap * I * eb >= lim || I * a->gate.stride[1] * eb >= lim ||
-            I * a->up.stride[1] * eb >= lim || H * a->w2.stride[1] * eb >= lim)
-            return fail(MOE_ERR_UNSUPPORTED, "config %d: operands too large for the tiled kernels", ci);
+        if (pl->ks[0].tile && (T * x_row >= lim || I * a->gate.stride[1] * eb >= lim ||
+                               I * a->up.stride[1] * eb >= lim))
+            return fail(MOE_ERR_UNSUPPORTED, "config %d: operands too large for the tiled gemm1", ci);
+        if (pl->ks[1].tile && (pl->A * I * eb >= lim || H * a->w2.stride[1] * eb >= lim))
+            return fail(MOE_ERR_UNSUPPORTED, "config %d: operands too large for the tiled gemm2", ci);
     }
 
     size_t off = 0;
@@ -362,9 +392,17 @@ int plan_fused(const moe_fused_args_t* a, Plan* pl) {
         return o;
     };
     pl->off_counts = take(align_scratch_bytes(pl->A, (int32_t)E));
-    pl->off_sorted = take((size_t)pl->cap * 4);
-    pl->off_bexp = take((size_t)(pl->cap / c.bm) * 4);
-    pl->off_npad = take(4);
+    for (int g = 0; g < 2; ++g) {
+        if (g == 1 && !pl->two_aligns) {
+            pl->off_sorted[1] = pl->off_sorted[0];
+            pl->off_bexp[1] = pl->off_bexp[0];
+            pl->off_npad[1] = pl->off_npad[0];
+            break;
+        }
+        pl->off_sorted[g] = take((size_t)pl->cap[g] * 4);
+        pl->off_bexp[g] = take((size_t)(pl->cap[g] / pl->ks[g].bm) * 4);
+        pl->off_npad[g] = take(4);
+    }
     pl->off_x = pl->off_xs = 0;
     if (fp4) {
         pl->off_x = take((size_t)T * (size_t)(H / 2));
@@ -372,11 +410,12 @@ int plan_fused(const moe_fused_args_t* a, Plan* pl) {
     } else if (pl->pack_x) {
         pl->off_x = take((size_t)T * (size_t)H * 2);
     }
+    // h rows by flat assignment index
     if (fp4) {
-        pl->off_h = take((size_t)pl->cap * (size_t)(I / 2));
-        pl->off_hs = take((size_t)pl->cap * (size_t)(I / 32));
+        pl->off_h = take((size_t)pl->A * (size_t)(I / 2));
+        pl->off_hs = take((size_t)pl->A * (size_t)(I / 32));
     } else {
-        pl->off_h = take((size_t)pl->cap * (size_t)I * 2);
+        pl->off_h = take((size_t)pl->A * (size_t)I * 2);
         pl->off_hs = 0;
     }
     pl->off_y = take((size_t)pl->A * (size_t)H * (fp4 ? 2 : 4));   // y: bf16 in MXFP4 mode
@@ -569,12 +608,13 @@ int moe_query_config(const moe_fused_args_t* args, moe_config_t* cfg) {
     int rc = plan_fused(args, &pl);
     if (rc) return rc;
     cfg->bucket = bucket_of(pl.T);
-    cfg->block_m = pl.cfg.bm;
-    const int fam = (args->mode == MOE_MODE_MXFP4 ? 10 : 0) + (pl.cfg.tile ? 2 : 0);
-    cfg->gemm1_kernel = fam + 1;
-    cfg->gemm2_kernel = fam + 2;
-    cfg->gemm1_split_k = pl.cfg.wk1;
-    cfg->gemm2_split_k = pl.cfg.wk2;
+    cfg->block_m = pl.ks[0].bm;
+    cfg->block_m2 = pl.ks[1].bm;
+    const int base = args->mode == MOE_MODE_MXFP4 ? 10 : 0;
+    cfg->gemm1_kernel = base + (pl.ks[0].tile ? 2 : 0) + 1;
+    cfg->gemm2_kernel = base + (pl.ks[1].tile ? 2 : 0) + 2;
+    cfg->gemm1_split_k = pl.ks[0].tile ? 1 : pl.ks[0].wk;
+    cfg->gemm2_split_k = pl.ks[1].tile ? 1 : pl.ks[1].wk;
     cfg->config_index = pl.cfg_index;
     cfg->num_configs = kNumConfigs;
     return ok();
@@ -601,27 +641,32 @@ int moe_fused_fwd(const moe_fused_args_t* args, void* ws, size_t ws_bytes, moe_s
     char* base = (char*)ws;
     const StageTimer tm{a.stage_events, s};
     const bool fp4 = pl.mode == MOE_MODE_MXFP4;
-    int32_t* sorted = (int32_t*)(base + pl.off_sorted);
-    int32_t* bexp = (int32_t*)(base + pl.off_bexp);
-    int32_t* npad = (int32_t*)(base + pl.off_npad);
+    int32_t *sorted[2], *bexp[2], *npad[2];
+    for (int g = 0; g < 2; ++g) {
+        sorted[g] = (int32_t*)(base + pl.off_sorted[g]);
+        bexp[g] = (int32_t*)(base + pl.off_bexp[g]);
+        npad[g] = (int32_t*)(base + pl.off_npad[g]);
+    }
     hipError_t e;
 
-    // stage 0: align
+    // stage 0: align (once per distinct block size of the two GEMMs)
     tm.begin(0);
-    AlignParams ap{};
-    ap.ids = (const int32_t*)a.topk_ids.data;
-    ap.is_t = a.topk_ids.stride[0];
-    ap.is_j = a.topk_ids.stride[1];
-    ap.T = (int32_t)pl.T;
-    ap.k = (int32_t)pl.k;
-    ap.A = (int32_t)pl.A;
-    ap.E = (int32_t)pl.E;
-    ap.bm = pl.cfg.bm;
-    ap.sorted = sorted;
-    ap.block_expert = bexp;
-    ap.n_padded = npad;
-    ap.counts = (int32_t*)(base + pl.off_counts);
-    if ((e = launch_align(ap, s)) != hipSuccess) return hip_fail(e, "align");
+    for (int g = 0; g < (pl.two_aligns ? 2 : 1); ++g) {
+        AlignParams ap{};
+        ap.ids = (const int32_t*)a.topk_ids.data;
+        ap.is_t = a.topk_ids.stride[0];
+        ap.is_j = a.topk_ids.stride[1];
+        ap.T = (int32_t)pl.T;
+        ap.k = (int32_t)pl.k;
+        ap.A = (int32_t)pl.A;
+        ap.E = (int32_t)pl.E;
+        ap.bm = pl.ks[g].bm;
+        ap.sorted = sorted[g];
+        ap.block_expert = bexp[g];
+        ap.n_padded = npad[g];
+        ap.counts = (int32_t*)(base + pl.off_counts);
+        if ((e = launch_align(ap, s)) != hipSuccess) return hip_fail(e, "align");
+    }
     tm.end(0);
 
     // stage 1: prepare the activation operand
@@ -657,13 +702,20 @@ int moe_fused_fwd(const moe_fused_args_t* args, void* ws, size_t ws_bytes, moe_s
     }
     tm.end(1);
 
-    const int32_t max_mblocks = (int32_t)(pl.cap / pl.cfg.bm);
+    // launch one GEMM with its resolved kernel
+    auto launch = [&](int g, const GemmParams& gp) -> hipError_t {
+        const KSpec& k = pl.ks[g];
+        if (k.tile) return launch_gemm_tile(fp4 ? 1 : 0, k.tile - 1, g + 1, gp, s);
+        GemmKernelId id{fp4 ? 1 : 0, g + 1, k.bm, k.wk,
+                        gemm_ring_steps(pl.mode, k.bm, k.nb, (g == 0 ? pl.H : pl.I) / k.wk), k.nb};
+        return launch_gemm(id, gp, s);
+    };
     // stage 2: gemm1 + SiLU(gate) * up
     tm.begin(2);
     GemmParams g1{};
-    g1.sorted = sorted;
-    g1.block_expert = bexp;
-    g1.n_padded = npad;
+    g1.sorted = sorted[0];
+    g1.block_expert = bexp[0];
+    g1.n_padded = npad[0];
     g1.A = (int32_t)pl.A;
     g1.k = (int32_t)pl.k;
     g1.E = (int32_t)pl.E;
@@ -690,23 +742,16 @@ int moe_fused_fwd(const moe_fused_args_t* args, void* ws, size_t ws_bytes, moe_s
     g1.out = base + pl.off_h;
     g1.out_sc = fp4 ? (uint8_t*)(base + pl.off_hs) : nullptr;
     g1.n_tile_groups = 2;
-    g1.max_mblocks = max_mblocks;
-    if (pl.cfg.tile) {
-        e = launch_gemm_tile(fp4 ? 1 : 0, pl.cfg.tile - 1, 1, g1, s);
-    } else {
-        GemmKernelId k1{fp4 ? 1 : 0, 1, pl.cfg.bm, pl.cfg.wk1,
-                        gemm_ring_steps(pl.mode, pl.cfg.bm, pl.cfg.nb, pl.H / pl.cfg.wk1), pl.cfg.nb};
-        e = launch_gemm(k1, g1, s);
-    }
-    if (e != hipSuccess) return hip_fail(e, "gemm1");
+    g1.max_mblocks = (int32_t)(pl.cap[0] / pl.ks[0].bm);
+    if ((e = launch(0, g1)) != hipSuccess) return hip_fail(e, "gemm1");
     tm.end(2);
 
     // stage 3: gemm2
     tm.begin(3);
     GemmParams g2{};
-    g2.sorted = sorted;
-    g2.block_expert = bexp;
-    g2.n_padded = npad;
+    g2.sorted = sorted[1];
+    g2.block_expert = bexp[1];
+    g2.n_padded = npad[1];
     g2.A = (int32_t)pl.A;
     g2.k = (int32_t)pl.k;
     g2.E = (int32_t)pl.E;
@@ -726,15 +771,8 @@ int moe_fused_fwd(const moe_fused_args_t* args, void* ws, size_t ws_bytes, moe_s
     g2.N = (int32_t)pl.H;
     g2.out = base + pl.off_y;
     g2.n_tile_groups = 2;
-    g2.max_mblocks = max_mblocks;
-    if (pl.cfg.tile) {
-        e = launch_gemm_tile(fp4 ? 1 : 0, pl.cfg.tile - 1, 2, g2, s);
-    } else {
-        GemmKernelId k2{fp4 ? 1 : 0, 2, pl.cfg.bm, pl.cfg.wk2,
-                        gemm_ring_steps(pl.mode, pl.cfg.bm, pl.cfg.nb, pl.I / pl.cfg.wk2), pl.cfg.nb};
-        e = launch_gemm(k2, g2, s);
-    }
-    if (e != hipSuccess) return hip_fail(e, "gemm2");
+    g2.max_mblocks = (int32_t)(pl.cap[1] / pl.ks[1].bm);
+    if ((e = launch(1, g2)) != hipSuccess) return hip_fail(e, "gemm2");
     tm.end(3);
 
     // stage 4: combine

@@ -172,8 +172,9 @@ struct GemmParams {
     int32_t K;              // contraction length
     int32_t N;              // output columns (stage 1: I, stage 2: H)
     // outputs
-    void* out;              // stage 1: h (bf16 [P, I] or fp4 [P, I/2]); stage 2: y [A, H] (fp32 / MXFP4: bf16)
-    uint8_t* out_sc;        // stage 1 MXFP4: h scales [P, I/32]
+    void* out;              // stage 1: h (bf16 [A, I] or fp4 [A, I/2]); stage 2: y [A, H] (fp32 / MXFP4: bf16);
+                            // both by flat assignment index
+    uint8_t* out_sc;        // stage 1 MXFP4: h scales [A, I/32]
     int32_t n_tile_groups;  // tiles along N are walked in groups of this size
     int32_t max_mblocks;
 };
