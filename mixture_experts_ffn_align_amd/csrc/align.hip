@@ -152,7 +152,7 @@ __device__ void layout_experts(const AlignParams& p, const int* tot, int* off, i
 }
 
 // Whole align in one workgroup.
-__global__ __launch_bounds__(kFusedThreads) void align_fused(AlignParams p) {
+__device__ void align_fused_body(const AlignParams& p) {
     extern __shared__ int lds[];
     const int E = p.E;
     int* wcnt = lds;                          // [kFusedWaves][E]
@@ -183,6 +183,19 @@ __global__ __launch_bounds__(kFusedThreads) void align_fused(AlignParams p) {
         for (int v = 0; v < kFusedWaves; ++v) wcnt[v * E + e] += off[e];
     __syncthreads();
     wave_scatter(p, lo, hi, eid, wcnt + w * E);
+}
+
+__global__ __launch_bounds__(kFusedThreads) void align_fused(AlignParams p) { align_fused_body(p); }
+
+// Workgroup 0 aligns; workgroups 1.. quantise the activation to MXFP4, one
+// thread per group of 32 values (neither depends on the other).
+__global__ __launch_bounds__(kFusedThreads) void align_fused_quant(AlignParams p, QuantParams q) {
+    if (blockIdx.x == 0) {
+        align_fused_body(p);
+        return;
+    }
+    const int64_t g = (int64_t)(blockIdx.x - 1) * kFusedThreads + threadIdx.x;
+    if (g < q.E * q.R * (q.K / 32)) quant_group_mxfp4(q, g);
 }
 
 // Multi-block phase 1: counts[b][e] for chunk b.
@@ -266,6 +279,17 @@ bool use_fused(int A, int E) {
 }
 
 }  // namespace
+
+bool align_single_launch(int64_t A, int32_t E) { return use_fused((int)A, E); }
+
+hipError_t launch_align_with_quant(const AlignParams& p, const QuantParams& q, hipStream_t s) {
+    if (!use_fused(p.A, p.E)) return hipErrorInvalidValue;
+    const int64_t groups = q.E * q.R * (q.K / 32);
+    const size_t lds = sizeof(int) * ((size_t)kFusedWaves * p.E + 2 * p.E + kFusedWaves + 1);
+    const int64_t grid = 1 + (groups + kFusedThreads - 1) / kFusedThreads;
+    hipLaunchKernelGGL(align_fused_quant, dim3((unsigned)grid), dim3(kFusedThreads), lds, s, p, q);
+    return hipGetLastError();
+}
 
 size_t align_scratch_bytes(int64_t A, int32_t E) {
     if (use_fused((int)A, E)) return 0;

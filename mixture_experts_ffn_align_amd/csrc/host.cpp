@@ -649,6 +649,23 @@ int moe_fused_fwd(const moe_fused_args_t* args, void* ws, size_t ws_bytes, moe_s
     }
     hipError_t e;
 
+    // MXFP4 activation quantisation: its own launch in stage 1, or folded
+    // into the single-workgroup align launch of stage 0
+    QuantParams qp{};
+    if (fp4) {
+        qp.src = (const uint16_t*)a.x.data;
+        qp.E = 1;
+        qp.R = pl.T;
+        qp.K = pl.H;
+        qp.ss_r = a.x.stride[0];
+        qp.ss_k = a.x.stride[1];
+        qp.codes = (uint8_t*)(base + pl.off_x);
+        qp.cs_r = pl.H / 2;
+        qp.scales = (uint8_t*)(base + pl.off_xs);
+        qp.xs_r = pl.H / 32;
+    }
+    const bool quant_in_align = fp4 && align_single_launch(pl.A, (int32_t)pl.E);
+
     // stage 0: align (once per distinct block size of the two GEMMs)
     tm.begin(0);
     for (int g = 0; g < (pl.two_aligns ? 2 : 1); ++g) {
@@ -665,7 +682,8 @@ int moe_fused_fwd(const moe_fused_args_t* args, void* ws, size_t ws_bytes, moe_s
         ap.block_expert = bexp[g];
         ap.n_padded = npad[g];
         ap.counts = (int32_t*)(base + pl.off_counts);
-        if ((e = launch_align(ap, s)) != hipSuccess) return hip_fail(e, "align");
+        e = (g == 0 && quant_in_align) ? launch_align_with_quant(ap, qp, s) : launch_align(ap, s);
+        if (e != hipSuccess) return hip_fail(e, "align");
     }
     tm.end(0);
 
@@ -674,18 +692,7 @@ int moe_fused_fwd(const moe_fused_args_t* args, void* ws, size_t ws_bytes, moe_s
     const void* a_op = a.x.data;
     int64_t a_row = a.x.stride[0];
     if (fp4) {
-        QuantParams qp{};
-        qp.src = (const uint16_t*)a.x.data;
-        qp.E = 1;
-        qp.R = pl.T;
-        qp.K = pl.H;
-        qp.ss_r = a.x.stride[0];
-        qp.ss_k = a.x.stride[1];
-        qp.codes = (uint8_t*)(base + pl.off_x);
-        qp.cs_r = pl.H / 2;
-        qp.scales = (uint8_t*)(base + pl.off_xs);
-        qp.xs_r = pl.H / 32;
-        if ((e = launch_quant_mxfp4(qp, s)) != hipSuccess) return hip_fail(e, "quant x");
+        if (!quant_in_align && (e = launch_quant_mxfp4(qp, s)) != hipSuccess) return hip_fail(e, "quant x");
         a_op = base + pl.off_x;
         a_row = pl.H / 2;
     } else if (pl.pack_x) {

@@ -128,6 +128,12 @@ struct AlignParams {
 // Scratch bytes the multi-block path needs for A assignments over E experts.
 size_t align_scratch_bytes(int64_t A, int32_t E);
 hipError_t launch_align(const AlignParams& p, hipStream_t s);
+// The align in one workgroup (A and E small enough) with the MXFP4
+// quantisation q of the activation in the other workgroups of the same
+// launch; false if the align needs several launches (nothing launched).
+bool align_single_launch(int64_t A, int32_t E);
+struct QuantParams;
+hipError_t launch_align_with_quant(const AlignParams& p, const QuantParams& q, hipStream_t s);
 
 struct QuantParams {
     const uint16_t* src;
@@ -139,6 +145,59 @@ struct QuantParams {
     int64_t E, R, K;            // leading count (1 for 2-D), rows, K
 };
 hipError_t launch_quant_mxfp4(const QuantParams& p, hipStream_t s);
+
+// Quantise group g (32 consecutive values of one row) of p; g < E * R * K/32.
+__device__ __forceinline__ void quant_group_mxfp4(const QuantParams& p, int64_t g) {
+    const int64_t groups_per_row = p.K / 32;
+    const int64_t kb = g % groups_per_row;
+    const int64_t rr = g / groups_per_row;
+    const int64_t r = rr % p.R;
+    const int64_t e = rr / p.R;
+    const uint16_t* src = p.src + e * p.ss_e + r * p.ss_r + kb * 32 * p.ss_k;
+    uint16_t v[32];
+    const bool vec = p.ss_k == 1 && ((uintptr_t)src & 15u) == 0;
+    if (vec) {
+        const uint4* s4 = reinterpret_cast<const uint4*>(src);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            uint4 q = s4[i];
+            uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                v[i * 8 + 2 * h] = (uint16_t)(w[h] & 0xffffu);
+                v[i * 8 + 2 * h + 1] = (uint16_t)(w[h] >> 16);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) v[i] = src[(int64_t)i * p.ss_k];
+    }
+    // |v| compares as an integer for finite bf16 values
+    uint32_t amax = 0;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        uint32_t a = v[i] & 0x7fffu;
+        amax = a > amax ? a : amax;
+    }
+    const int s = group_exponent(amax << 16);
+    const E2m1Thresholds th = e2m1_thresholds(s);
+    uint32_t packed[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) word |= e2m1_code((uint32_t)v[q * 8 + i] << 16, th) << (4 * i);
+        packed[q] = word;
+    }
+    uint8_t* dst = p.codes + e * p.cs_e + r * p.cs_r + kb * 16;
+    if (((uintptr_t)dst & 15u) == 0) {
+        *reinterpret_cast<uint4*>(dst) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dst[i] = (uint8_t)(packed[i / 4] >> (8 * (i % 4)));
+    }
+    p.scales[e * p.xs_e + r * p.xs_r + kb] = (uint8_t)(s + 127);
+}
 
 struct PackParams {
     const uint16_t* src;
