@@ -80,12 +80,20 @@ void gemm_stream(GemmParams p) {
     constexpr int WCOLS = STAGE == 1 ? NB * 8 : NB * 16;
     constexpr int TILE_N = WN * WCOLS;
     // 1 KB A fragments per LDS buffer: room for a chunk of at least 2U steps
-    constexpr int FRAGS = (U * WK * MB > 16) ? U * WK * MB : 16;
+    // (MXFP4 with a 4-step ring stages its weight scales in LDS and keeps
+    // 8-fragment A chunks so that three workgroups still fit a CU)
+    constexpr bool SC_LDS = MODE == 1 && U == 4;
+    constexpr int FRAGS_MIN = SC_LDS ? 8 : 16;
+    constexpr int FRAGS = (U * WK * MB > FRAGS_MIN) ? U * WK * MB : FRAGS_MIN;
     static_assert(FRAGS % 4 == 0 && 2 * FRAGS <= 64, "A staging must fit 64 KB of LDS");
     constexpr int RED_FLOATS = 4 * MB * NB * 4 * 64;
     constexpr int LDS_FLOATS = (WK > 1 && RED_FLOATS > 2 * FRAGS * 256) ? RED_FLOATS : 2 * FRAGS * 256;
     constexpr int AREGS = FRAGS / 4;      // fragments one wave stages per chunk (at most)
     __shared__ __attribute__((aligned(16))) float lds[LDS_FLOATS];
+    // MXFP4 weight scales of the wave's 64 rows over its whole K share
+    // (row-major, K/32 bytes per row, for K up to 4096), loaded once
+    constexpr int SC_ROW_MAX = 128 / WK;
+    __shared__ __attribute__((aligned(16))) uint8_t sc_lds[SC_LDS ? 4 * 64 * SC_ROW_MAX : 16];
 
     const int lane = lane_id();
     const int w = threadIdx.x >> 6;
@@ -233,13 +241,43 @@ void gemm_stream(GemmParams p) {
             asc[mi] = v;
         }
     };
+    // The weight scales of a row are one contiguous run of K/32 bytes; read
+    // window by window from global memory, a run is fetched again for every
+    // window once the weight stream has evicted it. Where the run fits
+    // (K <= 4096), each wave loads its 64 rows' runs once, straight into
+    // LDS, and the windows are read from there.
+    // (the host gives MXFP4 a 4-step ring only for a K share of at most
+    // 4096, so the run of every row fits)
+    const int sc_bpr = kw / 32;                          // scale bytes per row of the K share
+    uint8_t* const sc_wave = sc_lds + w * 64 * SC_ROW_MAX;
+    if constexpr (SC_LDS) {
+        // instruction i: rows i*rpi .. +rpi, lpr lanes x 16 bytes per row;
+        // LDS block i (1 KB) is rows i*rpi .. in row-major order
+        const int lpr = sc_bpr / 16, rpi = 64 / lpr;
+        const int rr = lane / lpr, cc = lane % lpr;
+        for (int i = 0; i < lpr; ++i) {
+            const int row = i * rpi + rr;                 // 0 .. 63
+            const int nb = row / 16, r = row % 16;
+            const bool second = STAGE == 1 && nb >= NB / 2;
+            const int wrow = STAGE == 1 ? n0 + (nb % (NB / 2)) * 16 + r : n0 + nb * 16 + r;
+            const uint8_t* src = (second ? p.b1_sc : p.b0_sc) + (int64_t)e * (second ? p.b1sc_e : p.b0sc_e) +
+                                 (int64_t)wrow * (second ? p.b1sc_r : p.b0sc_r) + wk * sc_bpr + cc * 16;
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
+                                             (__attribute__((address_space(3))) void*)(sc_wave + i * 1024), 16, 0,
+                                             0);
+        }
+    }
     auto load_scales = [&](uint32_t (&bdst)[NB][U], uint32_t (&adst)[MB][U], int s0) {
         if constexpr (MODE == 1) {
             s0 = s0 < steps - U ? s0 : steps - U;
             const int kb0 = (wk * kw + s0 * KSTEP) / 32;     // a multiple of 4*U
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-                const SW v = *reinterpret_cast<const SW*>(b_sc[nb] + kb0);
+                SW v;
+                if constexpr (SC_LDS)
+                    v = *reinterpret_cast<const SW*>(sc_wave + (nb * 16 + r16) * sc_bpr + s0 * (KSTEP / 32));
+                else
+                    v = *reinterpret_cast<const SW*>(b_sc[nb] + kb0);
 #pragma unroll
                 for (int u = 0; u < U; ++u) bdst[nb][u] = (uint32_t)v[u];
             }
@@ -463,7 +501,8 @@ int gemm_ring_steps(int mode, int bm, int nb, int64_t k_per_wave) {
     if (mode == 0 && nb == 2) return 8;
     if (bm >= 128) return 2;
     if (mode == 0) return 4;
-    return k_per_wave % (128 * 4) == 0 ? 4 : 2;
+    // a 4-step MXFP4 ring stages the share's weight scales in LDS (K <= 4096)
+    return k_per_wave % (128 * 4) == 0 && k_per_wave <= 4096 ? 4 : 2;
 }
 
 int gemm_k_granule(const GemmKernelId& id) {

@@ -25,7 +25,16 @@
 // contiguous bytes). 4 / SUBS stage buffers rotate, the loads of the stage
 // 4 / SUBS - 1 ahead are issued while a stage is multiplied, and one
 // workgroup barrier per stage publishes a landed stage and retires a consumed
-// one.
+// one. The 8-wave bf16 shapes run the two waves of each SIMD half a stage
+// apart instead (two barriers per stage): one multiplies from registers while
+// the other reads its fragments, so the matrix core is never left waiting
+// for a whole workgroup's LDS reads after a barrier.
+//
+// Epilogues. The weight fragment is the MFMA's first operand, so a lane's
+// accumulator holds 4 consecutive output columns of one row. h and y rows go
+// out through a small wave-private LDS patch and leave as 16-byte stores
+// that fill whole cache lines; y, read once by the combine much later, is
+// stored non-temporally.
 //
 // LDS layout. Rows are stored row-major, the 16-byte chunk c of tile row r at
 // chunk position c ^ g(r): g(r) = r / 4 (mod 4) for 64-byte rows and
@@ -39,6 +48,8 @@
 // blocks of one weight tile, so the row blocks of an expert stream its weight
 // tile through that XCD's L2 together (the token rows, a few MB, are re-read
 // once per weight tile from the L2 / MALL).
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -48,6 +59,7 @@ constexpr int kBlock = 1024;       // bytes one load instruction writes
 constexpr int kScStep = 4;         // e8m0 bytes of one row per k-step
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
 
 // BM rows x BW weight rows per workgroup of NW waves, SUBS k-steps of
 // 64 bytes per row per stage, NBUF stage buffers; a wave multiplies 16 WMI
@@ -99,7 +111,7 @@ __device__ __forceinline__ void wait_vm_lgkm() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
 }
 
-template <int MODE, int STAGE, int BM, int BW, int NW, int SUBS, int NBUF>
+template <int MODE, int STAGE, int BM, int BW, int NW, int SUBS, int NBUF, bool PP>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void gemm_tile(GemmParams p) {
     using TS = TileShape<MODE, BM, BW, NW, SUBS, NBUF>;
@@ -114,7 +126,7 @@ void gemm_tile(GemmParams p) {
     __shared__ __attribute__((aligned(16))) char lds3[NBUF == 4 ? BUF : 16];
 
     const int lane = lane_id();
-    const int w = threadIdx.x >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: addresses in SGPRs
     const int wm = w / kWN, wn = w % kWN;
     const int r16 = lane & 15, kg = lane >> 4;
 
@@ -229,41 +241,54 @@ void gemm_tile(GemmParams p) {
         if (STAGE == 1) return ni < 4 ? wn * 4 + ni : BW / 32 + wn * 4 + (ni - 4);
         return wn * 8 + ni;
     };
+    // fragments of one k-step u of a stage buffer: row block rb of the tile
+    // is LDS row 16 rb + r16, chunk 4 u + kg
+    struct Frags {
+        i32x4_t a[WMI], b[8];
+        uint32_t as[WMI], bs[8];
+    };
+    auto read_frags = [&](const char* buf, int u, Frags& f) {
+        const int rd = r16 * kRowBytes + swz(r16, 4 * u + kg) * 16;
+#pragma unroll
+        for (int mi = 0; mi < WMI; ++mi)
+            f.a[mi] = *reinterpret_cast<const i32x4_t*>(buf + (wm * WMI + mi) * 16 * kRowBytes + rd);
+#pragma unroll
+        for (int ni = 0; ni < 8; ++ni)
+            f.b[ni] = *reinterpret_cast<const i32x4_t*>(buf + (BM + b_rb(ni) * 16) * kRowBytes + rd);
+        if constexpr (MODE == 1) {
+            const uint8_t* sb = reinterpret_cast<const uint8_t*>(buf + TS::kScOff + u * TS::kScPlane);
+#pragma unroll
+            for (int mi = 0; mi < WMI; ++mi) f.as[mi] = sb[((wm * WMI + mi) * 16 + r16) * kScStep + kg];
+#pragma unroll
+            for (int ni = 0; ni < 8; ++ni) f.bs[ni] = sb[(BM + b_rb(ni) * 16 + r16) * kScStep + kg];
+        }
+    };
+    // weight fragment first: the accumulator then holds, in lane l, 4
+    // consecutive output columns 4 (l / 16) .. +3 of row l % 16, so the
+    // epilogues store 8 or 16 contiguous bytes per lane
+    auto mfma_frags = [&](const Frags& f) {
+#pragma unroll
+        for (int mi = 0; mi < WMI; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < 8; ++ni) {
+                if constexpr (MODE == 0) {
+                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, f.b[ni]),
+                                                                          __builtin_bit_cast(bf16x8_t, f.a[mi]),
+                                                                          acc[mi][ni], 0, 0, 0);
+                } else {
+                    const i32x8_t a8 = {f.a[mi][0], f.a[mi][1], f.a[mi][2], f.a[mi][3], 0, 0, 0, 0};
+                    const i32x8_t b8 = {f.b[ni][0], f.b[ni][1], f.b[ni][2], f.b[ni][3], 0, 0, 0, 0};
+                    acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b8, a8, acc[mi][ni], 4, 4, 0,
+                                                                                   (int)f.bs[ni], 0, (int)f.as[mi]);
+                }
+            }
+    };
     auto compute = [&](const char* buf) {
 #pragma unroll
         for (int u = 0; u < SUBS; ++u) {
-            // fragment row block rb: row 16 rb + r16, chunk 4 u + kg
-            const int rd = r16 * kRowBytes + swz(r16, 4 * u + kg) * 16;
-            i32x4_t af[WMI], bf[8];
-            uint32_t as[WMI], bs[8];
-#pragma unroll
-            for (int mi = 0; mi < WMI; ++mi)
-                af[mi] = *reinterpret_cast<const i32x4_t*>(buf + (wm * WMI + mi) * 16 * kRowBytes + rd);
-#pragma unroll
-            for (int ni = 0; ni < 8; ++ni)
-                bf[ni] = *reinterpret_cast<const i32x4_t*>(buf + (BM + b_rb(ni) * 16) * kRowBytes + rd);
-            if constexpr (MODE == 1) {
-                const uint8_t* sb = reinterpret_cast<const uint8_t*>(buf + TS::kScOff + u * TS::kScPlane);
-#pragma unroll
-                for (int mi = 0; mi < WMI; ++mi) as[mi] = sb[((wm * WMI + mi) * 16 + r16) * kScStep + kg];
-#pragma unroll
-                for (int ni = 0; ni < 8; ++ni) bs[ni] = sb[(BM + b_rb(ni) * 16 + r16) * kScStep + kg];
-            }
-#pragma unroll
-            for (int mi = 0; mi < WMI; ++mi)
-#pragma unroll
-                for (int ni = 0; ni < 8; ++ni) {
-                    if constexpr (MODE == 0) {
-                        acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8_t, af[mi]), __builtin_bit_cast(bf16x8_t, bf[ni]), acc[mi][ni],
-                            0, 0, 0);
-                    } else {
-                        const i32x8_t a8 = {af[mi][0], af[mi][1], af[mi][2], af[mi][3], 0, 0, 0, 0};
-                        const i32x8_t b8 = {bf[ni][0], bf[ni][1], bf[ni][2], bf[ni][3], 0, 0, 0, 0};
-                        acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                            a8, b8, acc[mi][ni], 4, 4, 0, (int)as[mi], 0, (int)bs[ni]);
-                    }
-                }
+            Frags f;
+            read_frags(buf, u, f);
+            mfma_frags(f);
         }
     };
     // stage s's loads have landed for every wave and every wave is done with
@@ -279,7 +304,91 @@ void gemm_tile(GemmParams p) {
 
     // ---- pipeline over kNBuf rotating buffers: stage s in buffer s % kNBuf,
     // stage s + kNBuf - 1 loading into the buffer stage s - 1 used
-    if constexpr (NBUF == 4) {
+    if constexpr (PP) {
+        // Two wave groups, one wave of each per SIMD, half a stage apart:
+        // while one group multiplies from registers, the other reads its next
+        // stage's fragments from LDS, so each SIMD's matrix core always has a
+        // wave with operands ready. Barriers B0, B1, ... separate phases;
+        // group 0 reads stage s in [B2s, B2s+1] and multiplies it in
+        // [B2s+1, B2s+2], group 1 reads it in [B2s+1, B2s+2] and multiplies in
+        // [B2s+2, B2s+3]. The loads of stage s + kNBuf - 1 go out at B2s from
+        // both groups into the buffer of stage s - 1, which both groups
+        // finished reading before B2s; every wave waits for its loads of
+        // stage s + 1 before B2s+2, the first barrier after which stage s + 1
+        // is read.
+        static_assert(NW == 8, "one wave of each group per SIMD");
+        const bool g1 = w >= NW / 2;
+        Frags f[SUBS];
+        auto bar = [&]() {
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_barrier();
+            __asm__ volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        auto read_stage = [&](const char* buf) {
+#pragma unroll
+            for (int u = 0; u < SUBS; ++u) read_frags(buf, u, f[u]);
+        };
+        auto mfma_stage = [&]() {
+#pragma unroll
+            for (int u = 0; u < SUBS; ++u) mfma_frags(f[u]);
+        };
+        // group 0, stage s: read buffer rd, refill buffer wr (stage s - 1's)
+        auto g0 = [&](const char* rd, char* wr, int s) {
+            issue(wr, s + NBUF - 1);
+            read_stage(rd);
+            __builtin_amdgcn_sched_barrier(0);
+            wait_vm_lgkm<63>();
+            bar();
+            mfma_stage();
+            __builtin_amdgcn_sched_barrier(0);
+            wait_vm_lgkm<(NBUF - 2) * kPerStage>();
+            bar();
+        };
+        // group 1, stage s: read buffer b, then refill it with stage s + kNBuf
+        auto g1s = [&](char* b, int s) {
+            bar();
+            read_stage(b);
+            __builtin_amdgcn_sched_barrier(0);
+            wait_vm_lgkm<(NBUF - 2) * kPerStage>();
+            bar();
+            issue(b, s + NBUF);
+            mfma_stage();
+        };
+        issue(lds0, 0);
+        if constexpr (NBUF == 4) {
+            issue(lds1, 1);
+            issue(lds2, 2);
+        }
+        wait_vm_lgkm<(NBUF - 2) * kPerStage>();
+        bar();   // B0
+        if (!g1) {
+            for (int s = 0; s < S; s += NBUF) {
+                if constexpr (NBUF == 4) {
+                    g0(lds0, lds3, s);
+                    g0(lds1, lds0, s + 1);
+                    g0(lds2, lds1, s + 2);
+                    g0(lds3, lds2, s + 3);
+                } else {
+                    g0(lds0, lds1, s);
+                    g0(lds1, lds0, s + 1);
+                }
+            }
+        } else {
+            issue(NBUF == 4 ? lds3 : lds1, NBUF - 1);
+            for (int s = 0; s < S; s += NBUF) {
+                if constexpr (NBUF == 4) {
+                    g1s(lds0, s);
+                    g1s(lds1, s + 1);
+                    g1s(lds2, s + 2);
+                    g1s(lds3, s + 3);
+                } else {
+                    g1s(lds0, s);
+                    g1s(lds1, s + 1);
+                }
+            }
+        }
+    } else if constexpr (NBUF == 4) {
         issue(lds0, 0);
         issue(lds1, 1);
         issue(lds2, 2);
@@ -311,70 +420,120 @@ void gemm_tile(GemmParams p) {
     // drain the loads past the end before the workgroup's LDS is released
     wait_vm_lgkm<0>();
 
-    // ---- epilogues: acc[mi][ni][i] is row wm*64 + mi*16 + kg*4 + i,
-    // column r16 of the ni-th column block
-    if constexpr (STAGE == 1 && MODE == 0) {
-        uint16_t* h = reinterpret_cast<uint16_t*>(p.out);
+    // ---- epilogues: acc[mi][ni][i] is tile row wm*16*WMI + mi*16 + r16,
+    // column 4 kg + i of the ni-th 16-column block; a padding row (flat
+    // assignment past A) stores nothing
+    auto row_assignment = [&](int mi) { return p.sorted[row0 + wm * 16 * WMI + mi * 16 + r16]; };
+    // Rows go out through LDS: a wave writes its 16 rows of one mi block into
+    // a private, padded LDS patch in the accumulator layout, reads them back
+    // row-contiguous and stores 16 bytes per lane, so one store instruction
+    // writes whole 128-byte lines of 2 to 8 rows. Every wave is past its last
+    // LDS read of the stage buffers before any patch is written.
+    auto through_lds = [&](auto write_patch, auto row_bytes_c, auto store_chunk) {
+        constexpr int RB = decltype(row_bytes_c)::value;   // bytes of one patch row
+        constexpr int RS = RB + 16;                        // padded LDS row stride
+        constexpr int LPR = RB / 16;                       // lanes per row
+        constexpr int RPI = 64 / LPR;                      // rows per instruction
+        static_assert(RPI * LPR == 64 && 16 * RS * (NW / 2 + NW % 2) <= BUF, "patch fits one stage buffer");
+        char* tb = (w < (NW + 1) / 2 ? lds0 : lds1) + (w % ((NW + 1) / 2)) * 16 * RS;
+        __builtin_amdgcn_s_barrier();
 #pragma unroll
-        for (int mi = 0; mi < WMI; ++mi)
+        for (int mi = 0; mi < WMI; ++mi) {
+            const int am = row_assignment(mi);
+            write_patch(mi, tb + r16 * RS);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int col = n0 + wn * 64 + j * 16 + r16;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int a = p.sorted[row0 + wm * 16 * WMI + mi * 16 + kg * 4 + i];   // by flat assignment
-                    if (a < p.A)
-                        h[(int64_t)a * p.N + col] = f32_to_bf16_bits(silu_mul(acc[mi][j][i], acc[mi][4 + j][i]));
-                }
+            for (int it = 0; it < 16 / RPI; ++it) {
+                const int R = it * RPI + lane / LPR, c = lane % LPR;
+                const i32x4_t v = *reinterpret_cast<const i32x4_t*>(tb + R * RS + c * 16);
+                const int a = __shfl(am, R);   // lane R holds row R's assignment
+                if (a < p.A) store_chunk(a, c, v);
             }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
+    };
+    if constexpr (STAGE == 1 && MODE == 0) {
+        // h by flat assignment: 64 bf16 columns per wave row
+        char* h = reinterpret_cast<char*>(p.out);
+        through_lds(
+            [&](int mi, char* prow) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    uint32_t v[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) v[i] = f32_to_bf16_bits(silu_mul(acc[mi][j][i], acc[mi][4 + j][i]));
+                    *reinterpret_cast<uint2*>(prow + (j * 16 + kg * 4) * 2) = uint2{v[0] | (v[1] << 16), v[2] | (v[3] << 16)};
+                }
+            },
+            std::integral_constant<int, 128>{},
+            [&](int a, int c, i32x4_t v) {
+                *reinterpret_cast<i32x4_t*>(h + ((int64_t)a * p.N + n0 + wn * 64) * 2 + c * 16) = v;
+            });
     } else if constexpr (STAGE == 1 && MODE == 1) {
         uint8_t* hq = reinterpret_cast<uint8_t*>(p.out);
 #pragma unroll
-        for (int mi = 0; mi < WMI; ++mi)
+        for (int mi = 0; mi < WMI; ++mi) {
+            const int a = row_assignment(mi);
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
-                const int c0 = n0 + wn * 64 + q * 32;   // first of the 32 h columns of this scale group
+                // the 32 h columns c0 .. c0 + 31 of one scale group: blocks
+                // 2q and 2q + 1, 4 columns per lane, over the 4 lanes kg
+                const int c0 = n0 + wn * 64 + q * 32;
+                uint32_t b[8];
+                uint32_t amax = 0;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float h0 = silu_mul(acc[mi][2 * q][i], acc[mi][4 + 2 * q][i]);
-                    const float h1 = silu_mul(acc[mi][2 * q + 1][i], acc[mi][4 + 2 * q + 1][i]);
-                    const uint32_t b0 = __float_as_uint(h0), b1 = __float_as_uint(h1);
-                    uint32_t amax = max(b0 & 0x7fffffffu, b1 & 0x7fffffffu);
+                for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-                    for (int off = 1; off < 16; off <<= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, off));
-                    const int sx = group_exponent(amax);
-                    const E2m1Thresholds th = e2m1_thresholds(sx);
-                    const uint32_t k0 = e2m1_code(b0, th), k1 = e2m1_code(b1, th);
-                    const uint32_t o0 = (uint32_t)__shfl_xor((int)k0, 1), o1 = (uint32_t)__shfl_xor((int)k1, 1);
-                    const int a = p.sorted[row0 + wm * 16 * WMI + mi * 16 + kg * 4 + i];   // by flat assignment
-                    if (a >= p.A) continue;
-                    uint8_t* rp = hq + (int64_t)a * (p.N / 2);
-                    if ((r16 & 1) == 0) {
-                        rp[(c0 + r16) / 2] = (uint8_t)(k0 | (o0 << 4));
-                        rp[(c0 + 16 + r16) / 2] = (uint8_t)(k1 | (o1 << 4));
+                    for (int i = 0; i < 4; ++i) {
+                        b[jj * 4 + i] =
+                            __float_as_uint(silu_mul(acc[mi][2 * q + jj][i], acc[mi][4 + 2 * q + jj][i]));
+                        amax = max(amax, b[jj * 4 + i] & 0x7fffffffu);
                     }
-                    if (r16 == 0) p.out_sc[(int64_t)a * (p.N / 32) + c0 / 32] = (uint8_t)(sx + 127);
-                }
-            }
-    } else {
-        // y rows: fp32, or bf16 (RNE) in MXFP4 mode
-#pragma unroll
-        for (int mi = 0; mi < WMI; ++mi)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int a = p.sorted[row0 + wm * 16 * WMI + mi * 16 + kg * 4 + i];
+                amax = max(amax, (uint32_t)__shfl_xor((int)amax, 16));
+                amax = max(amax, (uint32_t)__shfl_xor((int)amax, 32));
+                const int sx = group_exponent(amax);
+                const E2m1Thresholds th = e2m1_thresholds(sx);
                 if (a >= p.A) continue;
-                const int64_t off = (int64_t)a * p.N + n0 + wn * 128 + r16;
-                if constexpr (MODE == 1) {
-                    uint16_t* yr = reinterpret_cast<uint16_t*>(p.out) + off;
+                uint8_t* rp = hq + (int64_t)a * (p.N / 2);
 #pragma unroll
-                    for (int ni = 0; ni < 8; ++ni) yr[ni * 16] = f32_to_bf16_bits(acc[mi][ni][i]);
-                } else {
-                    float* yr = reinterpret_cast<float*>(p.out) + off;
-#pragma unroll
-                    for (int ni = 0; ni < 8; ++ni) yr[ni * 16] = acc[mi][ni][i];
+                for (int jj = 0; jj < 2; ++jj) {
+                    // even column in the low nibble
+                    const uint32_t w16 = e2m1_code(b[jj * 4], th) | (e2m1_code(b[jj * 4 + 1], th) << 4) |
+                                         (e2m1_code(b[jj * 4 + 2], th) << 8) | (e2m1_code(b[jj * 4 + 3], th) << 12);
+                    *reinterpret_cast<uint16_t*>(rp + (c0 + jj * 16 + kg * 4) / 2) = (uint16_t)w16;
                 }
+                if (kg == 0) p.out_sc[(int64_t)a * (p.N / 32) + c0 / 32] = (uint8_t)(sx + 127);
             }
+        }
+    } else {
+        // y rows by flat assignment, 128 columns per wave row: fp32, or bf16
+        // (RNE) in MXFP4 mode
+        constexpr int YB = MODE == 1 ? 2 : 4;
+        char* y = reinterpret_cast<char*>(p.out);
+        through_lds(
+            [&](int mi, char* prow) {
+#pragma unroll
+                for (int ni = 0; ni < 8; ++ni) {
+                    if constexpr (MODE == 1) {
+                        const uint2 pk = {
+                            f32_to_bf16_bits(acc[mi][ni][0]) | ((uint32_t)f32_to_bf16_bits(acc[mi][ni][1]) << 16),
+                            f32_to_bf16_bits(acc[mi][ni][2]) | ((uint32_t)f32_to_bf16_bits(acc[mi][ni][3]) << 16)};
+                        *reinterpret_cast<uint2*>(prow + (ni * 16 + kg * 4) * 2) = pk;
+                    } else {
+                        *reinterpret_cast<f32x4_t*>(prow + (ni * 16 + kg * 4) * 4) = acc[mi][ni];
+                    }
+                }
+            },
+            std::integral_constant<int, 128 * YB>{},
+            [&](int a, int c, i32x4_t v) {
+                // y is read once, by the combine, long after: stream it past the caches
+                __builtin_nontemporal_store(
+                    v, reinterpret_cast<i32x4_t*>(y + ((int64_t)a * p.N + n0 + wn * 128) * YB + c * 16));
+            });
     }
 }
 
@@ -382,7 +541,7 @@ void gemm_tile(GemmParams p) {
 // except MXFP4 with 256-row blocks: 64 bytes (four buffers; the e2m1 k-step
 // is four times deeper, so a stage is already long)
 template <int MODE, int STAGE, int BM, int BW, int NW, int SUBS = (MODE == 0 || BM <= 64 ? 2 : 1),
-          int NBUF = 4 / SUBS>
+          int NBUF = 4 / SUBS, bool PP = (NW == 8 && MODE == 0)>
 hipError_t launch_one(const GemmParams& p, hipStream_t s) {
     using TS = TileShape<MODE, BM, BW, NW, SUBS, NBUF>;
     const int64_t n_tiles = p.N / (STAGE == 1 ? BW / 2 : BW);
@@ -390,8 +549,8 @@ hipError_t launch_one(const GemmParams& p, hipStream_t s) {
     const int64_t n_groups = (n_tiles + TS::kGroupN - 1) / TS::kGroupN;
     const int64_t grid = m_groups * n_groups * TS::kGroupM * TS::kGroupN;
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL((gemm_tile<MODE, STAGE, BM, BW, NW, SUBS, NBUF>), dim3((unsigned)grid), dim3(TS::kThreads), 0,
-                       s, p);
+    hipLaunchKernelGGL((gemm_tile<MODE, STAGE, BM, BW, NW, SUBS, NBUF, PP>), dim3((unsigned)grid),
+                       dim3(TS::kThreads), 0, s, p);
     return hipGetLastError();
 }
 
