@@ -29,6 +29,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+FP4_PEAK_TFLOPS = 10100.0      # MI355X dense MXFP4 MFMA
 METRIC = "fused-MoE fwd µs/call + TFLOP/s & %roofline at T=512/4096/16384 tokens"
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "gemm1_bf16_qwen3_235b_t512_counters.md")
 KERNEL_SOURCES = ("mixture_experts_ffn_align_amd/csrc/gemm_stream.hip",
@@ -109,6 +110,9 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the T=4096/16384 lines")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy three times (counter calibration)")
+    ap.add_argument("--mxfp4", default="",
+                    help="comma-separated token buckets: instead of the bf16 line, one JSON line per "
+                         "bucket for the MXFP4 TP2 shard (E=512, top-10)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
@@ -130,6 +134,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         log("[bench] copied 1 GiB three times")
+        return
+    if args.mxfp4:
+        mxfp4_buckets([int(t) for t in args.mxfp4.split(",")], args, dev)
         return
     sh = W.QWEN3_235B_BF16
     T, H, I, E, k = 512, sh.hidden, sh.inter, sh.experts, sh.top_k
@@ -322,6 +329,95 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def mxfp4_buckets(buckets, args, dev):
+    """MXFP4 TP2 shard (H=4096, I=512, E=512, top-10): per token bucket, the
+    fused forward (align + activation quantisation, gemm1 + SiLU*up with h
+    quantised, gemm2, combine) on router ids/weights already computed. A call
+    is captured once in a HIP graph and replayed back to back, so the time is
+    the GPU's, not the host's argument marshalling; the stage split comes from
+    a separate eager pass with HIP events (about 2 us of marker cost each)."""
+    import torch
+    import mixture_experts_ffn_align_amd as moe
+    from mixture_experts_ffn_align_amd import workloads as W
+
+    sh = W.QWEN35_397B_TP2_FP4_512
+    H, I, E, k = sh.hidden, sh.inter, sh.experts, sh.top_k
+    log(f"[bench] drawing and quantising weights {sh.name}")
+    g = torch.Generator(device=dev).manual_seed(0)
+    w13, w2 = W.draw_weights(sh, g, dev)
+    gate, up = W.packed_views(w13, I)
+    (gq, gs), (uq, us), (wq, wsc) = moe.moe_quant_mxfp4(gate), moe.moe_quant_mxfp4(up), moe.moe_quant_mxfp4(w2)
+    del w13, w2, gate, up
+    torch.cuda.empty_cache()
+    hip = HipEvents()
+    nst = len(moe.STAGES)
+    per_expert = 3 * I * H // 2 + 3 * I * H // 32          # e2m1 codes + e8m0 scales of gate, up, down
+    for T in buckets:
+        gx = torch.Generator(device=dev).manual_seed(T)
+        x = torch.randn(T, H, generator=gx, device=dev).to(torch.bfloat16)
+        logits = torch.randn(T, E, generator=gx, device=dev)
+        ids, wts = moe.moe_topk_softmax(logits, k)
+        out = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+        kw = dict(gate_scale=gs, up_scale=us, w2_scale=wsc, mode=moe.MODE_MXFP4)
+        ws = torch.empty(moe.moe_fused_workspace_size(x, gq, uq, wq, ids, wts, **kw), dtype=torch.uint8, device=dev)
+        cfg = moe.moe_query_config(x, gq, uq, wq, ids, wts, **kw)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):                       # warm up off the capture
+            for _ in range(3):
+                moe.moe_fused_fwd(x, gq, uq, wq, ids, wts, out=out, workspace=ws, **kw)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        eager = out.clone()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            moe.moe_fused_fwd(x, gq, uq, wq, ids, wts, out=out, workspace=ws, **kw)
+        reps = max(5, min(200, int(2e5 / (T + 50))))
+        for _ in range(3):
+            graph.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(out, eager):
+            raise RuntimeError(f"T={T}: graph replay differs from the eager call")
+        stream = torch.cuda.current_stream().cuda_stream
+        ev = hip.create(2)
+        hip.record(ev[0], stream)
+        for _ in range(reps):
+            graph.replay()
+        hip.record(ev[1], stream)
+        torch.cuda.synchronize()
+        us_call = hip.elapsed_ms(ev[0], ev[1]) * 1e3 / reps
+        hip.destroy(ev)
+        del graph
+        evs = hip.create(2 * nst)
+        st = {s: [] for s in moe.STAGES}
+        for _ in range(10):
+            moe.moe_fused_fwd(x, gq, uq, wq, ids, wts, out=out, workspace=ws, stage_events=evs, stream=stream, **kw)
+            torch.cuda.synchronize()
+            for i, s in enumerate(moe.STAGES):
+                st[s].append(hip.elapsed_ms(evs[2 * i], evs[2 * i + 1]) * 1e3)
+        hip.destroy(evs)
+        touched = int(torch.unique(ids).numel())
+        A = T * k
+        byts = touched * per_expert + T * H * 2 * 2 + 8 * A
+        flops = 6 * H * I * A
+        hbm_s, mfma_s = byts / (HBM_PEAK_GBS * 1e9), flops / (FP4_PEAK_TFLOPS * 1e12)
+        line = {
+            "workload": f"{sh.name}, fused forward on given top-k ids/weights",
+            "tokens": T, "touched_experts": touched, "us_per_call": round(us_call, 1),
+            "timing": f"HIP graph of one call, {reps} replays back to back",
+            "algorithmic_bytes": byts, "tflops": round(flops / (us_call * 1e-6) / 1e12, 2),
+            "bound": "hbm" if hbm_s >= mfma_s else "mfma",
+            "roofline_frac": round(max(hbm_s, mfma_s) / (us_call * 1e-6), 3),
+            "hbm_gbs": round(byts / (us_call * 1e-6) / 1e9, 1),
+            "stage_us_eager_events": {s: round(sorted(v)[len(v) // 2], 1) for s, v in st.items()},
+            "config": {kk: cfg[kk] for kk in ("config_index", "block_m", "block_m2", "gemm1_kernel",
+                                               "gemm2_kernel", "gemm1_split_k", "gemm2_split_k")},
+        }
+        print(json.dumps(line), flush=True)
+        del x, logits, ids, wts, out, ws
+        torch.cuda.empty_cache()
 
 
 def cpu_baseline(inp, w13, w2, T, budget_s):

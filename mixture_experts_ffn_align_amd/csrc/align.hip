@@ -5,10 +5,13 @@
 //
 // A counting sort in three phases: histogram, scan, scatter. Each wave owns a
 // contiguous range of flat indices a = t*k + j and ranks each round of 64 by
-// a bitonic sort across the wave, so the output keeps ascending a inside every
-// expert. Up to 16384 assignments run all three phases in one workgroup of
+// matching experts across the wave with ballots (one per bit of the expert
+// id), so the output keeps ascending a inside every expert. Up to 16384 assignments run all three phases in one workgroup of
 // 1024 threads (one launch); larger problems use three launches over
-// 4096-index chunks.
+// 4096-index chunks. When the two GEMMs use different block sizes, the same
+// pass also writes the order padded to the second block size (an element's
+// place there is its place in the first layout, shifted by the difference of
+// its expert's two padded offsets).
 #include "moe_internal.h"
 
 namespace moe {
@@ -42,50 +45,58 @@ __device__ void wave_load(const AlignParams& p, int lo, int hi, int (&eid)[R]) {
     }
 }
 
+// Lanes of a wave holding the same expert as this lane, from one ballot per
+// bit of the expert id (nbits bits cover 0 .. E-1); lanes with e < 0 are in
+// no lane's set.
+__device__ __forceinline__ uint64_t match_expert(int e, int nbits) {
+    uint64_t m = __ballot(e >= 0);
+    for (int b = 0; b < nbits; ++b) {
+        const bool bit = (e >> b) & 1;
+        const uint64_t on = __ballot(bit);
+        m &= bit ? on : ~on;
+    }
+    return m;
+}
+
+// set bits of m below this lane
+__device__ __forceinline__ int rank_below(uint64_t m) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+__device__ __forceinline__ int expert_bits(int E) { return E > 1 ? 32 - __clz(E - 1) : 0; }
+
+// per-expert counts of a wave's n indices (LDS atomics)
 template <int R>
-__device__ void wave_count(const int (&eid)[R], int* cnt) {
+__device__ void wave_count(const int (&eid)[R], int* cnt, int n) {
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+    for (int r = 0; r < R; ++r) {
+        if (r * kWave >= n) break;                 // the wave's n indices are done
         if (eid[r] >= 0) atomicAdd(&cnt[eid[r]], 1);
+    }
 }
 
 // Scatter [lo, hi) using base[e] as the running output position of expert e.
-// Each round of 64 indices is ranked by sorting the keys (expert << 6 | lane)
-// across the wave with a bitonic network: equal experts end up adjacent and in
-// lane order, so an element's rank inside its expert is its distance from the
-// start of its run. The last lane of a run advances base[e] for the next round.
+// In each round of 64 indices an element's rank inside its expert is the
+// number of lower lanes with the same expert, so the order inside an expert
+// stays ascending; the highest lane of a group advances base[e] for the next
+// round. off / off2: both layouts' padded offsets (second layout optional).
 template <int R>
-__device__ void wave_scatter(const AlignParams& p, int lo, int hi, const int (&eid)[R], int* base) {
+__device__ void wave_scatter(const AlignParams& p, int lo, int hi, const int (&eid)[R], int* base,
+                             const int* off, const int* off2, int nbits) {
     const int lane = lane_id();
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const int a0 = lo + r * kWave;
         if (a0 >= hi) break;
         const int e = eid[r];
-        uint32_t key = e >= 0 ? ((uint32_t)e << 6) | (uint32_t)lane : 0x80000000u | (uint32_t)lane;
-#pragma unroll
-        for (int k = 2; k <= kWave; k <<= 1) {
-#pragma unroll
-            for (int j = k >> 1; j > 0; j >>= 1) {
-                const uint32_t o = (uint32_t)__shfl_xor((int)key, j);
-                const bool ascending = (lane & k) == 0;
-                const bool lower = (lane & j) == 0;
-                key = (lower == ascending) ? min(key, o) : max(key, o);
-            }
-        }
-        const bool valid = (key >> 31) == 0;
-        const uint32_t ek = key >> 6;
-        const uint32_t prev = (uint32_t)__shfl_up((int)ek, 1);
-        const uint32_t next = (uint32_t)__shfl_down((int)ek, 1);
-        const uint64_t starts = __ballot(lane == 0 || prev != ek);
-        const bool is_end = lane == kWave - 1 || next != ek;
-        const uint64_t upto = lane == kWave - 1 ? ~0ull : ((2ull << lane) - 1);
-        const int start = 63 - __clzll((long long)(starts & upto));
-        const int rank = lane - start;
-        if (valid) {
-            const int b = base[ek];
-            p.sorted[b + rank] = a0 + (int)(key & 63u);
-            if (is_end) base[ek] = b + rank + 1;
+        const uint64_t m = match_expert(e, nbits);
+        if (e >= 0) {
+            const int rank = rank_below(m);
+            const int b = base[e];
+            const int v = a0 + lane;
+            p.sorted[b + rank] = v;
+            if (p.sorted2) p.sorted2[b + rank - off[e] + off2[e]] = v;
+            if ((m >> lane) == 1ull) base[e] = b + rank + 1;
         }
     }
 }
@@ -125,10 +136,12 @@ __device__ int block_exclusive_scan(int* v, int n, int* wave_tot) {
 }
 
 // Given tot[e] (assignments per expert) in LDS: the padded offsets off[e],
-// block_expert, the sentinels and n_padded.
+// block_expert and n_padded. (Every slot of sorted already holds the sentinel
+// A from an earlier pass; the scatter overwrites the real ones.)
 template <int NT>
-__device__ void layout_experts(const AlignParams& p, const int* tot, int* off, int* scratch) {
-    const int E = p.E, bm = p.bm;
+__device__ void layout_experts(const AlignParams& p, int bm, int32_t* block_expert, int32_t* n_padded,
+                               const int* tot, int* off, int* scratch) {
+    const int E = p.E;
     for (int e = threadIdx.x; e < E; e += NT) off[e] = (tot[e] + bm - 1) / bm * bm;
     __syncthreads();
     const int npad = block_exclusive_scan<NT>(off, E, scratch);
@@ -142,13 +155,23 @@ __device__ void layout_experts(const AlignParams& p, const int* tot, int* off, i
             const int mid = (lo + hi + 1) >> 1;
             if (off[mid] <= pos) lo = mid; else hi = mid - 1;
         }
-        const int e = lo;
-        p.block_expert[b] = e;
-        const int fill_from = off[e] + tot[e];
-        const int end = pos + bm;
-        for (int q = (fill_from > pos ? fill_from : pos); q < end; ++q) p.sorted[q] = p.A;
+        block_expert[b] = lo;
     }
-    if (threadIdx.x == 0) *p.n_padded = npad;
+    if (threadIdx.x == 0) *n_padded = npad;
+}
+
+// the sentinel A in slots [i0, i1) of both layouts, i += stride
+__device__ __forceinline__ void fill_sentinels(const AlignParams& p, int i0, int stride) {
+    for (int i = i0; i < p.cap; i += stride) p.sorted[i] = p.A;
+    if (p.sorted2)
+        for (int i = i0; i < p.cap2; i += stride) p.sorted2[i] = p.A;
+}
+
+// both layouts (the second only when asked for)
+template <int NT>
+__device__ void layout_both(const AlignParams& p, const int* tot, int* off, int* off2, int* scratch) {
+    layout_experts<NT>(p, p.bm, p.block_expert, p.n_padded, tot, off, scratch);
+    if (p.sorted2) layout_experts<NT>(p, p.bm2, p.block_expert2, p.n_padded2, tot, off2, scratch);
 }
 
 // Whole align in one workgroup.
@@ -158,15 +181,20 @@ __device__ void align_fused_body(const AlignParams& p) {
     int* wcnt = lds;                          // [kFusedWaves][E]
     int* tot = wcnt + kFusedWaves * E;        // [E]
     int* off = tot + E;                       // [E]
-    int* scratch = off + E;                   // [kFusedWaves + 1]
+    int* off2 = off + E;                      // [E]
+    int* scratch = off2 + E;                  // [kFusedWaves + 1]
     const int w = threadIdx.x >> 6;
     for (int i = threadIdx.x; i < kFusedWaves * E; i += kFusedThreads) wcnt[i] = 0;
+    // sentinels everywhere first (coalesced); the barriers below order them
+    // before the scatter's stores
+    fill_sentinels(p, threadIdx.x, kFusedThreads);
     __syncthreads();
     const int per = (p.A + kFusedWaves - 1) / kFusedWaves;
     const int lo = min(p.A, w * per), hi = min(p.A, lo + per);
     int eid[kFusedMaxA / kFusedThreads];
     wave_load(p, lo, hi, eid);
-    wave_count(eid, wcnt + w * E);
+    const int nbits = expert_bits(E);
+    wave_count(eid, wcnt + w * E, hi - lo);
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += kFusedThreads) {
         int run = 0;
@@ -178,11 +206,11 @@ __device__ void align_fused_body(const AlignParams& p) {
         tot[e] = run;
     }
     __syncthreads();
-    layout_experts<kFusedThreads>(p, tot, off, scratch);
+    layout_both<kFusedThreads>(p, tot, off, off2, scratch);
     for (int e = threadIdx.x; e < E; e += kFusedThreads)
         for (int v = 0; v < kFusedWaves; ++v) wcnt[v * E + e] += off[e];
     __syncthreads();
-    wave_scatter(p, lo, hi, eid, wcnt + w * E);
+    wave_scatter(p, lo, hi, eid, wcnt + w * E, off, off2, nbits);
 }
 
 __global__ __launch_bounds__(kFusedThreads) void align_fused(AlignParams p) { align_fused_body(p); }
@@ -202,13 +230,14 @@ __global__ __launch_bounds__(kFusedThreads) void align_fused_quant(AlignParams p
 __global__ __launch_bounds__(kThreads) void align_count(AlignParams p) {
     extern __shared__ int lds[];
     const int E = p.E;
+    fill_sentinels(p, blockIdx.x * kThreads + threadIdx.x, gridDim.x * kThreads);
     for (int i = threadIdx.x; i < E; i += kThreads) lds[i] = 0;
     __syncthreads();
     const int w = threadIdx.x >> 6;
     const int lo = min(p.A, (int)blockIdx.x * kChunk + w * kWaveItems), hi = min(p.A, lo + kWaveItems);
     int eid[kWaveItems / kWave];
     wave_load(p, lo, hi, eid);
-    wave_count(eid, lds);
+    wave_count(eid, lds, hi - lo);
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += kThreads) p.counts[(int64_t)blockIdx.x * E + e] = lds[e];
 }
@@ -219,7 +248,8 @@ __global__ __launch_bounds__(kThreads) void align_scan(AlignParams p, int nchunk
     const int E = p.E;
     int* tot = lds;
     int* off = tot + E;
-    int* scratch = off + E;
+    int* off2 = off + E;
+    int* scratch = off2 + E;
     // counts of one expert are read 16 chunks at a time, all loads in flight
     constexpr int kBatch = 16;
     for (int e = threadIdx.x; e < E; e += kThreads) {
@@ -237,7 +267,13 @@ __global__ __launch_bounds__(kThreads) void align_scan(AlignParams p, int nchunk
         tot[e] = run;
     }
     __syncthreads();
-    layout_experts<kThreads>(p, tot, off, scratch);
+    layout_both<kThreads>(p, tot, off, off2, scratch);
+    // both layouts' offsets for the scatter, after the chunk counts
+    int32_t* offs = p.counts + (int64_t)nchunks * E;
+    for (int e = threadIdx.x; e < E; e += kThreads) {
+        offs[e] = off[e];
+        offs[E + e] = p.sorted2 ? off2[e] : 0;
+    }
     for (int e = threadIdx.x; e < E; e += kThreads)
         for (int b0 = 0; b0 < nchunks; b0 += kBatch) {
             int c[kBatch];
@@ -250,17 +286,25 @@ __global__ __launch_bounds__(kThreads) void align_scan(AlignParams p, int nchunk
 }
 
 // Multi-block phase 3: stable scatter of chunk b.
-__global__ __launch_bounds__(kThreads) void align_scatter(AlignParams p) {
+__global__ __launch_bounds__(kThreads) void align_scatter(AlignParams p, int nchunks) {
     extern __shared__ int lds[];
     const int E = p.E;
-    int* wcnt = lds;   // [kWaves][E]
+    int* wcnt = lds;                  // [kWaves][E]
+    int* off = wcnt + kWaves * E;     // [E]
+    int* off2 = off + E;              // [E]
     for (int i = threadIdx.x; i < kWaves * E; i += kThreads) wcnt[i] = 0;
+    const int32_t* offs = p.counts + (int64_t)nchunks * E;
+    for (int e = threadIdx.x; e < E; e += kThreads) {
+        off[e] = offs[e];
+        off2[e] = offs[E + e];
+    }
     __syncthreads();
     const int w = threadIdx.x >> 6;
     const int lo = min(p.A, (int)blockIdx.x * kChunk + w * kWaveItems), hi = min(p.A, lo + kWaveItems);
     int eid[kWaveItems / kWave];
     wave_load(p, lo, hi, eid);
-    wave_count(eid, wcnt + w * E);
+    const int nbits = expert_bits(E);
+    wave_count(eid, wcnt + w * E, hi - lo);
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += kThreads) {
         int run = p.counts[(int64_t)blockIdx.x * E + e];
@@ -271,11 +315,11 @@ __global__ __launch_bounds__(kThreads) void align_scatter(AlignParams p) {
         }
     }
     __syncthreads();
-    wave_scatter(p, lo, hi, eid, wcnt + w * E);
+    wave_scatter(p, lo, hi, eid, wcnt + w * E, off, off2, nbits);
 }
 
 bool use_fused(int A, int E) {
-    return A <= kFusedMaxA && (size_t)(kFusedWaves + 2) * E * sizeof(int) + 256 <= 64 * 1024;
+    return A <= kFusedMaxA && (size_t)(kFusedWaves + 3) * E * sizeof(int) + 256 <= 64 * 1024;
 }
 
 }  // namespace
@@ -285,7 +329,7 @@ bool align_single_launch(int64_t A, int32_t E) { return use_fused((int)A, E); }
 hipError_t launch_align_with_quant(const AlignParams& p, const QuantParams& q, hipStream_t s) {
     if (!use_fused(p.A, p.E)) return hipErrorInvalidValue;
     const int64_t groups = q.E * q.R * (q.K / 32);
-    const size_t lds = sizeof(int) * ((size_t)kFusedWaves * p.E + 2 * p.E + kFusedWaves + 1);
+    const size_t lds = sizeof(int) * ((size_t)kFusedWaves * p.E + 3 * p.E + kFusedWaves + 1);
     const int64_t grid = 1 + (groups + kFusedThreads - 1) / kFusedThreads;
     hipLaunchKernelGGL(align_fused_quant, dim3((unsigned)grid), dim3(kFusedThreads), lds, s, p, q);
     return hipGetLastError();
@@ -294,23 +338,23 @@ hipError_t launch_align_with_quant(const AlignParams& p, const QuantParams& q, h
 size_t align_scratch_bytes(int64_t A, int32_t E) {
     if (use_fused((int)A, E)) return 0;
     const int64_t nchunks = (A + kChunk - 1) / kChunk;
-    return (size_t)nchunks * (size_t)E * sizeof(int32_t);
+    return (size_t)(nchunks + 2) * (size_t)E * sizeof(int32_t);
 }
 
 hipError_t launch_align(const AlignParams& p, hipStream_t s) {
     const int E = p.E;
     if (use_fused(p.A, E)) {
-        const size_t lds = sizeof(int) * ((size_t)kFusedWaves * E + 2 * E + kFusedWaves + 1);
+        const size_t lds = sizeof(int) * ((size_t)kFusedWaves * E + 3 * E + kFusedWaves + 1);
         hipLaunchKernelGGL(align_fused, dim3(1), dim3(kFusedThreads), lds, s, p);
         return hipGetLastError();
     }
     const int nchunks = (p.A + kChunk - 1) / kChunk;
     const size_t lds_c = sizeof(int) * (size_t)E;
     hipLaunchKernelGGL(align_count, dim3(nchunks), dim3(kThreads), lds_c, s, p);
-    const size_t lds_s = sizeof(int) * (2 * (size_t)E + kWaves + 1);
+    const size_t lds_s = sizeof(int) * (3 * (size_t)E + kWaves + 1);
     hipLaunchKernelGGL(align_scan, dim3(1), dim3(kThreads), lds_s, s, p, nchunks);
-    const size_t lds_x = sizeof(int) * (size_t)kWaves * E;
-    hipLaunchKernelGGL(align_scatter, dim3(nchunks), dim3(kThreads), lds_x, s, p);
+    const size_t lds_x = sizeof(int) * ((size_t)kWaves + 2) * E;
+    hipLaunchKernelGGL(align_scatter, dim3(nchunks), dim3(kThreads), lds_x, s, p, nchunks);
     return hipGetLastError();
 }
 

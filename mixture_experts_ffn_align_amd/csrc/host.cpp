@@ -542,6 +542,7 @@ int moe_align(const moe_tensor_t* ids, int32_t num_experts, int32_t block_m, con
     p.A = (int32_t)A;
     p.E = num_experts;
     p.bm = block_m;
+    p.cap = (int32_t)cap;
     p.sorted = (int32_t*)sorted_ids->data;
     p.block_expert = (int32_t*)block_expert->data;
     p.n_padded = (int32_t*)n_padded->data;
@@ -666,9 +667,10 @@ int moe_fused_fwd(const moe_fused_args_t* args, void* ws, size_t ws_bytes, moe_s
     }
     const bool quant_in_align = fp4 && align_single_launch(pl.A, (int32_t)pl.E);
 
-    // stage 0: align (once per distinct block size of the two GEMMs)
+    // stage 0: align; when the two GEMMs use different block sizes, the same
+    // pass writes the second padded layout too
     tm.begin(0);
-    for (int g = 0; g < (pl.two_aligns ? 2 : 1); ++g) {
+    {
         AlignParams ap{};
         ap.ids = (const int32_t*)a.topk_ids.data;
         ap.is_t = a.topk_ids.stride[0];
@@ -677,12 +679,20 @@ int moe_fused_fwd(const moe_fused_args_t* args, void* ws, size_t ws_bytes, moe_s
         ap.k = (int32_t)pl.k;
         ap.A = (int32_t)pl.A;
         ap.E = (int32_t)pl.E;
-        ap.bm = pl.ks[g].bm;
-        ap.sorted = sorted[g];
-        ap.block_expert = bexp[g];
-        ap.n_padded = npad[g];
+        ap.bm = pl.ks[0].bm;
+        ap.cap = (int32_t)pl.cap[0];
+        ap.sorted = sorted[0];
+        ap.block_expert = bexp[0];
+        ap.n_padded = npad[0];
         ap.counts = (int32_t*)(base + pl.off_counts);
-        e = (g == 0 && quant_in_align) ? launch_align_with_quant(ap, qp, s) : launch_align(ap, s);
+        if (pl.two_aligns) {
+            ap.bm2 = pl.ks[1].bm;
+            ap.cap2 = (int32_t)pl.cap[1];
+            ap.sorted2 = sorted[1];
+            ap.block_expert2 = bexp[1];
+            ap.n_padded2 = npad[1];
+        }
+        e = quant_in_align ? launch_align_with_quant(ap, qp, s) : launch_align(ap, s);
         if (e != hipSuccess) return hip_fail(e, "align");
     }
     tm.end(0);

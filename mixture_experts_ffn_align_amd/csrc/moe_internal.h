@@ -120,10 +120,16 @@ struct AlignParams {
     const int32_t* ids;
     int64_t is_t, is_j;
     int32_t T, k, A, E, bm;
+    int32_t cap, cap2;      // entries of sorted / sorted2 (every one is written)
     int32_t* sorted;        // [cap]
     int32_t* block_expert;  // [cap / bm]
     int32_t* n_padded;      // [1]
-    int32_t* counts;        // [nchunks * E] scratch (multi-block path)
+    int32_t* counts;        // [nchunks * E + 2 E] scratch (multi-block path)
+    // optional second layout of the same order padded to bm2 (sorted2 null: none)
+    int32_t bm2;
+    int32_t* sorted2;
+    int32_t* block_expert2;
+    int32_t* n_padded2;
 };
 // Scratch bytes the multi-block path needs for A assignments over E experts.
 size_t align_scratch_bytes(int64_t A, int32_t E);
