@@ -446,6 +446,168 @@ void gemm_stream(GemmParams p) {
     }
 }
 
+// MXFP4 gemm2 when a wave's whole K is one ring round (K = 4 steps of 128,
+// the TP2 shard's I = 512): a workgroup takes NT consecutive 256-column
+// tiles of one row block instead of one. The h rows (the A operand, all of K)
+// are staged in LDS once and serve every tile; each wave DMA-loads the scale
+// rows of all its tiles once; the weight ring runs on across tiles (slot u
+// of tile j + 1 loads right after slot u of tile j is multiplied), so tile
+// j's epilogue and tile j + 1's first MFMAs overlap its loads. The weight
+// fragment is the MFMA's first operand: a lane's accumulator holds 4
+// consecutive output columns of one row and stores them as one 8-byte write.
+template <int BM, int NT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8)))
+void gemm_stream_nt(GemmParams p) {
+    constexpr int MB = BM / 16, NB = 4, U = 4;
+    constexpr int TILE_N = 4 * NB * 16;                       // 256 columns, 64 per wave
+    __shared__ __attribute__((aligned(16))) uint8_t a_lds[MB * U * 1024];    // fragment (mi, u): 1 KB
+    __shared__ __attribute__((aligned(16))) uint8_t sc_lds[4 * NT * 1024];   // wave, tile: 64 rows x 16 B
+    const int lane = lane_id();
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r16 = lane & 15, kg = lane >> 4;
+
+    // workgroups of one row block are consecutive, NT tiles each
+    const int n_tiles = p.N / TILE_N;
+    const int n_groups = (n_tiles + NT - 1) / NT;
+    const int tg = (int)(blockIdx.x % (uint32_t)n_groups);
+    const int mb = (int)(blockIdx.x / (uint32_t)n_groups);
+    if (mb >= p.max_mblocks) return;
+    const int n_blocks = *p.n_padded / BM;
+    if (mb >= n_blocks) return;
+    const int e = p.block_expert[mb];
+    const int row0 = mb * BM;
+    const int nt0 = tg * NT;
+    const int ntn = min(NT, n_tiles - nt0);                   // tiles of this workgroup, >= 1
+    auto col0 = [&](int j) { return (nt0 + j) * TILE_N + w * (NB * 16); };   // the wave's first column
+
+    // weight scale rows of every tile: one 16-byte run (K/32 bytes) per row,
+    // lane l of the wave's DMA for tile j fetches row col0(j) + l
+    for (int j = 0; j < ntn; ++j)
+        __builtin_amdgcn_global_load_lds(
+            reinterpret_cast<const void*>(p.b0_sc + (int64_t)e * p.b0sc_e + (int64_t)(col0(j) + lane) * p.b0sc_r),
+            (__attribute__((address_space(3))) void*)(sc_lds + (w * NT + j) * 1024), 16, 0, 0);
+
+    // h rows of the block: flat assignment a (a padding row re-reads row 0)
+    int arow[MB];
+#pragma unroll
+    for (int mi = 0; mi < MB; ++mi) {
+        const int a = p.sorted[row0 + mi * 16 + r16];
+        arow[mi] = a;
+    }
+    // A fragments: wave w stages (mi, u) = f for f = w, w + 4, ...
+    i32x4_t areg[MB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+        const int f = w + 4 * i, mi = f / U, u = f % U;
+        const int64_t r = arow[mi] < p.A ? arow[mi] : 0;
+        areg[i] = *reinterpret_cast<const i32x4_t*>(reinterpret_cast<const char*>(p.a) + r * p.a_row + u * 64 +
+                                                    kg * 16);
+    }
+    // A scales: the whole K of a row is one 16-byte window; byte 4u + kg is
+    // this lane's scale for step u, packed so that byte u is step u
+    uint32_t asc[MB];
+#pragma unroll
+    for (int mi = 0; mi < MB; ++mi) {
+        const int64_t r = arow[mi] < p.A ? arow[mi] : 0;
+        const i32x4_t v = *reinterpret_cast<const i32x4_t*>(p.a_sc + r * p.a_sc_row);
+        uint32_t pk = 0;
+#pragma unroll
+        for (int u = 0; u < U; ++u) pk |= (((uint32_t)v[u] >> (8 * kg)) & 0xffu) << (8 * u);
+        asc[mi] = pk;
+    }
+    // weight ring: slot u holds step u of the current tile
+    const char* bbase = reinterpret_cast<const char*>(p.b0) + (int64_t)e * p.b0_e;
+    i32x4_t fb[U][NB];
+    auto load_B = [&](int u, int j) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+            fb[u][nb] = *reinterpret_cast<const i32x4_t*>(bbase + (int64_t)(col0(j) + nb * 16 + r16) * p.b0_r +
+                                                          u * 64 + kg * 16);
+    };
+#pragma unroll
+    for (int u = 0; u < U; ++u) load_B(u, 0);
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+        *reinterpret_cast<i32x4_t*>(a_lds + (w + 4 * i) * 1024 + lane * 16) = areg[i];
+    __syncthreads();
+
+    uint16_t* y = reinterpret_cast<uint16_t*>(p.out);
+    // the accumulators are carried around the tile loop (zeroed after each
+    // epilogue), so every MFMA accumulates in place
+    f32x4_t acc[MB][NB];
+#pragma unroll
+    for (int mi = 0; mi < MB; ++mi)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            float z;
+            __asm__("v_mov_b32 %0, 0" : "=v"(z));
+            acc[mi][nb] = f32x4_t{z, z, z, z};
+        }
+#pragma unroll 1
+    for (int j = 0; j < ntn; ++j) {
+        // this tile's weight scales, packed like the A scales
+        uint32_t bsc[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const i32x4_t v = *reinterpret_cast<const i32x4_t*>(sc_lds + (w * NT + j) * 1024 + (nb * 16 + r16) * 16);
+            uint32_t pk = 0;
+#pragma unroll
+            for (int u = 0; u < U; ++u) pk |= (((uint32_t)v[u] >> (8 * kg)) & 0xffu) << (8 * u);
+            bsc[nb] = pk;
+        }
+        const int jn = j + 1 < ntn ? j + 1 : j;               // past the last tile: re-read it (L2 hit)
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int mi = 0; mi < MB; ++mi) {
+                const i32x4_t af = *reinterpret_cast<const i32x4_t*>(a_lds + (mi * U + u) * 1024 + lane * 16);
+                const i32x8_t a8 = {af[0], af[1], af[2], af[3], 0, 0, 0, 0};
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    const i32x8_t b8 = {fb[u][nb][0], fb[u][nb][1], fb[u][nb][2], fb[u][nb][3], 0, 0, 0, 0};
+                    acc[mi][nb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        b8, a8, acc[mi][nb], 4, 4, 0, (int)(bsc[nb] >> (8 * u)), 0, (int)(asc[mi] >> (8 * u)));
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            load_B(u, jn);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // The MFMAs read operands from every lane, so they must run with all
+        // lanes on: pin the results here, before the per-row branch below,
+        // which the compiler would otherwise sink them into.
+#pragma unroll
+        for (int mi = 0; mi < MB; ++mi)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) __asm__ volatile("" : "+v"(acc[mi][nb]));
+        // y rows by flat assignment (bf16, RNE): lane holds columns 4 kg ..
+        // +3 of column block nb for row r16
+#pragma unroll
+        for (int mi = 0; mi < MB; ++mi) {
+            if (arow[mi] >= p.A) continue;
+            uint16_t* yr = y + (int64_t)arow[mi] * p.N + col0(j) + kg * 4;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+                const u32x2_t pk = {
+                    f32_to_bf16_bits(acc[mi][nb][0]) | ((uint32_t)f32_to_bf16_bits(acc[mi][nb][1]) << 16),
+                    f32_to_bf16_bits(acc[mi][nb][2]) | ((uint32_t)f32_to_bf16_bits(acc[mi][nb][3]) << 16)};
+                __builtin_nontemporal_store(pk, reinterpret_cast<u32x2_t*>(yr + nb * 16));
+            }
+        }
+        // zeroed through registers the compiler cannot see as constants, so
+        // that the first MFMA of the next tile accumulates in place too
+#pragma unroll
+        for (int mi = 0; mi < MB; ++mi)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                float z;
+                __asm__("v_mov_b32 %0, 0" : "=v"(z));
+                acc[mi][nb] = f32x4_t{z, z, z, z};
+            }
+    }
+}
+
 typedef void (*GemmFn)(GemmParams);
 
 template <int MODE, int STAGE, int BM, int WK, int U, int NB = 4>
@@ -488,6 +650,14 @@ GemmFn table_u(int bm, int wk, int u, int nb) {
 // wave's share of K allows it, else 2); with 128 rows the accumulators leave
 // room for 2; narrow bf16 waves hold 8.
 GemmFn lookup(const GemmKernelId& id) {
+    if (id.nt != 1) {
+        if (id.mode != 1 || id.stage != 2 || id.wk != 1 || id.u != 4 || id.nb != 4) return nullptr;
+#define MOE_NT(B, T) \
+    if (id.bm == B && id.nt == T) return gemm_stream_nt<B, T>;
+        MOE_NT(16, 2) MOE_NT(16, 4) MOE_NT(16, 8) MOE_NT(32, 2) MOE_NT(32, 4) MOE_NT(32, 8)
+#undef MOE_NT
+        return nullptr;
+    }
     if (id.mode == 0)
         return id.stage == 1 ? table_u<0, 1>(id.bm, id.wk, id.u, id.nb) : table_u<0, 2>(id.bm, id.wk, id.u, id.nb);
     if (id.mode == 1)
@@ -519,6 +689,15 @@ bool gemm_supported(const GemmKernelId& id) { return lookup(id) != nullptr; }
 hipError_t launch_gemm(const GemmKernelId& id, const GemmParams& p, hipStream_t s) {
     GemmFn fn = lookup(id);
     if (!fn) return hipErrorInvalidValue;
+    if (id.nt != 1) {
+        // K must be exactly one 4-step ring round; N whole 256-column tiles
+        if (p.K != 4 * 128 || p.N % 256 != 0) return hipErrorInvalidValue;
+        const int64_t groups = (p.N / 256 + id.nt - 1) / id.nt;
+        const int64_t grid = groups * (int64_t)p.max_mblocks;
+        if (grid == 0) return hipSuccess;
+        hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(256), 0, s, p);
+        return hipGetLastError();
+    }
     const int tile_n = gemm_tile_n(id);
     const int n_tiles = p.N / tile_n;
     const int G = p.n_tile_groups;

@@ -133,8 +133,9 @@ bool valid_bm(int bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128 || 
 // strided and contiguous calls execute the same arithmetic.
 struct Cfg {
     int bm, wk1, wk2, nb;
-    int tile;    // 0: weight-streaming GEMMs; 1 + shape: LDS-tiled GEMMs of that tile shape
-    int g2;      // -1, or the entry whose gemm2 kernel runs gemm2 (own block size and align)
+    int tile;     // 0: weight-streaming GEMMs; 1 + shape: LDS-tiled GEMMs of that tile shape
+    int g2;       // -1, or the entry whose gemm2 kernel runs gemm2 (own block size and align)
+    int nt2 = 1;  // MXFP4 gemm2 on the stream with K = 512: 256-column tiles per workgroup
 };
 const Cfg kConfigs[] = {
     {16, 4, 4, 4, 0, -1}, {32, 4, 4, 4, 0, -1}, {64, 2, 2, 4, 0, -1},
@@ -148,6 +149,10 @@ const Cfg kConfigs[] = {
     {16, 1, 1, 4, 0, 15}, {16, 2, 2, 4, 0, 15}, {16, 4, 4, 4, 0, 15},
     {16, 1, 1, 4, 0, 14}, {16, 2, 2, 4, 0, 14}, {16, 4, 4, 4, 0, 14},
     {64, 1, 1, 4, 0, 13},
+    // MXFP4, K = 512: gemm2 workgroups take 2, 4 or 8 column tiles of a row block
+    {16, 1, 1, 4, 0, -1, 2}, {16, 1, 1, 4, 0, -1, 4}, {16, 1, 1, 4, 0, -1, 8},
+    {32, 1, 1, 4, 0, -1, 4}, {16, 4, 1, 4, 0, -1, 2}, {16, 2, 1, 4, 0, -1, 2},
+    {16, 2, 1, 4, 0, -1, 4}, {32, 1, 1, 4, 0, -1, 8},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -179,7 +184,8 @@ int tile_config(int md, int shape, int64_t H, int64_t I) {
 //    typical busiest expert of the bucket in one block (each expert's
 //    weights stream from HBM once) and whose K split grows only while the
 //    grid would not fill the chip; its gemm2 moves to an LDS-staged tile
-//    (own block size, second align) where that measured faster.
+//    (own block size, second layout) where that measured faster, or, for
+//    MXFP4 with I = 512, to workgroups that take 2-8 column tiles each.
 int default_config(int mode, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k) {
     const int64_t bucket = bucket_of(T);
     const double rows = (double)bucket * (double)k / (double)E;   // expected rows per expert
@@ -196,6 +202,16 @@ int default_config(int mode, int64_t T, int64_t H, int64_t I, int64_t E, int64_t
         else if (rows >= 64.0) c = tile_config(1, 2, H, I);
     }
     if (c >= 0) return c;
+    // MXFP4 with I = 512: gemm2 on the multi-tile weight stream (one align)
+    // from 2 tokens up to about 32 rows per expert
+    if (md == 1 && I == 4 * 128 && rows > 0.025 && rows < 32.0) {
+        const int want_bm = rows >= 8.0 ? 32 : 16, want_wk = rows < 0.5 ? 2 : 1;
+        const int want_nt = rows < 0.5 ? 2 : (rows < 2.0 ? 8 : 4);
+        for (c = 0; c < kNumConfigs; ++c)
+            if (kConfigs[c].bm == want_bm && kConfigs[c].wk1 == want_wk && kConfigs[c].wk2 == 1 &&
+                kConfigs[c].nt2 == want_nt && !kConfigs[c].tile && kConfigs[c].g2 < 0)
+                return c;
+    }
     int bm;
     if (md == 1)    // the fp4 stream prefers short blocks; 128 rows spill
         bm = busy <= 32.0 ? 16 : 64;
@@ -226,6 +242,7 @@ int default_config(int mode, int64_t T, int64_t H, int64_t I, int64_t E, int64_t
 struct KSpec {
     int bm, wk, nb;
     int tile;    // 0: register weight stream; 1 + shape: LDS-tiled
+    int nt = 1;  // register stream: column tiles per workgroup
 };
 
 struct Plan {
@@ -331,7 +348,7 @@ int plan_fused(const moe_fused_args_t* a, Plan* pl) {
     // chunks
     auto resolve = [&](const Cfg& c, int stage, KSpec* ks) -> int {
         const int64_t K = stage == 1 ? H : I, N = stage == 1 ? I : H;
-        *ks = KSpec{c.bm, stage == 1 ? c.wk1 : c.wk2, c.nb, c.tile};
+        *ks = KSpec{c.bm, stage == 1 ? c.wk1 : c.wk2, c.nb, c.tile, stage == 2 ? c.nt2 : 1};
         if (c.tile) {
             const int shape = c.tile - 1;
             if (!gemm_tile_supported(md, shape))
@@ -350,7 +367,9 @@ int plan_fused(const moe_fused_args_t* a, Plan* pl) {
         if (K % gran != 0)
             return fail(MOE_ERR_UNSUPPORTED, "config %d: gemm%d K = %lld must be a multiple of %d", ci, stage,
                         (long long)K, gran);
-        GemmKernelId id{md, stage, c.bm, w, gemm_ring_steps(a->mode, c.bm, c.nb, K / w), c.nb};
+        GemmKernelId id{md, stage, c.bm, w, gemm_ring_steps(a->mode, c.bm, c.nb, K / w), c.nb, ks->nt};
+        if (ks->nt != 1 && K != 4 * 128)
+            return fail(MOE_ERR_UNSUPPORTED, "config %d: multi-tile gemm2 needs K = 512", ci);
         if (!gemm_supported(id)) return fail(MOE_ERR_UNSUPPORTED, "config %d not built", ci);
         if (N % gemm_tile_n(id) != 0)
             return fail(MOE_ERR_UNSUPPORTED, "config %d: gemm%d N not a multiple of the tile width", ci, stage);
@@ -724,7 +743,7 @@ int moe_fused_fwd(const moe_fused_args_t* args, void* ws, size_t ws_bytes, moe_s
         const KSpec& k = pl.ks[g];
         if (k.tile) return launch_gemm_tile(fp4 ? 1 : 0, k.tile - 1, g + 1, gp, s);
         GemmKernelId id{fp4 ? 1 : 0, g + 1, k.bm, k.wk,
-                        gemm_ring_steps(pl.mode, k.bm, k.nb, (g == 0 ? pl.H : pl.I) / k.wk), k.nb};
+                        gemm_ring_steps(pl.mode, k.bm, k.nb, (g == 0 ? pl.H : pl.I) / k.wk), k.nb, k.nt};
         return launch_gemm(id, gp, s);
     };
     // stage 2: gemm1 + SiLU(gate) * up

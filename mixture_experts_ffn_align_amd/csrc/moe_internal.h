@@ -251,6 +251,7 @@ struct GemmKernelId {
     int wk;      // waves splitting K: 1, 2 or 4
     int u;       // weight steps in each wave's load ring (from gemm_ring_steps)
     int nb;      // 16-column MFMA blocks per wave: 4, or 2 (bf16 weight stream)
+    int nt = 1;  // MXFP4 gemm2 with K = 512: 256-column tiles per workgroup (1, 2, 4, 8)
 };
 // Ring depth for a wave's share of K.
 int gemm_ring_steps(int mode, int bm, int nb, int64_t k_per_wave);
