@@ -113,6 +113,9 @@ def main():
     ap.add_argument("--mxfp4", default="",
                     help="comma-separated token buckets: instead of the bf16 line, one JSON line per "
                          "bucket for the MXFP4 TP2 shard (E=512, top-10)")
+    ap.add_argument("--bf16", default="",
+                    help="comma-separated token buckets: one JSON line per bucket for the bf16 "
+                         "Qwen3-235B-shaped layer (graph-timed fused forward, packed w13 views)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
@@ -137,6 +140,9 @@ def main():
         return
     if args.mxfp4:
         mxfp4_buckets([int(t) for t in args.mxfp4.split(",")], args, dev)
+        return
+    if args.bf16:
+        bf16_buckets([int(t) for t in args.bf16.split(",")], args, dev)
         return
     sh = W.QWEN3_235B_BF16
     T, H, I, E, k = 512, sh.hidden, sh.inter, sh.experts, sh.top_k
@@ -329,6 +335,85 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def graph_time_us(call, reps):
+    """One call captured in a HIP graph, replayed back to back: GPU time per
+    call (the eager result is checked against the replay first)."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            out = call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    eager = out.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        out = call()
+    for _ in range(3):
+        graph.replay()
+    torch.cuda.synchronize()
+    if not torch.equal(out, eager):
+        raise RuntimeError("graph replay differs from the eager call")
+    hip = HipEvents()
+    stream = torch.cuda.current_stream().cuda_stream
+    ev = hip.create(2)
+    hip.record(ev[0], stream)
+    for _ in range(reps):
+        graph.replay()
+    hip.record(ev[1], stream)
+    torch.cuda.synchronize()
+    us = hip.elapsed_ms(ev[0], ev[1]) * 1e3 / reps
+    hip.destroy(ev)
+    del graph
+    return us
+
+
+def bf16_buckets(buckets, args, dev):
+    """bf16 Qwen3-235B-shaped layer (H=4096, I=1536, E=128, top-8): per token
+    bucket, the fused forward on router ids computed beforehand, gate/up as
+    packed w13 views, graph-timed."""
+    import torch
+    import mixture_experts_ffn_align_amd as moe
+    from mixture_experts_ffn_align_amd import workloads as W
+
+    sh = W.QWEN3_235B_BF16
+    H, I, E, k = sh.hidden, sh.inter, sh.experts, sh.top_k
+    log(f"[bench] drawing weights {sh.name}")
+    g = torch.Generator(device=dev).manual_seed(0)
+    w13, w2 = W.draw_weights(sh, g, dev)
+    gate, up = W.packed_views(w13, I)
+    per_expert = 3 * I * H * 2
+    for T in buckets:
+        inp = W.make_inputs(sh, T, seed=T, device=dev, weights=(w13, w2))
+        ids, wts = moe.moe_topk_softmax(inp["logits"], k)
+        out = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(moe.moe_fused_workspace_size(inp["x"], gate, up, w2, ids, wts), dtype=torch.uint8,
+                         device=dev)
+        cfg = moe.moe_query_config(inp["x"], gate, up, w2, ids, wts)
+        reps = max(5, min(200, int(2e5 / (T + 50))))
+        us_call = graph_time_us(lambda: moe.moe_fused_fwd(inp["x"], gate, up, w2, ids, wts, out=out, workspace=ws),
+                                reps)
+        touched = int(torch.unique(ids).numel())
+        A = T * k
+        byts = touched * per_expert + T * H * 2 * 2 + 8 * A
+        flops = 6 * H * I * A
+        hbm_s, mfma_s = byts / (HBM_PEAK_GBS * 1e9), flops / (BF16_PEAK_TFLOPS * 1e12)
+        print(json.dumps({
+            "workload": f"{sh.name}, fused forward on given top-k ids/weights, packed w13 views",
+            "tokens": T, "touched_experts": touched, "us_per_call": round(us_call, 1),
+            "timing": f"HIP graph of one call, {reps} replays back to back",
+            "algorithmic_bytes": byts, "tflops": round(flops / (us_call * 1e-6) / 1e12, 2),
+            "bound": "hbm" if hbm_s >= mfma_s else "mfma",
+            "roofline_frac": round(max(hbm_s, mfma_s) / (us_call * 1e-6), 3),
+            "hbm_gbs": round(byts / (us_call * 1e-6) / 1e9, 1),
+            "config": {kk: cfg[kk] for kk in ("config_index", "block_m", "block_m2", "gemm1_kernel",
+                                               "gemm2_kernel", "gemm1_split_k", "gemm2_split_k")},
+        }), flush=True)
+        del inp, ids, wts, out, ws
+        torch.cuda.empty_cache()
 
 
 def mxfp4_buckets(buckets, args, dev):

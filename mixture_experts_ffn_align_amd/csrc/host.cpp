@@ -177,7 +177,7 @@ int tile_config(int md, int shape, int64_t H, int64_t I) {
 // Default configuration per token bucket, from measurements on MI355X
 // (Qwen3-235B-shaped bf16 and the TP2 MXFP4 shard):
 //  * enough rows per expert: LDS-tiled GEMMs (bf16: 64 x 256 tiles with
-//    three stages in flight from 4 expected rows per expert, 128 x 512 from
+//    three stages in flight from 0.1 expected rows per expert, 128 x 512 from
 //    192, 256 x 256 from 512; MXFP4: 64 x 512 from 64 rows, 256 x 256 from
 //    128);
 //  * otherwise the register weight stream, whose block rows cover the
@@ -196,7 +196,7 @@ int default_config(int mode, int64_t T, int64_t H, int64_t I, int64_t E, int64_t
     if (md == 0) {
         if (rows >= 512.0) c = tile_config(0, 0, H, I);
         else if (rows >= 192.0) c = tile_config(0, 1, H, I);
-        else if (rows >= 4.0) c = tile_config(0, 4, H, I);
+        else if (rows >= 0.1) c = tile_config(0, 4, H, I);
     } else {
         if (rows >= 128.0) c = tile_config(1, 0, H, I);
         else if (rows >= 64.0) c = tile_config(1, 2, H, I);
@@ -219,7 +219,8 @@ int default_config(int mode, int64_t T, int64_t H, int64_t I, int64_t E, int64_t
         bm = busy <= 16.0 ? 16 : (busy <= 32.0 ? 32 : (rows < 192.0 ? 64 : 128));
     const int64_t blocks = experts * std::max<int64_t>(1, (int64_t)(rows / bm + 0.999));
     int wk = 1;
-    while (wk < 4 && (bm < 64 || wk < 2) && blocks * (I / (32 * (4 / wk))) < 1024) wk <<= 1;
+    const int wk_max = md == 0 ? 2 : 4;   // bf16: a 4-way K split measured slower than 2
+    while (wk < wk_max && (bm < 64 || wk < 2) && blocks * (I / (32 * (4 / wk))) < 1024) wk <<= 1;
     // gemm2 from an LDS-staged tile once enough experts are touched to fill
     // the chip with its wider workgroups and the gain covers the second align
     int g2 = -1;
