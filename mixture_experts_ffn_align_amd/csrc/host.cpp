@@ -178,7 +178,7 @@ int tile_config(int md, int shape, int64_t H, int64_t I) {
 // (Qwen3-235B-shaped bf16 and the TP2 MXFP4 shard):
 //  * enough rows per expert: LDS-tiled GEMMs (bf16: 64 x 256 tiles with
 //    three stages in flight from 0.1 expected rows per expert, 128 x 512 from
-//    192, 256 x 256 from 512; MXFP4: 64 x 512 from 64 rows, 256 x 256 from
+//    64, 256 x 256 from 512; MXFP4: 64 x 512 from 64 rows, 256 x 256 from
 //    128);
 //  * otherwise the register weight stream, whose block rows cover the
 //    typical busiest expert of the bucket in one block (each expert's
@@ -195,7 +195,7 @@ int default_config(int mode, int64_t T, int64_t H, int64_t I, int64_t E, int64_t
     int c = -1;
     if (md == 0) {
         if (rows >= 512.0) c = tile_config(0, 0, H, I);
-        else if (rows >= 192.0) c = tile_config(0, 1, H, I);
+        else if (rows >= 64.0) c = tile_config(0, 1, H, I);
         else if (rows >= 0.1) c = tile_config(0, 4, H, I);
     } else {
         if (rows >= 128.0) c = tile_config(1, 0, H, I);
