@@ -571,7 +571,7 @@ int gemm_tile_cols(int shape, int stage) {
 }
 
 // K that is a whole number of stage rotations: two 128-byte stages (four for
-// bf16 shape 4), four 64-byte MXFP4 stages
+// bf16 shape 4), four 64-byte or two 128-byte MXFP4 stages (512 values)
 int gemm_tile_k_granule(int mode, int shape) {
     if (mode == 1) return 4 * 128;
     return shape == 4 ? 4 * 64 : 2 * 64;
@@ -589,7 +589,10 @@ hipError_t launch_gemm_tile(int mode, int shape, int stage, const GemmParams& p,
 #define MOE_TILE4(MD, BM, BW, NW) \
     return stage == 1 ? launch_one<MD, 1, BM, BW, NW, 2, 4>(p, s) : launch_one<MD, 2, BM, BW, NW, 2, 4>(p, s)
     if (mode == 1) {
-        if (shape == 0) MOE_TILE(1, 256, 256, 8);
+        // gemm2 (K = I) runs faster with two 128-byte stages; gemm1 keeps
+        // four 64-byte ones
+        if (shape == 0)
+            return stage == 1 ? launch_one<1, 1, 256, 256, 8>(p, s) : launch_one<1, 2, 256, 256, 8, 2, 2>(p, s);
         if (shape == 2) MOE_TILE(1, 64, 512, 4);
         if (shape == 3) MOE_TILE(1, 32, 512, 4);
         // four buffers need four 256-value stages per rotation
