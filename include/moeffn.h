@@ -171,9 +171,9 @@ int moe_quant_mxfp4(const moe_tensor_t *src, const moe_tensor_t *codes,
  *   force_config  -1 for the built-in choice, else an index into the
  *               library's config list (tests of tile invariance).
  * Numerics: fp32 accumulation; h rounded to bf16 (bf16 mode) or quantised to
- * MXFP4 per 32 columns (MXFP4 mode); per-slot results y in fp32; combine
- * acc = fmaf(w_tj, y_tj, acc) over j = 0..k-1 in slot order from +0, then one
- * round to bf16. The tile configuration depends only on (mode, T, H, I, E, k),
+ * MXFP4 per 32 columns (MXFP4 mode); per-slot results y rounded to bf16
+ * (RNE) in both modes; combine acc = fmaf(w_tj, y_tj, acc) over j = 0..k-1 in
+ * slot order from +0 with y widened exactly to fp32, then one round to bf16. The tile configuration depends only on (mode, T, H, I, E, k),
  * never on strides, so every layout runs the same arithmetic.
  */
 typedef struct {

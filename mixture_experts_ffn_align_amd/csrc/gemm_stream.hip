@@ -426,8 +426,7 @@ void gemm_stream(GemmParams p) {
             }
         }
     } else {
-        // y rows: fp32, or bf16 (RNE) in MXFP4 mode
-        float* y = reinterpret_cast<float*>(p.out);
+        // y rows in bf16 (RNE)
         uint16_t* y16 = reinterpret_cast<uint16_t*>(p.out);
 #pragma unroll
         for (int unit = 0; unit < MB * NB; ++unit) {
@@ -439,8 +438,7 @@ void gemm_stream(GemmParams p) {
             for (int i = 0; i < 4; ++i) {
                 const int a = p.sorted[row0 + mi * 16 + kg * 4 + i];
                 if (a >= p.A) continue;
-                if constexpr (MODE == 1) y16[(int64_t)a * p.N + col] = f32_to_bf16_bits(t[i]);
-                else y[(int64_t)a * p.N + col] = t[i];
+                y16[(int64_t)a * p.N + col] = f32_to_bf16_bits(t[i]);
             }
         }
     }

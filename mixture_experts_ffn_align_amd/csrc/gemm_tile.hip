@@ -510,22 +510,17 @@ void gemm_tile(GemmParams p) {
             }
         }
     } else {
-        // y rows by flat assignment, 128 columns per wave row: fp32, or bf16
-        // (RNE) in MXFP4 mode
-        constexpr int YB = MODE == 1 ? 2 : 4;
+        // y rows by flat assignment, 128 columns per wave row, bf16 (RNE)
+        constexpr int YB = 2;
         char* y = reinterpret_cast<char*>(p.out);
         through_lds(
             [&](int mi, char* prow) {
 #pragma unroll
                 for (int ni = 0; ni < 8; ++ni) {
-                    if constexpr (MODE == 1) {
-                        const uint2 pk = {
-                            f32_to_bf16_bits(acc[mi][ni][0]) | ((uint32_t)f32_to_bf16_bits(acc[mi][ni][1]) << 16),
-                            f32_to_bf16_bits(acc[mi][ni][2]) | ((uint32_t)f32_to_bf16_bits(acc[mi][ni][3]) << 16)};
-                        *reinterpret_cast<uint2*>(prow + (ni * 16 + kg * 4) * 2) = pk;
-                    } else {
-                        *reinterpret_cast<f32x4_t*>(prow + (ni * 16 + kg * 4) * 4) = acc[mi][ni];
-                    }
+                    const uint2 pk = {
+                        f32_to_bf16_bits(acc[mi][ni][0]) | ((uint32_t)f32_to_bf16_bits(acc[mi][ni][1]) << 16),
+                        f32_to_bf16_bits(acc[mi][ni][2]) | ((uint32_t)f32_to_bf16_bits(acc[mi][ni][3]) << 16)};
+                    *reinterpret_cast<uint2*>(prow + (ni * 16 + kg * 4) * 2) = pk;
                 }
             },
             std::integral_constant<int, 128 * YB>{},

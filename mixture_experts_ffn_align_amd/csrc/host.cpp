@@ -438,7 +438,7 @@ int plan_fused(const moe_fused_args_t* a, Plan* pl) {
         pl->off_h = take((size_t)pl->A * (size_t)I * 2);
         pl->off_hs = 0;
     }
-    pl->off_y = take((size_t)pl->A * (size_t)H * (fp4 ? 2 : 4));   // y: bf16 in MXFP4 mode
+    pl->off_y = take((size_t)pl->A * (size_t)H * 2);   // y: bf16
     pl->total = off;
     return MOE_OK;
 }
@@ -815,8 +815,7 @@ int moe_fused_fwd(const moe_fused_args_t* args, void* ws, size_t ws_bytes, moe_s
     // stage 4: combine
     tm.begin(4);
     CombineParams cp{};
-    cp.y = base + pl.off_y;
-    cp.y_bf16 = fp4 ? 1 : 0;
+    cp.y = reinterpret_cast<const uint16_t*>(base + pl.off_y);
     cp.ids = (const int32_t*)a.topk_ids.data;
     cp.is_t = a.topk_ids.stride[0];
     cp.is_j = a.topk_ids.stride[1];

@@ -275,8 +275,7 @@ bool gemm_tile_supported(int mode, int shape);
 hipError_t launch_gemm_tile(int mode, int shape, int stage, const GemmParams& p, hipStream_t s);
 
 struct CombineParams {
-    const void* y;          // [A, H] fp32, or bf16 when y_bf16
-    int32_t y_bf16;
+    const uint16_t* y;      // [A, H] bf16
     const int32_t* ids;
     int64_t is_t, is_j;
     const float* w;

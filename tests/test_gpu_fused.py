@@ -60,7 +60,7 @@ def test_tiny_bf16_every_token(T):
     assert_routing_equal(gpu, orc)
     out = _fused_bf16(inp, *gpu)
     r = _check_bf16(inp, out, *orc, np.arange(T))
-    assert r < 2e-3          # only bf16 rounding of h and out separates the two
+    assert r < 3e-3          # only bf16 rounding of h, y and out separates the two
 
 
 def test_tiny_bf16_tile_configs():
