@@ -116,6 +116,9 @@ def main():
     ap.add_argument("--bf16", default="",
                     help="comma-separated token buckets: one JSON line per bucket for the bf16 "
                          "Qwen3-235B-shaped layer (graph-timed fused forward, packed w13 views)")
+    ap.add_argument("--ep", type=int, default=0,
+                    help="with --bf16: time one expert-parallel shard of S (experts [0, E/S), global "
+                         "ids, per-slot rows out) and the tokens' home combine instead of the whole layer")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
@@ -140,6 +143,9 @@ def main():
         return
     if args.mxfp4:
         mxfp4_buckets([int(t) for t in args.mxfp4.split(",")], args, dev)
+        return
+    if args.bf16 and args.ep > 1:
+        ep_buckets([int(t) for t in args.bf16.split(",")], args.ep, dev)
         return
     if args.bf16:
         bf16_buckets([int(t) for t in args.bf16.split(",")], args, dev)
@@ -413,6 +419,61 @@ def bf16_buckets(buckets, args, dev):
                                                "gemm2_kernel", "gemm1_split_k", "gemm2_split_k")},
         }), flush=True)
         del inp, ids, wts, out, ws
+        torch.cuda.empty_cache()
+
+
+def ep_buckets(buckets, S, dev):
+    """One expert-parallel shard of the bf16 Qwen3-235B-shaped layer: shard 0
+    of S holds experts [0, E/S) as views into packed w13, takes the global
+    top-8 ids, and writes the per-slot rows of its slots (what an all-to-all
+    would return to the tokens' home ranks); then the home combine of all T*k
+    rows. Both graph-timed; inputs as in --bf16."""
+    import torch
+    import mixture_experts_ffn_align_amd as moe
+    from mixture_experts_ffn_align_amd import workloads as W
+
+    sh = W.QWEN3_235B_BF16
+    H, I, E, k = sh.hidden, sh.inter, sh.experts, sh.top_k
+    es = E // S
+    log(f"[bench] drawing weights {sh.name}")
+    g = torch.Generator(device=dev).manual_seed(0)
+    w13, w2 = W.draw_weights(sh, g, dev)
+    gate, up = W.packed_views(w13, I)
+    gs, us, w2s = gate[:es], up[:es], w2[:es]
+    per_expert = 3 * I * H * 2
+    for T in buckets:
+        inp = W.make_inputs(sh, T, seed=T, device=dev, weights=(w13, w2))
+        ids, wts = moe.moe_topk_softmax(inp["logits"], k)
+        y = torch.zeros((T, k, H), dtype=torch.bfloat16, device=dev)   # foreign rows stay 0
+        out = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+        kw = dict(expert_offset=0, num_global_experts=E, y_rows=y)
+        ws = torch.empty(moe.moe_fused_workspace_size(inp["x"], gs, us, w2s, ids, wts, **kw),
+                         dtype=torch.uint8, device=dev)
+        reps = max(5, min(200, int(2e5 / (T / S + 50))))
+        us_shard = graph_time_us(lambda: moe.moe_fused_fwd(inp["x"], gs, us, w2s, ids, wts, workspace=ws, **kw),
+                                 reps)
+        us_comb = graph_time_us(lambda: moe.moe_combine(y, ids, wts, E, out=out), reps)
+        local = (ids < es)
+        n_local = int(local.sum().item())
+        touched = int(torch.unique(ids[local]).numel())
+        byts = touched * per_expert + T * H * 2 + n_local * H * 2 + 4 * T * k
+        flops = 6 * H * I * n_local
+        hbm_s, mfma_s = byts / (HBM_PEAK_GBS * 1e9), flops / (BF16_PEAK_TFLOPS * 1e12)
+        comb_bytes = T * k * H * 2 + T * H * 2 + 8 * T * k
+        print(json.dumps({
+            "workload": f"{sh.name}, expert-parallel shard 0 of {S} (experts [0, {es})), global ids, "
+                        "per-slot rows out; then the home combine of all rows",
+            "tokens": T, "local_slots": n_local, "touched_local_experts": touched,
+            "shard_us_per_call": round(us_shard, 1),
+            "shard_algorithmic_bytes": byts,
+            "shard_bound": "hbm" if hbm_s >= mfma_s else "mfma",
+            "shard_roofline_frac": round(max(hbm_s, mfma_s) / (us_shard * 1e-6), 3),
+            "shard_hbm_gbs": round(byts / (us_shard * 1e-6) / 1e9, 1),
+            "combine_us_per_call": round(us_comb, 1),
+            "combine_hbm_gbs": round(comb_bytes / (us_comb * 1e-6) / 1e9, 1),
+            "timing": f"HIP graph of one call, {reps} replays back to back",
+        }), flush=True)
+        del inp, ids, wts, y, out, ws
         torch.cuda.empty_cache()
 
 

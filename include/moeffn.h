@@ -160,9 +160,11 @@ int moe_quant_mxfp4(const moe_tensor_t *src, const moe_tensor_t *codes,
  *   gate_scale, up_scale   MXFP4 only: E8M0 [E, I, H/32], last stride 1.
  *   w2          bf16 [E, H, I] | FP4X2 [E, H, I/2]; last stride 1.
  *   w2_scale    MXFP4 only: E8M0 [E, H, I/32], last stride 1.
- *   topk_ids    [T, k] int32, any strides; ids outside [0, E) are skipped.
+ *   topk_ids    [T, k] int32, any strides. Expert ids are global: the
+ *               weights hold experts expert_offset .. expert_offset + E - 1,
+ *               and a slot whose id lies outside that range is skipped.
  *   topk_weights [T, k] float32, any strides.
- *   out         [T, H] bf16 out, any strides.
+ *   out         [T, H] bf16 out, any strides; ignored when y_rows is given.
  *   stage_events NULL, or 2*MOE_NUM_STAGES hipEvent_t handles created by the
  *               caller; event 2s is recorded before stage s and 2s+1 after
  *               it, on the call's stream; NULL entries are skipped. Stages:
@@ -173,8 +175,9 @@ int moe_quant_mxfp4(const moe_tensor_t *src, const moe_tensor_t *codes,
  * Numerics: fp32 accumulation; h rounded to bf16 (bf16 mode) or quantised to
  * MXFP4 per 32 columns (MXFP4 mode); per-slot results y rounded to bf16
  * (RNE) in both modes; combine acc = fmaf(w_tj, y_tj, acc) over j = 0..k-1 in
- * slot order from +0 with y widened exactly to fp32, then one round to bf16. The tile configuration depends only on (mode, T, H, I, E, k),
- * never on strides, so every layout runs the same arithmetic.
+ * slot order from +0 with y widened exactly to fp32, then one round to bf16.
+ * The tile configuration depends only on (mode, T, H, I, k) and the global
+ * expert count, never on strides, so every layout runs the same arithmetic.
  */
 typedef struct {
     int32_t mode;
@@ -188,6 +191,23 @@ typedef struct {
     moe_tensor_t out;
     void *const *stage_events;
     int32_t force_config;
+    /* Expert-parallel shard (Liger-Kernel PR #1377, Notes: the expert-
+     * parallel path; one GPU here holds one shard):
+     *   expert_offset       global id of the first local expert, >= 0.
+     *   num_global_experts  experts over all shards (0: E); it only sizes
+     *                       the tile choice, which then matches the
+     *                       unsharded call (same K order, same bits).
+     *   y_rows              data NULL: combine into out. Otherwise [T, k, H]
+     *                       bf16 out with stride(0) == k * stride(1), last
+     *                       stride 1, 16-byte aligned rows: row (t, j) gets
+     *                       the per-slot result y_tj (bf16) of every local
+     *                       slot, other rows are left untouched, and out is
+     *                       not written. Every shard can write its slots into
+     *                       one buffer (rows sent home); moe_combine then
+     *                       gives the unsharded call's out, bit for bit. */
+    int32_t expert_offset;
+    moe_tensor_t y_rows;
+    int32_t num_global_experts;
     int32_t reserved;
 } moe_fused_args_t;
 
@@ -209,10 +229,27 @@ typedef struct {
 int moe_query_config(const moe_fused_args_t *args, moe_config_t *cfg);
 /* Validate args and report the workspace bytes moe_fused_fwd needs. Host only. */
 int moe_fused_workspace_size(const moe_fused_args_t *args, size_t *bytes);
-/* The fused forward: align, (prepare), gemm1 + act, gemm2, combine.
+/* The fused forward: align, (prepare), gemm1 + act, gemm2, combine (or the
+ * y_rows output).
  * ws: caller-owned device scratch, 256-byte aligned, >= the reported size;
  * its contents on entry do not matter. T = 0 returns MOE_OK with no launch. */
 int moe_fused_fwd(const moe_fused_args_t *args, void *ws, size_t ws_bytes, moe_stream_t stream);
+
+/* ------------------------------------------------------------ combine --
+ * moe_combine: step 6 on its own, for per-slot results computed elsewhere
+ * (the rows y_rows of expert-parallel shards, sent back to the tokens' home).
+ *   y_rows        [T, k, H] bf16, last stride 1, 16-byte aligned rows.
+ *   topk_ids      [T, k] int32, any strides: slot (t, j) counts when
+ *                 0 <= id < num_experts (global ids), else it is skipped and
+ *                 its row is not read.
+ *   topk_weights  [T, k] float32, any strides.
+ *   out           [T, H] bf16 out, any strides.
+ * out_t = bf16(acc), acc = fmaf(w_tj, y_tj, acc) over counted j in slot
+ * order from +0, exactly the fused call's combine. T = 0 is a no-op.
+ */
+int moe_combine(const moe_tensor_t *y_rows, const moe_tensor_t *topk_ids,
+                const moe_tensor_t *topk_weights, int32_t num_experts, const moe_tensor_t *out,
+                moe_stream_t stream);
 
 /* ------------------------------------------------------------- errors --
  * Static text for a status code; never NULL. */

@@ -18,7 +18,7 @@ from ._abi import (DT_BF16, DT_E8M0, DT_F32, DT_FP4X2, DT_I32, MODE_BF16, MODE_M
                    MoEError)
 
 __all__ = ["moe_topk_softmax", "moe_align", "moe_align_capacity", "moe_quant_mxfp4",
-           "moe_fused_fwd", "moe_fused_workspace_size", "moe_query_config", "MoEError",
+           "moe_fused_fwd", "moe_fused_workspace_size", "moe_query_config", "moe_combine", "MoEError",
            "MODE_BF16", "MODE_MXFP4", "STAGES", "library_path"]
 
 _TORCH_DT = {torch.bfloat16: DT_BF16, torch.float32: DT_F32, torch.int32: DT_I32}
@@ -112,7 +112,8 @@ def moe_quant_mxfp4(src: torch.Tensor, codes: Optional[torch.Tensor] = None,
 
 
 def _fused_args(x, gate, up, w2, topk_ids, topk_weights, out, gate_scale=None, up_scale=None,
-                w2_scale=None, mode=MODE_BF16, stage_events=None, force_config=-1):
+                w2_scale=None, mode=MODE_BF16, stage_events=None, force_config=-1, expert_offset=0,
+                num_global_experts=0, y_rows=None):
     a = _abi.FusedArgs()
     a.mode = mode
     a.activation = _abi.ACT_SILU
@@ -127,6 +128,9 @@ def _fused_args(x, gate, up, w2, topk_ids, topk_weights, out, gate_scale=None, u
     a.topk_weights = _desc(topk_weights)
     a.out = _desc(out)
     a.force_config = force_config
+    a.expert_offset = expert_offset
+    a.num_global_experts = num_global_experts
+    a.y_rows = _desc(y_rows)
     keep = None
     if stage_events is not None:
         keep = (ctypes.c_void_p * len(stage_events))(*[e or None for e in stage_events])
@@ -169,18 +173,24 @@ def moe_fused_fwd(x: torch.Tensor, gate: torch.Tensor, up: torch.Tensor, w2: tor
                   out: Optional[torch.Tensor] = None, *, gate_scale=None, up_scale=None,
                   w2_scale=None, mode: int = MODE_BF16, workspace: Optional[torch.Tensor] = None,
                   stage_events: Optional[Sequence[int]] = None, force_config: int = -1,
-                  stream=None) -> torch.Tensor:
+                  expert_offset: int = 0, num_global_experts: int = 0,
+                  y_rows: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Fused MoE forward: align, (quantise x), gemm1 + SiLU*up, gemm2, combine.
 
     bf16 mode: gate/up [E, I, H] and w2 [E, H, I] bf16 (any expert/row strides).
     MXFP4 mode: gate/up/w2 are uint8 code tensors [.., K/2] with uint8 e8m0
     scales [.., K/32]. stage_events: 10 raw hipEvent_t handles (0 skips one) or None.
+    Expert-parallel shard: the weights hold global experts expert_offset ..
+    expert_offset + E - 1 of num_global_experts; other slots are skipped. With
+    y_rows ([T, k, H] bf16) the per-slot results of local slots go there and
+    the call returns y_rows without combining.
     """
     L = _abi.load()
-    if out is None:
+    if out is None and y_rows is None:
         out = torch.empty(x.shape, dtype=torch.bfloat16, device=x.device)
     a, keep = _fused_args(x, gate, up, w2, topk_ids, topk_weights, out, gate_scale, up_scale,
-                          w2_scale, mode, stage_events, force_config)
+                          w2_scale, mode, stage_events, force_config, expert_offset,
+                          num_global_experts, y_rows)
     n = ctypes.c_size_t(0)
     _abi.check(L.moe_fused_workspace_size(ctypes.byref(a), ctypes.byref(n)))
     if workspace is None:
@@ -188,4 +198,17 @@ def moe_fused_fwd(x: torch.Tensor, gate: torch.Tensor, up: torch.Tensor, w2: tor
     _abi.check(L.moe_fused_fwd(ctypes.byref(a), workspace.data_ptr() if workspace.numel() else 0,
                                workspace.numel(), _stream(stream)))
     del keep
+    return y_rows if y_rows is not None else out
+
+
+def moe_combine(y_rows: torch.Tensor, topk_ids: torch.Tensor, topk_weights: torch.Tensor,
+                num_experts: int, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """out[t] = bf16(slot-ordered fmaf sum of w[t, j] * y_rows[t, j]) over ids in [0, num_experts)."""
+    L = _abi.load()
+    T, _, H = y_rows.shape
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=y_rows.device)
+    dy, di, dw, do = _desc(y_rows), _desc(topk_ids), _desc(topk_weights), _desc(out)
+    _abi.check(L.moe_combine(ctypes.byref(dy), ctypes.byref(di), ctypes.byref(dw), num_experts,
+                             ctypes.byref(do), _stream(stream)))
     return out

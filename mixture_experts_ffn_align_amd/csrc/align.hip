@@ -28,8 +28,8 @@ constexpr int kFusedMaxA = 16384;
 __device__ __forceinline__ int expert_of(const AlignParams& p, int a) {
     int t = (int)((unsigned)a / (unsigned)p.k);
     int j = a - t * p.k;
-    int e = p.ids[(int64_t)t * p.is_t + (int64_t)j * p.is_j];
-    return (e >= 0 && e < p.E) ? e : -1;
+    const int64_t e = (int64_t)p.ids[(int64_t)t * p.is_t + (int64_t)j * p.is_j] - p.e_off;
+    return (e >= 0 && e < p.E) ? (int)e : -1;
 }
 
 // Experts of a wave's indices [lo, hi), lane-strided: eid[r] is the expert

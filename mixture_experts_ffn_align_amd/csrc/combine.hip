@@ -1,8 +1,10 @@
-// Combine: out[t, n] = bf16(sum over slots j = 0..k-1 of w[t, j] * y[t*k + j, n]),
+// Combine: out[t, n] = bf16(sum over slots j = 0..k-1 of w[t, j] * y[t, j, n]),
 // y stored in bf16 and widened exactly to fp32, accumulated with fmaf in slot
-// order from +0 and rounded once. Slots whose id lies outside [0, E) contribute
-// nothing. No atomics, so the result is the same on every run and for every
-// input layout.
+// order from +0 and rounded once. Slots whose id lies outside
+// [e_off, e_off + E) contribute nothing and their rows are not read. No
+// atomics, so the result is the same on every run and for every input layout.
+#include <algorithm>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -11,21 +13,16 @@ namespace {
 // Each thread produces CP (4 or 8) consecutive columns of one token: one 8- or
 // 16-byte load of y per slot.
 template <int CP>
-__global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
-    const int ncol = p.H / CP;
-    const int nqb = (ncol + 255) / 256;               // workgroups per token
-    const int t = blockIdx.x / nqb;
-    const int q = (blockIdx.x % nqb) * 256 + threadIdx.x;
+__device__ __forceinline__ void combine_one(const CombineParams& p, int64_t t, int q) {
     const int n = q * CP;
-    if (q >= ncol) return;
     float acc[CP];
 #pragma unroll
     for (int i = 0; i < CP; ++i) acc[i] = 0.f;
     for (int j = 0; j < p.k; ++j) {
-        const int e = p.ids[(int64_t)t * p.is_t + (int64_t)j * p.is_j];
+        const int64_t e = (int64_t)p.ids[(int64_t)t * p.is_t + (int64_t)j * p.is_j] - p.e_off;
         if (e < 0 || e >= p.E) continue;
         const float wt = p.w[(int64_t)t * p.ws_t + (int64_t)j * p.ws_j];
-        const uint16_t* src = p.y + ((int64_t)t * p.k + j) * p.H + n;
+        const uint16_t* src = p.y + (int64_t)t * p.ys_t + (int64_t)j * p.ys_j + n;
         uint32_t u[CP / 2];
         if constexpr (CP == 8) {
             const uint4 v = *reinterpret_cast<const uint4*>(src);
@@ -56,13 +53,28 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
     }
 }
 
+// Workgroup b covers token b / nqb, column group b % nqb; the grid is capped
+// and strides over the (token, column group) pairs.
+template <int CP>
+__global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
+    const int ncol = p.H / CP;
+    const int nqb = (ncol + 255) / 256;               // workgroups per token
+    const int64_t total = (int64_t)p.T * nqb;
+    for (int64_t b = blockIdx.x; b < total; b += gridDim.x) {
+        const int64_t t = b / nqb;
+        const int q = (int)(b % nqb) * 256 + threadIdx.x;
+        if (q < ncol) combine_one<CP>(p, t, q);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t s) {
     if (p.T == 0) return hipSuccess;
     const int cp = p.H % 8 == 0 ? 8 : 4;
     const int64_t ncol = p.H / cp;
-    dim3 grid((unsigned)(((ncol + 255) / 256) * (int64_t)p.T));
+    const int64_t blocks = ((ncol + 255) / 256) * (int64_t)p.T;
+    dim3 grid((unsigned)std::min<int64_t>(blocks, (int64_t)1 << 22));
     if (cp == 8) hipLaunchKernelGGL(combine_kernel<8>, grid, dim3(256), 0, s, p);
     else hipLaunchKernelGGL(combine_kernel<4>, grid, dim3(256), 0, s, p);
     return hipGetLastError();

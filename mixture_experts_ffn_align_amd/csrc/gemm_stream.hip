@@ -438,7 +438,7 @@ void gemm_stream(GemmParams p) {
             for (int i = 0; i < 4; ++i) {
                 const int a = p.sorted[row0 + mi * 16 + kg * 4 + i];
                 if (a >= p.A) continue;
-                y16[(int64_t)a * p.N + col] = f32_to_bf16_bits(t[i]);
+                y16[(int64_t)a * p.out_row + col] = f32_to_bf16_bits(t[i]);
             }
         }
     }
@@ -583,7 +583,7 @@ void gemm_stream_nt(GemmParams p) {
 #pragma unroll
         for (int mi = 0; mi < MB; ++mi) {
             if (arow[mi] >= p.A) continue;
-            uint16_t* yr = y + (int64_t)arow[mi] * p.N + col0(j) + kg * 4;
+            uint16_t* yr = y + (int64_t)arow[mi] * p.out_row + col0(j) + kg * 4;
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
                 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));

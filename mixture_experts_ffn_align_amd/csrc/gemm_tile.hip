@@ -527,7 +527,7 @@ void gemm_tile(GemmParams p) {
             [&](int a, int c, i32x4_t v) {
                 // y is read once, by the combine, long after: stream it past the caches
                 __builtin_nontemporal_store(
-                    v, reinterpret_cast<i32x4_t*>(y + ((int64_t)a * p.N + n0 + wn * 128) * YB + c * 16));
+                    v, reinterpret_cast<i32x4_t*>(y + ((int64_t)a * p.out_row + n0 + wn * 128) * YB + c * 16));
             });
     }
 }

@@ -9,6 +9,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -186,7 +187,12 @@ int tile_config(int md, int shape, int64_t H, int64_t I) {
 //    grid would not fill the chip; its gemm2 moves to an LDS-staged tile
 //    (own block size, second layout) where that measured faster, or, for
 //    MXFP4 with I = 512, to workgroups that take 2-8 column tiles each.
-int default_config(int mode, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k) {
+// E counts the experts over all shards of an expert-parallel group and sets
+// the rows per expert; E_local (the call's own experts) only steps a bf16
+// tile down to a smaller one while the gemm1 grid would not give every CU two
+// workgroups. Tiles never split K, so that step keeps the sums bit-identical
+// to the unsharded call, and the register stream's K split is chosen from E.
+int default_config(int mode, int64_t T, int64_t H, int64_t I, int64_t E, int64_t E_local, int64_t k) {
     const int64_t bucket = bucket_of(T);
     const double rows = (double)bucket * (double)k / (double)E;   // expected rows per expert
     const double busy = rows + 3.0 * __builtin_sqrt(rows);          // typical maximum
@@ -194,9 +200,18 @@ int default_config(int mode, int64_t T, int64_t H, int64_t I, int64_t E, int64_t
     const int64_t experts = std::min<int64_t>(bucket * k, E);      // touched at most
     int c = -1;
     if (md == 0) {
-        if (rows >= 512.0) c = tile_config(0, 0, H, I);
-        else if (rows >= 64.0) c = tile_config(0, 1, H, I);
-        else if (rows >= 0.1) c = tile_config(0, 4, H, I);
+        int shape = -1;
+        if (rows >= 512.0) shape = 0;
+        else if (rows >= 64.0) shape = 1;
+        else if (rows >= 0.1) shape = 4;
+        const int64_t touched = std::min<int64_t>(bucket * k, E_local);
+        auto grid = [&](int sh) {
+            const int bm = gemm_tile_rows(0, sh);
+            return touched * (int64_t)std::ceil(rows / bm) * (I / gemm_tile_cols(sh, 1));
+        };
+        while ((shape == 0 || shape == 1) && grid(shape) < 2 * 256 && tile_config(0, shape == 0 ? 1 : 4, H, I) >= 0)
+            shape = shape == 0 ? 1 : 4;
+        if (shape >= 0) c = tile_config(0, shape, H, I);
     } else {
         if (rows >= 128.0) c = tile_config(1, 0, H, I);
         else if (rows >= 64.0) c = tile_config(1, 2, H, I);
@@ -254,11 +269,22 @@ struct Plan {
     int64_t cap[2];        // sorted capacity of each GEMM's block size
     bool two_aligns;       // the GEMMs use different block sizes
     bool pack_x;
+    int64_t e_off;         // global id of local expert 0
+    bool y_out;            // per-slot rows go to the caller's y_rows; no combine
+    int64_t y_row;         // element stride between the rows of y
     // workspace offsets
     size_t off_counts, off_sorted[2], off_bexp[2], off_npad[2], off_x, off_xs, off_h, off_hs, off_y, total;
 };
 
 int kstep(int mode) { return mode == MOE_MODE_MXFP4 ? 128 : 32; }
+
+// Element stride between consecutive flat rows a = t*k + j of a [T, k, H]
+// y_rows tensor whose token stride is k times its slot stride.
+int64_t y_rows_stride(const moe_tensor_t& y) {
+    const int64_t T = y.size[0], k = y.size[1], H = y.size[2];
+    if (k > 1) return y.stride[1];
+    return T > 1 ? y.stride[0] : H;
+}
 
 // Validate a fused call and build its plan. No device calls.
 int plan_fused(const moe_fused_args_t* a, Plan* pl) {
@@ -295,11 +321,31 @@ int plan_fused(const moe_fused_args_t* a, Plan* pl) {
     const int64_t k = a->topk_ids.size[1];
     if ((rc = check_shape(a->topk_ids, "topk_ids", {T, k}))) return rc;
     if ((rc = check_shape(a->topk_weights, "topk_weights", {T, k}))) return rc;
-    if ((rc = check_desc(&a->out, "out", MOE_DT_BF16, 2))) return rc;
-    if ((rc = check_shape(a->out, "out", {T, H}))) return rc;
+    // expert-parallel shard: global ids, local experts [e_off, e_off + E)
+    if (a->expert_offset < 0) return fail(MOE_ERR_ARG, "expert_offset = %d is negative", a->expert_offset);
+    if (a->num_global_experts < 0 ||
+        (a->num_global_experts > 0 && (int64_t)a->num_global_experts < (int64_t)a->expert_offset + E))
+        return fail(MOE_ERR_ARG, "num_global_experts = %d below expert_offset + E = %lld", a->num_global_experts,
+                    (long long)a->expert_offset + E);
+    const int64_t E_cfg = a->num_global_experts > 0 ? a->num_global_experts : E;
+    const bool y_out = a->y_rows.data != nullptr;
+    if (y_out) {
+        if ((rc = check_desc(&a->y_rows, "y_rows", MOE_DT_BF16, 3))) return rc;
+        if ((rc = check_shape(a->y_rows, "y_rows", {T, k, H}))) return rc;
+        const moe_tensor_t& y = a->y_rows;
+        const int64_t row = y_rows_stride(y);
+        if ((H > 1 && y.stride[2] != 1) || row < H || (k > 1 && T > 1 && y.stride[0] != k * y.stride[1]) ||
+            !aligned16(y.data) || (row * 2) % 16 != 0)
+            return fail(MOE_ERR_LAYOUT,
+                        "y_rows: needs last stride 1, stride(0) == k * stride(1) and 16-byte aligned rows");
+    } else {
+        if ((rc = check_desc(&a->out, "out", MOE_DT_BF16, 2))) return rc;
+        if ((rc = check_shape(a->out, "out", {T, H}))) return rc;
+    }
 
     // sizes this build handles
     if (E < 1 || E > 1024) return fail(MOE_ERR_UNSUPPORTED, "E = %lld outside [1, 1024]", (long long)E);
+    if (E_cfg > (1 << 20)) return fail(MOE_ERR_UNSUPPORTED, "num_global_experts = %lld too large", (long long)E_cfg);
     if (k < 1 || k > 64) return fail(MOE_ERR_UNSUPPORTED, "k = %lld outside [1, 64]", (long long)k);
     const int ks = kstep(a->mode);
     if (H < ks || I < ks || H % 64 != 0 || H % ks != 0 || I % ks != 0 || I % 32 != 0)
@@ -334,12 +380,13 @@ int plan_fused(const moe_fused_args_t* a, Plan* pl) {
     }
     // outputs must not alias inputs
     const moe_tensor_t* ins[6] = {&a->x, &a->gate, &a->up, &a->w2, &a->topk_ids, &a->topk_weights};
+    const moe_tensor_t& dst = y_out ? a->y_rows : a->out;
     for (auto* t : ins)
-        if (overlaps(a->out, *t)) return fail(MOE_ERR_LAYOUT, "out overlaps an input");
+        if (overlaps(dst, *t)) return fail(MOE_ERR_LAYOUT, "%s overlaps an input", y_out ? "y_rows" : "out");
 
     // configuration
     int ci = a->force_config;
-    if (ci < 0) ci = default_config(a->mode, T, H, I, E, k);
+    if (ci < 0) ci = default_config(a->mode, T, H, I, E_cfg, E, k);
     if (ci >= kNumConfigs) return fail(MOE_ERR_ARG, "force_config %d out of range", ci);
     const Cfg c1 = kConfigs[ci];
     const Cfg c2 = c1.g2 >= 0 ? kConfigs[c1.g2] : c1;
@@ -387,6 +434,9 @@ int plan_fused(const moe_fused_args_t* a, Plan* pl) {
     pl->k = k;
     pl->A = T * k;
     pl->cfg_index = ci;
+    pl->e_off = a->expert_offset;
+    pl->y_out = y_out;
+    pl->y_row = y_out ? y_rows_stride(a->y_rows) : H;
     pl->cap[0] = align_capacity(pl->A, E, pl->ks[0].bm);
     pl->cap[1] = align_capacity(pl->A, E, pl->ks[1].bm);
     pl->two_aligns = pl->ks[0].bm != pl->ks[1].bm;
@@ -438,7 +488,7 @@ int plan_fused(const moe_fused_args_t* a, Plan* pl) {
         pl->off_h = take((size_t)pl->A * (size_t)I * 2);
         pl->off_hs = 0;
     }
-    pl->off_y = take((size_t)pl->A * (size_t)H * 2);   // y: bf16
+    pl->off_y = y_out ? 0 : take((size_t)pl->A * (size_t)H * 2);   // y: bf16 (the caller's y_rows if given)
     pl->total = off;
     return MOE_OK;
 }
@@ -623,6 +673,52 @@ int moe_quant_mxfp4(const moe_tensor_t* src, const moe_tensor_t* codes, const mo
     return ok();
 }
 
+int moe_combine(const moe_tensor_t* y_rows, const moe_tensor_t* topk_ids, const moe_tensor_t* topk_weights,
+                int32_t num_experts, const moe_tensor_t* out, moe_stream_t stream) {
+    int rc;
+    if ((rc = check_desc(y_rows, "y_rows", MOE_DT_BF16, 3))) return rc;
+    const int64_t T = y_rows->size[0], k = y_rows->size[1], H = y_rows->size[2];
+    if ((rc = check_desc(topk_ids, "topk_ids", MOE_DT_I32, 2))) return rc;
+    if ((rc = check_desc(topk_weights, "topk_weights", MOE_DT_F32, 2))) return rc;
+    if ((rc = check_desc(out, "out", MOE_DT_BF16, 2))) return rc;
+    if ((rc = check_shape(*topk_ids, "topk_ids", {T, k}))) return rc;
+    if ((rc = check_shape(*topk_weights, "topk_weights", {T, k}))) return rc;
+    if ((rc = check_shape(*out, "out", {T, H}))) return rc;
+    if (num_experts < 1) return fail(MOE_ERR_ARG, "num_experts = %d must be >= 1", num_experts);
+    if (k < 1 || k > 64 || H < 4 || H % 4 != 0 || H > (1 << 24) || T > ((int64_t)1 << 24))
+        return fail(MOE_ERR_UNSUPPORTED, "k = %lld and H = %lld (a multiple of 4) outside what this build handles",
+                    (long long)k, (long long)H);
+    const moe_tensor_t& y = *y_rows;
+    if (y.stride[2] != 1 || !aligned16(y.data) || (T > 1 && (y.stride[0] * 2) % 16 != 0) ||
+        (k > 1 && (y.stride[1] * 2) % 16 != 0))
+        return fail(MOE_ERR_LAYOUT, "y_rows: needs last stride 1 and 16-byte aligned rows");
+    const moe_tensor_t* ins[3] = {y_rows, topk_ids, topk_weights};
+    for (auto* t : ins)
+        if (overlaps(*out, *t)) return fail(MOE_ERR_LAYOUT, "out overlaps an input");
+    if (T == 0) return ok();
+    CombineParams cp{};
+    cp.y = (const uint16_t*)y.data;
+    cp.ys_t = y.stride[0];
+    cp.ys_j = y.stride[1];
+    cp.e_off = 0;
+    cp.ids = (const int32_t*)topk_ids->data;
+    cp.is_t = topk_ids->stride[0];
+    cp.is_j = topk_ids->stride[1];
+    cp.w = (const float*)topk_weights->data;
+    cp.ws_t = topk_weights->stride[0];
+    cp.ws_j = topk_weights->stride[1];
+    cp.out = (uint16_t*)out->data;
+    cp.os_t = out->stride[0];
+    cp.os_h = out->stride[1];
+    cp.T = (int32_t)T;
+    cp.k = (int32_t)k;
+    cp.E = num_experts;
+    cp.H = (int32_t)H;
+    hipError_t e = launch_combine(cp, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "combine");
+    return ok();
+}
+
 int moe_query_config(const moe_fused_args_t* args, moe_config_t* cfg) {
     if (!cfg) return fail(MOE_ERR_NULL, "cfg is NULL");
     Plan pl;
@@ -699,6 +795,7 @@ int moe_fused_fwd(const moe_fused_args_t* args, void* ws, size_t ws_bytes, moe_s
         ap.k = (int32_t)pl.k;
         ap.A = (int32_t)pl.A;
         ap.E = (int32_t)pl.E;
+        ap.e_off = pl.e_off;
         ap.bm = pl.ks[0].bm;
         ap.cap = (int32_t)pl.cap[0];
         ap.sorted = sorted[0];
@@ -806,16 +903,24 @@ int moe_fused_fwd(const moe_fused_args_t* args, void* ws, size_t ws_bytes, moe_s
     }
     g2.K = (int32_t)pl.I;
     g2.N = (int32_t)pl.H;
-    g2.out = base + pl.off_y;
+    g2.out = pl.y_out ? a.y_rows.data : (void*)(base + pl.off_y);
+    g2.out_row = pl.y_row;
     g2.n_tile_groups = 2;
     g2.max_mblocks = (int32_t)(pl.cap[1] / pl.ks[1].bm);
     if ((e = launch(1, g2)) != hipSuccess) return hip_fail(e, "gemm2");
     tm.end(3);
 
-    // stage 4: combine
+    // stage 4: combine (the caller combines y_rows itself)
     tm.begin(4);
+    if (pl.y_out) {
+        tm.end(4);
+        return ok();
+    }
     CombineParams cp{};
     cp.y = reinterpret_cast<const uint16_t*>(base + pl.off_y);
+    cp.ys_t = pl.k * pl.H;
+    cp.ys_j = pl.H;
+    cp.e_off = pl.e_off;
     cp.ids = (const int32_t*)a.topk_ids.data;
     cp.is_t = a.topk_ids.stride[0];
     cp.is_j = a.topk_ids.stride[1];

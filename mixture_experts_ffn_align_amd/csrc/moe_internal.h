@@ -120,6 +120,7 @@ struct AlignParams {
     const int32_t* ids;
     int64_t is_t, is_j;
     int32_t T, k, A, E, bm;
+    int64_t e_off;          // global id of local expert 0: slot ids are e_off + local
     int32_t cap, cap2;      // entries of sorted / sorted2 (every one is written)
     int32_t* sorted;        // [cap]
     int32_t* block_expert;  // [cap / bm]
@@ -237,8 +238,9 @@ struct GemmParams {
     int32_t K;              // contraction length
     int32_t N;              // output columns (stage 1: I, stage 2: H)
     // outputs
-    void* out;              // stage 1: h (bf16 [A, I] or fp4 [A, I/2]); stage 2: y [A, H] (fp32 / MXFP4: bf16);
-                            // both by flat assignment index
+    void* out;              // stage 1: h (bf16 [A, I] or fp4 [A, I/2]); stage 2: y (bf16 rows of out_row
+                            // elements); both by flat assignment index
+    int64_t out_row;        // stage 2: element stride between y rows
     uint8_t* out_sc;        // stage 1 MXFP4: h scales [A, I/32]
     int32_t n_tile_groups;  // tiles along N are walked in groups of this size
     int32_t max_mblocks;
@@ -275,7 +277,9 @@ bool gemm_tile_supported(int mode, int shape);
 hipError_t launch_gemm_tile(int mode, int shape, int stage, const GemmParams& p, hipStream_t s);
 
 struct CombineParams {
-    const uint16_t* y;      // [A, H] bf16
+    const uint16_t* y;      // bf16 row of slot (t, j) at t * ys_t + j * ys_j
+    int64_t ys_t, ys_j;
+    int64_t e_off;          // slot counts when 0 <= id - e_off < E
     const int32_t* ids;
     int64_t is_t, is_j;
     const float* w;

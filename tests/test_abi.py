@@ -166,3 +166,49 @@ def test_align_and_route_argument_checks():
     nb = ctypes.c_size_t(0)
     assert L.moe_align_workspace_size(4, 2, 8, 16, ctypes.byref(nb)) == 0 and nb.value == 0
     assert L.moe_align_workspace_size(40000, 8, 128, 16, ctypes.byref(nb)) == 0 and nb.value > 0
+
+
+def test_expert_parallel_shard_checks():
+    """Expert-parallel shard arguments are checked on the host: a negative
+    offset or a global expert count below offset + E is MOE_ERR_ARG, a y_rows
+    tensor the gemm2 epilogue cannot write is MOE_ERR_LAYOUT, and with y_rows
+    the call needs no y segment of its own in the workspace."""
+    T, H, k = 8, 256, 2
+    x, gate, up, w2, ids, w = _bf16_case(T=T, H=H, k=k)
+    st = _status(lambda: moe.moe_fused_workspace_size(x, gate, up, w2, ids, w, expert_offset=-1))
+    assert st == "MOE_ERR_ARG"
+    st = _status(lambda: moe.moe_fused_workspace_size(x, gate, up, w2, ids, w, expert_offset=8,
+                                                      num_global_experts=15))
+    assert st == "MOE_ERR_ARG"
+    plain = moe.moe_fused_workspace_size(x, gate, up, w2, ids, w)
+    y = torch.zeros(T, k, H, dtype=torch.bfloat16)
+    with_y = moe.moe_fused_workspace_size(x, gate, up, w2, ids, w, expert_offset=8,
+                                          num_global_experts=16, y_rows=y)
+    assert with_y <= plain - T * k * H * 2
+    # padded rows are fine, slot-major rows or a transposed last dim are not
+    ypad = torch.zeros(T, k, H + 64, dtype=torch.bfloat16)[:, :, :H]
+    moe.moe_fused_workspace_size(x, gate, up, w2, ids, w, y_rows=ypad)
+    yslot = torch.zeros(k, T, H, dtype=torch.bfloat16).transpose(0, 1)
+    assert _status(lambda: moe.moe_fused_workspace_size(x, gate, up, w2, ids, w, y_rows=yslot)) == \
+        "MOE_ERR_LAYOUT"
+    yt = torch.zeros(T, H, k, dtype=torch.bfloat16).transpose(1, 2)
+    assert _status(lambda: moe.moe_fused_workspace_size(x, gate, up, w2, ids, w, y_rows=yt)) == \
+        "MOE_ERR_LAYOUT"
+    # the global expert count, not the shard's, picks the tiles
+    xb, gb, ub, w2b, idb, wb = _bf16_case(T=512, H=H, E=8, k=8)
+    shard = moe.moe_query_config(xb, gb, ub, w2b, idb, wb, expert_offset=0, num_global_experts=128)
+    xg, gg, ug, w2g, idg, wg = _bf16_case(T=512, H=H, E=128, k=8)
+    assert shard == moe.moe_query_config(xg, gg, ug, w2g, idg, wg)
+
+
+def test_combine_argument_checks():
+    T, k, H = 4, 2, 256
+    y = torch.zeros(T, k, H, dtype=torch.bfloat16)
+    ids = torch.zeros(T, k, dtype=torch.int32)
+    w = torch.zeros(T, k, dtype=torch.float32)
+    assert _status(lambda: moe.moe_combine(y, ids[:, :1], w, 8, stream=0)) == "MOE_ERR_SHAPE"
+    assert _status(lambda: moe.moe_combine(y, ids, w, 0, stream=0)) == "MOE_ERR_ARG"
+    assert _status(lambda: moe.moe_combine(y[:, :, 1:253], ids, w, 8, stream=0)) == "MOE_ERR_LAYOUT"
+    assert _status(lambda: moe.moe_combine(y.float(), ids, w, 8, stream=0)) == "MOE_ERR_DTYPE"
+    out = moe.moe_combine(y[:0], ids[:0], w[:0], 8, stream=0)
+    assert out.shape == (0, H)
