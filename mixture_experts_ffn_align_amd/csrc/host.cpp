@@ -131,7 +131,8 @@ bool valid_bm(int bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128 || 
 //
 // The list of tile configurations the fused forward can run. The choice
 // depends only on (mode, T, H, I, E, k), never on strides or addresses, so
-// strided and contiguous calls execute the same arithmetic.
+// strided and contiguous calls execute the same arithmetic. Entries are only
+// ever appended: the tuned table and force_config refer to them by index.
 struct Cfg {
     int bm, wk1, wk2, nb;
     int tile;     // 0: weight-streaming GEMMs; 1 + shape: LDS-tiled GEMMs of that tile shape
@@ -157,6 +158,22 @@ const Cfg kConfigs[] = {
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
+// Per-bucket choices measured by the tuner (mixture_experts_ffn_align_amd/
+// tune.py): every valid config timed on the layer's synthetic inputs, the
+// fastest one whose output passes the error gate against the built-in
+// choice kept. Exact matches only; other shapes use the rules below.
+struct TunedRow {
+    int mode;
+    int64_t H, I, E, E_local, k;
+    int bucket;
+    int config;
+    float us;    // measured GPU time per call (reference only)
+};
+const TunedRow kTuned[] = {
+#include "tuned_configs.inc"
+    {-1, 0, 0, 0, 0, 0, 0, -1, 0.f},   // end
+};
+
 int bucket_of(int64_t T) {
     int b = 1;
     while (b < T && b < 32768) b <<= 1;
@@ -179,7 +196,7 @@ int tile_config(int md, int shape, int64_t H, int64_t I) {
 // (Qwen3-235B-shaped bf16 and the TP2 MXFP4 shard):
 //  * enough rows per expert: LDS-tiled GEMMs (bf16: 64 x 256 tiles with
 //    three stages in flight from 0.1 expected rows per expert, 128 x 512 from
-//    64, 256 x 256 from 512; MXFP4: 64 x 512 from 64 rows, 256 x 256 from
+//    64, 256 x 256 from 128; MXFP4: 64 x 512 from 64 rows, 256 x 256 from
 //    128);
 //  * otherwise the register weight stream, whose block rows cover the
 //    typical busiest expert of the bucket in one block (each expert's
@@ -188,11 +205,12 @@ int tile_config(int md, int shape, int64_t H, int64_t I) {
 //    (own block size, second layout) where that measured faster, or, for
 //    MXFP4 with I = 512, to workgroups that take 2-8 column tiles each.
 // E counts the experts over all shards of an expert-parallel group and sets
-// the rows per expert; E_local (the call's own experts) only steps a bf16
-// tile down to a smaller one while the gemm1 grid would not give every CU two
-// workgroups. Tiles never split K, so that step keeps the sums bit-identical
-// to the unsharded call, and the register stream's K split is chosen from E.
-int default_config(int mode, int64_t T, int64_t H, int64_t I, int64_t E, int64_t E_local, int64_t k) {
+// the rows per expert; E_local (the call's own experts) only moves a bf16
+// shard with 64-128 rows per expert to 256 x 256 tiles when its 128 x 512
+// grid would leave half the CUs idle. Tiles never split K, so the tile shape
+// keeps the sums bit-identical to the unsharded call, and the register
+// stream's K split is chosen from E alone.
+int heuristic_config(int mode, int64_t T, int64_t H, int64_t I, int64_t E, int64_t E_local, int64_t k) {
     const int64_t bucket = bucket_of(T);
     const double rows = (double)bucket * (double)k / (double)E;   // expected rows per expert
     const double busy = rows + 3.0 * __builtin_sqrt(rows);          // typical maximum
@@ -201,17 +219,14 @@ int default_config(int mode, int64_t T, int64_t H, int64_t I, int64_t E, int64_t
     int c = -1;
     if (md == 0) {
         int shape = -1;
-        if (rows >= 512.0) shape = 0;
+        if (rows >= 128.0) shape = 0;
         else if (rows >= 64.0) shape = 1;
         else if (rows >= 0.1) shape = 4;
-        const int64_t touched = std::min<int64_t>(bucket * k, E_local);
-        auto grid = [&](int sh) {
-            const int bm = gemm_tile_rows(0, sh);
-            return touched * (int64_t)std::ceil(rows / bm) * (I / gemm_tile_cols(sh, 1));
-        };
-        while ((shape == 0 || shape == 1) && grid(shape) < 2 * 256 && tile_config(0, shape == 0 ? 1 : 4, H, I) >= 0)
-            shape = shape == 0 ? 1 : 4;
+        const int64_t grid1 = std::min<int64_t>(bucket * k, E_local) * (int64_t)std::ceil(rows / 128.0) *
+                              (I / gemm_tile_cols(1, 1));
+        if (shape == 1 && grid1 < 128 && tile_config(0, 0, H, I) >= 0) shape = 0;
         if (shape >= 0) c = tile_config(0, shape, H, I);
+        if (c < 0 && shape >= 0 && shape != 4) c = tile_config(0, 4, H, I);
     } else {
         if (rows >= 128.0) c = tile_config(1, 0, H, I);
         else if (rows >= 64.0) c = tile_config(1, 2, H, I);
@@ -251,6 +266,16 @@ int default_config(int mode, int64_t T, int64_t H, int64_t I, int64_t E, int64_t
             kConfigs[c].g2 < 0)
             return c;
     return 0;
+}
+
+// The tuned table's entry for this exact layer and bucket, else the rules.
+int default_config(int mode, int64_t T, int64_t H, int64_t I, int64_t E, int64_t E_local, int64_t k) {
+    const int bucket = bucket_of(T);
+    for (const TunedRow& r : kTuned)
+        if (r.mode == mode && r.H == H && r.I == I && r.E == E && r.E_local == E_local && r.k == k &&
+            r.bucket == bucket && r.config >= 0 && r.config < kNumConfigs)
+            return r.config;
+    return heuristic_config(mode, T, H, I, E, E_local, k);
 }
 
 // One GEMM's resolved kernel: rows per sorted block, K split and column
