@@ -11,9 +11,10 @@ tensors as ``uint8`` (two e2m1 codes per byte, element 2i in the low nibble)
 plus ``uint8`` e8m0 scale bytes. Strides are whatever the arrays carry.
 
 Each function cites what it follows in its C counterpart's comment. Parity
-status: route, align, mxfp4 quantisation and the FFN/combine are pinned by the
-``-m "not gpu"`` tests in ``tests/test_oracle_*.py`` (brute force, closed forms,
-invariants, a dense-MLP special case and the pages' printed numbers).
+status: route, align, mxfp4 quantisation, the FFN/combine and the RMSNorm are
+pinned by the ``-m "not gpu"`` tests in ``tests/test_oracle_*.py`` (brute
+force, closed forms, invariants, a dense-MLP special case and the pages'
+printed numbers).
 """
 from __future__ import annotations
 
@@ -85,6 +86,8 @@ def lib():
         L.orc_ffn.argtypes = [ctypes.POINTER(_FfnArgs), vp, i64, vp, vp]
         L.orc_ffn.restype = i32
         L.orc_ffn_args_size.restype = i64
+        L.orc_rmsnorm.argtypes = [vp, i64, i64, i64, i64, vp, i64, ctypes.c_double, vp, vp]
+        L.orc_rmsnorm.restype = i32
         L.orc_e2m1_value.argtypes = [i32]
         L.orc_e2m1_value.restype = ctypes.c_double
         L.orc_e8m0_value.argtypes = [i32]
@@ -254,3 +257,20 @@ def ffn(x_bits: np.ndarray, ids: np.ndarray, wts: np.ndarray, *, num_experts: in
 def bf16_bits_to_f64(b: np.ndarray) -> np.ndarray:
     """Widen bf16 bit patterns to float64 (exact)."""
     return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+# ---------------------------------------------------------------- rmsnorm
+
+def rmsnorm(x_bits: np.ndarray, weight: np.ndarray, eps: float) -> tuple[np.ndarray, np.ndarray]:
+    """RMSNorm of bf16 bits x [T, H] (any strides) with float64 weight [H]
+    (any stride). Returns (float64 [T, H], bf16 bits uint16 [T, H])."""
+    assert x_bits.dtype == np.uint16 and x_bits.ndim == 2
+    weight = np.asarray(weight, dtype=np.float64)
+    T, H = x_bits.shape
+    acc = np.empty((T, H), dtype=np.float64)
+    bits = np.empty((T, H), dtype=np.uint16)
+    rc = lib().orc_rmsnorm(_ptr(x_bits), T, H, _es(x_bits, 0), _es(x_bits, 1), _ptr(weight),
+                           _es(weight, 0), float(eps), _ptr(acc), _ptr(bits))
+    if rc != 0:
+        raise ValueError("orc_rmsnorm failed")
+    return acc, bits

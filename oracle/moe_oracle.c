@@ -27,6 +27,9 @@
  *   mxfp4  - e2m1 codes with one e8m0 scale per 32 elements along K
  *            (aiter PR, Details: float4_e2m1fn_x2, QuantType.per_1x32) for
  *            weights and activations.
+ *   rmsnorm - the row normalisation ahead of the FFN, reading x through
+ *            both of its strides in both passes (LightLLM issue #1467,
+ *            Summary, Reproduction and Expected Behavior).
  *
  * Readings where the pages are silent (each listed with its reason in the
  * design notes): ties in top-k go to the lower expert index and slots are in
@@ -430,6 +433,38 @@ int orc_ffn(const orc_ffn_args *a, const int64_t *toks, int64_t n_toks, double *
         free(xh); free(wrow); free(hrow); free(hf); free(hq); free(hs); free(acc);
     }
     return err ? ORC_EARG : ORC_OK;
+}
+
+/* ------------------------------------------------------------- rmsnorm */
+
+/*
+ * RMSNorm of T rows of H bf16 values, x[t*xs_t + h*xs_h] (LightLLM issue
+ * #1467: the mean of squares and the normalisation both read the element
+ * through xs_h; its reference scales the normalised row by the weight):
+ *   ms_t = (sum over h of x^2) / H, r_t = 1 / sqrt(ms_t + eps),
+ *   y = x * r_t * w[h * w_s],
+ * in double, sums in ascending h. out_acc[t*H + h] keeps y, out_bf16 its
+ * rounding to bf16 through fp32.
+ */
+int orc_rmsnorm(const uint16_t *x, int64_t T, int64_t H, int64_t xs_t, int64_t xs_h, const double *w,
+                int64_t w_s, double eps, double *out_acc, uint16_t *out_bf16)
+{
+    if (H < 1 || eps < 0.0)
+        return ORC_EARG;
+    for (int64_t t = 0; t < T; ++t) {
+        double ss = 0.0;
+        for (int64_t h = 0; h < H; ++h) {
+            double v = orc_bf16_to_double(x[t * xs_t + h * xs_h]);
+            ss += v * v;
+        }
+        double r = 1.0 / sqrt(ss / (double)H + eps);
+        for (int64_t h = 0; h < H; ++h) {
+            double y = orc_bf16_to_double(x[t * xs_t + h * xs_h]) * r * w[h * w_s];
+            out_acc[t * H + h] = y;
+            out_bf16[t * H + h] = orc_float_to_bf16((float)y);
+        }
+    }
+    return ORC_OK;
 }
 
 /* Size of orc_ffn_args, so the Python side can check its mirror. */
