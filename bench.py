@@ -119,6 +119,9 @@ def main():
     ap.add_argument("--ep", type=int, default=0,
                     help="with --bf16: time one expert-parallel shard of S (experts [0, E/S), global "
                          "ids, per-slot rows out) and the tokens' home combine instead of the whole layer")
+    ap.add_argument("--norm", default="",
+                    help="comma-separated token counts: the RMSNorm pre-pass on its own (contiguous and "
+                         "transposed x) and inside the bf16 fused forward, one JSON line each")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
@@ -143,6 +146,9 @@ def main():
         return
     if args.mxfp4:
         mxfp4_buckets([int(t) for t in args.mxfp4.split(",")], args, dev)
+        return
+    if args.norm:
+        norm_lines([int(t) for t in args.norm.split(",")], dev)
         return
     if args.bf16 and args.ep > 1:
         ep_buckets([int(t) for t in args.bf16.split(",")], args.ep, dev)
@@ -474,6 +480,52 @@ def ep_buckets(buckets, S, dev):
             "timing": f"HIP graph of one call, {reps} replays back to back",
         }), flush=True)
         del inp, ids, wts, y, out, ws
+        torch.cuda.empty_cache()
+
+
+def norm_lines(tokens, dev):
+    """RMSNorm of H=4096 bf16 rows (weight fp32 uniform [0, 1), eps 1e-6):
+    moe_rmsnorm on a contiguous and on a transposed x, and the bf16
+    Qwen3-235B-shaped fused forward with and without norm_weight. Graph-timed."""
+    import torch
+    import mixture_experts_ffn_align_amd as moe
+    from mixture_experts_ffn_align_amd import workloads as W
+
+    sh = W.QWEN3_235B_BF16
+    H, I, k = sh.hidden, sh.inter, sh.top_k
+    log(f"[bench] drawing weights {sh.name}")
+    g = torch.Generator(device=dev).manual_seed(0)
+    w13, w2 = W.draw_weights(sh, g, dev)
+    gate, up = W.packed_views(w13, I)
+    nw = torch.rand(H, generator=torch.Generator().manual_seed(1)).to(dev)
+    for T in tokens:
+        inp = W.make_inputs(sh, T, seed=T, device=dev, weights=(w13, w2))
+        x = inp["x"]
+        xt = x.t().contiguous().t()
+        xn = torch.empty_like(x)
+        ids, wts = moe.moe_topk_softmax(inp["logits"], k)
+        out = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(moe.moe_fused_workspace_size(x, gate, up, w2, ids, wts, norm_weight=nw),
+                         dtype=torch.uint8, device=dev)
+        reps = max(5, min(200, int(2e6 / (T + 50))))
+        us_rows = graph_time_us(lambda: moe.moe_rmsnorm(x, nw, 1e-6, out=xn), reps)
+        us_cols = graph_time_us(lambda: moe.moe_rmsnorm(xt, nw, 1e-6, out=xn), reps)
+        fr = max(5, min(100, int(2e5 / (T + 50))))
+        us_f = graph_time_us(lambda: moe.moe_fused_fwd(x, gate, up, w2, ids, wts, out=out, workspace=ws), fr)
+        us_fn = graph_time_us(lambda: moe.moe_fused_fwd(x, gate, up, w2, ids, wts, out=out, workspace=ws,
+                                                        norm_weight=nw, norm_eps=1e-6), fr)
+        byts = T * H * 2 * 2 + H * 4
+        print(json.dumps({
+            "workload": f"RMSNorm of [T, {H}] bf16 rows, fp32 weight; {sh.name} fused forward with it",
+            "tokens": T,
+            "rmsnorm_us": round(us_rows, 2), "rmsnorm_gbs": round(byts / (us_rows * 1e-6) / 1e9, 1),
+            "rmsnorm_hbm_frac": round(byts / (us_rows * 1e-6) / 1e9 / HBM_PEAK_GBS, 3),
+            "rmsnorm_transposed_x_us": round(us_cols, 2),
+            "rmsnorm_transposed_x_gbs": round(byts / (us_cols * 1e-6) / 1e9, 1),
+            "fused_us": round(us_f, 1), "fused_with_norm_us": round(us_fn, 1),
+            "timing": "HIP graph of one call, replayed back to back",
+        }), flush=True)
+        del inp, x, xt, xn, ids, wts, out, ws
         torch.cuda.empty_cache()
 
 

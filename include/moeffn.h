@@ -168,8 +168,8 @@ int moe_quant_mxfp4(const moe_tensor_t *src, const moe_tensor_t *codes,
  *   stage_events NULL, or 2*MOE_NUM_STAGES hipEvent_t handles created by the
  *               caller; event 2s is recorded before stage s and 2s+1 after
  *               it, on the call's stream; NULL entries are skipped. Stages:
- *               0 align, 1 prepare (activation quantise or re-layout; may be
- *               empty), 2 gemm1 + act, 3 gemm2, 4 combine.
+ *               0 align, 1 prepare (RMSNorm, activation quantise or
+ *               re-layout; may be empty), 2 gemm1 + act, 3 gemm2, 4 combine.
  *   force_config  -1 for the built-in choice, else an index into the
  *               library's config list (tests of tile invariance).
  * Numerics: fp32 accumulation; h rounded to bf16 (bf16 mode) or quantised to
@@ -208,7 +208,14 @@ typedef struct {
     int32_t expert_offset;
     moe_tensor_t y_rows;
     int32_t num_global_experts;
-    int32_t reserved;
+    /* RMSNorm pre-pass (LightLLM issue #1467, Summary: both passes read x
+     * through its strides): norm_weight data NULL: x goes to gemm1 as it is.
+     * Otherwise [H] bf16 or float32, any stride, and gemm1 (and, in MXFP4
+     * mode, the activation quantisation) reads moe_rmsnorm(x, norm_weight,
+     * norm_eps) instead of x; the result is bit-identical to calling
+     * moe_rmsnorm first and passing its output as x. */
+    float norm_eps;
+    moe_tensor_t norm_weight;
 } moe_fused_args_t;
 
 /* The tile configuration a call would use. */
@@ -234,6 +241,22 @@ int moe_fused_workspace_size(const moe_fused_args_t *args, size_t *bytes);
  * ws: caller-owned device scratch, 256-byte aligned, >= the reported size;
  * its contents on entry do not matter. T = 0 returns MOE_OK with no launch. */
 int moe_fused_fwd(const moe_fused_args_t *args, void *ws, size_t ws_bytes, moe_stream_t stream);
+
+/* ------------------------------------------------------------ rmsnorm --
+ * moe_rmsnorm: the RMSNorm ahead of the expert FFN (LightLLM issue #1467,
+ * Summary and Expected Behavior).
+ *   x       [T, H] bf16, any strides; H a multiple of 8.
+ *   weight  [H] bf16 or float32, any stride.
+ *   eps     >= 0, added to the mean of squares.
+ *   out     [T, H] bf16 out, any strides, not overlapping x or weight.
+ * out[t, h] = bf16_RNE((x[t, h] * r_t) * weight[h]) in fp32, with
+ * r_t = 1 / sqrt(ss_t / H + eps) and ss_t the fp32 sum of x[t, h]^2 in one
+ * fixed order (64 partial fmaf chains over 8-element chunks c = q, q + 64,
+ * ..., then a 64-way pairwise tree), the same for every layout of x and out,
+ * so strided and contiguous inputs give identical bits. T = 0 is a no-op.
+ */
+int moe_rmsnorm(const moe_tensor_t *x, const moe_tensor_t *weight, float eps, const moe_tensor_t *out,
+                moe_stream_t stream);
 
 /* ------------------------------------------------------------ combine --
  * moe_combine: step 6 on its own, for per-slot results computed elsewhere

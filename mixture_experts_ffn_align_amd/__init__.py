@@ -18,7 +18,8 @@ from ._abi import (DT_BF16, DT_E8M0, DT_F32, DT_FP4X2, DT_I32, MODE_BF16, MODE_M
                    MoEError)
 
 __all__ = ["moe_topk_softmax", "moe_align", "moe_align_capacity", "moe_quant_mxfp4",
-           "moe_fused_fwd", "moe_fused_workspace_size", "moe_query_config", "moe_combine", "MoEError",
+           "moe_fused_fwd", "moe_fused_workspace_size", "moe_query_config", "moe_combine",
+           "moe_rmsnorm", "MoEError",
            "MODE_BF16", "MODE_MXFP4", "STAGES", "library_path"]
 
 _TORCH_DT = {torch.bfloat16: DT_BF16, torch.float32: DT_F32, torch.int32: DT_I32}
@@ -113,7 +114,7 @@ def moe_quant_mxfp4(src: torch.Tensor, codes: Optional[torch.Tensor] = None,
 
 def _fused_args(x, gate, up, w2, topk_ids, topk_weights, out, gate_scale=None, up_scale=None,
                 w2_scale=None, mode=MODE_BF16, stage_events=None, force_config=-1, expert_offset=0,
-                num_global_experts=0, y_rows=None):
+                num_global_experts=0, y_rows=None, norm_weight=None, norm_eps=1e-6):
     a = _abi.FusedArgs()
     a.mode = mode
     a.activation = _abi.ACT_SILU
@@ -131,6 +132,8 @@ def _fused_args(x, gate, up, w2, topk_ids, topk_weights, out, gate_scale=None, u
     a.expert_offset = expert_offset
     a.num_global_experts = num_global_experts
     a.y_rows = _desc(y_rows)
+    a.norm_weight = _desc(norm_weight)
+    a.norm_eps = float(norm_eps)
     keep = None
     if stage_events is not None:
         keep = (ctypes.c_void_p * len(stage_events))(*[e or None for e in stage_events])
@@ -174,7 +177,8 @@ def moe_fused_fwd(x: torch.Tensor, gate: torch.Tensor, up: torch.Tensor, w2: tor
                   w2_scale=None, mode: int = MODE_BF16, workspace: Optional[torch.Tensor] = None,
                   stage_events: Optional[Sequence[int]] = None, force_config: int = -1,
                   expert_offset: int = 0, num_global_experts: int = 0,
-                  y_rows: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+                  y_rows: Optional[torch.Tensor] = None, norm_weight: Optional[torch.Tensor] = None,
+                  norm_eps: float = 1e-6, stream=None) -> torch.Tensor:
     """Fused MoE forward: align, (quantise x), gemm1 + SiLU*up, gemm2, combine.
 
     bf16 mode: gate/up [E, I, H] and w2 [E, H, I] bf16 (any expert/row strides).
@@ -183,14 +187,15 @@ def moe_fused_fwd(x: torch.Tensor, gate: torch.Tensor, up: torch.Tensor, w2: tor
     Expert-parallel shard: the weights hold global experts expert_offset ..
     expert_offset + E - 1 of num_global_experts; other slots are skipped. With
     y_rows ([T, k, H] bf16) the per-slot results of local slots go there and
-    the call returns y_rows without combining.
+    the call returns y_rows without combining. norm_weight ([H] bf16 or fp32):
+    gemm1 reads moe_rmsnorm(x, norm_weight, norm_eps) instead of x.
     """
     L = _abi.load()
     if out is None and y_rows is None:
         out = torch.empty(x.shape, dtype=torch.bfloat16, device=x.device)
     a, keep = _fused_args(x, gate, up, w2, topk_ids, topk_weights, out, gate_scale, up_scale,
                           w2_scale, mode, stage_events, force_config, expert_offset,
-                          num_global_experts, y_rows)
+                          num_global_experts, y_rows, norm_weight, norm_eps)
     n = ctypes.c_size_t(0)
     _abi.check(L.moe_fused_workspace_size(ctypes.byref(a), ctypes.byref(n)))
     if workspace is None:
@@ -199,6 +204,17 @@ def moe_fused_fwd(x: torch.Tensor, gate: torch.Tensor, up: torch.Tensor, w2: tor
                                workspace.numel(), _stream(stream)))
     del keep
     return y_rows if y_rows is not None else out
+
+
+def moe_rmsnorm(x: torch.Tensor, weight: torch.Tensor, eps: float = 1e-6,
+                out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """out[t] = bf16((x[t] * r_t) * weight), r_t = 1/sqrt(mean(x[t]^2) + eps), fp32 inside."""
+    L = _abi.load()
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.bfloat16, device=x.device)
+    dx, dw, do = _desc(x), _desc(weight), _desc(out)
+    _abi.check(L.moe_rmsnorm(ctypes.byref(dx), ctypes.byref(dw), float(eps), ctypes.byref(do), _stream(stream)))
+    return out
 
 
 def moe_combine(y_rows: torch.Tensor, topk_ids: torch.Tensor, topk_weights: torch.Tensor,

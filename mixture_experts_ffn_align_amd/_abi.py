@@ -37,7 +37,8 @@ class FusedArgs(ctypes.Structure):
                 ("topk_ids", TensorDesc), ("topk_weights", TensorDesc), ("out", TensorDesc),
                 ("stage_events", ctypes.c_void_p), ("force_config", ctypes.c_int32),
                 ("expert_offset", ctypes.c_int32), ("y_rows", TensorDesc),
-                ("num_global_experts", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("num_global_experts", ctypes.c_int32), ("norm_eps", ctypes.c_float),
+                ("norm_weight", TensorDesc)]
 
 
 class Config(ctypes.Structure):
@@ -50,7 +51,7 @@ class Config(ctypes.Structure):
 
 EXPORTS = ("moe_topk_softmax", "moe_align", "moe_align_capacity", "moe_align_workspace_size",
            "moe_quant_mxfp4", "moe_query_config", "moe_fused_workspace_size", "moe_fused_fwd",
-           "moe_combine", "moe_strerror", "moe_last_error")
+           "moe_combine", "moe_rmsnorm", "moe_strerror", "moe_last_error")
 
 _lib = None
 
@@ -82,11 +83,13 @@ def load() -> ctypes.CDLL:
     L.moe_fused_workspace_size.argtypes = [P(FusedArgs), P(ctypes.c_size_t)]
     L.moe_fused_fwd.argtypes = [P(FusedArgs), vp, ctypes.c_size_t, vp]
     L.moe_combine.argtypes = [TD, TD, TD, i32, TD, vp]
+    L.moe_rmsnorm.argtypes = [TD, TD, ctypes.c_float, TD, vp]
     L.moe_strerror.argtypes = [ctypes.c_int]
     L.moe_strerror.restype = ctypes.c_char_p
     L.moe_last_error.restype = ctypes.c_char_p
     for name in ("moe_topk_softmax", "moe_align", "moe_align_workspace_size", "moe_quant_mxfp4",
-                 "moe_query_config", "moe_fused_workspace_size", "moe_fused_fwd", "moe_combine"):
+                 "moe_query_config", "moe_fused_workspace_size", "moe_fused_fwd", "moe_combine",
+                 "moe_rmsnorm"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L

@@ -297,8 +297,9 @@ struct Plan {
     int64_t e_off;         // global id of local expert 0
     bool y_out;            // per-slot rows go to the caller's y_rows; no combine
     int64_t y_row;         // element stride between the rows of y
+    bool norm;             // RMSNorm pre-pass into the xn segment
     // workspace offsets
-    size_t off_counts, off_sorted[2], off_bexp[2], off_npad[2], off_x, off_xs, off_h, off_hs, off_y, total;
+    size_t off_counts, off_sorted[2], off_bexp[2], off_npad[2], off_x, off_xs, off_xn, off_h, off_hs, off_y, total;
 };
 
 int kstep(int mode) { return mode == MOE_MODE_MXFP4 ? 128 : 32; }
@@ -309,6 +310,30 @@ int64_t y_rows_stride(const moe_tensor_t& y) {
     const int64_t T = y.size[0], k = y.size[1], H = y.size[2];
     if (k > 1) return y.stride[1];
     return T > 1 ? y.stride[0] : H;
+}
+
+// RMSNorm weight: [H] bf16 or fp32, any stride.
+int check_norm_weight(const moe_tensor_t* w, int64_t H) {
+    if (!w) return fail(MOE_ERR_NULL, "norm weight descriptor is NULL");
+    int rc;
+    if (w->dtype != MOE_DT_BF16 && w->dtype != MOE_DT_F32)
+        return fail(MOE_ERR_DTYPE, "norm weight: dtype %s, expected bf16 or f32", dtype_name(w->dtype));
+    if ((rc = check_desc(w, "norm weight", w->dtype, 1))) return rc;
+    if (w->size[0] != H)
+        return fail(MOE_ERR_SHAPE, "norm weight: size %lld, expected H = %lld", (long long)w->size[0], (long long)H);
+    return MOE_OK;
+}
+
+void norm_params(NormParams* np, const moe_tensor_t& x, const moe_tensor_t& w, float eps) {
+    np->x = (const uint16_t*)x.data;
+    np->xs_t = x.stride[0];
+    np->xs_h = x.size[1] > 1 ? x.stride[1] : 1;
+    np->w = w.data;
+    np->w_f32 = w.dtype == MOE_DT_F32 ? 1 : 0;
+    np->ws = w.size[0] > 1 ? w.stride[0] : 1;
+    np->eps = eps;
+    np->T = x.size[0];
+    np->H = x.size[1];
 }
 
 // Validate a fused call and build its plan. No device calls.
@@ -353,6 +378,12 @@ int plan_fused(const moe_fused_args_t* a, Plan* pl) {
         return fail(MOE_ERR_ARG, "num_global_experts = %d below expert_offset + E = %lld", a->num_global_experts,
                     (long long)a->expert_offset + E);
     const int64_t E_cfg = a->num_global_experts > 0 ? a->num_global_experts : E;
+    const bool norm = a->norm_weight.data != nullptr;
+    if (norm) {
+        if ((rc = check_norm_weight(&a->norm_weight, H))) return rc;
+        if (!(a->norm_eps >= 0.f) || a->norm_eps == __builtin_inff())
+            return fail(MOE_ERR_ARG, "norm_eps must be finite and >= 0");
+    }
     const bool y_out = a->y_rows.data != nullptr;
     if (y_out) {
         if ((rc = check_desc(&a->y_rows, "y_rows", MOE_DT_BF16, 3))) return rc;
@@ -404,7 +435,7 @@ int plan_fused(const moe_fused_args_t* a, Plan* pl) {
         }
     }
     // outputs must not alias inputs
-    const moe_tensor_t* ins[6] = {&a->x, &a->gate, &a->up, &a->w2, &a->topk_ids, &a->topk_weights};
+    const moe_tensor_t* ins[7] = {&a->x, &a->gate, &a->up, &a->w2, &a->topk_ids, &a->topk_weights, &a->norm_weight};
     const moe_tensor_t& dst = y_out ? a->y_rows : a->out;
     for (auto* t : ins)
         if (overlaps(dst, *t)) return fail(MOE_ERR_LAYOUT, "%s overlaps an input", y_out ? "y_rows" : "out");
@@ -467,11 +498,12 @@ int plan_fused(const moe_fused_args_t* a, Plan* pl) {
     pl->two_aligns = pl->ks[0].bm != pl->ks[1].bm;
     const bool x_direct = a->x.stride[1] == 1 && aligned16(a->x.data) &&
                           (T <= 1 || (a->x.stride[0] * 2) % 16 == 0);
-    pl->pack_x = !fp4 && !x_direct;
+    pl->norm = norm;
+    pl->pack_x = !fp4 && !x_direct && !norm;
     {
         // the tiled kernels address every operand row with a 32-bit offset
         const int64_t eb = fp4 ? 1 : 2;
-        const int64_t x_row = fp4 ? H / 2 : (pl->pack_x ? H * 2 : a->x.stride[0] * 2);
+        const int64_t x_row = fp4 ? H / 2 : (pl->pack_x || norm ? H * 2 : a->x.stride[0] * 2);
         const int64_t lim = (int64_t)1 << 31;
         if (pl->ks[0].tile && (T * x_row >= lim || I * a->gate.stride[1] * eb >= lim ||
                                I * a->up.stride[1] * eb >= lim))
@@ -498,7 +530,8 @@ int plan_fused(const moe_fused_args_t* a, Plan* pl) {
         pl->off_bexp[g] = take((size_t)(pl->cap[g] / pl->ks[g].bm) * 4);
         pl->off_npad[g] = take(4);
     }
-    pl->off_x = pl->off_xs = 0;
+    pl->off_x = pl->off_xs = pl->off_xn = 0;
+    if (norm) pl->off_xn = take((size_t)T * (size_t)H * 2);   // normalised rows, bf16
     if (fp4) {
         pl->off_x = take((size_t)T * (size_t)(H / 2));
         pl->off_xs = take((size_t)T * (size_t)(H / 32));
@@ -698,6 +731,30 @@ int moe_quant_mxfp4(const moe_tensor_t* src, const moe_tensor_t* codes, const mo
     return ok();
 }
 
+int moe_rmsnorm(const moe_tensor_t* x, const moe_tensor_t* weight, float eps, const moe_tensor_t* out,
+                moe_stream_t stream) {
+    int rc;
+    if ((rc = check_desc(x, "x", MOE_DT_BF16, 2))) return rc;
+    const int64_t T = x->size[0], H = x->size[1];
+    if ((rc = check_norm_weight(weight, H))) return rc;
+    if ((rc = check_desc(out, "out", MOE_DT_BF16, 2))) return rc;
+    if ((rc = check_shape(*out, "out", {T, H}))) return rc;
+    if (!(eps >= 0.f) || eps == __builtin_inff()) return fail(MOE_ERR_ARG, "eps must be finite and >= 0");
+    if (H < 8 || H % 8 != 0 || H > ((int64_t)1 << 24) || T > ((int64_t)1 << 30))
+        return fail(MOE_ERR_UNSUPPORTED, "H = %lld must be a positive multiple of 8 (T = %lld)", (long long)H,
+                    (long long)T);
+    if (overlaps(*out, *x) || overlaps(*out, *weight)) return fail(MOE_ERR_LAYOUT, "out overlaps an input");
+    if (T == 0) return ok();
+    NormParams np{};
+    norm_params(&np, *x, *weight, eps);
+    np.out = (uint16_t*)out->data;
+    np.os_t = out->stride[0];
+    np.os_h = H > 1 ? out->stride[1] : 1;
+    hipError_t e = launch_rmsnorm(np, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "rmsnorm");
+    return ok();
+}
+
 int moe_combine(const moe_tensor_t* y_rows, const moe_tensor_t* topk_ids, const moe_tensor_t* topk_weights,
                 int32_t num_experts, const moe_tensor_t* out, moe_stream_t stream) {
     int rc;
@@ -806,7 +863,7 @@ int moe_fused_fwd(const moe_fused_args_t* args, void* ws, size_t ws_bytes, moe_s
         qp.scales = (uint8_t*)(base + pl.off_xs);
         qp.xs_r = pl.H / 32;
     }
-    const bool quant_in_align = fp4 && align_single_launch(pl.A, (int32_t)pl.E);
+    const bool quant_in_align = fp4 && !pl.norm && align_single_launch(pl.A, (int32_t)pl.E);
 
     // stage 0: align; when the two GEMMs use different block sizes, the same
     // pass writes the second padded layout too
@@ -843,6 +900,19 @@ int moe_fused_fwd(const moe_fused_args_t* args, void* ws, size_t ws_bytes, moe_s
     tm.begin(1);
     const void* a_op = a.x.data;
     int64_t a_row = a.x.stride[0];
+    if (pl.norm) {
+        NormParams np{};
+        norm_params(&np, a.x, a.norm_weight, a.norm_eps);
+        np.out = (uint16_t*)(base + pl.off_xn);
+        np.os_t = pl.H;
+        np.os_h = 1;
+        if ((e = launch_rmsnorm(np, s)) != hipSuccess) return hip_fail(e, "rmsnorm");
+        a_op = base + pl.off_xn;
+        a_row = pl.H;
+        qp.src = (const uint16_t*)(base + pl.off_xn);
+        qp.ss_r = pl.H;
+        qp.ss_k = 1;
+    }
     if (fp4) {
         if (!quant_in_align && (e = launch_quant_mxfp4(qp, s)) != hipSuccess) return hip_fail(e, "quant x");
         a_op = base + pl.off_x;

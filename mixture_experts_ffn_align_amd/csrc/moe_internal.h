@@ -214,6 +214,21 @@ struct PackParams {
 };
 hipError_t launch_pack_bf16(const PackParams& p, hipStream_t s);
 
+// RMSNorm of activation rows: out[t, h] = bf16((x[t, h] * r_t) * w[h]) with
+// r_t = 1 / sqrt(sum_h x[t, h]^2 / H + eps); H a multiple of 8.
+struct NormParams {
+    const uint16_t* x;
+    int64_t xs_t, xs_h;     // element strides
+    const void* w;          // [H] bf16, or fp32 when w_f32
+    int32_t w_f32;
+    int64_t ws;             // element stride of w
+    float eps;
+    uint16_t* out;
+    int64_t os_t, os_h;
+    int64_t T, H;
+};
+hipError_t launch_rmsnorm(const NormParams& p, hipStream_t s);
+
 // One grouped GEMM launch. Stage 1: A = gathered x rows, B = gate/up rows,
 // epilogue SiLU(g)*u -> h. Stage 2: A = h rows, B = w2 rows, epilogue scatter
 // of y rows (fp32; bf16 in MXFP4 mode) to their flat assignment index.

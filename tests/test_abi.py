@@ -212,3 +212,25 @@ def test_combine_argument_checks():
     assert _status(lambda: moe.moe_combine(y.float(), ids, w, 8, stream=0)) == "MOE_ERR_DTYPE"
     out = moe.moe_combine(y[:0], ids[:0], w[:0], 8, stream=0)
     assert out.shape == (0, H)
+
+
+def test_rmsnorm_argument_checks():
+    x, gate, up, w2, ids, w = _bf16_case(T=8, H=256)
+    nw = torch.ones(256, dtype=torch.bfloat16)
+    base = moe.moe_fused_workspace_size(x, gate, up, w2, ids, w)
+    with_norm = moe.moe_fused_workspace_size(x, gate, up, w2, ids, w, norm_weight=nw)
+    assert with_norm == base + 8 * 256 * 2          # one bf16 [T, H] segment (a multiple of 256 bytes)
+    assert _status(lambda: moe.moe_fused_workspace_size(x, gate, up, w2, ids, w, norm_weight=nw[:128])) == \
+        "MOE_ERR_SHAPE"
+    assert _status(lambda: moe.moe_fused_workspace_size(x, gate, up, w2, ids, w,
+                                                        norm_weight=nw.to(torch.int32))) == "MOE_ERR_DTYPE"
+    assert _status(lambda: moe.moe_fused_workspace_size(x, gate, up, w2, ids, w, norm_weight=nw,
+                                                        norm_eps=-1.0)) == "MOE_ERR_ARG"
+    moe.moe_fused_workspace_size(x, gate, up, w2, ids, w, norm_weight=nw.float())
+    assert _status(lambda: moe.moe_rmsnorm(torch.zeros(4, 12, dtype=torch.bfloat16),
+                                           torch.ones(12), 1e-6, stream=0)) == "MOE_ERR_UNSUPPORTED"
+    assert _status(lambda: moe.moe_rmsnorm(torch.zeros(4, 16, dtype=torch.bfloat16),
+                                           torch.ones(8), 1e-6, stream=0)) == "MOE_ERR_SHAPE"
+    xs = torch.zeros(4, 16, dtype=torch.bfloat16)
+    assert _status(lambda: moe.moe_rmsnorm(xs, torch.ones(16), 1e-6, out=xs, stream=0)) == "MOE_ERR_LAYOUT"
+    assert moe.moe_rmsnorm(torch.zeros(0, 16, dtype=torch.bfloat16), torch.ones(16), stream=0).shape == (0, 16)

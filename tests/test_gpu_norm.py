@@ -1,0 +1,128 @@
+"""GPU parity of the RMSNorm pre-pass.
+
+* ``moe_rmsnorm`` against the oracle: at most one bf16 ulp apart, and equal in
+  at least 99.9% of elements (the GPU sums in fp32 in its fixed order, the
+  oracle in double), for T = 1, 7, 333, 4099 rows of H = 4096, bf16 and fp32
+  weights (uniform [0, 1), eps = 1e-6, as in the issue's reproduction);
+* every layout gives the same bits: a transposed x (last-dim stride T), rows
+  with a padded stride and a base that is not 16-byte aligned, a strided out;
+* the fused forward with ``norm_weight`` equals the fused forward on
+  ``moe_rmsnorm``'s output bit for bit, in bf16 and MXFP4, with contiguous
+  and transposed x, and matches the oracle (RMSNorm, then the FFN).
+"""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_ffn_align_amd as moe
+from mixture_experts_ffn_align_amd import workloads as W
+from harness import (bf16_to_f64, np_, np_bits, oracle_ffn_tokens, oracle_quant_experts,
+                     quantise_weights_gpu, rel_l2, route_both, sample_tokens, err_ratio)
+import oracle
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+EPS = 1e-6
+
+
+def _weight(H, f32, seed=0):
+    w = torch.rand(H, generator=torch.Generator().manual_seed(seed), dtype=torch.float32)
+    return (w if f32 else w.to(torch.bfloat16)).to(DEV)
+
+
+def _ulp_diff(a, b):
+    """Distance in bf16 steps between two bit arrays of finite values."""
+    def key(u):
+        u = u.astype(np.int64)
+        return np.where(u & 0x8000, -(u & 0x7FFF), u & 0x7FFF)
+    return np.abs(key(a) - key(b))
+
+
+@pytest.mark.parametrize("f32", [False, True], ids=["w_bf16", "w_f32"])
+@pytest.mark.parametrize("T", [1, 7, 333, 4099])
+def test_rmsnorm_matches_oracle(T, f32):
+    H = 4096
+    x = torch.randn(T, H, generator=torch.Generator(device=DEV).manual_seed(T), device=DEV).to(torch.bfloat16)
+    w = _weight(H, f32, T)
+    out = moe.moe_rmsnorm(x, w, EPS)
+    _, ob = oracle.rmsnorm(np_bits(x), w.double().cpu().numpy(), EPS)
+    d = _ulp_diff(np_bits(out), ob)
+    print(f"T={T} max ulp {d.max()}, exact {np.mean(d == 0):.6f}")
+    assert d.max() <= 1 and np.mean(d == 0) >= 0.999
+
+
+def test_rmsnorm_layouts_same_bits():
+    T, H = 333, 4096
+    g = torch.Generator(device=DEV).manual_seed(4)
+    x = torch.randn(T, H, generator=g, device=DEV).to(torch.bfloat16)
+    w = _weight(H, False, 1)
+    ref = np_bits(moe.moe_rmsnorm(x, w, EPS))
+    xt = x.t().contiguous().t()                                   # strides (1, T)
+    assert np.array_equal(np_bits(moe.moe_rmsnorm(xt, w, EPS)), ref)
+    buf = torch.empty(T * (H + 24) + 8, dtype=torch.bfloat16, device=DEV)
+    xp = buf[3:3 + T * (H + 24)].view(T, H + 24)[:, :H]           # padded rows, base off by 6 bytes
+    xp.copy_(x)
+    assert np.array_equal(np_bits(moe.moe_rmsnorm(xp, w, EPS)), ref)
+    outt = torch.empty(H, T, dtype=torch.bfloat16, device=DEV).t()
+    moe.moe_rmsnorm(x, w, EPS, out=outt)
+    assert np.array_equal(np_bits(outt.contiguous()), ref)
+    wstr = torch.empty(2 * H, dtype=torch.bfloat16, device=DEV)[::2]
+    wstr.copy_(w)
+    assert np.array_equal(np_bits(moe.moe_rmsnorm(x, wstr, EPS)), ref)
+
+
+@pytest.fixture(scope="module")
+def w235():
+    g = torch.Generator(device=DEV).manual_seed(99)
+    return W.draw_weights(W.QWEN3_235B_BF16, g, DEV)
+
+
+@pytest.mark.parametrize("T", [5, 512])
+def test_fused_bf16_with_norm(w235, T):
+    sh = W.QWEN3_235B_BF16
+    inp = W.make_inputs(sh, T, seed=300 + T, device=DEV, weights=w235)
+    (ids, wts), (oi, ow) = route_both(inp)
+    gate, up = W.packed_views(inp["w13"], sh.inter)
+    nw = _weight(sh.hidden, False, T)
+    out = moe.moe_fused_fwd(inp["x"], gate, up, inp["w2"], ids, wts, norm_weight=nw, norm_eps=EPS)
+    xn = moe.moe_rmsnorm(inp["x"], nw, EPS)
+    ref = moe.moe_fused_fwd(xn, gate, up, inp["w2"], ids, wts)
+    assert np.array_equal(np_bits(out), np_bits(ref))
+    xt = inp["x"].t().contiguous().t()
+    out_t = moe.moe_fused_fwd(xt, gate, up, inp["w2"], ids, wts, norm_weight=nw, norm_eps=EPS)
+    assert np.array_equal(np_bits(out_t), np_bits(out))
+    # oracle: RMSNorm in double (rounded to bf16), then the FFN on those rows
+    _, xob = oracle.rmsnorm(np_bits(inp["x"]), nw.double().cpu().numpy(), EPS)
+    toks = sample_tokens(T, 6)
+    inp_n = dict(inp, x=torch.from_numpy(xob.view(np.int16)).view(torch.bfloat16))
+    acc, _ = oracle_ffn_tokens(inp_n, oi, ow, toks)
+    got = bf16_to_f64(out[torch.from_numpy(toks).to(DEV)])
+    r = rel_l2(got, acc)
+    print(f"T={T} rel_l2={r:.3e}")
+    assert r <= 1e-2
+
+
+@pytest.mark.parametrize("T", [64, 2048])
+def test_fused_mxfp4_with_norm(T):
+    sh = W.QWEN35_397B_TP2_FP4_512
+    g = torch.Generator(device=DEV).manual_seed(31)
+    w13, w2 = W.draw_weights(sh, g, DEV)
+    (gq, gs), (uq, us), (wq, wsc) = quantise_weights_gpu(w13, w2, sh.inter)
+    inp = W.make_inputs(sh, T, seed=T + 1, device=DEV, weights=(w13, w2))
+    (ids, wts), (oi, ow) = route_both(inp)
+    nw = _weight(sh.hidden, True, T)
+    kw = dict(gate_scale=gs, up_scale=us, w2_scale=wsc, mode=moe.MODE_MXFP4)
+    out = moe.moe_fused_fwd(inp["x"], gq, uq, wq, ids, wts, norm_weight=nw, norm_eps=EPS, **kw)
+    xn = moe.moe_rmsnorm(inp["x"], nw, EPS)
+    ref = moe.moe_fused_fwd(xn, gq, uq, wq, ids, wts, **kw)
+    assert np.array_equal(np_bits(out), np_bits(ref))
+    toks = sample_tokens(T, 4)
+    used = sorted({int(e) for e in oi[toks].ravel()})
+    mx = oracle_quant_experts(w13, w2, sh.inter, used)
+    _, xob = oracle.rmsnorm(np_bits(inp["x"]), nw.double().cpu().numpy(), EPS)
+    inp_n = dict(inp, x=torch.from_numpy(xob.view(np.int16)).view(torch.bfloat16))
+    acc, _ = oracle_ffn_tokens(inp_n, oi, ow, toks, mx=mx)
+    got = bf16_to_f64(out[torch.from_numpy(toks).to(DEV)])
+    r, er = rel_l2(got, acc), err_ratio(got, acc)
+    print(f"T={T} rel_l2={r:.3e} err_ratio={er:.3e}")
+    assert r <= 2e-2 and er <= 0.05
