@@ -88,6 +88,9 @@ def lib():
         L.orc_ffn_args_size.restype = i64
         L.orc_rmsnorm.argtypes = [vp, i64, i64, i64, i64, vp, i64, ctypes.c_double, vp, vp]
         L.orc_rmsnorm.restype = i32
+        L.orc_ffn_bwd.argtypes = [ctypes.POINTER(_FfnArgs), vp, i64, i64, vp, i64, vp, vp, vp, vp, i64,
+                                  vp, vp, vp]
+        L.orc_ffn_bwd.restype = i32
         L.orc_e2m1_value.argtypes = [i32]
         L.orc_e2m1_value.restype = ctypes.c_double
         L.orc_e8m0_value.argtypes = [i32]
@@ -274,3 +277,50 @@ def rmsnorm(x_bits: np.ndarray, weight: np.ndarray, eps: float) -> tuple[np.ndar
     if rc != 0:
         raise ValueError("orc_rmsnorm failed")
     return acc, bits
+
+
+# --------------------------------------------------------------- backward
+
+def ffn_bwd(x_bits: np.ndarray, ids: np.ndarray, wts: np.ndarray, dout_bits: np.ndarray, *,
+            num_experts: int, gate: np.ndarray, up: np.ndarray, w2: np.ndarray,
+            toks: Optional[np.ndarray] = None, exps: Optional[np.ndarray] = None,
+            round_h: bool = True):
+    """Gradients of sum(dout * out) for the bf16 forward (plain definition).
+
+    x, dout: bf16 bits [T, H] (any strides); gate/up [E, I, H], w2 [E, H, I]
+    bf16 bits (any strides). dx/dw for the tokens ``toks`` (all if None), the
+    weight gradients for the experts ``exps`` (none if None). Returns
+    (dx float64 [n, H], dx bf16 bits [n, H], dw float64 [n, k],
+     dgate float64 [m, I, H], dup float64 [m, I, H], dw2 float64 [m, H, I]).
+    """
+    a = _FfnArgs()
+    T, H = x_bits.shape
+    assert x_bits.dtype == np.uint16 and dout_bits.dtype == np.uint16 and dout_bits.shape == (T, H)
+    a.mode, a.round_h = 0, int(round_h)
+    a.T, a.H, a.E, a.k = T, H, num_experts, ids.shape[1]
+    a.I = gate.shape[1]
+    a.x, a.xs_t, a.xs_h = _ptr(x_bits), _es(x_bits, 0), _es(x_bits, 1)
+    a.gate, a.up, a.w2 = _ptr(gate), _ptr(up), _ptr(w2)
+    a.gs_e, a.gs_r, a.gs_c = (_es(gate, d) for d in range(3))
+    a.us_e, a.us_r, a.us_c = (_es(up, d) for d in range(3))
+    a.w2s_e, a.w2s_r, a.w2s_c = (_es(w2, d) for d in range(3))
+    assert ids.dtype == np.int32 and wts.dtype == np.float32 and ids.shape == wts.shape
+    a.ids, a.is_t, a.is_j = _ptr(ids), _es(ids, 0), _es(ids, 1)
+    a.wts, a.ws_t, a.ws_j = _ptr(wts), _es(wts, 0), _es(wts, 1)
+    toks = np.arange(T, dtype=np.int64) if toks is None else np.ascontiguousarray(toks, dtype=np.int64)
+    exps = np.zeros(0, dtype=np.int64) if exps is None else np.ascontiguousarray(exps, dtype=np.int64)
+    n, m, I, k = toks.size, exps.size, a.I, a.k
+    dx = np.zeros((n, H))
+    dxb = np.zeros((n, H), dtype=np.uint16)
+    dw = np.zeros((n, k))
+    dg = np.zeros((m, I, H))
+    du = np.zeros((m, I, H))
+    dw2 = np.zeros((m, H, I))
+    keep = [x_bits, ids, wts, dout_bits, gate, up, w2, toks, exps]
+    rc = lib().orc_ffn_bwd(ctypes.byref(a), _ptr(dout_bits), _es(dout_bits, 0), _es(dout_bits, 1),
+                           _ptr(toks), n, _ptr(dx), _ptr(dxb), _ptr(dw), _ptr(exps), m,
+                           _ptr(dg), _ptr(du), _ptr(dw2))
+    del keep
+    if rc != 0:
+        raise ValueError("orc_ffn_bwd failed")
+    return dx, dxb, dw, dg, du, dw2

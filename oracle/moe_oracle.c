@@ -30,6 +30,10 @@
  *   rmsnorm - the row normalisation ahead of the FFN, reading x through
  *            both of its strides in both passes (LightLLM issue #1467,
  *            Summary, Reproduction and Expected Behavior).
+ *   backward - the gradients of L = sum over t, n of dout[t, n] * out[t, n]
+ *            with respect to x, the top-k weights and the three weight
+ *            tensors, by the chain rule through the forward above (Liger PR
+ *            #1377, Notes: the grad-enabled path of the same fused MoE).
  *
  * Readings where the pages are silent (each listed with its reason in the
  * design notes): ties in top-k go to the lower expert index and slots are in
@@ -431,6 +435,158 @@ int orc_ffn(const orc_ffn_args *a, const int64_t *toks, int64_t n_toks, double *
             }
         }
         free(xh); free(wrow); free(hrow); free(hf); free(hq); free(hs); free(acc);
+    }
+    return err ? ORC_EARG : ORC_OK;
+}
+
+/* ------------------------------------------------------------ backward */
+
+/*
+ * Slot quantities of one (token t, expert e) pair in bf16 mode: x row xv[H]
+ * and dout row dv[H] as doubles; fills g, u (pre-activations), hb (h with
+ * the method's rounding when round_h), q = W2_e^T dout (q_i = sum over n of
+ * dout_n W2[n, i]) and returns dL/dw = sum over n of dout_n * y_n with
+ * y_n = sum over i of W2[n, i] hb_i.
+ */
+static double orc_bwd_slot(const orc_ffn_args *a, int64_t e, const double *xv, const double *dv, double *g,
+                           double *u, double *hb, double *q)
+{
+    const int64_t H = a->H, I = a->I;
+    for (int64_t i = 0; i < I; ++i) {
+        const uint16_t *gr = a->gate + e * a->gs_e + i * a->gs_r;
+        const uint16_t *ur = a->up + e * a->us_e + i * a->us_r;
+        double gs = 0.0, us = 0.0;
+        for (int64_t c = 0; c < H; ++c) {
+            gs += xv[c] * orc_bf16_to_double(gr[c * a->gs_c]);
+            us += xv[c] * orc_bf16_to_double(ur[c * a->us_c]);
+        }
+        g[i] = gs;
+        u[i] = us;
+        double h = orc_silu_mul(gs, us);
+        hb[i] = a->round_h ? orc_bf16_to_double(orc_float_to_bf16((float)h)) : h;
+        q[i] = 0.0;
+    }
+    double dw = 0.0;
+    for (int64_t n = 0; n < H; ++n) {
+        const uint16_t *wr = a->w2 + e * a->w2s_e + n * a->w2s_r;
+        double y = 0.0;
+        for (int64_t i = 0; i < I; ++i) {
+            double wv = orc_bf16_to_double(wr[i * a->w2s_c]);
+            y += wv * hb[i];
+            q[i] += dv[n] * wv;
+        }
+        dw += dv[n] * y;
+    }
+    return dw;
+}
+
+/* d SiLU(g) / dg = s (1 + g (1 - s)), s the logistic function of g. */
+static double orc_dsilu(double g)
+{
+    double s = 1.0 / (1.0 + exp(-g));
+    return s * (1.0 + g * (1.0 - s));
+}
+
+static void orc_row(const uint16_t *p, int64_t s, int64_t n, double *out)
+{
+    for (int64_t c = 0; c < n; ++c)
+        out[c] = orc_bf16_to_double(p[c * s]);
+}
+
+/*
+ * Backward of the bf16 forward (round_h as in orc_ffn; the pages' grad path
+ * uses the same rounding points as the forward it differentiates).
+ * For the tokens toks[0..n_toks): dx[r, c] = sum over valid slots j of
+ *   sum over i of (dg_i G_e[i, c] + du_i U_e[i, c]), and dw[r, j] = dL/dw_tj
+ *   (0 for a skipped slot); dx_bf16 is dx rounded through fp32.
+ * For the experts exps[0..n_exps): dgate[m] [I, H], dup[m] [I, H] and
+ *   dw2[m] [H, I], summed over every slot routed to the expert in ascending
+ *   (t, j): dW2[n, i] += w dout_n hb_i, dG[i, c] += dg_i x_c,
+ *   dU[i, c] += du_i x_c,
+ * with dh_i = w q_i, dg_i = dh_i u_i SiLU'(g_i), du_i = dh_i SiLU(g_i).
+ */
+int orc_ffn_bwd(const orc_ffn_args *a, const uint16_t *dout, int64_t ds_t, int64_t ds_h, const int64_t *toks,
+                int64_t n_toks, double *dx, uint16_t *dx_bf16, double *dw, const int64_t *exps, int64_t n_exps,
+                double *dgate, double *dup, double *dw2)
+{
+    if (a->mode != 0)
+        return ORC_EARG;
+    const int64_t H = a->H, I = a->I, k = a->k;
+    int err = 0;
+#pragma omp parallel
+    {
+        double *xv = malloc(sizeof(double) * (size_t)H), *dv = malloc(sizeof(double) * (size_t)H);
+        double *g = malloc(sizeof(double) * (size_t)I), *u = malloc(sizeof(double) * (size_t)I);
+        double *hb = malloc(sizeof(double) * (size_t)I), *q = malloc(sizeof(double) * (size_t)I);
+        double *dg = malloc(sizeof(double) * (size_t)I), *du = malloc(sizeof(double) * (size_t)I);
+        if (!xv || !dv || !g || !u || !hb || !q || !dg || !du) {
+#pragma omp atomic write
+            err = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t r = 0; r < n_toks; ++r) {
+                const int64_t t = toks[r];
+                orc_row(a->x + t * a->xs_t, a->xs_h, H, xv);
+                orc_row(dout + t * ds_t, ds_h, H, dv);
+                double *dxr = dx + r * H;
+                for (int64_t c = 0; c < H; ++c)
+                    dxr[c] = 0.0;
+                for (int64_t j = 0; j < k; ++j) {
+                    const int64_t e = a->ids[t * a->is_t + j * a->is_j];
+                    dw[r * k + j] = 0.0;
+                    if (e < 0 || e >= a->E)
+                        continue;
+                    const double wt = (double)a->wts[t * a->ws_t + j * a->ws_j];
+                    dw[r * k + j] = orc_bwd_slot(a, e, xv, dv, g, u, hb, q);
+                    for (int64_t i = 0; i < I; ++i) {
+                        const double dh = wt * q[i];
+                        dg[i] = dh * u[i] * orc_dsilu(g[i]);
+                        du[i] = dh * g[i] / (1.0 + exp(-g[i]));
+                    }
+                    for (int64_t i = 0; i < I; ++i) {
+                        const uint16_t *gr = a->gate + e * a->gs_e + i * a->gs_r;
+                        const uint16_t *ur = a->up + e * a->us_e + i * a->us_r;
+                        for (int64_t c = 0; c < H; ++c)
+                            dxr[c] += dg[i] * orc_bf16_to_double(gr[c * a->gs_c]) +
+                                      du[i] * orc_bf16_to_double(ur[c * a->us_c]);
+                    }
+                }
+                for (int64_t c = 0; c < H; ++c)
+                    dx_bf16[r * H + c] = orc_float_to_bf16((float)dxr[c]);
+            }
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t m = 0; m < n_exps; ++m) {
+                const int64_t e = exps[m];
+                double *dG = dgate + m * I * H, *dU = dup + m * I * H, *dW = dw2 + m * H * I;
+                memset(dG, 0, sizeof(double) * (size_t)(I * H));
+                memset(dU, 0, sizeof(double) * (size_t)(I * H));
+                memset(dW, 0, sizeof(double) * (size_t)(H * I));
+                for (int64_t t = 0; t < a->T; ++t) {
+                    for (int64_t j = 0; j < k; ++j) {
+                        if (a->ids[t * a->is_t + j * a->is_j] != e)
+                            continue;
+                        const double wt = (double)a->wts[t * a->ws_t + j * a->ws_j];
+                        orc_row(a->x + t * a->xs_t, a->xs_h, H, xv);
+                        orc_row(dout + t * ds_t, ds_h, H, dv);
+                        (void)orc_bwd_slot(a, e, xv, dv, g, u, hb, q);
+                        for (int64_t i = 0; i < I; ++i) {
+                            const double dh = wt * q[i];
+                            dg[i] = dh * u[i] * orc_dsilu(g[i]);
+                            du[i] = dh * g[i] / (1.0 + exp(-g[i]));
+                        }
+                        for (int64_t n = 0; n < H; ++n)
+                            for (int64_t i = 0; i < I; ++i)
+                                dW[n * I + i] += wt * dv[n] * hb[i];
+                        for (int64_t i = 0; i < I; ++i)
+                            for (int64_t c = 0; c < H; ++c) {
+                                dG[i * H + c] += dg[i] * xv[c];
+                                dU[i * H + c] += du[i] * xv[c];
+                            }
+                    }
+                }
+            }
+        }
+        free(xv); free(dv); free(g); free(u); free(hb); free(q); free(dg); free(du);
     }
     return err ? ORC_EARG : ORC_OK;
 }
