@@ -242,6 +242,45 @@ int moe_fused_workspace_size(const moe_fused_args_t *args, size_t *bytes);
  * its contents on entry do not matter. T = 0 returns MOE_OK with no launch. */
 int moe_fused_fwd(const moe_fused_args_t *args, void *ws, size_t ws_bytes, moe_stream_t stream);
 
+/* ----------------------------------------------------------- backward --
+ * moe_fused_bwd: gradients of L = sum over t, n of dout[t, n] * out[t, n]
+ * for the bf16 forward (Liger-Kernel PR #1377, Notes: the grad-enabled path
+ * of the same fused MoE; here it takes the same strided inputs as the
+ * forward, packed w13 views included).
+ *   fwd          the forward's arguments. mode MOE_MODE_BF16; out is not
+ *                written (give dx's descriptor or leave it empty);
+ *                expert_offset works as in the forward; y_rows and
+ *                norm_weight must be empty (MOE_ERR_UNSUPPORTED otherwise).
+ *   dout         [T, H] bf16, any strides.
+ *   dx           [T, H] bf16 out, any strides.
+ *   dgate, dup   [E, I, H] out, float32 or bf16, last stride 1, expert and row
+ *                strides free (views of one packed dw13 [E, 2I, H] work),
+ *                rows 16-byte (f32) or 8-byte (bf16) aligned. Every expert's
+ *                gradient is written, zeros for an expert without slots.
+ *   dw2          [E, H, I] out, same rules.
+ *   dtopk_weights [T, k] float32 out, any strides: dL/dw_tj, 0 for a
+ *                skipped slot.
+ * Per slot (t, j) of expert e, with g, u, h and its bf16 rounding hb exactly
+ * as the forward computes them (g, u recomputed): q = w2_e^T dout_t,
+ * dw_tj = <q, hb>, dh = w_tj q, dg = dh u SiLU'(g), du = dh SiLU(g); dg, du
+ * and w_tj hb are rounded to bf16 before the GEMMs that use them. dx_t sums
+ * the slots in order in fp32; each weight gradient sums its expert's slots in
+ * sorted (t, j) order in fp32. Sizes: H and I multiples of 128. Every check
+ * runs before the first launch; the workspace is the caller's.
+ */
+typedef struct {
+    moe_fused_args_t fwd;
+    moe_tensor_t dout;
+    moe_tensor_t dx;
+    moe_tensor_t dgate, dup;
+    moe_tensor_t dw2;
+    moe_tensor_t dtopk_weights;
+} moe_bwd_args_t;
+
+/* Validate args and report the workspace bytes moe_fused_bwd needs. Host only. */
+int moe_fused_bwd_workspace_size(const moe_bwd_args_t *args, size_t *bytes);
+int moe_fused_bwd(const moe_bwd_args_t *args, void *ws, size_t ws_bytes, moe_stream_t stream);
+
 /* ------------------------------------------------------------ rmsnorm --
  * moe_rmsnorm: the RMSNorm ahead of the expert FFN (LightLLM issue #1467,
  * Summary and Expected Behavior).

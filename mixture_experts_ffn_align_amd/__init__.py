@@ -19,7 +19,7 @@ from ._abi import (DT_BF16, DT_E8M0, DT_F32, DT_FP4X2, DT_I32, MODE_BF16, MODE_M
 
 __all__ = ["moe_topk_softmax", "moe_align", "moe_align_capacity", "moe_quant_mxfp4",
            "moe_fused_fwd", "moe_fused_workspace_size", "moe_query_config", "moe_combine",
-           "moe_rmsnorm", "MoEError",
+           "moe_rmsnorm", "moe_fused_bwd", "moe_fused_bwd_workspace_size", "MoEError",
            "MODE_BF16", "MODE_MXFP4", "STAGES", "library_path"]
 
 _TORCH_DT = {torch.bfloat16: DT_BF16, torch.float32: DT_F32, torch.int32: DT_I32}
@@ -204,6 +204,68 @@ def moe_fused_fwd(x: torch.Tensor, gate: torch.Tensor, up: torch.Tensor, w2: tor
                                workspace.numel(), _stream(stream)))
     del keep
     return y_rows if y_rows is not None else out
+
+
+def _bwd_args(x, gate, up, w2, topk_ids, topk_weights, dout, dx, dgate, dup, dw2, dtopk_weights,
+              expert_offset=0, num_global_experts=0):
+    b = _abi.BwdArgs()
+    fa, _ = _fused_args(x, gate, up, w2, topk_ids, topk_weights, dx, expert_offset=expert_offset,
+                        num_global_experts=num_global_experts)
+    b.fwd = fa
+    b.dout, b.dx = _desc(dout), _desc(dx)
+    b.dgate, b.dup, b.dw2 = _desc(dgate), _desc(dup), _desc(dw2)
+    b.dtopk_weights = _desc(dtopk_weights)
+    return b
+
+
+def moe_fused_bwd_workspace_size(x, gate, up, w2, topk_ids, topk_weights, dout, *, grad_dtype=torch.float32,
+                                 expert_offset=0, num_global_experts=0) -> int:
+    E, I, H = gate.shape
+    T, k = topk_ids.shape
+    dev = x.device
+    shapes = [torch.empty(x.shape, dtype=torch.bfloat16, device=dev),
+              torch.empty((E, I, H), dtype=grad_dtype, device=dev), torch.empty((E, I, H), dtype=grad_dtype, device=dev),
+              torch.empty((E, H, I), dtype=grad_dtype, device=dev), torch.empty((T, k), dtype=torch.float32, device=dev)]
+    b = _bwd_args(x, gate, up, w2, topk_ids, topk_weights, dout, *shapes, expert_offset=expert_offset,
+                  num_global_experts=num_global_experts)
+    n = ctypes.c_size_t(0)
+    _abi.check(_abi.load().moe_fused_bwd_workspace_size(ctypes.byref(b), ctypes.byref(n)))
+    return n.value
+
+
+def moe_fused_bwd(x, gate, up, w2, topk_ids, topk_weights, dout, *, dx=None, dgate=None, dup=None, dw2=None,
+                  dtopk_weights=None, grad_dtype=torch.float32, expert_offset: int = 0,
+                  num_global_experts: int = 0, workspace: Optional[torch.Tensor] = None, stream=None):
+    """Gradients of sum(dout * out) for the bf16 fused forward.
+
+    Returns (dx [T, H] bf16, dgate [E, I, H], dup [E, I, H], dw2 [E, H, I] in
+    grad_dtype (float32 or bfloat16), dtopk_weights [T, k] float32). Outputs
+    may be passed in with any allowed strides (dgate/dup as views of one
+    packed dw13 [E, 2I, H], for instance).
+    """
+    L = _abi.load()
+    E, I, H = gate.shape
+    T, k = topk_ids.shape
+    dev = x.device
+    if dx is None:
+        dx = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    if dgate is None:
+        dgate = torch.empty((E, I, H), dtype=grad_dtype, device=dev)
+    if dup is None:
+        dup = torch.empty((E, I, H), dtype=grad_dtype, device=dev)
+    if dw2 is None:
+        dw2 = torch.empty((E, H, I), dtype=grad_dtype, device=dev)
+    if dtopk_weights is None:
+        dtopk_weights = torch.empty((T, k), dtype=torch.float32, device=dev)
+    b = _bwd_args(x, gate, up, w2, topk_ids, topk_weights, dout, dx, dgate, dup, dw2, dtopk_weights,
+                  expert_offset, num_global_experts)
+    n = ctypes.c_size_t(0)
+    _abi.check(L.moe_fused_bwd_workspace_size(ctypes.byref(b), ctypes.byref(n)))
+    if workspace is None:
+        workspace = _workspace(n.value, dev)
+    _abi.check(L.moe_fused_bwd(ctypes.byref(b), workspace.data_ptr() if workspace.numel() else 0,
+                               workspace.numel(), _stream(stream)))
+    return dx, dgate, dup, dw2, dtopk_weights
 
 
 def moe_rmsnorm(x: torch.Tensor, weight: torch.Tensor, eps: float = 1e-6,

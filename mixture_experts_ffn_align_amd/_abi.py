@@ -41,6 +41,11 @@ class FusedArgs(ctypes.Structure):
                 ("norm_weight", TensorDesc)]
 
 
+class BwdArgs(ctypes.Structure):
+    _fields_ = [("fwd", FusedArgs), ("dout", TensorDesc), ("dx", TensorDesc), ("dgate", TensorDesc),
+                ("dup", TensorDesc), ("dw2", TensorDesc), ("dtopk_weights", TensorDesc)]
+
+
 class Config(ctypes.Structure):
     _fields_ = [("bucket", ctypes.c_int32), ("block_m", ctypes.c_int32),
                 ("gemm1_kernel", ctypes.c_int32), ("gemm2_kernel", ctypes.c_int32),
@@ -51,7 +56,8 @@ class Config(ctypes.Structure):
 
 EXPORTS = ("moe_topk_softmax", "moe_align", "moe_align_capacity", "moe_align_workspace_size",
            "moe_quant_mxfp4", "moe_query_config", "moe_fused_workspace_size", "moe_fused_fwd",
-           "moe_combine", "moe_rmsnorm", "moe_strerror", "moe_last_error")
+           "moe_combine", "moe_rmsnorm", "moe_fused_bwd_workspace_size", "moe_fused_bwd",
+           "moe_strerror", "moe_last_error")
 
 _lib = None
 
@@ -84,12 +90,14 @@ def load() -> ctypes.CDLL:
     L.moe_fused_fwd.argtypes = [P(FusedArgs), vp, ctypes.c_size_t, vp]
     L.moe_combine.argtypes = [TD, TD, TD, i32, TD, vp]
     L.moe_rmsnorm.argtypes = [TD, TD, ctypes.c_float, TD, vp]
+    L.moe_fused_bwd_workspace_size.argtypes = [P(BwdArgs), P(ctypes.c_size_t)]
+    L.moe_fused_bwd.argtypes = [P(BwdArgs), vp, ctypes.c_size_t, vp]
     L.moe_strerror.argtypes = [ctypes.c_int]
     L.moe_strerror.restype = ctypes.c_char_p
     L.moe_last_error.restype = ctypes.c_char_p
     for name in ("moe_topk_softmax", "moe_align", "moe_align_workspace_size", "moe_quant_mxfp4",
                  "moe_query_config", "moe_fused_workspace_size", "moe_fused_fwd", "moe_combine",
-                 "moe_rmsnorm"):
+                 "moe_rmsnorm", "moe_fused_bwd_workspace_size", "moe_fused_bwd"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L

@@ -52,13 +52,6 @@ struct Frag<1> {          // fp4: 32 codes (16 bytes) per lane per step
     i32x4_t v;
 };
 
-__device__ __forceinline__ float silu_mul(float g, float u) {
-    // g / (1 + e^-g): for very negative g, e^-g overflows to +inf and the
-    // reciprocal gives 0, so the result is a signed zero, never NaN.
-    float e = __expf(-g);
-    return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
-}
-
 // Occupancy target per SIMD: the weight stream needs as many waves in flight
 // as the register file allows, so the allocation is capped (bf16: 4 waves
 // for 16 rows, 3 for 32, 2 for 64 and 128; MXFP4, whose ring also carries

@@ -89,13 +89,6 @@ struct TileShape {
     static constexpr int kGroupN = 1;
 };
 
-__device__ __forceinline__ float silu_mul(float g, float u) {
-    // g / (1 + e^-g): for very negative g, e^-g overflows to +inf and the
-    // reciprocal gives 0, so the result is a signed zero, never NaN.
-    const float e = __expf(-g);
-    return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
-}
-
 // 16-byte chunk position of chunk c in tile row r (rows of 64 or 128 bytes;
 // see the LDS layout above)
 template <int CPR>

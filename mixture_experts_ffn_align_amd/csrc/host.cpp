@@ -117,6 +117,25 @@ bool overlaps(const moe_tensor_t& a, const moe_tensor_t& b) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Two 3-D views of one buffer whose element sets are disjoint although their
+// byte ranges interleave: same sizes and strides, rows that do not overlap
+// (row stride >= row length, last stride 1), and one view shifted from the
+// other by whole rows inside an expert block of P = stride(0) / stride(1)
+// rows, with the shifted rows staying clear of the other view's rows modulo
+// P. Packed halves w[:, :I] and w[:, I:] of [E, 2I, H] are the case meant.
+bool interleaved_disjoint(const moe_tensor_t& a, const moe_tensor_t& b) {
+    if (a.ndim != 3 || b.ndim != 3 || a.dtype != b.dtype) return false;
+    for (int i = 0; i < 3; ++i)
+        if (a.size[i] != b.size[i] || a.stride[i] != b.stride[i]) return false;
+    const int64_t s0 = a.stride[0], s1 = a.stride[1], eb = elem_bytes(a.dtype);
+    if (a.stride[2] != 1 || s1 < a.size[2] || s1 <= 0 || s0 <= 0 || s0 % s1 != 0) return false;
+    const int64_t diff = (int64_t)((uintptr_t)b.data - (uintptr_t)a.data);
+    const int64_t d = diff < 0 ? -diff : diff;
+    if (d % (eb * s1) != 0) return false;
+    const int64_t dr = d / (eb * s1), P = s0 / s1, rows = a.size[1];
+    return dr < P && dr >= rows && dr + rows <= P;
+}
+
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 int64_t align_capacity(int64_t A, int64_t E, int64_t bm) {
@@ -547,6 +566,101 @@ int plan_fused(const moe_fused_args_t* a, Plan* pl) {
         pl->off_hs = 0;
     }
     pl->off_y = y_out ? 0 : take((size_t)pl->A * (size_t)H * 2);   // y: bf16 (the caller's y_rows if given)
+    pl->total = off;
+    return MOE_OK;
+}
+
+// ------------------------------------------------------------ backward
+
+struct BwdPlan {
+    Plan fwd;              // the forward's checked sizes
+    int64_t cap;           // sorted capacity at block_m 64
+    bool pack_x, pack_d;   // activation rows re-laid out (unit stride, aligned)
+    bool wgrad_f32;
+    size_t off_counts, off_sorted, off_bexp, off_npad, off_ebf, off_ebl, off_xp, off_dp, off_gu, off_q, off_dgu,
+        off_wh, off_dxa, total;
+};
+
+constexpr int kBwdBM = 64;
+
+// A weight gradient output: f32 or bf16, last stride 1, rows aligned for the
+// epilogue's 4-element stores.
+int check_wgrad(const moe_tensor_t* t, const char* name, std::initializer_list<int64_t> shape, int* dtype) {
+    if (!t) return fail(MOE_ERR_NULL, "%s: descriptor is NULL", name);
+    if (t->dtype != MOE_DT_F32 && t->dtype != MOE_DT_BF16)
+        return fail(MOE_ERR_DTYPE, "%s: dtype %s, expected f32 or bf16", name, dtype_name(t->dtype));
+    int rc;
+    if ((rc = check_desc(t, name, t->dtype, 3))) return rc;
+    if ((rc = check_shape(*t, name, shape))) return rc;
+    const int64_t al = t->dtype == MOE_DT_F32 ? 16 : 8, eb = elem_bytes(t->dtype);
+    if (t->stride[2] != 1 || ((uintptr_t)t->data % al) != 0 || (t->stride[1] * eb) % al != 0 ||
+        (t->stride[0] * eb) % al != 0)
+        return fail(MOE_ERR_LAYOUT, "%s: needs last stride 1 and %lld-byte aligned rows", name, (long long)al);
+    *dtype = t->dtype;
+    return MOE_OK;
+}
+
+bool rows_direct(const moe_tensor_t& x) {
+    return x.stride[1] == 1 && aligned16(x.data) && (x.size[0] <= 1 || (x.stride[0] * 2) % 16 == 0);
+}
+
+int plan_bwd(const moe_bwd_args_t* b, BwdPlan* pl) {
+    if (!b) return fail(MOE_ERR_NULL, "args is NULL");
+    if (b->fwd.mode != MOE_MODE_BF16) return fail(MOE_ERR_UNSUPPORTED, "the backward is built for bf16 mode only");
+    if (b->fwd.y_rows.data || b->fwd.norm_weight.data)
+        return fail(MOE_ERR_UNSUPPORTED, "the backward takes neither y_rows nor norm_weight");
+    moe_fused_args_t fa = b->fwd;
+    fa.out = b->dx;          // dx takes out's place in the forward's checks
+    fa.force_config = -1;
+    int rc;
+    if ((rc = plan_fused(&fa, &pl->fwd))) return rc;
+    const Plan& f = pl->fwd;
+    const int64_t T = f.T, H = f.H, I = f.I, E = f.E, k = f.k, A = f.A;
+    if (H % 128 != 0 || I % 128 != 0)
+        return fail(MOE_ERR_UNSUPPORTED, "backward: H = %lld and I = %lld must be multiples of 128", (long long)H,
+                    (long long)I);
+    if ((rc = check_desc(&b->dout, "dout", MOE_DT_BF16, 2))) return rc;
+    if ((rc = check_shape(b->dout, "dout", {T, H}))) return rc;
+    int dt_g, dt_u, dt_2;
+    if ((rc = check_wgrad(&b->dgate, "dgate", {E, I, H}, &dt_g))) return rc;
+    if ((rc = check_wgrad(&b->dup, "dup", {E, I, H}, &dt_u))) return rc;
+    if ((rc = check_wgrad(&b->dw2, "dw2", {E, H, I}, &dt_2))) return rc;
+    if (dt_g != dt_u || dt_g != dt_2) return fail(MOE_ERR_DTYPE, "dgate, dup and dw2 must share one dtype");
+    if ((rc = check_desc(&b->dtopk_weights, "dtopk_weights", MOE_DT_F32, 2))) return rc;
+    if ((rc = check_shape(b->dtopk_weights, "dtopk_weights", {T, k}))) return rc;
+    const moe_tensor_t* ins[7] = {&b->fwd.x, &b->fwd.gate, &b->fwd.up, &b->fwd.w2, &b->fwd.topk_ids,
+                                  &b->fwd.topk_weights, &b->dout};
+    const moe_tensor_t* outs[5] = {&b->dx, &b->dgate, &b->dup, &b->dw2, &b->dtopk_weights};
+    for (int i = 0; i < 5; ++i) {
+        for (auto* t : ins)
+            if (overlaps(*outs[i], *t)) return fail(MOE_ERR_LAYOUT, "a gradient output overlaps an input");
+        for (int j = i + 1; j < 5; ++j)
+            if (overlaps(*outs[i], *outs[j]) && !interleaved_disjoint(*outs[i], *outs[j]))
+                return fail(MOE_ERR_LAYOUT, "gradient outputs overlap each other");
+    }
+    pl->wgrad_f32 = dt_g == MOE_DT_F32;
+    pl->pack_x = !rows_direct(b->fwd.x);
+    pl->pack_d = !rows_direct(b->dout);
+    pl->cap = align_capacity(A, (int32_t)E, kBwdBM);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t o = off;
+        off = round_up(off + bytes, 256);
+        return o;
+    };
+    pl->off_counts = take(align_scratch_bytes(A, (int32_t)E));
+    pl->off_sorted = take((size_t)pl->cap * 4);
+    pl->off_bexp = take((size_t)(pl->cap / kBwdBM) * 4);
+    pl->off_npad = take(4);
+    pl->off_ebf = take((size_t)E * 4);
+    pl->off_ebl = take((size_t)E * 4);
+    pl->off_xp = pl->pack_x ? take((size_t)T * H * 2) : 0;
+    pl->off_dp = pl->pack_d ? take((size_t)T * H * 2) : 0;
+    pl->off_gu = take((size_t)A * 2 * I * 4);
+    pl->off_q = take((size_t)A * I * 4);
+    pl->off_dgu = take((size_t)A * 2 * I * 2);
+    pl->off_wh = take((size_t)A * I * 2);
+    pl->off_dxa = take((size_t)A * H * 4);
     pl->total = off;
     return MOE_OK;
 }
@@ -1031,6 +1145,207 @@ int moe_fused_fwd(const moe_fused_args_t* args, void* ws, size_t ws_bytes, moe_s
     cp.H = (int32_t)pl.H;
     if ((e = launch_combine(cp, s)) != hipSuccess) return hip_fail(e, "combine");
     tm.end(4);
+    return ok();
+}
+
+int moe_fused_bwd_workspace_size(const moe_bwd_args_t* args, size_t* bytes) {
+    if (!bytes) return fail(MOE_ERR_NULL, "bytes is NULL");
+    BwdPlan pl;
+    int rc = plan_bwd(args, &pl);
+    if (rc) return rc;
+    *bytes = pl.total;
+    return ok();
+}
+
+int moe_fused_bwd(const moe_bwd_args_t* args, void* ws, size_t ws_bytes, moe_stream_t stream) {
+    BwdPlan pl;
+    int rc = plan_bwd(args, &pl);
+    if (rc) return rc;
+    const Plan& f = pl.fwd;
+    if (f.T == 0) return ok();
+    if (!ws || ((uintptr_t)ws & 255u) || ws_bytes < pl.total)
+        return fail(MOE_ERR_WORKSPACE, "backward needs %zu bytes of 256-byte aligned workspace", pl.total);
+    const moe_bwd_args_t& b = *args;
+    const moe_fused_args_t& a = b.fwd;
+    hipStream_t s = (hipStream_t)stream;
+    char* base = (char*)ws;
+    const int64_t T = f.T, H = f.H, I = f.I, E = f.E, k = f.k, A = f.A;
+    int32_t* sorted = (int32_t*)(base + pl.off_sorted);
+    int32_t* bexp = (int32_t*)(base + pl.off_bexp);
+    int32_t* npad = (int32_t*)(base + pl.off_npad);
+    int32_t* ebf = (int32_t*)(base + pl.off_ebf);
+    int32_t* ebl = (int32_t*)(base + pl.off_ebl);
+    float* gu = (float*)(base + pl.off_gu);
+    float* q = (float*)(base + pl.off_q);
+    uint16_t* dgu = (uint16_t*)(base + pl.off_dgu);
+    uint16_t* wh = (uint16_t*)(base + pl.off_wh);
+    float* dxa = (float*)(base + pl.off_dxa);
+    const int max_blocks = (int)(pl.cap / kBwdBM);
+    hipError_t e;
+
+    // align at block_m 64, and each expert's range of sorted blocks
+    AlignParams ap{};
+    ap.ids = (const int32_t*)a.topk_ids.data;
+    ap.is_t = a.topk_ids.stride[0];
+    ap.is_j = a.topk_ids.stride[1];
+    ap.T = (int32_t)T;
+    ap.k = (int32_t)k;
+    ap.A = (int32_t)A;
+    ap.E = (int32_t)E;
+    ap.e_off = f.e_off;
+    ap.bm = kBwdBM;
+    ap.cap = (int32_t)pl.cap;
+    ap.sorted = sorted;
+    ap.block_expert = bexp;
+    ap.n_padded = npad;
+    ap.counts = (int32_t*)(base + pl.off_counts);
+    if ((e = launch_align(ap, s)) != hipSuccess) return hip_fail(e, "align");
+    if ((e = launch_bwd_expert_blocks(bexp, npad, kBwdBM, max_blocks, ebf, ebl, (int)E, s)) != hipSuccess)
+        return hip_fail(e, "expert blocks");
+
+    // activation rows with unit stride and 16-byte alignment
+    auto rows_of = [&](const moe_tensor_t& t, bool pack, size_t off, const uint16_t** ptr, int64_t* row) {
+        if (!pack) {
+            *ptr = (const uint16_t*)t.data;
+            *row = t.size[0] > 1 ? t.stride[0] : H;
+            return hipSuccess;
+        }
+        PackParams pp{};
+        pp.src = (const uint16_t*)t.data;
+        pp.s_t = t.stride[0];
+        pp.s_h = t.stride[1];
+        pp.dst = (uint16_t*)(base + off);
+        pp.T = T;
+        pp.H = H;
+        *ptr = pp.dst;
+        *row = H;
+        return launch_pack_bf16(pp, s);
+    };
+    const uint16_t *xr, *dr;
+    int64_t x_row, d_row;
+    if ((e = rows_of(a.x, pl.pack_x, pl.off_xp, &xr, &x_row)) != hipSuccess) return hip_fail(e, "pack x");
+    if ((e = rows_of(b.dout, pl.pack_d, pl.off_dp, &dr, &d_row)) != hipSuccess) return hip_fail(e, "pack dout");
+
+    const int64_t no_split = (int64_t)1 << 62;
+    auto act_src = [&](const uint16_t* p0, int64_t row, int kind) {
+        BwdRowSrc r{};
+        r.base[0] = r.base[1] = p0;
+        r.r_stride[0] = r.r_stride[1] = row;
+        r.split = no_split;
+        r.kind = kind;
+        return r;
+    };
+    BwdRowSrc w13{};
+    w13.base[0] = (const uint16_t*)a.gate.data;
+    w13.base[1] = (const uint16_t*)a.up.data;
+    w13.e_stride[0] = a.gate.stride[0];
+    w13.e_stride[1] = a.up.stride[0];
+    w13.r_stride[0] = a.gate.stride[1];
+    w13.r_stride[1] = a.up.stride[1];
+    w13.split = I;
+    w13.kind = 0;
+    BwdRowSrc w2s{};
+    w2s.base[0] = w2s.base[1] = (const uint16_t*)a.w2.data;
+    w2s.e_stride[0] = w2s.e_stride[1] = a.w2.stride[0];
+    w2s.r_stride[0] = w2s.r_stride[1] = a.w2.stride[1];
+    w2s.split = no_split;
+    w2s.kind = 0;
+    BwdGemmParams g{};
+    g.sorted = sorted;
+    g.block_expert = bexp;
+    g.n_padded = npad;
+    g.eb_first = ebf;
+    g.eb_last = ebl;
+    g.A = (int32_t)A;
+    g.k = (int32_t)k;
+
+    // g | u = x_t [gate_e; up_e]^T, by sorted row blocks
+    g.a = act_src(xr, x_row, 1);
+    g.b = w13;
+    g.K = (int32_t)H;
+    g.n_tiles = (int32_t)(2 * I / 128);
+    g.rows_out = gu;
+    g.rows_ld = 2 * I;
+    if ((e = launch_bwd_gemm(0, 0, 0, g, (int64_t)max_blocks * g.n_tiles, s)) != hipSuccess)
+        return hip_fail(e, "recompute gemm1");
+    // q = dout_t w2_e (K = H, the rows of w2)
+    g.a = act_src(dr, d_row, 1);
+    g.b = w2s;
+    g.K = (int32_t)H;
+    g.n_tiles = (int32_t)(I / 128);
+    g.rows_out = q;
+    g.rows_ld = I;
+    if ((e = launch_bwd_gemm(0, 1, 0, g, (int64_t)max_blocks * g.n_tiles, s)) != hipSuccess)
+        return hip_fail(e, "dout w2");
+    // per slot: dw, dg | du, w hb
+    BwdActParams bp{};
+    bp.gu = gu;
+    bp.q = q;
+    bp.dgu = dgu;
+    bp.wh = wh;
+    bp.ids = (const int32_t*)a.topk_ids.data;
+    bp.is_t = a.topk_ids.stride[0];
+    bp.is_j = a.topk_ids.stride[1];
+    bp.w = (const float*)a.topk_weights.data;
+    bp.ws_t = a.topk_weights.stride[0];
+    bp.ws_j = a.topk_weights.stride[1];
+    bp.dw = (float*)b.dtopk_weights.data;
+    bp.dws_t = b.dtopk_weights.stride[0];
+    bp.dws_j = b.dtopk_weights.stride[1];
+    bp.e_off = f.e_off;
+    bp.E = (int32_t)E;
+    bp.k = (int32_t)k;
+    bp.I = (int32_t)I;
+    bp.A = A;
+    if ((e = launch_bwd_act(bp, s)) != hipSuccess) return hip_fail(e, "backward activation");
+    // per-slot dx = [dg | du] [gate_e; up_e] (K = 2I, the rows of w13)
+    g.a = act_src(dgu, 2 * I, 2);
+    g.b = w13;
+    g.K = (int32_t)(2 * I);
+    g.n_tiles = (int32_t)(H / 128);
+    g.rows_out = dxa;
+    g.rows_ld = H;
+    if ((e = launch_bwd_gemm(0, 1, 0, g, (int64_t)max_blocks * g.n_tiles, s)) != hipSuccess)
+        return hip_fail(e, "dx gemm");
+    // dW2_e = sum over the expert's slots of dout_t (w hb)^T
+    g.a = act_src(dr, d_row, 1);
+    g.b = act_src(wh, I, 2);
+    g.m_tiles = (int32_t)(H / kBwdBM);
+    g.n_tiles = (int32_t)(I / 128);
+    g.out[0] = g.out[1] = b.dw2.data;
+    g.out_e[0] = g.out_e[1] = b.dw2.stride[0];
+    g.out_r[0] = g.out_r[1] = b.dw2.stride[1];
+    g.out_split = no_split;
+    g.out_f32 = pl.wgrad_f32 ? 1 : 0;
+    if ((e = launch_bwd_gemm(1, 1, 1, g, E * g.m_tiles * g.n_tiles, s)) != hipSuccess) return hip_fail(e, "dw2 gemm");
+    // [dG_e; dU_e] = sum over the expert's slots of [dg; du] x_t^T
+    g.a = act_src(dgu, 2 * I, 2);
+    g.b = act_src(xr, x_row, 1);
+    g.m_tiles = (int32_t)(2 * I / kBwdBM);
+    g.n_tiles = (int32_t)(H / 128);
+    g.out[0] = b.dgate.data;
+    g.out[1] = b.dup.data;
+    g.out_e[0] = b.dgate.stride[0];
+    g.out_e[1] = b.dup.stride[0];
+    g.out_r[0] = b.dgate.stride[1];
+    g.out_r[1] = b.dup.stride[1];
+    g.out_split = I;
+    if ((e = launch_bwd_gemm(1, 1, 1, g, E * g.m_tiles * g.n_tiles, s)) != hipSuccess) return hip_fail(e, "dw13 gemm");
+    // dx_t = sum over slots, in order
+    BwdDxParams dp{};
+    dp.dxa = dxa;
+    dp.ids = (const int32_t*)a.topk_ids.data;
+    dp.is_t = a.topk_ids.stride[0];
+    dp.is_j = a.topk_ids.stride[1];
+    dp.e_off = f.e_off;
+    dp.E = (int32_t)E;
+    dp.k = (int32_t)k;
+    dp.T = T;
+    dp.H = H;
+    dp.dx = (uint16_t*)b.dx.data;
+    dp.os_t = b.dx.stride[0];
+    dp.os_h = b.dx.stride[1];
+    if ((e = launch_bwd_dx(dp, s)) != hipSuccess) return hip_fail(e, "dx combine");
     return ok();
 }
 

@@ -31,6 +31,14 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
     return __uint_as_float((uint32_t)b << 16);
 }
 
+// SiLU(g) * u = g / (1 + e^-g) * u, the activation of every gemm1 epilogue
+// (and of the backward's recompute): for very negative g, e^-g overflows to
+// +inf and the reciprocal gives 0, so the result is a signed zero, never NaN.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+    const float e = __expf(-g);
+    return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
+}
+
 // ---------------------------------------------------------- e2m1 coding
 //
 // One group of 32 values shares the exponent s = floor(log2(amax)) - 2,
@@ -228,6 +236,67 @@ struct NormParams {
     int64_t T, H;
 };
 hipError_t launch_rmsnorm(const NormParams& p, hipStream_t s);
+
+// ------------------------------------------------------------- backward
+
+// Rows of one GEMM operand. kind 0: row index in weight space (rows at or
+// past split come from base[1]), expert e adds e * e_stride; kind 1: a sorted
+// position, row = its token (a / k); kind 2: a sorted position, row = its
+// assignment a. Sorted positions holding the sentinel read as zero rows.
+struct BwdRowSrc {
+    const uint16_t* base[2];
+    int64_t e_stride[2], r_stride[2];   // elements
+    int64_t split;
+    int32_t kind;
+};
+struct BwdGemmParams {
+    BwdRowSrc a, b;
+    const int32_t* sorted;
+    const int32_t* block_expert;
+    const int32_t* n_padded;
+    const int32_t* eb_first;   // first and last sorted block of each expert
+    const int32_t* eb_last;
+    int32_t A, k;
+    int32_t K;                 // group 0: contraction length
+    int32_t n_tiles, m_tiles;
+    float* rows_out;           // group 0: fp32 rows by assignment
+    int64_t rows_ld;
+    void* out[2];              // group 1: weight gradients, rows at or past out_split in out[1]
+    int64_t out_e[2], out_r[2];
+    int64_t out_split;
+    int32_t out_f32;
+};
+hipError_t launch_bwd_gemm(int a_kmajor, int b_kmajor, int group, const BwdGemmParams& p, int64_t blocks,
+                           hipStream_t s);
+struct BwdActParams {
+    const float* gu;           // [A, 2I] recomputed g | u
+    const float* q;            // [A, I]
+    uint16_t* dgu;             // [A, 2I] bf16 dg | du
+    uint16_t* wh;              // [A, I] bf16 w * hb
+    const int32_t* ids;
+    int64_t is_t, is_j;
+    const float* w;
+    int64_t ws_t, ws_j;
+    float* dw;
+    int64_t dws_t, dws_j;
+    int64_t e_off;
+    int32_t E, k, I;
+    int64_t A;
+};
+hipError_t launch_bwd_act(const BwdActParams& p, hipStream_t s);
+struct BwdDxParams {
+    const float* dxa;          // [A, H] per-slot dx
+    const int32_t* ids;
+    int64_t is_t, is_j;
+    int64_t e_off;
+    int32_t E, k;
+    int64_t T, H;
+    uint16_t* dx;
+    int64_t os_t, os_h;
+};
+hipError_t launch_bwd_dx(const BwdDxParams& p, hipStream_t s);
+hipError_t launch_bwd_expert_blocks(const int32_t* block_expert, const int32_t* n_padded, int bm, int max_blocks,
+                                    int32_t* first, int32_t* last, int E, hipStream_t s);
 
 // One grouped GEMM launch. Stage 1: A = gathered x rows, B = gate/up rows,
 // epilogue SiLU(g)*u -> h. Stage 2: A = h rows, B = w2 rows, epilogue scatter

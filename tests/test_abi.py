@@ -234,3 +234,52 @@ def test_rmsnorm_argument_checks():
     xs = torch.zeros(4, 16, dtype=torch.bfloat16)
     assert _status(lambda: moe.moe_rmsnorm(xs, torch.ones(16), 1e-6, out=xs, stream=0)) == "MOE_ERR_LAYOUT"
     assert moe.moe_rmsnorm(torch.zeros(0, 16, dtype=torch.bfloat16), torch.ones(16), stream=0).shape == (0, 16)
+
+
+def test_backward_argument_checks():
+    x, gate, up, w2, ids, w = _bf16_case(T=8, H=256, I=128)
+    dout = torch.zeros(8, 256, dtype=torch.bfloat16)
+    n = moe.moe_fused_bwd_workspace_size(x, gate, up, w2, ids, w, dout)
+    assert n >= 8 * 2 * (2 * 128 * 4 + 128 * 4 + 2 * 128 * 2 + 128 * 2 + 256 * 4)
+    E, I, H = 8, 128, 256
+    f32 = dict(dgate=torch.zeros(E, I, H), dup=torch.zeros(E, I, H), dw2=torch.zeros(E, H, I))
+    assert _status(lambda: moe.moe_fused_bwd(x, gate, up, w2, ids, w, dout, stream=0,
+                                             **dict(f32, dw2=torch.zeros(E, H, I, dtype=torch.bfloat16)))) == \
+        "MOE_ERR_DTYPE"
+    assert _status(lambda: moe.moe_fused_bwd(x, gate, up, w2, ids, w, dout, stream=0,
+                                             **dict(f32, dgate=torch.zeros(E, I, H)[:, :, :H - 8]))) == \
+        "MOE_ERR_SHAPE"
+    assert _status(lambda: moe.moe_fused_bwd(x, gate, up, w2, ids, w, dout, dx=dout, stream=0, **f32)) == \
+        "MOE_ERR_LAYOUT"
+    dw13 = torch.zeros(E, 2 * I, H)
+    assert _status(lambda: moe.moe_fused_bwd(x, gate, up, w2, ids, w, dout, stream=0, dgate=dw13[:, :I + 8],
+                                             dup=dw13[:, I:], dw2=f32["dw2"])) == "MOE_ERR_SHAPE"
+    # the halves of one packed dw13 are accepted, overlapping outputs are not
+    n2 = moe.moe_fused_bwd_workspace_size(x, gate, up, w2, ids, w, dout)
+    assert n2 == n
+    assert _status(lambda: moe.moe_fused_bwd(x, gate, up, w2, ids, w, dout, stream=0, dgate=dw13[:, :I + 1][:, 1:],
+                                             dup=dw13[:, :I], dw2=f32["dw2"])) == "MOE_ERR_LAYOUT"
+    xs, gs, us, w2s, ids_s, w_s = _bf16_case(T=8, H=192, I=128)
+    assert _status(lambda: moe.moe_fused_bwd_workspace_size(xs, gs, us, w2s, ids_s, w_s,
+                                                            torch.zeros(8, 192, dtype=torch.bfloat16))) == \
+        "MOE_ERR_UNSUPPORTED"                                   # H = 192 is not a multiple of 128
+
+
+def test_backward_packed_dw13_halves_accepted():
+    """dgate/dup as w13-style halves of one [E, 2I, H] gradient interleave in
+    memory without sharing an element: accepted. Halves shifted so that their
+    rows meet: rejected."""
+    E, I, H, T, k = 8, 128, 256, 8, 2
+    x, gate, up, w2, ids, w = _bf16_case(T=T, H=H, I=I, E=E, k=k)
+    dout = torch.zeros(T, H, dtype=torch.bfloat16)
+    dx = torch.zeros(T, H, dtype=torch.bfloat16)
+    dw13 = torch.zeros(E, 2 * I, H)
+
+    def size(dg, du):
+        b = moe._bwd_args(x, gate, up, w2, ids, w, dout, dx, dg, du, torch.zeros(E, H, I), torch.zeros(T, k))
+        n = ctypes.c_size_t(0)
+        return _abi.load().moe_fused_bwd_workspace_size(ctypes.byref(b), ctypes.byref(n))
+
+    assert size(dw13[:, :I], dw13[:, I:]) == 0
+    assert size(dw13[:, I:], dw13[:, :I]) == 0
+    assert _abi.STATUS[size(dw13[:, :I], dw13[:, I - 8:2 * I - 8])] == "MOE_ERR_LAYOUT"
