@@ -122,6 +122,9 @@ def main():
     ap.add_argument("--norm", default="",
                     help="comma-separated token counts: the RMSNorm pre-pass on its own (contiguous and "
                          "transposed x) and inside the bf16 fused forward, one JSON line each")
+    ap.add_argument("--bwd", default="",
+                    help="comma-separated token counts: the backward of the bf16 Qwen3-235B-shaped layer "
+                         "(fp32 weight gradients), one JSON line each")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
@@ -149,6 +152,9 @@ def main():
         return
     if args.norm:
         norm_lines([int(t) for t in args.norm.split(",")], dev)
+        return
+    if args.bwd:
+        bwd_lines([int(t) for t in args.bwd.split(",")], dev)
         return
     if args.bf16 and args.ep > 1:
         ep_buckets([int(t) for t in args.bf16.split(",")], args.ep, dev)
@@ -480,6 +486,58 @@ def ep_buckets(buckets, S, dev):
             "timing": f"HIP graph of one call, {reps} replays back to back",
         }), flush=True)
         del inp, ids, wts, y, out, ws
+        torch.cuda.empty_cache()
+
+
+def bwd_lines(tokens, dev):
+    """Backward of the bf16 Qwen3-235B-shaped layer: gradients of sum(dout * out)
+    for x, the top-k weights and all three weight tensors (fp32), one call
+    graph-timed. Algorithmic flops: 16 H I per slot (recompute 4, q 2, dx 4,
+    dW2 2, dW13 4); bytes: touched experts' w13 read twice and w2 once in
+    bf16, the fp32 gradients of all E experts written (zeros included), plus
+    x, dout and dx."""
+    import torch
+    import mixture_experts_ffn_align_amd as moe
+    from mixture_experts_ffn_align_amd import workloads as W
+
+    sh = W.QWEN3_235B_BF16
+    H, I, E, k = sh.hidden, sh.inter, sh.experts, sh.top_k
+    log(f"[bench] drawing weights {sh.name}")
+    g = torch.Generator(device=dev).manual_seed(0)
+    w13, w2 = W.draw_weights(sh, g, dev)
+    gate, up = W.packed_views(w13, I)
+    dgate = torch.empty((E, I, H), dtype=torch.float32, device=dev)
+    dup = torch.empty_like(dgate)
+    dw2 = torch.empty((E, H, I), dtype=torch.float32, device=dev)
+    for T in tokens:
+        inp = W.make_inputs(sh, T, seed=T, device=dev, weights=(w13, w2))
+        ids, wts = moe.moe_topk_softmax(inp["logits"], k)
+        dout = torch.randn(T, H, generator=torch.Generator(device=dev).manual_seed(T + 7), device=dev).to(torch.bfloat16)
+        dx = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+        dwt = torch.empty(T, k, dtype=torch.float32, device=dev)
+        ws = torch.empty(moe.moe_fused_bwd_workspace_size(inp["x"], gate, up, w2, ids, wts, dout),
+                         dtype=torch.uint8, device=dev)
+
+        def call():
+            moe.moe_fused_bwd(inp["x"], gate, up, w2, ids, wts, dout, dx=dx, dgate=dgate, dup=dup, dw2=dw2,
+                              dtopk_weights=dwt, workspace=ws)
+            return dx
+        reps = max(3, min(50, int(5e4 / (T + 50))))
+        us = graph_time_us(call, reps)
+        touched = int(torch.unique(ids).numel())
+        A = T * k
+        flops = 16 * H * I * A
+        byts = touched * (2 * 2 * I * H * 2 + I * H * 2) + E * 3 * I * H * 4 + T * H * 2 * 3 + 8 * A
+        hbm_s, mfma_s = byts / (HBM_PEAK_GBS * 1e9), flops / (BF16_PEAK_TFLOPS * 1e12)
+        print(json.dumps({
+            "workload": f"{sh.name} backward: dx, top-k weight, gate/up/w2 gradients (fp32), packed w13 views",
+            "tokens": T, "touched_experts": touched, "us_per_call": round(us, 1),
+            "tflops": round(flops / (us * 1e-6) / 1e12, 1), "algorithmic_bytes": byts,
+            "bound": "hbm" if hbm_s >= mfma_s else "mfma",
+            "roofline_frac": round(max(hbm_s, mfma_s) / (us * 1e-6), 3),
+            "timing": f"HIP graph of one call, {reps} replays back to back",
+        }), flush=True)
+        del inp, ids, wts, dout, dx, dwt, ws
         torch.cuda.empty_cache()
 
 

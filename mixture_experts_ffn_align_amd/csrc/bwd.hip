@@ -15,13 +15,14 @@
 // over an expert's rows run in a fixed order, so results do not vary from
 // run to run.
 //
-// One MFMA kernel serves all five GEMMs: 64 x 128 output tiles, 4 waves of
-// 32 x 64, K in stages of 64 staged through LDS in rows of 128 bytes (K
-// contiguous, 16-byte chunks XOR-swizzled by the row). An operand is read
-// either by rows (K contiguous in memory: activations, gate/up rows) or
-// K-major (rows of memory are K: w2 rows for q, gate/up rows for dx, all
-// activations for the weight gradients); a K-major stage is loaded as 8 x 8
-// blocks and transposed in registers before it is written to LDS.
+// One MFMA kernel serves all five GEMMs: BM x 128 output tiles (BM 64 over
+// sorted row blocks, 128 over weight space), 4 waves of BM/2 x 64, K in
+// stages of 64 staged through LDS in rows of 128 bytes (K contiguous, 16-byte
+// chunks XOR-swizzled by the row). An operand is read either by rows (K
+// contiguous in memory: activations, gate/up rows) or K-major (rows of memory
+// are K: w2 rows for q, gate/up rows for dx, all activations for the weight
+// gradients); a K-major stage is loaded by every thread as a 4 x 8 block and
+// transposed in registers before it is written to LDS.
 #include <algorithm>
 
 #include "moe_internal.h"
@@ -29,9 +30,8 @@
 namespace moe {
 namespace {
 
-constexpr int kBM = 64, kBN = 128, kBK = 64;
+constexpr int kBN = 128, kBK = 64;
 constexpr int kRowB = kBK * 2;                       // bytes per LDS tile row
-constexpr int kTileB = (kBM + kBN) * kRowB;          // one stage: A then B
 
 __device__ __forceinline__ int swz(int r, int c) { return c ^ (r & 7); }
 
@@ -50,28 +50,29 @@ __device__ __forceinline__ uint4 load16(const uint16_t* ptr) {
     return ptr ? *reinterpret_cast<const uint4*>(ptr) : make_uint4(0u, 0u, 0u, 0u);
 }
 
-// 8 x 8 bf16 block: v[i] holds 8 consecutive columns of row i; column c of
-// the result holds rows 0..7 of column c.
-__device__ __forceinline__ void transpose8(const uint4 (&v)[8], uint4 (&o)[8]) {
+// 4 x 8 bf16 block: v[i] holds 8 consecutive columns of row i; entry c of
+// the result holds rows 0..3 of column c.
+__device__ __forceinline__ void transpose4x8(const uint4 (&v)[4], uint2 (&o)[8]) {
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
         const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-        uint32_t w[4];
+        uint32_t w[2];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < 2; ++q) {
             const uint32_t lo = (&v[2 * q].x)[c >> 1], hi = (&v[2 * q + 1].x)[c >> 1];
             w[q] = __builtin_amdgcn_perm(hi, lo, sel);
         }
-        o[c] = make_uint4(w[0], w[1], w[2], w[3]);
+        o[c] = make_uint2(w[0], w[1]);
     }
 }
 
 // One operand's share of a stage in registers. ROWS: R rows x 8 chunks over
-// 256 threads. KMAJOR: thread u < R owns k rows 8 (u % 8) .. + 7 of columns
-// 8 (u / 8) .. + 7.
+// 256 threads. KMAJOR (R = 128): thread u owns k rows 4 (u % 16) .. + 3 of
+// columns 8 (u / 16) .. + 7.
 template <int MODE, int R>
 struct Stage {
-    static constexpr int kRowsN = MODE == 0 ? R * 8 / 256 : 8;
+    static_assert(MODE == 0 || R == 128, "K-major operands are 128 columns wide");
+    static constexpr int kRowsN = MODE == 0 ? R * 8 / 256 : 4;
     uint4 v[kRowsN];
 };
 
@@ -81,6 +82,7 @@ struct Operand {
     int e;
     int64_t col0;                        // KMAJOR: first column of the tile
     const uint16_t* rows[MODE == 0 ? R * 8 / 256 : 1];   // ROWS: resolved once
+    int32_t ent[4];                      // KMAJOR over sorted positions: the next stage's entries
 
     __device__ void init(const BwdRowSrc& src, const BwdGemmParams& p, int e_, int64_t row0, int64_t c0) {
         s = &src;
@@ -94,8 +96,20 @@ struct Operand {
             }
         }
     }
+    // KMAJOR over sorted positions: fetch the sorted entries of the stage
+    // whose k rows start at kidx one stage ahead of its loads
+    __device__ void prep(const BwdGemmParams& p, int64_t kidx) {
+        if constexpr (MODE == 1) {
+            if (s->kind != 0) {
+                const int kq = threadIdx.x & 15;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ent[i] = p.sorted[kidx + 4 * kq + i];
+            }
+        }
+    }
     // k rows start at kidx (a K index of the source for KMAJOR, an offset
-    // into the rows for ROWS)
+    // into the rows for ROWS); KMAJOR over sorted positions uses the entries
+    // prep fetched for this stage
     __device__ void load(const BwdGemmParams& p, int64_t kidx, Stage<MODE, R>& st) const {
         if constexpr (MODE == 0) {
 #pragma unroll
@@ -105,13 +119,17 @@ struct Operand {
             }
         } else {
             const int u = threadIdx.x;
-            if (u < R) {
-                const int kg = u & 7, cg = u >> 3;
+            const int kq = u & 15, cg = u >> 4;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const uint16_t* r = src_row(*s, p, kidx + 8 * kg + i, e);
-                    st.v[i] = load16(r ? r + col0 + 8 * cg : nullptr);
+            for (int i = 0; i < 4; ++i) {
+                const uint16_t* r;
+                if (s->kind == 0) {
+                    r = src_row(*s, p, kidx + 4 * kq + i, e);
+                } else {
+                    const int a = ent[i];
+                    r = a < p.A ? s->base[0] + (int64_t)(s->kind == 1 ? a / p.k : a) * s->r_stride[0] : nullptr;
                 }
+                st.v[i] = load16(r ? r + col0 + 8 * cg : nullptr);
             }
         }
     }
@@ -124,15 +142,13 @@ struct Operand {
             }
         } else {
             const int u = threadIdx.x;
-            if (u < R) {
-                const int kg = u & 7, cg = u >> 3;
-                uint4 o[8];
-                transpose8(st.v, o);
+            const int kq = u & 15, cg = u >> 4;
+            uint2 o[8];
+            transpose4x8(st.v, o);
 #pragma unroll
-                for (int c = 0; c < 8; ++c) {
-                    const int r = 8 * cg + c;
-                    *reinterpret_cast<uint4*>(tile + r * kRowB + swz(r, kg) * 16) = o[c];
-                }
+            for (int c = 0; c < 8; ++c) {
+                const int r = 8 * cg + c;
+                *reinterpret_cast<uint2*>(tile + r * kRowB + swz(r, kq >> 1) * 16 + (kq & 1) * 8) = o[c];
             }
         }
     }
@@ -140,10 +156,12 @@ struct Operand {
 
 // A: M x K, B: N x K in LDS; C[m, n] = sum_k A[m, k] B[n, k].
 // G = 0: M runs over 64 sorted rows of one expert (rows_out by assignment);
-// G = 1: M, N over weight space, K over the expert's sorted rows.
+// G = 1: M, N over weight space (BM = 128), K over the expert's sorted rows.
 template <int AM, int BMODE, int G>
 __global__ __launch_bounds__(256) void bwd_gemm_kernel(BwdGemmParams p) {
-    __shared__ __attribute__((aligned(16))) char lds[2][kTileB];
+    constexpr int kBM = G == 0 ? 64 : 128;
+    constexpr int kMB = kBM / 32;                    // 16-row blocks per wave
+    __shared__ __attribute__((aligned(16))) char lds[2][(kBM + kBN) * kRowB];
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = w & 1, wn = w >> 1;
@@ -174,17 +192,23 @@ __global__ __launch_bounds__(256) void bwd_gemm_kernel(BwdGemmParams p) {
     B.init(p.b, p, e, n0, n0);
     auto kidx = [&](int s) -> int64_t { return G == 0 ? (int64_t)s * kBK : kb0 + (int64_t)s * kBK; };
 
-    f32x4_t acc[4][2];
+    f32x4_t acc[4][kMB];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < kMB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     Stage<AM, kBM> sa;
     Stage<BMODE, kBN> sb;
     if (S > 0) {
+        A.prep(p, kidx(0));
+        B.prep(p, kidx(0));
         A.load(p, AM == 0 ? 0 : kidx(0), sa);
         B.load(p, BMODE == 0 ? 0 : kidx(0), sb);
+        if (S > 1) {
+            A.prep(p, kidx(1));
+            B.prep(p, kidx(1));
+        }
         A.store(lds[0], sa);
         B.store(lds[0] + kBM * kRowB, sb);
     }
@@ -194,16 +218,20 @@ __global__ __launch_bounds__(256) void bwd_gemm_kernel(BwdGemmParams p) {
         if (more) {
             A.load(p, AM == 0 ? (int64_t)(s + 1) * kBK : kidx(s + 1), sa);
             B.load(p, BMODE == 0 ? (int64_t)(s + 1) * kBK : kidx(s + 1), sb);
+            if (s + 2 < S) {
+                A.prep(p, kidx(s + 2));
+                B.prep(p, kidx(s + 2));
+            }
         }
         const char* ta = lds[s & 1];
         const char* tb = ta + kBM * kRowB;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             const int ck = ks * 4 + (lane >> 4);
-            uint4 fa[2], fb[4];
+            uint4 fa[kMB], fb[4];
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb) {
-                const int r = wm * 32 + mb * 16 + (lane & 15);
+            for (int mb = 0; mb < kMB; ++mb) {
+                const int r = wm * (kBM / 2) + mb * 16 + (lane & 15);
                 fa[mb] = *reinterpret_cast<const uint4*>(ta + r * kRowB + swz(r, ck) * 16);
             }
 #pragma unroll
@@ -214,7 +242,7 @@ __global__ __launch_bounds__(256) void bwd_gemm_kernel(BwdGemmParams p) {
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-                for (int mb = 0; mb < 2; ++mb)
+                for (int mb = 0; mb < kMB; ++mb)
                     acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                         __builtin_bit_cast(bf16x8_t, fb[nb]), __builtin_bit_cast(bf16x8_t, fa[mb]), acc[nb][mb], 0,
                         0, 0);
@@ -225,10 +253,10 @@ __global__ __launch_bounds__(256) void bwd_gemm_kernel(BwdGemmParams p) {
         }
         __syncthreads();
     }
-    // lane holds C[m = wm 32 + mb 16 + lane % 16][n = wn 64 + nb 16 + 4 (lane / 16) + i]
+    // lane holds C[m = wm BM/2 + mb 16 + lane % 16][n = wn 64 + nb 16 + 4 (lane / 16) + i]
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-        const int m = wm * 32 + mb * 16 + (lane & 15);
+    for (int mb = 0; mb < kMB; ++mb) {
+        const int m = wm * (kBM / 2) + mb * 16 + (lane & 15);
         if constexpr (G == 0) {
             const int a = p.sorted[m0 + m];
             if (a >= p.A) continue;

@@ -581,7 +581,8 @@ struct BwdPlan {
         off_wh, off_dxa, total;
 };
 
-constexpr int kBwdBM = 64;
+constexpr int kBwdBM = 64;       // sorted block rows (one K stage of the weight-gradient GEMMs)
+constexpr int kBwdWgradBM = 128; // weight-space rows per weight-gradient tile
 
 // A weight gradient output: f32 or bf16, last stride 1, rows aligned for the
 // epilogue's 4-element stores.
@@ -1310,7 +1311,7 @@ int moe_fused_bwd(const moe_bwd_args_t* args, void* ws, size_t ws_bytes, moe_str
     // dW2_e = sum over the expert's slots of dout_t (w hb)^T
     g.a = act_src(dr, d_row, 1);
     g.b = act_src(wh, I, 2);
-    g.m_tiles = (int32_t)(H / kBwdBM);
+    g.m_tiles = (int32_t)(H / kBwdWgradBM);
     g.n_tiles = (int32_t)(I / 128);
     g.out[0] = g.out[1] = b.dw2.data;
     g.out_e[0] = g.out_e[1] = b.dw2.stride[0];
@@ -1321,7 +1322,7 @@ int moe_fused_bwd(const moe_bwd_args_t* args, void* ws, size_t ws_bytes, moe_str
     // [dG_e; dU_e] = sum over the expert's slots of [dg; du] x_t^T
     g.a = act_src(dgu, 2 * I, 2);
     g.b = act_src(xr, x_row, 1);
-    g.m_tiles = (int32_t)(2 * I / kBwdBM);
+    g.m_tiles = (int32_t)(2 * I / kBwdWgradBM);
     g.n_tiles = (int32_t)(H / 128);
     g.out[0] = b.dgate.data;
     g.out[1] = b.dup.data;
