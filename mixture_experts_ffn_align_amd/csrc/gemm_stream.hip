@@ -646,6 +646,7 @@ GemmFn lookup(const GemmKernelId& id) {
 #define MOE_NT(B, T) \
     if (id.bm == B && id.nt == T) return gemm_stream_nt<B, T>;
         MOE_NT(16, 2) MOE_NT(16, 4) MOE_NT(16, 8) MOE_NT(32, 2) MOE_NT(32, 4) MOE_NT(32, 8)
+        MOE_NT(64, 2) MOE_NT(64, 4) MOE_NT(64, 8)
 #undef MOE_NT
         return nullptr;
     }

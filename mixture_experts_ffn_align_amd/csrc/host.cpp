@@ -174,6 +174,8 @@ const Cfg kConfigs[] = {
     {16, 1, 1, 4, 0, -1, 2}, {16, 1, 1, 4, 0, -1, 4}, {16, 1, 1, 4, 0, -1, 8},
     {32, 1, 1, 4, 0, -1, 4}, {16, 4, 1, 4, 0, -1, 2}, {16, 2, 1, 4, 0, -1, 2},
     {16, 2, 1, 4, 0, -1, 4}, {32, 1, 1, 4, 0, -1, 8},
+    // the same with 64-row blocks (mid T)
+    {64, 1, 1, 4, 0, -1, 2}, {64, 1, 1, 4, 0, -1, 4}, {64, 1, 1, 4, 0, -1, 8},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
