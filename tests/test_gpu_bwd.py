@@ -8,7 +8,9 @@
 * strides: packed w13 views, router-replay id slices, a transposed x and a
   transposed dout, dgate/dup as views of one packed dw13 all give the same
   bits as contiguous inputs; two runs give the same bits; bf16 weight
-  gradients are the fp32 ones rounded to nearest even.
+  gradients are the fp32 ones rounded to nearest even;
+* an expert-parallel shard's backward: its weight gradients equal the full
+  backward's, its dx and dw the full backward's with other shards' ids masked.
 """
 import numpy as np
 import pytest
@@ -116,3 +118,24 @@ def test_bwd_strides_and_determinism(w235):
     for a, b in zip(bf[1:4], ref[1:4]):
         assert torch.equal(a, b.to(torch.bfloat16))
     assert torch.equal(bf[0], ref[0]) and torch.equal(bf[4], ref[4])
+
+
+def test_bwd_expert_parallel_shard(w235):
+    """A shard's backward (experts [o, o + Es), global ids): its weight
+    gradients equal the full backward's for those experts bit for bit, and
+    dx, dw equal the full backward with the other shards' ids masked."""
+    sh = W.QWEN3_235B_BF16
+    T = 200
+    inp = W.make_inputs(sh, T, seed=91, device=DEV, weights=w235)
+    (ids, w), _ = route_both(inp)
+    dout = _dout(T, sh.hidden, 5)
+    gate, up = W.packed_views(inp["w13"], sh.inter)
+    full = [t.clone() for t in moe.moe_fused_bwd(inp["x"], gate, up, inp["w2"], ids, w, dout)]
+    o, es = 48, 16
+    part = moe.moe_fused_bwd(inp["x"], gate[o:o + es], up[o:o + es], inp["w2"][o:o + es], ids, w, dout,
+                             expert_offset=o, num_global_experts=sh.experts)
+    for a, b in zip(part[1:4], full[1:4]):
+        assert torch.equal(a, b[o:o + es])
+    masked = torch.where((ids < o) | (ids >= o + es), torch.full_like(ids, -1), ids)
+    ref = moe.moe_fused_bwd(inp["x"], gate, up, inp["w2"], masked, w, dout)
+    assert torch.equal(part[0], ref[0]) and torch.equal(part[4], ref[4])
