@@ -492,10 +492,12 @@ def ep_buckets(buckets, S, dev):
 def bwd_lines(tokens, dev):
     """Backward of the bf16 Qwen3-235B-shaped layer: gradients of sum(dout * out)
     for x, the top-k weights and all three weight tensors (fp32), one call
-    graph-timed. Algorithmic flops: 16 H I per slot (recompute 4, q 2, dx 4,
-    dW2 2, dW13 4); bytes: touched experts' w13 read twice and w2 once in
-    bf16, the fp32 gradients of all E experts written (zeros included), plus
-    x, dout and dx."""
+    graph-timed, with the weight gradients overwritten and with them
+    accumulated (added to the given ones, experts without slots untouched).
+    Algorithmic flops: 16 H I per slot (recompute 4, q 2, dx 4, dW2 2, dW13
+    4); bytes: touched experts' w13 read twice and w2 once in bf16, plus the
+    fp32 gradients of all E experts written (overwrite) or of the touched
+    experts read and written (accumulate), plus x, dout and dx."""
     import torch
     import mixture_experts_ffn_align_amd as moe
     from mixture_experts_ffn_align_amd import workloads as W
@@ -518,23 +520,31 @@ def bwd_lines(tokens, dev):
         ws = torch.empty(moe.moe_fused_bwd_workspace_size(inp["x"], gate, up, w2, ids, wts, dout),
                          dtype=torch.uint8, device=dev)
 
-        def call():
+        def call(accumulate=False):
             moe.moe_fused_bwd(inp["x"], gate, up, w2, ids, wts, dout, dx=dx, dgate=dgate, dup=dup, dw2=dw2,
-                              dtopk_weights=dwt, workspace=ws)
+                              dtopk_weights=dwt, workspace=ws, accumulate=accumulate)
             return dx
         reps = max(3, min(50, int(5e4 / (T + 50))))
         us = graph_time_us(call, reps)
+        us_acc = graph_time_us(lambda: call(True), reps)
         touched = int(torch.unique(ids).numel())
         A = T * k
         flops = 16 * H * I * A
-        byts = touched * (2 * 2 * I * H * 2 + I * H * 2) + E * 3 * I * H * 4 + T * H * 2 * 3 + 8 * A
-        hbm_s, mfma_s = byts / (HBM_PEAK_GBS * 1e9), flops / (BF16_PEAK_TFLOPS * 1e12)
+        common = touched * (2 * 2 * I * H * 2 + I * H * 2) + T * H * 2 * 3 + 8 * A
+        byts = common + E * 3 * I * H * 4
+        byts_acc = common + touched * 3 * I * H * 4 * 2
+        mfma_s = flops / (BF16_PEAK_TFLOPS * 1e12)
+
+        def frac(b, t):
+            return round(max(b / (HBM_PEAK_GBS * 1e9), mfma_s) / (t * 1e-6), 3)
         print(json.dumps({
             "workload": f"{sh.name} backward: dx, top-k weight, gate/up/w2 gradients (fp32), packed w13 views",
             "tokens": T, "touched_experts": touched, "us_per_call": round(us, 1),
             "tflops": round(flops / (us * 1e-6) / 1e12, 1), "algorithmic_bytes": byts,
-            "bound": "hbm" if hbm_s >= mfma_s else "mfma",
-            "roofline_frac": round(max(hbm_s, mfma_s) / (us * 1e-6), 3),
+            "bound": "hbm" if byts / (HBM_PEAK_GBS * 1e9) >= mfma_s else "mfma",
+            "roofline_frac": frac(byts, us),
+            "accumulate_us_per_call": round(us_acc, 1), "accumulate_algorithmic_bytes": byts_acc,
+            "accumulate_roofline_frac": frac(byts_acc, us_acc),
             "timing": f"HIP graph of one call, {reps} replays back to back",
         }), flush=True)
         del inp, ids, wts, dout, dx, dwt, ws

@@ -255,11 +255,16 @@ int moe_fused_fwd(const moe_fused_args_t *args, void *ws, size_t ws_bytes, moe_s
  *   dx           [T, H] bf16 out, any strides.
  *   dgate, dup   [E, I, H] out, float32 or bf16, last stride 1, expert and row
  *                strides free (views of one packed dw13 [E, 2I, H] work),
- *                rows 16-byte (f32) or 8-byte (bf16) aligned. Every expert's
- *                gradient is written, zeros for an expert without slots.
+ *                rows 16-byte (f32) or 8-byte (bf16) aligned.
  *   dw2          [E, H, I] out, same rules.
  *   dtopk_weights [T, k] float32 out, any strides: dL/dw_tj, 0 for a
  *                skipped slot.
+ *   accumulate   0: dgate, dup, dw2 are overwritten (zeros for an expert
+ *                without slots). 1: this call's gradients are added to
+ *                them (g = g + new in fp32, rounded once for bf16) and
+ *                experts without slots are left untouched, as when
+ *                gradients accumulate over micro-batches. dx and
+ *                dtopk_weights are always overwritten.
  * Per slot (t, j) of expert e, with g, u, h and its bf16 rounding hb exactly
  * as the forward computes them (g, u recomputed): q = w2_e^T dout_t,
  * dw_tj = <q, hb>, dh = w_tj q, dg = dh u SiLU'(g), du = dh SiLU(g); dg, du
@@ -275,6 +280,8 @@ typedef struct {
     moe_tensor_t dgate, dup;
     moe_tensor_t dw2;
     moe_tensor_t dtopk_weights;
+    int32_t accumulate;
+    int32_t reserved;
 } moe_bwd_args_t;
 
 /* Validate args and report the workspace bytes moe_fused_bwd needs. Host only. */

@@ -207,7 +207,7 @@ def moe_fused_fwd(x: torch.Tensor, gate: torch.Tensor, up: torch.Tensor, w2: tor
 
 
 def _bwd_args(x, gate, up, w2, topk_ids, topk_weights, dout, dx, dgate, dup, dw2, dtopk_weights,
-              expert_offset=0, num_global_experts=0):
+              expert_offset=0, num_global_experts=0, accumulate=False):
     b = _abi.BwdArgs()
     fa, _ = _fused_args(x, gate, up, w2, topk_ids, topk_weights, dx, expert_offset=expert_offset,
                         num_global_experts=num_global_experts)
@@ -215,6 +215,7 @@ def _bwd_args(x, gate, up, w2, topk_ids, topk_weights, dout, dx, dgate, dup, dw2
     b.dout, b.dx = _desc(dout), _desc(dx)
     b.dgate, b.dup, b.dw2 = _desc(dgate), _desc(dup), _desc(dw2)
     b.dtopk_weights = _desc(dtopk_weights)
+    b.accumulate = int(bool(accumulate))
     return b
 
 
@@ -235,13 +236,16 @@ def moe_fused_bwd_workspace_size(x, gate, up, w2, topk_ids, topk_weights, dout, 
 
 def moe_fused_bwd(x, gate, up, w2, topk_ids, topk_weights, dout, *, dx=None, dgate=None, dup=None, dw2=None,
                   dtopk_weights=None, grad_dtype=torch.float32, expert_offset: int = 0,
-                  num_global_experts: int = 0, workspace: Optional[torch.Tensor] = None, stream=None):
+                  num_global_experts: int = 0, accumulate: bool = False,
+                  workspace: Optional[torch.Tensor] = None, stream=None):
     """Gradients of sum(dout * out) for the bf16 fused forward.
 
     Returns (dx [T, H] bf16, dgate [E, I, H], dup [E, I, H], dw2 [E, H, I] in
     grad_dtype (float32 or bfloat16), dtopk_weights [T, k] float32). Outputs
     may be passed in with any allowed strides (dgate/dup as views of one
-    packed dw13 [E, 2I, H], for instance).
+    packed dw13 [E, 2I, H], for instance). accumulate=True adds the weight
+    gradients into the given dgate/dup/dw2 and leaves experts without slots
+    untouched.
     """
     L = _abi.load()
     E, I, H = gate.shape
@@ -258,7 +262,7 @@ def moe_fused_bwd(x, gate, up, w2, topk_ids, topk_weights, dout, *, dx=None, dga
     if dtopk_weights is None:
         dtopk_weights = torch.empty((T, k), dtype=torch.float32, device=dev)
     b = _bwd_args(x, gate, up, w2, topk_ids, topk_weights, dout, dx, dgate, dup, dw2, dtopk_weights,
-                  expert_offset, num_global_experts)
+                  expert_offset, num_global_experts, accumulate)
     n = ctypes.c_size_t(0)
     _abi.check(L.moe_fused_bwd_workspace_size(ctypes.byref(b), ctypes.byref(n)))
     if workspace is None:

@@ -43,7 +43,8 @@ class FusedArgs(ctypes.Structure):
 
 class BwdArgs(ctypes.Structure):
     _fields_ = [("fwd", FusedArgs), ("dout", TensorDesc), ("dx", TensorDesc), ("dgate", TensorDesc),
-                ("dup", TensorDesc), ("dw2", TensorDesc), ("dtopk_weights", TensorDesc)]
+                ("dup", TensorDesc), ("dw2", TensorDesc), ("dtopk_weights", TensorDesc),
+                ("accumulate", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class Config(ctypes.Structure):

@@ -182,6 +182,7 @@ __global__ __launch_bounds__(256) void bwd_gemm_kernel(BwdGemmParams p) {
         const int first = p.eb_first[e];
         S = p.eb_last[e] - first + 1;
         kb0 = (int64_t)first * kBK;
+        if (p.out_accumulate && S <= 0) return;   // nothing to add
     }
     const int64_t n0 = (int64_t)nt * kBN;
     Operand<AM, kBM> A;
@@ -271,12 +272,23 @@ __global__ __launch_bounds__(256) void bwd_gemm_kernel(BwdGemmParams p) {
             if (p.out_f32) {
                 float* row = reinterpret_cast<float*>(p.out[h]) + off;
 #pragma unroll
-                for (int nb = 0; nb < 4; ++nb) *reinterpret_cast<f32x4_t*>(row + nb * 16) = acc[nb][mb];
+                for (int nb = 0; nb < 4; ++nb) {
+                    f32x4_t v = acc[nb][mb];
+                    if (p.out_accumulate) v = *reinterpret_cast<const f32x4_t*>(row + nb * 16) + v;
+                    *reinterpret_cast<f32x4_t*>(row + nb * 16) = v;
+                }
             } else {
                 uint16_t* row = reinterpret_cast<uint16_t*>(p.out[h]) + off;
 #pragma unroll
                 for (int nb = 0; nb < 4; ++nb) {
-                    const f32x4_t v = acc[nb][mb];
+                    f32x4_t v = acc[nb][mb];
+                    if (p.out_accumulate) {
+                        const uint2 o = *reinterpret_cast<const uint2*>(row + nb * 16);
+                        v[0] = __uint_as_float(o.x << 16) + v[0];
+                        v[1] = __uint_as_float(o.x & 0xffff0000u) + v[1];
+                        v[2] = __uint_as_float(o.y << 16) + v[2];
+                        v[3] = __uint_as_float(o.y & 0xffff0000u) + v[3];
+                    }
                     *reinterpret_cast<uint2*>(row + nb * 16) =
                         make_uint2(f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16),
                                    f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16));

@@ -630,6 +630,7 @@ int plan_bwd(const moe_bwd_args_t* b, BwdPlan* pl) {
     if ((rc = check_wgrad(&b->dw2, "dw2", {E, H, I}, &dt_2))) return rc;
     if (dt_g != dt_u || dt_g != dt_2) return fail(MOE_ERR_DTYPE, "dgate, dup and dw2 must share one dtype");
     if ((rc = check_desc(&b->dtopk_weights, "dtopk_weights", MOE_DT_F32, 2))) return rc;
+    if (b->accumulate != 0 && b->accumulate != 1) return fail(MOE_ERR_ARG, "accumulate must be 0 or 1");
     if ((rc = check_shape(b->dtopk_weights, "dtopk_weights", {T, k}))) return rc;
     const moe_tensor_t* ins[7] = {&b->fwd.x, &b->fwd.gate, &b->fwd.up, &b->fwd.w2, &b->fwd.topk_ids,
                                   &b->fwd.topk_weights, &b->dout};
@@ -1320,6 +1321,7 @@ int moe_fused_bwd(const moe_bwd_args_t* args, void* ws, size_t ws_bytes, moe_str
     g.out_r[0] = g.out_r[1] = b.dw2.stride[1];
     g.out_split = no_split;
     g.out_f32 = pl.wgrad_f32 ? 1 : 0;
+    g.out_accumulate = b.accumulate;
     if ((e = launch_bwd_gemm(1, 1, 1, g, E * g.m_tiles * g.n_tiles, s)) != hipSuccess) return hip_fail(e, "dw2 gemm");
     // [dG_e; dU_e] = sum over the expert's slots of [dg; du] x_t^T
     g.a = act_src(dgu, 2 * I, 2);

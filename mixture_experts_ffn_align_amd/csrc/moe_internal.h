@@ -265,6 +265,7 @@ struct BwdGemmParams {
     int64_t out_e[2], out_r[2];
     int64_t out_split;
     int32_t out_f32;
+    int32_t out_accumulate;    // group 1: add into the existing values; experts without rows are skipped
 };
 hipError_t launch_bwd_gemm(int a_kmajor, int b_kmajor, int group, const BwdGemmParams& p, int64_t blocks,
                            hipStream_t s);

@@ -139,3 +139,29 @@ def test_bwd_expert_parallel_shard(w235):
     masked = torch.where((ids < o) | (ids >= o + es), torch.full_like(ids, -1), ids)
     ref = moe.moe_fused_bwd(inp["x"], gate, up, inp["w2"], masked, w, dout)
     assert torch.equal(part[0], ref[0]) and torch.equal(part[4], ref[4])
+
+
+@pytest.mark.parametrize("gdt", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_bwd_accumulate(w235, gdt):
+    """accumulate=True adds this call's weight gradients to the given ones
+    (g + new in fp32, rounded once for bf16) and leaves experts without
+    slots untouched; dx and dw are the same as without it."""
+    sh = W.QWEN3_235B_BF16
+    T = 24
+    inp = W.make_inputs(sh, T, seed=17, device=DEV, weights=w235)
+    (ids, w), _ = route_both(inp)
+    dout = _dout(T, sh.hidden, 6)
+    gate, up = W.packed_views(inp["w13"], sh.inter)
+    ref = [t.clone() for t in moe.moe_fused_bwd(inp["x"], gate, up, inp["w2"], ids, w, dout)]
+    g = torch.Generator(device=DEV).manual_seed(1)
+    prev = [torch.randn(t.shape, generator=g, device=DEV).to(gdt) for t in ref[1:4]]
+    acc = [t.clone() for t in prev]
+    out = moe.moe_fused_bwd(inp["x"], gate, up, inp["w2"], ids, w, dout, dgate=acc[0], dup=acc[1], dw2=acc[2],
+                            accumulate=True)
+    used = torch.zeros(sh.experts, dtype=torch.bool, device=DEV)
+    used[ids.long().flatten()] = True
+    for a, p, r in zip(acc, prev, ref[1:4]):
+        want = (p.float() + r).to(gdt)
+        assert torch.equal(a[used], want[used])
+        assert torch.equal(a[~used], p[~used])
+    assert torch.equal(out[0], ref[0]) and torch.equal(out[4], ref[4])
