@@ -224,7 +224,8 @@ typedef struct {
     int32_t block_m;       /* rows per sorted block of gemm1 */
     int32_t gemm1_kernel;  /* kernel family of gemm1: 1 bf16 weight-streaming, 3 bf16 LDS-tiled,
                               11 and 13 the same two in MXFP4 mode */
-    int32_t gemm2_kernel;  /* kernel family of gemm2: gemm1's plus one */
+    int32_t gemm2_kernel;  /* kernel family of gemm2: gemm1's plus one, or 16: MXFP4 gemm2 with the
+                              combine folded in (few tokens, I = 512; bit-identical results) */
     int32_t gemm1_split_k; /* waves splitting K inside a workgroup */
     int32_t gemm2_split_k;
     int32_t config_index;  /* index into the library's config list */

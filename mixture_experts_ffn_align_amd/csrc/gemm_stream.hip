@@ -678,6 +678,91 @@ int gemm_tile_n(const GemmKernelId& id) {
 
 bool gemm_supported(const GemmKernelId& id) { return lookup(id) != nullptr; }
 
+namespace {
+
+// MXFP4 gemm2 and combine in one pass, for a few tokens: one wave per token t
+// and 16 output columns n0 .. n0 + 15. For each slot j of t in order, the
+// wave multiplies the 16 w2 rows of the slot's expert by the slot's h row
+// with the same MFMA sequence as the weight streams (weights as the first
+// operand, K = 512 in four 128-steps from zero), rounds y to bf16 and adds
+// w_tj * y with fmaf, exactly as the separate combine does; so the output
+// is bit-identical to gemm2 followed by the combine, without y in memory.
+// Lanes 0, 16, 32, 48 hold the token's 4 consecutive columns each; the
+// other lanes compute copies of the same row that are not stored.
+__global__ __launch_bounds__(64) void gemm2_combine_kernel(Gemm2CombineParams q) {
+    const GemmParams& p = q.g;
+    const CombineParams& c = q.c;
+    constexpr int U = 4;
+    const int lane = lane_id();
+    const int r16 = lane & 15, kg = lane >> 4;
+    const int ncb = p.N / 16;
+    const int64_t t = blockIdx.x / (uint32_t)ncb;
+    const int n0 = (int)(blockIdx.x % (uint32_t)ncb) * 16;
+    if (t >= c.T) return;
+    float out_acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < c.k; ++j) {
+        const int64_t e = (int64_t)c.ids[t * c.is_t + (int64_t)j * c.is_j] - c.e_off;
+        if (e < 0 || e >= c.E) continue;
+        const float wt = c.w[t * c.ws_t + (int64_t)j * c.ws_j];
+        const int64_t a = t * c.k + j;
+        const char* wr = reinterpret_cast<const char*>(p.b0) + e * p.b0_e + (int64_t)(n0 + r16) * p.b0_r;
+        const char* hr = reinterpret_cast<const char*>(p.a) + a * p.a_row;
+        i32x4_t fb[U], fa[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            fb[u] = *reinterpret_cast<const i32x4_t*>(wr + u * 64 + kg * 16);
+            fa[u] = *reinterpret_cast<const i32x4_t*>(hr + u * 64 + kg * 16);
+        }
+        const i32x4_t vb = *reinterpret_cast<const i32x4_t*>(p.b0_sc + e * p.b0sc_e + (int64_t)(n0 + r16) * p.b0sc_r);
+        const i32x4_t va = *reinterpret_cast<const i32x4_t*>(p.a_sc + a * p.a_sc_row);
+        uint32_t bsc = 0, asc = 0;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            bsc |= (((uint32_t)vb[u] >> (8 * kg)) & 0xffu) << (8 * u);
+            asc |= (((uint32_t)va[u] >> (8 * kg)) & 0xffu) << (8 * u);
+        }
+        f32x4_t acc;
+        {
+            float z;
+            __asm__("v_mov_b32 %0, 0" : "=v"(z));
+            acc = f32x4_t{z, z, z, z};
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const i32x8_t b8 = {fb[u][0], fb[u][1], fb[u][2], fb[u][3], 0, 0, 0, 0};
+            const i32x8_t a8 = {fa[u][0], fa[u][1], fa[u][2], fa[u][3], 0, 0, 0, 0};
+            acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b8, a8, acc, 4, 4, 0, (int)(bsc >> (8 * u)), 0,
+                                                                    (int)(asc >> (8 * u)));
+        }
+        __asm__ volatile("" : "+v"(acc));
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            out_acc[i] = __builtin_fmaf(wt, bf16_bits_to_f32(f32_to_bf16_bits(acc[i])), out_acc[i]);
+    }
+    if (r16 != 0) return;
+    uint16_t* o = c.out + t * c.os_t;
+    const int n = n0 + 4 * kg;
+    uint32_t b[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) b[i] = f32_to_bf16_bits(out_acc[i]);
+    if (c.os_h == 1 && (((uintptr_t)(o + n)) & 7u) == 0) {
+        *reinterpret_cast<uint2*>(o + n) = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[(int64_t)(n + i) * c.os_h] = (uint16_t)b[i];
+    }
+}
+
+}  // namespace
+
+hipError_t launch_gemm2_combine(const Gemm2CombineParams& p, hipStream_t s) {
+    if (p.g.K != 4 * 128 || p.g.N % 16 != 0) return hipErrorInvalidValue;
+    const int64_t grid = p.c.T * (int64_t)(p.g.N / 16);
+    if (grid == 0) return hipSuccess;
+    hipLaunchKernelGGL(gemm2_combine_kernel, dim3((unsigned)grid), dim3(64), 0, s, p);
+    return hipGetLastError();
+}
+
 hipError_t launch_gemm(const GemmKernelId& id, const GemmParams& p, hipStream_t s) {
     GemmFn fn = lookup(id);
     if (!fn) return hipErrorInvalidValue;

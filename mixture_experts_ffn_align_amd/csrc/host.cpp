@@ -157,6 +157,7 @@ struct Cfg {
     int tile;     // 0: weight-streaming GEMMs; 1 + shape: LDS-tiled GEMMs of that tile shape
     int g2;       // -1, or the entry whose gemm2 kernel runs gemm2 (own block size and align)
     int nt2 = 1;  // MXFP4 gemm2 on the stream with K = 512: 256-column tiles per workgroup
+    int fuse = 0; // 1: MXFP4 gemm2 (K = 512) and the combine in one kernel, per token (few tokens)
 };
 const Cfg kConfigs[] = {
     {16, 4, 4, 4, 0, -1}, {32, 4, 4, 4, 0, -1}, {64, 2, 2, 4, 0, -1},
@@ -176,6 +177,8 @@ const Cfg kConfigs[] = {
     {16, 2, 1, 4, 0, -1, 4}, {32, 1, 1, 4, 0, -1, 8},
     // the same with 64-row blocks (mid T)
     {64, 1, 1, 4, 0, -1, 2}, {64, 1, 1, 4, 0, -1, 4}, {64, 1, 1, 4, 0, -1, 8},
+    // MXFP4, K = 512, few tokens: gemm1 on the stream, gemm2 fused with the combine
+    {16, 1, 1, 4, 0, -1, 1, 1}, {16, 2, 1, 4, 0, -1, 1, 1}, {16, 4, 1, 4, 0, -1, 1, 1},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -319,6 +322,7 @@ struct Plan {
     bool y_out;            // per-slot rows go to the caller's y_rows; no combine
     int64_t y_row;         // element stride between the rows of y
     bool norm;             // RMSNorm pre-pass into the xn segment
+    bool fuse;             // gemm2 and the combine in one kernel (no y, no second layout)
     // workspace offsets
     size_t off_counts, off_sorted[2], off_bexp[2], off_npad[2], off_x, off_xs, off_xn, off_h, off_hs, off_y, total;
 };
@@ -463,7 +467,11 @@ int plan_fused(const moe_fused_args_t* a, Plan* pl) {
 
     // configuration
     int ci = a->force_config;
-    if (ci < 0) ci = default_config(a->mode, T, H, I, E_cfg, E, k);
+    if (ci < 0) {
+        ci = default_config(a->mode, T, H, I, E_cfg, E, k);
+        // a tuned gemm2 fused with the combine cannot write per-slot rows
+        if (y_out && ci < kNumConfigs && kConfigs[ci].fuse) ci = heuristic_config(a->mode, T, H, I, E_cfg, E, k);
+    }
     if (ci >= kNumConfigs) return fail(MOE_ERR_ARG, "force_config %d out of range", ci);
     const Cfg c1 = kConfigs[ci];
     const Cfg c2 = c1.g2 >= 0 ? kConfigs[c1.g2] : c1;
@@ -501,7 +509,15 @@ int plan_fused(const moe_fused_args_t* a, Plan* pl) {
         return MOE_OK;
     };
     if ((rc = resolve(c1, 1, &pl->ks[0]))) return rc;
-    if ((rc = resolve(c2, 2, &pl->ks[1]))) return rc;
+    pl->fuse = c1.fuse != 0;
+    if (pl->fuse) {
+        if (!fp4 || I != 4 * 128 || H % 16 != 0 || T > (1 << 20))
+            return fail(MOE_ERR_UNSUPPORTED, "config %d: fused gemm2 + combine needs MXFP4 with I = 512", ci);
+        if (y_out) return fail(MOE_ERR_UNSUPPORTED, "config %d: fused gemm2 + combine writes out, not y_rows", ci);
+        pl->ks[1] = pl->ks[0];   // no second layout
+    } else if ((rc = resolve(c2, 2, &pl->ks[1]))) {
+        return rc;
+    }
 
     pl->mode = a->mode;
     pl->T = T;
@@ -567,7 +583,7 @@ int plan_fused(const moe_fused_args_t* a, Plan* pl) {
         pl->off_h = take((size_t)pl->A * (size_t)I * 2);
         pl->off_hs = 0;
     }
-    pl->off_y = y_out ? 0 : take((size_t)pl->A * (size_t)H * 2);   // y: bf16 (the caller's y_rows if given)
+    pl->off_y = (y_out || pl->fuse) ? 0 : take((size_t)pl->A * (size_t)H * 2);   // y: bf16 (or y_rows; none fused)
     pl->total = off;
     return MOE_OK;
 }
@@ -929,9 +945,9 @@ int moe_query_config(const moe_fused_args_t* args, moe_config_t* cfg) {
     cfg->block_m2 = pl.ks[1].bm;
     const int base = args->mode == MOE_MODE_MXFP4 ? 10 : 0;
     cfg->gemm1_kernel = base + (pl.ks[0].tile ? 2 : 0) + 1;
-    cfg->gemm2_kernel = base + (pl.ks[1].tile ? 2 : 0) + 2;
+    cfg->gemm2_kernel = pl.fuse ? 16 : base + (pl.ks[1].tile ? 2 : 0) + 2;
     cfg->gemm1_split_k = pl.ks[0].tile ? 1 : pl.ks[0].wk;
-    cfg->gemm2_split_k = pl.ks[1].tile ? 1 : pl.ks[1].wk;
+    cfg->gemm2_split_k = pl.ks[1].tile || pl.fuse ? 1 : pl.ks[1].wk;
     cfg->config_index = pl.cfg_index;
     cfg->num_configs = kNumConfigs;
     return ok();
@@ -1093,6 +1109,26 @@ int moe_fused_fwd(const moe_fused_args_t* args, void* ws, size_t ws_bytes, moe_s
     if ((e = launch(0, g1)) != hipSuccess) return hip_fail(e, "gemm1");
     tm.end(2);
 
+    // the combine's arguments (the separate combine, or folded into gemm2)
+    CombineParams cp{};
+    cp.y = reinterpret_cast<const uint16_t*>(base + pl.off_y);
+    cp.ys_t = pl.k * pl.H;
+    cp.ys_j = pl.H;
+    cp.e_off = pl.e_off;
+    cp.ids = (const int32_t*)a.topk_ids.data;
+    cp.is_t = a.topk_ids.stride[0];
+    cp.is_j = a.topk_ids.stride[1];
+    cp.w = (const float*)a.topk_weights.data;
+    cp.ws_t = a.topk_weights.stride[0];
+    cp.ws_j = a.topk_weights.stride[1];
+    cp.out = (uint16_t*)a.out.data;
+    cp.os_t = a.out.stride[0];
+    cp.os_h = a.out.stride[1];
+    cp.T = (int32_t)pl.T;
+    cp.k = (int32_t)pl.k;
+    cp.E = (int32_t)pl.E;
+    cp.H = (int32_t)pl.H;
+
     // stage 3: gemm2
     tm.begin(3);
     GemmParams g2{};
@@ -1120,34 +1156,16 @@ int moe_fused_fwd(const moe_fused_args_t* args, void* ws, size_t ws_bytes, moe_s
     g2.out_row = pl.y_row;
     g2.n_tile_groups = 2;
     g2.max_mblocks = (int32_t)(pl.cap[1] / pl.ks[1].bm);
-    if ((e = launch(1, g2)) != hipSuccess) return hip_fail(e, "gemm2");
+    if (pl.fuse) {
+        if ((e = launch_gemm2_combine(Gemm2CombineParams{g2, cp}, s)) != hipSuccess) return hip_fail(e, "gemm2");
+    } else if ((e = launch(1, g2)) != hipSuccess) {
+        return hip_fail(e, "gemm2");
+    }
     tm.end(3);
 
-    // stage 4: combine (the caller combines y_rows itself)
+    // stage 4: combine (the caller combines y_rows itself; fused into gemm2)
     tm.begin(4);
-    if (pl.y_out) {
-        tm.end(4);
-        return ok();
-    }
-    CombineParams cp{};
-    cp.y = reinterpret_cast<const uint16_t*>(base + pl.off_y);
-    cp.ys_t = pl.k * pl.H;
-    cp.ys_j = pl.H;
-    cp.e_off = pl.e_off;
-    cp.ids = (const int32_t*)a.topk_ids.data;
-    cp.is_t = a.topk_ids.stride[0];
-    cp.is_j = a.topk_ids.stride[1];
-    cp.w = (const float*)a.topk_weights.data;
-    cp.ws_t = a.topk_weights.stride[0];
-    cp.ws_j = a.topk_weights.stride[1];
-    cp.out = (uint16_t*)a.out.data;
-    cp.os_t = a.out.stride[0];
-    cp.os_h = a.out.stride[1];
-    cp.T = (int32_t)pl.T;
-    cp.k = (int32_t)pl.k;
-    cp.E = (int32_t)pl.E;
-    cp.H = (int32_t)pl.H;
-    if ((e = launch_combine(cp, s)) != hipSuccess) return hip_fail(e, "combine");
+    if (!pl.y_out && !pl.fuse && (e = launch_combine(cp, s)) != hipSuccess) return hip_fail(e, "combine");
     tm.end(4);
     return ok();
 }

@@ -375,4 +375,12 @@ struct CombineParams {
 };
 hipError_t launch_combine(const CombineParams& p, hipStream_t s);
 
+// MXFP4 gemm2 with the combine folded in, for a few tokens: g describes
+// gemm2 (h codes and scales by flat assignment, w2, K = 512), c the combine.
+struct Gemm2CombineParams {
+    GemmParams g;
+    CombineParams c;
+};
+hipError_t launch_gemm2_combine(const Gemm2CombineParams& p, hipStream_t s);
+
 }  // namespace moe

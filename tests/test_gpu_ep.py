@@ -143,3 +143,21 @@ def test_combine_strided_rows_and_ids():
     outt = torch.empty((sh.hidden, T), dtype=torch.bfloat16, device=DEV).t()
     moe.moe_combine(y, ids, w, sh.experts, out=outt)
     assert (_bits(outt) == _bits(full)).all()
+
+
+def test_mxfp4_rows_out_at_one_token():
+    """Per-slot rows at T = 1 (where the tuned choice folds the combine into
+    gemm2) fall back to a kernel that writes rows; combined they equal the
+    plain call bit for bit."""
+    sh = W.QWEN35_397B_TP2_FP4_512
+    g = torch.Generator(device=DEV).manual_seed(79)
+    w13, w2 = W.draw_weights(sh, g, DEV)
+    (gq, gs), (uq, us), (wq, wsc) = quantise_weights_gpu(w13, w2, sh.inter)
+    inp = W.make_inputs(sh, 1, seed=1, device=DEV, weights=(w13, w2))
+    (ids, w), _ = route_both(inp)
+    kw = dict(gate_scale=gs, up_scale=us, w2_scale=wsc, mode=moe.MODE_MXFP4)
+    full = moe.moe_fused_fwd(inp["x"], gq, uq, wq, ids, w, **kw)
+    assert moe.moe_query_config(inp["x"], gq, uq, wq, ids, w, **kw)["gemm2_kernel"] == 16
+    y = torch.zeros((1, sh.top_k, sh.hidden), dtype=torch.bfloat16, device=DEV)
+    moe.moe_fused_fwd(inp["x"], gq, uq, wq, ids, w, y_rows=y, **kw)
+    assert (_bits(moe.moe_combine(y, ids, w, sh.experts)) == _bits(full)).all()
