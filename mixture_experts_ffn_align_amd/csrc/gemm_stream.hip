@@ -680,86 +680,327 @@ bool gemm_supported(const GemmKernelId& id) { return lookup(id) != nullptr; }
 
 namespace {
 
-// MXFP4 gemm2 and combine in one pass, for a few tokens: one wave per token t
-// and 16 output columns n0 .. n0 + 15. For each slot j of t in order, the
-// wave multiplies the 16 w2 rows of the slot's expert by the slot's h row
-// with the same MFMA sequence as the weight streams (weights as the first
-// operand, K = 512 in four 128-steps from zero), rounds y to bf16 and adds
-// w_tj * y with fmaf, exactly as the separate combine does; so the output
-// is bit-identical to gemm2 followed by the combine, without y in memory.
-// Lanes 0, 16, 32, 48 hold the token's 4 consecutive columns each; the
-// other lanes compute copies of the same row that are not stored.
-__global__ __launch_bounds__(64) void gemm2_combine_kernel(Gemm2CombineParams q) {
+// MXFP4 gemm2 and combine in one pass, for a few tokens: one workgroup per
+// token t and 16 output columns n0 .. n0 + 15, of W = min(ceil(k / S), 16)
+// waves. Wave w takes slots j = w, w + W, ... (S of them per round), issuing
+// the loads of a round before it waits on any; for a slot it multiplies the 16 w2 rows of
+// the slot's expert by the slot's h row with the same MFMA sequence as the
+// weight streams (weights as the first operand, K = 512 in four 128-steps
+// from zero) and leaves y rounded to bf16 in LDS. Then 16 lanes of wave 0
+// add w_tj * y over j in slot order with fmaf, exactly as the separate
+// combine does; so the output is bit-identical to gemm2 followed by the
+// combine, without y in memory.
+constexpr int kG2cMaxK = 64;
+
+// LOOP: k > S * W, the slots in rounds of S * W (a loop makes the compiler's
+// waits cover earlier loads, so the common single round has no loop)
+template <int S, bool LOOP>
+__global__ __launch_bounds__(1024) void gemm2_combine_kernel(Gemm2CombineParams q) {
     const GemmParams& p = q.g;
     const CombineParams& c = q.c;
     constexpr int U = 4;
+    __shared__ float ys[kG2cMaxK][16];
+    __shared__ float wts[kG2cMaxK];
+    __shared__ int eid[kG2cMaxK];                    // local expert, or -1
     const int lane = lane_id();
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int W = blockDim.x >> 6;
     const int r16 = lane & 15, kg = lane >> 4;
     const int ncb = p.N / 16;
     const int64_t t = blockIdx.x / (uint32_t)ncb;
     const int n0 = (int)(blockIdx.x % (uint32_t)ncb) * 16;
     if (t >= c.T) return;
-    float out_acc[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < c.k; ++j) {
+    // the token's ids and weights once, so that no wave waits on them
+    // between its weight loads
+    if (threadIdx.x < c.k) {
+        const int j = threadIdx.x;
         const int64_t e = (int64_t)c.ids[t * c.is_t + (int64_t)j * c.is_j] - c.e_off;
-        if (e < 0 || e >= c.E) continue;
-        const float wt = c.w[t * c.ws_t + (int64_t)j * c.ws_j];
-        const int64_t a = t * c.k + j;
-        const char* wr = reinterpret_cast<const char*>(p.b0) + e * p.b0_e + (int64_t)(n0 + r16) * p.b0_r;
-        const char* hr = reinterpret_cast<const char*>(p.a) + a * p.a_row;
-        i32x4_t fb[U], fa[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            fb[u] = *reinterpret_cast<const i32x4_t*>(wr + u * 64 + kg * 16);
-            fa[u] = *reinterpret_cast<const i32x4_t*>(hr + u * 64 + kg * 16);
-        }
-        const i32x4_t vb = *reinterpret_cast<const i32x4_t*>(p.b0_sc + e * p.b0sc_e + (int64_t)(n0 + r16) * p.b0sc_r);
-        const i32x4_t va = *reinterpret_cast<const i32x4_t*>(p.a_sc + a * p.a_sc_row);
-        uint32_t bsc = 0, asc = 0;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            bsc |= (((uint32_t)vb[u] >> (8 * kg)) & 0xffu) << (8 * u);
-            asc |= (((uint32_t)va[u] >> (8 * kg)) & 0xffu) << (8 * u);
-        }
-        f32x4_t acc;
-        {
-            float z;
-            __asm__("v_mov_b32 %0, 0" : "=v"(z));
-            acc = f32x4_t{z, z, z, z};
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const i32x8_t b8 = {fb[u][0], fb[u][1], fb[u][2], fb[u][3], 0, 0, 0, 0};
-            const i32x8_t a8 = {fa[u][0], fa[u][1], fa[u][2], fa[u][3], 0, 0, 0, 0};
-            acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b8, a8, acc, 4, 4, 0, (int)(bsc >> (8 * u)), 0,
-                                                                    (int)(asc >> (8 * u)));
-        }
-        __asm__ volatile("" : "+v"(acc));
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            out_acc[i] = __builtin_fmaf(wt, bf16_bits_to_f32(f32_to_bf16_bits(acc[i])), out_acc[i]);
+        eid[j] = e >= 0 && e < c.E ? (int)e : -1;
+        wts[j] = c.w[t * c.ws_t + (int64_t)j * c.ws_j];
     }
-    if (r16 != 0) return;
-    uint16_t* o = c.out + t * c.os_t;
-    const int n = n0 + 4 * kg;
-    uint32_t b[4];
+    __syncthreads();
+    auto round = [&](const int base) {
+        bool ok[S];
+        i32x4_t fb[S][U], fa[S][U], vb[S], va[S];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) b[i] = f32_to_bf16_bits(out_acc[i]);
-    if (c.os_h == 1 && (((uintptr_t)(o + n)) & 7u) == 0) {
-        *reinterpret_cast<uint2*>(o + n) = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
+        for (int h = 0; h < S; ++h) {
+            const int j = base + w + h * W;
+            const int64_t e = j < c.k ? __builtin_amdgcn_readfirstlane(eid[j]) : -1;
+            ok[h] = e >= 0;
+            if (ok[h]) {
+                const int64_t a = t * c.k + j;
+                const char* wr = reinterpret_cast<const char*>(p.b0) + e * p.b0_e + (int64_t)(n0 + r16) * p.b0_r;
+                const char* hr = reinterpret_cast<const char*>(p.a) + a * p.a_row;
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    fb[h][u] = *reinterpret_cast<const i32x4_t*>(wr + u * 64 + kg * 16);
+                    fa[h][u] = *reinterpret_cast<const i32x4_t*>(hr + u * 64 + kg * 16);
+                }
+                vb[h] = *reinterpret_cast<const i32x4_t*>(p.b0_sc + e * p.b0sc_e + (int64_t)(n0 + r16) * p.b0sc_r);
+                va[h] = *reinterpret_cast<const i32x4_t*>(p.a_sc + a * p.a_sc_row);
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < S; ++h) {
+            if (!ok[h]) continue;
+            // byte 4u + kg of a scale window is this lane's for step u
+            f32x4_t acc;
+            {
+                float z;
+                __asm__("v_mov_b32 %0, 0" : "=v"(z));
+                acc = f32x4_t{z, z, z, z};
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const i32x8_t b8 = {fb[h][u][0], fb[h][u][1], fb[h][u][2], fb[h][u][3], 0, 0, 0, 0};
+                const i32x8_t a8 = {fa[h][u][0], fa[h][u][1], fa[h][u][2], fa[h][u][3], 0, 0, 0, 0};
+                acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b8, a8, acc, 4, 4, 0,
+                                                                        (int)((uint32_t)vb[h][u] >> (8 * kg)), 0,
+                                                                        (int)((uint32_t)va[h][u] >> (8 * kg)));
+            }
+            __asm__ volatile("" : "+v"(acc));
+            // lane (r16, kg) holds columns 4 kg + i; every r16 the same
+            if (r16 == 0) {
+                const int j = base + w + h * W;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ys[j][4 * kg + i] = bf16_bits_to_f32(f32_to_bf16_bits(acc[i]));
+            }
+        }
+    };
+    if constexpr (LOOP) {
+        for (int base = 0; base < c.k; base += S * W) round(base);
     } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o[(int64_t)(n + i) * c.os_h] = (uint16_t)b[i];
+        round(0);
     }
+    __syncthreads();
+    if (w != 0 || lane >= 16) return;
+    float out_acc = 0.f;
+    for (int j = 0; j < c.k; ++j)
+        if (eid[j] >= 0) out_acc = __builtin_fmaf(wts[j], ys[j][lane], out_acc);
+    c.out[t * c.os_t + (int64_t)(n0 + lane) * c.os_h] = (uint16_t)f32_to_bf16_bits(out_acc);
 }
 
 }  // namespace
 
+namespace {
+
+// MXFP4 gemm1 for a few tokens, without the align. Workgroup (slot a, h
+// columns c0 .. c0 + 31): 4 waves take K = H in quarters, each chaining its
+// MFMAs over its quarter in ascending 128-steps from zero (weights first:
+// gate rows c0 .. c0 + 31 in blocks 0, 1, up rows in blocks 2, 3); the
+// partial sums meet in LDS and are added in wave order ((p0 + p1) + p2) +
+// p3, exactly as the register weight stream with a 4-way K split does. The
+// workgroup first quantises its token's activation row into LDS with the
+// quantisation kernel's arithmetic. So the h codes and scales are
+// bit-identical to the aligned path's with that split. Every lane
+// multiplies the same token row, so the 16 MFMA columns hold copies of one
+// result.
+//
+// With one to a few tokens the weight stream is all the traffic and each
+// wave has little else to do, so a wave issues the loads of up to 8 steps
+// (4 blocks x 16 bytes per lane and step, plus the scale bytes) before it
+// waits on any: 32 KB in flight per wave, which is what keeps HBM busy with
+// a few hundred waves on the chip.
+constexpr int kSmallMaxH = 8192;
+constexpr int kSmallChunk = 8;
+
+// STEPS: 128-steps per wave, H / 512 (a compile-time count keeps the load
+// waits exact)
+template <int STEPS>
+__global__ __launch_bounds__(256) void gemm1_small_kernel(Gemm1SmallParams p) {
+    __shared__ uint4 xcode[kSmallMaxH / 32];         // the row's e2m1 codes, 32 per entry
+    __shared__ uint8_t xscale[kSmallMaxH / 32];
+    __shared__ float red[4][4][4][64];
+    const int tid = threadIdx.x;
+    const int lane = lane_id();
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r16 = lane & 15, kg = lane >> 4;
+    const int ncb = p.I / 32;
+    const int a = (int)(blockIdx.x / (uint32_t)ncb);
+    const int c0 = (int)(blockIdx.x % (uint32_t)ncb) * 32;
+    if (a >= p.A) return;
+    const int64_t t = a / p.k, j = a % p.k;
+    const int64_t e = (int64_t)p.ids[t * p.is_t + j * p.is_j] - p.e_off;
+    if (e < 0 || e >= p.E) return;                   // the same for the whole workgroup
+    const int kq = p.H / 4;                          // this wave's quarter of K
+    const int kbase = w * kq;
+    const uint8_t* wr[4];
+    const uint8_t* sr[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const int row = c0 + 16 * (b & 1) + r16;
+        wr[b] = b < 2 ? p.gate + e * p.g_e + (int64_t)row * p.g_r : p.up + e * p.u_e + (int64_t)row * p.u_r;
+        sr[b] = b < 2 ? p.gate_sc + e * p.gs_e + (int64_t)row * p.gs_r
+                      : p.up_sc + e * p.us_e + (int64_t)row * p.us_r;
+    }
+    f32x4_t acc[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        float z;
+        __asm__("v_mov_b32 %0, 0" : "=v"(z));
+        acc[b] = f32x4_t{z, z, z, z};
+    }
+    // the activation row is quantised 8 values per thread and pass (groups
+    // of 32 are 4 neighbouring lanes); a contiguous row is loaded before the
+    // weights so that its wait does not cover them
+    const uint16_t* xr = p.x + t * p.xs_t;
+    const bool xvec = p.xs_h == 1 && (((uintptr_t)xr) & 15u) == 0;
+    constexpr int kXPass = STEPS / 4;                // H = 2048 kXPass
+    auto quant8 = [&](const uint32_t (&v)[8], int h0) {
+        uint32_t amax = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax = max(amax, v[i] & 0x7fffu);
+        amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1));
+        amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2));
+        const int xs = group_exponent(amax << 16);
+        const E2m1Thresholds xth = e2m1_thresholds(xs);
+        uint32_t word = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) word |= e2m1_code(v[i] << 16, xth) << (4 * i);
+        reinterpret_cast<uint32_t*>(xcode)[h0 / 8] = word;
+        if ((tid & 3) == 0) xscale[h0 / 32] = (uint8_t)(xs + 127);
+    };
+    i32x4_t xv[kXPass];
+    if (xvec) {
+#pragma unroll
+        for (int q = 0; q < kXPass; ++q)
+            xv[q] = *reinterpret_cast<const i32x4_t*>(xr + 8 * tid + 2048 * q);
+    } else {
+        for (int h0 = 8 * tid; h0 < p.H; h0 += 8 * 256) {
+            uint32_t v[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = xr[(int64_t)(h0 + i) * p.xs_h];
+            quant8(v, h0);
+        }
+    }
+    constexpr int steps = STEPS;
+#pragma unroll
+    for (int u0 = 0; u0 < steps; u0 += kSmallChunk) {
+        i32x4_t wv[kSmallChunk][4];
+#pragma unroll
+        for (int u = 0; u < kSmallChunk; ++u) {
+            if (u0 + u < steps) {
+                const int k = kbase + 128 * (u0 + u) + 32 * kg;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) wv[u][b] = *reinterpret_cast<const i32x4_t*>(wr[b] + k / 2);
+            }
+        }
+        // scale byte 4u + kg of the row's window of 4 steps is this lane's
+        // for step u; a window is one aligned 16-byte load (H % 2048 == 0;
+        // a byte load per step would cost about as much issue time as a
+        // weight load)
+        i32x4_t sw[kSmallChunk / 4][4];
+#pragma unroll
+        for (int v = 0; v < kSmallChunk / 4; ++v)
+            if (u0 + 4 * v < steps)
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    sw[v][b] = *reinterpret_cast<const i32x4_t*>(sr[b] + kbase / 32 + 4 * (u0 + 4 * v));
+        if (u0 == 0) {
+            if (xvec) {
+                // keep the row's arithmetic behind the weight loads
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int q = 0; q < kXPass; ++q) __asm__ volatile("" : "+v"(xv[q]));
+#pragma unroll
+                for (int q = 0; q < kXPass; ++q) {
+                    uint32_t v[8];
+#pragma unroll
+                    for (int h = 0; h < 4; ++h) {
+                        v[2 * h] = (uint32_t)xv[q][h] & 0xffffu;
+                        v[2 * h + 1] = (uint32_t)xv[q][h] >> 16;
+                    }
+                    quant8(v, 8 * tid + 2048 * q);
+                }
+            }
+            __syncthreads();
+        }
+#pragma unroll
+        for (int u = 0; u < kSmallChunk; ++u) {
+            if (u0 + u < steps) {
+                const int k = kbase + 128 * (u0 + u) + 32 * kg;
+                const uint4 fa = xcode[k / 32];
+                const int asc = xscale[k / 32];
+                const i32x8_t a8 = {(int)fa.x, (int)fa.y, (int)fa.z, (int)fa.w, 0, 0, 0, 0};
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const i32x8_t b8 = {wv[u][b][0], wv[u][b][1], wv[u][b][2], wv[u][b][3], 0, 0, 0, 0};
+                    const int bsc = (int)((uint32_t)sw[u / 4][b][u % 4] >> (8 * kg));
+                    acc[b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b8, a8, acc[b], 4, 4, 0, bsc, 0, asc);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        __asm__ volatile("" : "+v"(acc[b]));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[w][b][i][lane] = acc[b][i];
+    }
+    __syncthreads();
+    if (w != 0) return;
+    // lane (r16, kg) holds h columns 4 kg + i (block 0 / 2) and 16 + 4 kg + i
+    // (block 1 / 3); every r16 holds the same values
+    float h[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            float g = 0.f, uu = 0.f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                g += red[q][half][i][lane];
+                uu += red[q][2 + half][i][lane];
+            }
+            h[half * 4 + i] = silu_mul(g, uu);
+        }
+    }
+    uint32_t amax = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = max(amax, __float_as_uint(h[i]) & 0x7fffffffu);
+    amax = max(amax, (uint32_t)__shfl_xor((int)amax, 16));
+    amax = max(amax, (uint32_t)__shfl_xor((int)amax, 32));
+    const int s = group_exponent(amax);
+    const E2m1Thresholds th = e2m1_thresholds(s);
+    if (r16 != 0) return;
+    uint8_t* rp = p.hq + (int64_t)a * (p.I / 2) + c0 / 2;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        uint32_t v2 = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v2 |= e2m1_code(__float_as_uint(h[half * 4 + i]), th) << (4 * i);
+        *reinterpret_cast<uint16_t*>(rp + (16 * half + 4 * kg) / 2) = (uint16_t)v2;
+    }
+    if (kg == 0) p.hs[(int64_t)a * (p.I / 32) + c0 / 32] = (uint8_t)(s + 127);
+}
+
+}  // namespace
+
+hipError_t launch_gemm1_small(const Gemm1SmallParams& p, hipStream_t s) {
+    if (p.H % 2048 != 0 || p.H > kSmallMaxH || p.I % 32 != 0) return hipErrorInvalidValue;
+    const int64_t grid = (int64_t)p.A * (p.I / 32);
+    if (grid == 0) return hipSuccess;
+    switch (p.H / 512) {
+        case 4: hipLaunchKernelGGL(gemm1_small_kernel<4>, dim3((unsigned)grid), dim3(256), 0, s, p); break;
+        case 8: hipLaunchKernelGGL(gemm1_small_kernel<8>, dim3((unsigned)grid), dim3(256), 0, s, p); break;
+        case 12: hipLaunchKernelGGL(gemm1_small_kernel<12>, dim3((unsigned)grid), dim3(256), 0, s, p); break;
+        default: hipLaunchKernelGGL(gemm1_small_kernel<16>, dim3((unsigned)grid), dim3(256), 0, s, p); break;
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_gemm2_combine(const Gemm2CombineParams& p, hipStream_t s) {
-    if (p.g.K != 4 * 128 || p.g.N % 16 != 0) return hipErrorInvalidValue;
+    if (p.g.K != 4 * 128 || p.g.N % 16 != 0 || p.c.k > kG2cMaxK) return hipErrorInvalidValue;
     const int64_t grid = p.c.T * (int64_t)(p.g.N / 16);
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL(gemm2_combine_kernel, dim3((unsigned)grid), dim3(64), 0, s, p);
+    // two slots per wave (one per wave measured no faster at any T), at
+    // most 16 waves
+    const int W = std::min((p.c.k + 1) / 2, 16);
+    const dim3 block(64 * W);
+    if (2 * W < p.c.k)
+        hipLaunchKernelGGL((gemm2_combine_kernel<2, true>), dim3((unsigned)grid), block, 0, s, p);
+    else
+        hipLaunchKernelGGL((gemm2_combine_kernel<2, false>), dim3((unsigned)grid), block, 0, s, p);
     return hipGetLastError();
 }
 

@@ -157,7 +157,8 @@ struct Cfg {
     int tile;     // 0: weight-streaming GEMMs; 1 + shape: LDS-tiled GEMMs of that tile shape
     int g2;       // -1, or the entry whose gemm2 kernel runs gemm2 (own block size and align)
     int nt2 = 1;  // MXFP4 gemm2 on the stream with K = 512: 256-column tiles per workgroup
-    int fuse = 0; // 1: MXFP4 gemm2 (K = 512) and the combine in one kernel, per token (few tokens)
+    int fuse = 0; // 1: MXFP4 gemm2 (K = 512) and the combine in one kernel, per token (few tokens);
+                  // 2: besides, gemm1 per slot without the align (expert from the ids)
 };
 const Cfg kConfigs[] = {
     {16, 4, 4, 4, 0, -1}, {32, 4, 4, 4, 0, -1}, {64, 2, 2, 4, 0, -1},
@@ -179,6 +180,8 @@ const Cfg kConfigs[] = {
     {64, 1, 1, 4, 0, -1, 2}, {64, 1, 1, 4, 0, -1, 4}, {64, 1, 1, 4, 0, -1, 8},
     // MXFP4, K = 512, few tokens: gemm1 on the stream, gemm2 fused with the combine
     {16, 1, 1, 4, 0, -1, 1, 1}, {16, 2, 1, 4, 0, -1, 1, 1}, {16, 4, 1, 4, 0, -1, 1, 1},
+    // the same with gemm1 per slot (K split 4) and no align
+    {16, 4, 1, 4, 0, -1, 1, 2},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -323,6 +326,7 @@ struct Plan {
     int64_t y_row;         // element stride between the rows of y
     bool norm;             // RMSNorm pre-pass into the xn segment
     bool fuse;             // gemm2 and the combine in one kernel (no y, no second layout)
+    bool small1;           // gemm1 per slot, without the align (implies fuse)
     // workspace offsets
     size_t off_counts, off_sorted[2], off_bexp[2], off_npad[2], off_x, off_xs, off_xn, off_h, off_hs, off_y, total;
 };
@@ -510,9 +514,13 @@ int plan_fused(const moe_fused_args_t* a, Plan* pl) {
     };
     if ((rc = resolve(c1, 1, &pl->ks[0]))) return rc;
     pl->fuse = c1.fuse != 0;
+    pl->small1 = c1.fuse == 2;
     if (pl->fuse) {
         if (!fp4 || I != 4 * 128 || H % 16 != 0 || T > (1 << 20))
             return fail(MOE_ERR_UNSUPPORTED, "config %d: fused gemm2 + combine needs MXFP4 with I = 512", ci);
+        if (pl->small1 && (H % 2048 != 0 || H > 8192 || T * k > (1 << 16)))
+            return fail(MOE_ERR_UNSUPPORTED,
+                        "config %d: gemm1 per slot needs H %% 2048 == 0, H <= 8192 and T*k <= 65536", ci);
         if (y_out) return fail(MOE_ERR_UNSUPPORTED, "config %d: fused gemm2 + combine writes out, not y_rows", ci);
         pl->ks[1] = pl->ks[0];   // no second layout
     } else if ((rc = resolve(c2, 2, &pl->ks[1]))) {
@@ -944,9 +952,9 @@ int moe_query_config(const moe_fused_args_t* args, moe_config_t* cfg) {
     cfg->block_m = pl.ks[0].bm;
     cfg->block_m2 = pl.ks[1].bm;
     const int base = args->mode == MOE_MODE_MXFP4 ? 10 : 0;
-    cfg->gemm1_kernel = base + (pl.ks[0].tile ? 2 : 0) + 1;
+    cfg->gemm1_kernel = pl.small1 ? 17 : base + (pl.ks[0].tile ? 2 : 0) + 1;
     cfg->gemm2_kernel = pl.fuse ? 16 : base + (pl.ks[1].tile ? 2 : 0) + 2;
-    cfg->gemm1_split_k = pl.ks[0].tile ? 1 : pl.ks[0].wk;
+    cfg->gemm1_split_k = pl.small1 ? 4 : (pl.ks[0].tile ? 1 : pl.ks[0].wk);
     cfg->gemm2_split_k = pl.ks[1].tile || pl.fuse ? 1 : pl.ks[1].wk;
     cfg->config_index = pl.cfg_index;
     cfg->num_configs = kNumConfigs;
@@ -1002,7 +1010,7 @@ int moe_fused_fwd(const moe_fused_args_t* args, void* ws, size_t ws_bytes, moe_s
     // stage 0: align; when the two GEMMs use different block sizes, the same
     // pass writes the second padded layout too
     tm.begin(0);
-    {
+    if (!pl.small1) {
         AlignParams ap{};
         ap.ids = (const int32_t*)a.topk_ids.data;
         ap.is_t = a.topk_ids.stride[0];
@@ -1047,7 +1055,7 @@ int moe_fused_fwd(const moe_fused_args_t* args, void* ws, size_t ws_bytes, moe_s
         qp.ss_r = pl.H;
         qp.ss_k = 1;
     }
-    if (fp4) {
+    if (fp4 && !pl.small1) {
         if (!quant_in_align && (e = launch_quant_mxfp4(qp, s)) != hipSuccess) return hip_fail(e, "quant x");
         a_op = base + pl.off_x;
         a_row = pl.H / 2;
@@ -1075,6 +1083,37 @@ int moe_fused_fwd(const moe_fused_args_t* args, void* ws, size_t ws_bytes, moe_s
     };
     // stage 2: gemm1 + SiLU(gate) * up
     tm.begin(2);
+    if (pl.small1) {
+        // per slot, from the bf16 activation (or its normalised rows)
+        Gemm1SmallParams sp{};
+        sp.x = pl.norm ? (const uint16_t*)(base + pl.off_xn) : (const uint16_t*)a.x.data;
+        sp.xs_t = pl.norm ? pl.H : a.x.stride[0];
+        sp.xs_h = pl.norm ? 1 : (pl.H > 1 ? a.x.stride[1] : 1);
+        sp.gate = (const uint8_t*)a.gate.data;
+        sp.up = (const uint8_t*)a.up.data;
+        sp.g_e = a.gate.stride[0];
+        sp.g_r = a.gate.stride[1];
+        sp.u_e = a.up.stride[0];
+        sp.u_r = a.up.stride[1];
+        sp.gate_sc = (const uint8_t*)a.gate_scale.data;
+        sp.up_sc = (const uint8_t*)a.up_scale.data;
+        sp.gs_e = a.gate_scale.stride[0];
+        sp.gs_r = a.gate_scale.stride[1];
+        sp.us_e = a.up_scale.stride[0];
+        sp.us_r = a.up_scale.stride[1];
+        sp.ids = (const int32_t*)a.topk_ids.data;
+        sp.is_t = a.topk_ids.stride[0];
+        sp.is_j = a.topk_ids.stride[1];
+        sp.e_off = pl.e_off;
+        sp.E = (int32_t)pl.E;
+        sp.k = (int32_t)pl.k;
+        sp.A = (int32_t)pl.A;
+        sp.H = (int32_t)pl.H;
+        sp.I = (int32_t)pl.I;
+        sp.hq = (uint8_t*)(base + pl.off_h);
+        sp.hs = (uint8_t*)(base + pl.off_hs);
+        if ((e = launch_gemm1_small(sp, s)) != hipSuccess) return hip_fail(e, "gemm1");
+    }
     GemmParams g1{};
     g1.sorted = sorted[0];
     g1.block_expert = bexp[0];
@@ -1106,7 +1145,7 @@ int moe_fused_fwd(const moe_fused_args_t* args, void* ws, size_t ws_bytes, moe_s
     g1.out_sc = fp4 ? (uint8_t*)(base + pl.off_hs) : nullptr;
     g1.n_tile_groups = 2;
     g1.max_mblocks = (int32_t)(pl.cap[0] / pl.ks[0].bm);
-    if ((e = launch(0, g1)) != hipSuccess) return hip_fail(e, "gemm1");
+    if (!pl.small1 && (e = launch(0, g1)) != hipSuccess) return hip_fail(e, "gemm1");
     tm.end(2);
 
     // the combine's arguments (the separate combine, or folded into gemm2)

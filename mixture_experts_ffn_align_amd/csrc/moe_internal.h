@@ -383,4 +383,25 @@ struct Gemm2CombineParams {
 };
 hipError_t launch_gemm2_combine(const Gemm2CombineParams& p, hipStream_t s);
 
+// MXFP4 gemm1 for a few tokens without the align: one workgroup per (slot,
+// 32 h columns); the expert comes from the ids, the activation row is
+// quantised into LDS. Writes h codes and scales by flat assignment.
+struct Gemm1SmallParams {
+    const uint16_t* x;          // bf16 activation rows
+    int64_t xs_t, xs_h;
+    const uint8_t* gate;        // fp4x2 codes and e8m0 scales, byte strides
+    const uint8_t* up;
+    int64_t g_e, g_r, u_e, u_r;
+    const uint8_t* gate_sc;
+    const uint8_t* up_sc;
+    int64_t gs_e, gs_r, us_e, us_r;
+    const int32_t* ids;
+    int64_t is_t, is_j;
+    int64_t e_off;
+    int32_t E, k, A, H, I;
+    uint8_t* hq;                // [A, I/2]
+    uint8_t* hs;                // [A, I/32]
+};
+hipError_t launch_gemm1_small(const Gemm1SmallParams& p, hipStream_t s);
+
 }  // namespace moe

@@ -301,3 +301,36 @@ def test_empty_batch_and_graph_capture():
         torch.cuda.synchronize()
         assert torch.equal(out, eager)
         _ = moe.moe_fused_fwd(inp["x"], gate, up, inp["w2"], ids, w, workspace=ws)
+
+
+@pytest.mark.parametrize("T", [1, 8, 32])
+def test_mxfp4_gemm1_per_slot_same_bits(fp4_weights, T):
+    """MXFP4 gemm1 per slot without the align (kernel family 17, K split 4)
+    gives the same bits as the register weight stream with the same split,
+    for contiguous and transposed activations and with the RMSNorm pre-pass;
+    and matches the oracle."""
+    shape = W.QWEN35_397B_TP2_FP4_512
+    w13, w2, ((gq, gs), (uq, us), (wq, wsc)) = fp4_weights(shape)
+    inp = W.make_inputs(shape, T, seed=70 + T, device=DEV, weights=(w13, w2))
+    gpu, orc = route_both(inp)
+    kw = dict(gate_scale=gs, up_scale=us, w2_scale=wsc, mode=moe.MODE_MXFP4)
+
+    def query(c):
+        return moe.moe_query_config(inp["x"], gq, uq, wq, *gpu, force_config=c, **kw)
+    fam = _configs_by_family(query)
+    small = fam[(17, 4, 1)]
+    stream = fam[(11, 4, 1)]
+    nw = torch.rand(shape.hidden, generator=torch.Generator(device=DEV).manual_seed(2), device=DEV)
+    xt = inp["x"].t().contiguous().t()
+    for x, extra in ((inp["x"], {}), (xt, {}), (inp["x"], dict(norm_weight=nw))):
+        ref = moe.moe_fused_fwd(x, gq, uq, wq, *gpu, force_config=stream[0], **extra, **kw).clone()
+        for c in small + stream[1:]:
+            got = moe.moe_fused_fwd(x, gq, uq, wq, *gpu, force_config=c, **extra, **kw)
+            assert torch.equal(got, ref), f"config {c}"
+    out = moe.moe_fused_fwd(inp["x"], gq, uq, wq, *gpu, force_config=small[0], **kw)
+    toks = sample_tokens(T, 4)
+    oi, ow = orc
+    used = sorted({int(e) for e in oi[toks].ravel()})
+    acc, _ = oracle_ffn_tokens(inp, oi, ow, toks, mx=oracle_quant_experts(w13, w2, shape.inter, used))
+    got = bf16_to_f64(out[torch.from_numpy(toks).to(DEV)])
+    assert rel_l2(got, acc) <= FP4_TOL and err_ratio(got, acc) <= FP4_ERR_RATIO
