@@ -18,23 +18,47 @@ __device__ __forceinline__ void combine_one(const CombineParams& p, int64_t t, i
     float acc[CP];
 #pragma unroll
     for (int i = 0; i < CP; ++i) acc[i] = 0.f;
-    for (int j = 0; j < p.k; ++j) {
-        const int64_t e = (int64_t)p.ids[(int64_t)t * p.is_t + (int64_t)j * p.is_j] - p.e_off;
-        if (e < 0 || e >= p.E) continue;
-        const float wt = p.w[(int64_t)t * p.ws_t + (int64_t)j * p.ws_j];
-        const uint16_t* src = p.y + (int64_t)t * p.ys_t + (int64_t)j * p.ys_j + n;
-        uint32_t u[CP / 2];
-        if constexpr (CP == 8) {
-            const uint4 v = *reinterpret_cast<const uint4*>(src);
-            u[0] = v.x; u[1] = v.y; u[2] = v.z; u[3] = v.w;
-        } else {
-            const uint2 v = *reinterpret_cast<const uint2*>(src);
-            u[0] = v.x; u[1] = v.y;
-        }
+    // slots in groups of 8: the group's ids and weights (the same for the
+    // whole workgroup), then its y loads, then the fmaf chain in slot order,
+    // so that a few tokens wait on one load latency per group, not per slot
+    for (int j0 = 0; j0 < p.k; j0 += 8) {
+        int32_t id[8];
+        float wt[8];
 #pragma unroll
-        for (int i = 0; i < CP / 2; ++i) {
-            acc[2 * i] = __builtin_fmaf(wt, __uint_as_float(u[i] << 16), acc[2 * i]);
-            acc[2 * i + 1] = __builtin_fmaf(wt, __uint_as_float(u[i] & 0xffff0000u), acc[2 * i + 1]);
+        for (int jj = 0; jj < 8; ++jj) {
+            const int j = min(j0 + jj, p.k - 1);     // past k: re-read the last slot, dropped below
+            id[jj] = p.ids[(int64_t)t * p.is_t + (int64_t)j * p.is_j];
+            wt[jj] = p.w[(int64_t)t * p.ws_t + (int64_t)j * p.ws_j];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        bool live[8];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+            const int64_t e = (int64_t)__builtin_amdgcn_readfirstlane(id[jj]) - p.e_off;
+            live[jj] = j0 + jj < p.k && e >= 0 && e < p.E;
+        }
+        uint32_t u[8][CP / 2];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+            if (!live[jj]) continue;
+            const uint16_t* src = p.y + (int64_t)t * p.ys_t + (int64_t)(j0 + jj) * p.ys_j + n;
+            if constexpr (CP == 8) {
+                const uint4 v = *reinterpret_cast<const uint4*>(src);
+                u[jj][0] = v.x; u[jj][1] = v.y; u[jj][2] = v.z; u[jj][3] = v.w;
+            } else {
+                const uint2 v = *reinterpret_cast<const uint2*>(src);
+                u[jj][0] = v.x; u[jj][1] = v.y;
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+            if (!live[jj]) continue;
+#pragma unroll
+            for (int i = 0; i < CP / 2; ++i) {
+                acc[2 * i] = __builtin_fmaf(wt[jj], __uint_as_float(u[jj][i] << 16), acc[2 * i]);
+                acc[2 * i + 1] = __builtin_fmaf(wt[jj], __uint_as_float(u[jj][i] & 0xffff0000u), acc[2 * i + 1]);
+            }
         }
     }
     uint16_t* o = p.out + (int64_t)t * p.os_t;
