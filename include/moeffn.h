@@ -223,10 +223,12 @@ typedef struct {
     int32_t bucket;        /* smallest power of two >= T, capped at 32768 */
     int32_t block_m;       /* rows per sorted block of gemm1 */
     int32_t gemm1_kernel;  /* kernel family of gemm1: 1 bf16 weight-streaming, 3 bf16 LDS-tiled,
-                              11 and 13 the same two in MXFP4 mode, 17 MXFP4 per slot without the
-                              align (few tokens; K split 4, bit-identical to 11 with that split) */
-    int32_t gemm2_kernel;  /* kernel family of gemm2: gemm1's plus one, or 16: MXFP4 gemm2 with the
-                              combine folded in (few tokens, I = 512; bit-identical results) */
+                              7 bf16 per slot without the align (few tokens; K split 4,
+                              bit-identical to 1 with that split); 11, 13 and 17 the same three in
+                              MXFP4 mode */
+    int32_t gemm2_kernel;  /* kernel family of gemm2: gemm1's plus one, or 6 / 16: gemm2 with the
+                              combine folded in (few tokens; bf16 with I a multiple of 256 from 512
+                              to 1536 and K split 4, MXFP4 with I = 512; bit-identical results) */
     int32_t gemm1_split_k; /* waves splitting K inside a workgroup */
     int32_t gemm2_split_k;
     int32_t config_index;  /* index into the library's config list */

@@ -974,6 +974,200 @@ __global__ __launch_bounds__(256) void gemm1_small_kernel(Gemm1SmallParams p) {
     if (kg == 0) p.hs[(int64_t)a * (p.I / 32) + c0 / 32] = (uint8_t)(s + 127);
 }
 
+// bf16 gemm1 for a few tokens, without the align: the bf16 counterpart of
+// the kernel above. Workgroup (slot a, h columns c0 .. c0 + 15): 4 waves take
+// K = H in quarters, each chaining 16x16x32 MFMAs over its quarter in
+// ascending 32-steps from zero (gate rows c0 .. c0 + 15 in block 0, up rows
+// in block 1); partial sums added in wave order from zero, SiLU(g) * u
+// rounded to bf16 once: the arithmetic of the bf16 weight stream with a
+// 4-way K split, so h is bit-identical to it. The token row is staged in LDS;
+// a wave streams its weights in chunks of 8 steps (16 KB per wave), the next
+// chunk's loads issued before the current chunk's MFMAs.
+// NCH: chunks per wave, H / 1024 (even: the row is staged 2048 values per
+// pass).
+template <int NCH>
+__global__ __launch_bounds__(256) void gemm1_small_bf16_kernel(Gemm1SmallParams p) {
+    __shared__ i32x4_t xs[kSmallMaxH / 8];           // the token row, 8 bf16 per entry
+    __shared__ float red[4][2][4][64];
+    const int tid = threadIdx.x;
+    const int lane = lane_id();
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r16 = lane & 15, kg = lane >> 4;
+    const int ncb = p.I / 16;
+    const int a = (int)(blockIdx.x / (uint32_t)ncb);
+    const int c0 = (int)(blockIdx.x % (uint32_t)ncb) * 16;
+    if (a >= p.A) return;
+    const int64_t t = a / p.k, j = a % p.k;
+    const int64_t e = (int64_t)p.ids[t * p.is_t + j * p.is_j] - p.e_off;
+    if (e < 0 || e >= p.E) return;                   // the same for the whole workgroup
+    constexpr int kq = NCH * 256;                    // this wave's quarter of K
+    const int kbase = w * kq;
+    const uint8_t* wr[2] = {p.gate + e * p.g_e + (int64_t)(c0 + r16) * p.g_r,
+                            p.up + e * p.u_e + (int64_t)(c0 + r16) * p.u_r};
+    f32x4_t acc[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        float z;
+        __asm__("v_mov_b32 %0, 0" : "=v"(z));
+        acc[b] = f32x4_t{z, z, z, z};
+    }
+    // the row: a contiguous one is loaded ahead of the weights, its wait
+    // covering only itself
+    constexpr int XP = NCH / 2;
+    const uint16_t* xr = p.x + t * p.xs_t;
+    const bool xvec = p.xs_h == 1 && (((uintptr_t)xr) & 15u) == 0;
+    i32x4_t xv[XP];
+    if (xvec) {
+#pragma unroll
+        for (int q = 0; q < XP; ++q) xv[q] = *reinterpret_cast<const i32x4_t*>(xr + 8 * tid + 2048 * q);
+    }
+    i32x4_t wv[2][8][2];
+    auto load_chunk = [&](int buf, int c) {
+#pragma unroll
+        for (int st = 0; st < 8; ++st) {
+            const int k = kbase + 256 * c + 32 * st + 8 * kg;
+#pragma unroll
+            for (int b = 0; b < 2; ++b) wv[buf][st][b] = *reinterpret_cast<const i32x4_t*>(wr[b] + 2 * k);
+        }
+    };
+    load_chunk(0, 0);
+    if (xvec) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int q = 0; q < XP; ++q) __asm__ volatile("" : "+v"(xv[q]));
+#pragma unroll
+        for (int q = 0; q < XP; ++q) xs[tid + 256 * q] = xv[q];
+    } else {
+        for (int h0 = 8 * tid; h0 < p.H; h0 += 8 * 256) {
+            i32x4_t v;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                v[i] = (int)((uint32_t)xr[(int64_t)(h0 + 2 * i) * p.xs_h] |
+                             ((uint32_t)xr[(int64_t)(h0 + 2 * i + 1) * p.xs_h] << 16));
+            xs[h0 / 8] = v;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        if (c + 1 < NCH) load_chunk((c + 1) & 1, c + 1);
+        __builtin_amdgcn_sched_barrier(0);           // the next chunk's loads stay ahead
+#pragma unroll
+        for (int st = 0; st < 8; ++st) {
+            const int k = kbase + 256 * c + 32 * st + 8 * kg;
+            const bf16x8_t xa = __builtin_bit_cast(bf16x8_t, xs[k / 8]);
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+                acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wv[c & 1][st][b]), xa,
+                                                                 acc[b], 0, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        __asm__ volatile("" : "+v"(acc[b]));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[w][b][i][lane] = acc[b][i];
+    }
+    __syncthreads();
+    if (w != 0) return;
+    // lane (r16, kg) holds h columns 4 kg + i; every r16 the same
+    uint32_t hb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float g = 0.f, uu = 0.f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            g += red[q][0][i][lane];
+            uu += red[q][1][i][lane];
+        }
+        hb[i] = f32_to_bf16_bits(silu_mul(g, uu));
+    }
+    if (r16 != 0) return;
+    uint16_t* hrow = reinterpret_cast<uint16_t*>(p.hq) + (int64_t)a * p.I + c0 + 4 * kg;
+    *reinterpret_cast<uint2*>(hrow) = make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
+}
+
+// bf16 gemm2 and combine in one pass, for a few tokens: one workgroup of 16
+// waves per token t and 16 output columns n0 .. n0 + 15. Wave w takes K
+// quarter w % 4 of slot j0 + w / 4 for each round of 4 slots j0 = 0, 4, ...:
+// 16x16x32 MFMAs chained over the quarter in ascending 32-steps from zero,
+// the 4 partial sums added in quarter order from zero and rounded to bf16 -
+// the bf16 weight stream's gemm2 with a 4-way K split - then w_tj * y added
+// over j in slot order with fmaf as the separate combine does; so the output
+// is bit-identical to those two, without y in memory.
+// STEPS: 32-steps per K quarter, I / 128.
+template <int STEPS>
+__global__ __launch_bounds__(1024) void gemm2_combine_bf16_kernel(Gemm2CombineParams q) {
+    const GemmParams& p = q.g;
+    const CombineParams& c = q.c;
+    __shared__ float red[4][4][4][64];
+    __shared__ float ys[kG2cMaxK][16];
+    __shared__ float wts[kG2cMaxK];
+    __shared__ int eid[kG2cMaxK];                    // local expert, or -1
+    const int lane = lane_id();
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int qk = w & 3, sl = w >> 2;
+    const int r16 = lane & 15, kg = lane >> 4;
+    const int ncb = p.N / 16;
+    const int64_t t = blockIdx.x / (uint32_t)ncb;
+    const int n0 = (int)(blockIdx.x % (uint32_t)ncb) * 16;
+    if (t >= c.T) return;
+    if (threadIdx.x < c.k) {
+        const int j = threadIdx.x;
+        const int64_t e = (int64_t)c.ids[t * c.is_t + (int64_t)j * c.is_j] - c.e_off;
+        eid[j] = e >= 0 && e < c.E ? (int)e : -1;
+        wts[j] = c.w[t * c.ws_t + (int64_t)j * c.ws_j];
+    }
+    __syncthreads();
+    const int kbase = qk * STEPS * 32;
+    for (int j0 = 0; j0 < c.k; j0 += 4) {
+        const int j = j0 + sl;
+        const int64_t e = j < c.k ? __builtin_amdgcn_readfirstlane(eid[j]) : -1;
+        f32x4_t acc;
+        {
+            float z;
+            __asm__("v_mov_b32 %0, 0" : "=v"(z));
+            acc = f32x4_t{z, z, z, z};
+        }
+        if (e >= 0) {
+            const char* wr = reinterpret_cast<const char*>(p.b0) + (e * p.b0_e + (int64_t)(n0 + r16) * p.b0_r) * 2;
+            const char* hr = reinterpret_cast<const char*>(p.a) + (t * c.k + j) * p.a_row * 2;
+            i32x4_t fb[STEPS], fa[STEPS];
+#pragma unroll
+            for (int st = 0; st < STEPS; ++st) {
+                const int k = kbase + 32 * st + 8 * kg;
+                fb[st] = *reinterpret_cast<const i32x4_t*>(wr + 2 * k);
+                fa[st] = *reinterpret_cast<const i32x4_t*>(hr + 2 * k);
+            }
+            __builtin_amdgcn_sched_barrier(0);       // every load issued before the first wait
+#pragma unroll
+            for (int st = 0; st < STEPS; ++st)
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, fb[st]),
+                                                              __builtin_bit_cast(bf16x8_t, fa[st]), acc, 0, 0, 0);
+        }
+        __asm__ volatile("" : "+v"(acc));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[qk][sl][i][lane] = acc[i];
+        __syncthreads();
+        // lane (r16, kg) holds columns 4 kg + i; every r16 the same
+        if (qk == 0 && e >= 0 && r16 == 0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float y = 0.f;
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq) y += red[qq][sl][i][lane];
+                ys[j][4 * kg + i] = bf16_bits_to_f32(f32_to_bf16_bits(y));
+            }
+        }
+        __syncthreads();
+    }
+    if (w != 0 || lane >= 16) return;
+    float out_acc = 0.f;
+    for (int j = 0; j < c.k; ++j)
+        if (eid[j] >= 0) out_acc = __builtin_fmaf(wts[j], ys[j][lane], out_acc);
+    c.out[t * c.os_t + (int64_t)(n0 + lane) * c.os_h] = (uint16_t)f32_to_bf16_bits(out_acc);
+}
+
 }  // namespace
 
 hipError_t launch_gemm1_small(const Gemm1SmallParams& p, hipStream_t s) {
@@ -985,6 +1179,38 @@ hipError_t launch_gemm1_small(const Gemm1SmallParams& p, hipStream_t s) {
         case 8: hipLaunchKernelGGL(gemm1_small_kernel<8>, dim3((unsigned)grid), dim3(256), 0, s, p); break;
         case 12: hipLaunchKernelGGL(gemm1_small_kernel<12>, dim3((unsigned)grid), dim3(256), 0, s, p); break;
         default: hipLaunchKernelGGL(gemm1_small_kernel<16>, dim3((unsigned)grid), dim3(256), 0, s, p); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm1_small_bf16(const Gemm1SmallParams& p, hipStream_t s) {
+    if (p.H % 2048 != 0 || p.H > kSmallMaxH || p.I % 16 != 0) return hipErrorInvalidValue;
+    const int64_t grid = (int64_t)p.A * (p.I / 16);
+    if (grid == 0) return hipSuccess;
+    switch (p.H / 1024) {
+        case 2: hipLaunchKernelGGL(gemm1_small_bf16_kernel<2>, dim3((unsigned)grid), dim3(256), 0, s, p); break;
+        case 4: hipLaunchKernelGGL(gemm1_small_bf16_kernel<4>, dim3((unsigned)grid), dim3(256), 0, s, p); break;
+        case 6: hipLaunchKernelGGL(gemm1_small_bf16_kernel<6>, dim3((unsigned)grid), dim3(256), 0, s, p); break;
+        default: hipLaunchKernelGGL(gemm1_small_bf16_kernel<8>, dim3((unsigned)grid), dim3(256), 0, s, p); break;
+    }
+    return hipGetLastError();
+}
+
+bool gemm2_combine_bf16_supported(int64_t I) {
+    return I % 128 == 0 && I / 128 >= 4 && I / 128 <= 12 && (I / 128) % 2 == 0;
+}
+
+hipError_t launch_gemm2_combine_bf16(const Gemm2CombineParams& p, hipStream_t s) {
+    if (!gemm2_combine_bf16_supported(p.g.K) || p.g.N % 16 != 0 || p.c.k > kG2cMaxK) return hipErrorInvalidValue;
+    const int64_t grid = p.c.T * (int64_t)(p.g.N / 16);
+    if (grid == 0) return hipSuccess;
+    const dim3 g((unsigned)grid), b(1024);
+    switch (p.g.K / 128) {
+        case 4: hipLaunchKernelGGL(gemm2_combine_bf16_kernel<4>, g, b, 0, s, p); break;
+        case 6: hipLaunchKernelGGL(gemm2_combine_bf16_kernel<6>, g, b, 0, s, p); break;
+        case 8: hipLaunchKernelGGL(gemm2_combine_bf16_kernel<8>, g, b, 0, s, p); break;
+        case 10: hipLaunchKernelGGL(gemm2_combine_bf16_kernel<10>, g, b, 0, s, p); break;
+        default: hipLaunchKernelGGL(gemm2_combine_bf16_kernel<12>, g, b, 0, s, p); break;
     }
     return hipGetLastError();
 }

@@ -157,8 +157,8 @@ struct Cfg {
     int tile;     // 0: weight-streaming GEMMs; 1 + shape: LDS-tiled GEMMs of that tile shape
     int g2;       // -1, or the entry whose gemm2 kernel runs gemm2 (own block size and align)
     int nt2 = 1;  // MXFP4 gemm2 on the stream with K = 512: 256-column tiles per workgroup
-    int fuse = 0; // 1: MXFP4 gemm2 (K = 512) and the combine in one kernel, per token (few tokens);
-                  // 2: besides, gemm1 per slot without the align (expert from the ids)
+    int fuse = 0; // 1: gemm2 and the combine in one kernel, per token (few tokens; MXFP4 K = 512, bf16
+                  // K split 4); 2: besides, gemm1 per slot without the align (expert from the ids)
 };
 const Cfg kConfigs[] = {
     {16, 4, 4, 4, 0, -1}, {32, 4, 4, 4, 0, -1}, {64, 2, 2, 4, 0, -1},
@@ -516,8 +516,12 @@ int plan_fused(const moe_fused_args_t* a, Plan* pl) {
     pl->fuse = c1.fuse != 0;
     pl->small1 = c1.fuse == 2;
     if (pl->fuse) {
-        if (!fp4 || I != 4 * 128 || H % 16 != 0 || T > (1 << 20))
-            return fail(MOE_ERR_UNSUPPORTED, "config %d: fused gemm2 + combine needs MXFP4 with I = 512", ci);
+        if (fp4 ? I != 4 * 128 : !gemm2_combine_bf16_supported(I))
+            return fail(MOE_ERR_UNSUPPORTED,
+                        "config %d: fused gemm2 + combine needs I = 512 (MXFP4) or I in {512, 768, ..., 1536} (bf16)",
+                        ci);
+        if (H % 16 != 0 || T > (1 << 20))
+            return fail(MOE_ERR_UNSUPPORTED, "config %d: fused gemm2 + combine needs H %% 16 == 0, T <= 2^20", ci);
         if (pl->small1 && (H % 2048 != 0 || H > 8192 || T * k > (1 << 16)))
             return fail(MOE_ERR_UNSUPPORTED,
                         "config %d: gemm1 per slot needs H %% 2048 == 0, H <= 8192 and T*k <= 65536", ci);
@@ -952,10 +956,10 @@ int moe_query_config(const moe_fused_args_t* args, moe_config_t* cfg) {
     cfg->block_m = pl.ks[0].bm;
     cfg->block_m2 = pl.ks[1].bm;
     const int base = args->mode == MOE_MODE_MXFP4 ? 10 : 0;
-    cfg->gemm1_kernel = pl.small1 ? 17 : base + (pl.ks[0].tile ? 2 : 0) + 1;
-    cfg->gemm2_kernel = pl.fuse ? 16 : base + (pl.ks[1].tile ? 2 : 0) + 2;
+    cfg->gemm1_kernel = pl.small1 ? base + 7 : base + (pl.ks[0].tile ? 2 : 0) + 1;
+    cfg->gemm2_kernel = pl.fuse ? base + 6 : base + (pl.ks[1].tile ? 2 : 0) + 2;
     cfg->gemm1_split_k = pl.small1 ? 4 : (pl.ks[0].tile ? 1 : pl.ks[0].wk);
-    cfg->gemm2_split_k = pl.ks[1].tile || pl.fuse ? 1 : pl.ks[1].wk;
+    cfg->gemm2_split_k = pl.fuse ? (base ? 1 : 4) : (pl.ks[1].tile ? 1 : pl.ks[1].wk);
     cfg->config_index = pl.cfg_index;
     cfg->num_configs = kNumConfigs;
     return ok();
@@ -1112,7 +1116,15 @@ int moe_fused_fwd(const moe_fused_args_t* args, void* ws, size_t ws_bytes, moe_s
         sp.I = (int32_t)pl.I;
         sp.hq = (uint8_t*)(base + pl.off_h);
         sp.hs = (uint8_t*)(base + pl.off_hs);
-        if ((e = launch_gemm1_small(sp, s)) != hipSuccess) return hip_fail(e, "gemm1");
+        if (!fp4) {
+            // bf16 weights: byte strides
+            sp.g_e *= 2;
+            sp.g_r *= 2;
+            sp.u_e *= 2;
+            sp.u_r *= 2;
+        }
+        if ((e = fp4 ? launch_gemm1_small(sp, s) : launch_gemm1_small_bf16(sp, s)) != hipSuccess)
+            return hip_fail(e, "gemm1");
     }
     GemmParams g1{};
     g1.sorted = sorted[0];
@@ -1196,7 +1208,9 @@ int moe_fused_fwd(const moe_fused_args_t* args, void* ws, size_t ws_bytes, moe_s
     g2.n_tile_groups = 2;
     g2.max_mblocks = (int32_t)(pl.cap[1] / pl.ks[1].bm);
     if (pl.fuse) {
-        if ((e = launch_gemm2_combine(Gemm2CombineParams{g2, cp}, s)) != hipSuccess) return hip_fail(e, "gemm2");
+        const Gemm2CombineParams gc{g2, cp};
+        if ((e = fp4 ? launch_gemm2_combine(gc, s) : launch_gemm2_combine_bf16(gc, s)) != hipSuccess)
+            return hip_fail(e, "gemm2");
     } else if ((e = launch(1, g2)) != hipSuccess) {
         return hip_fail(e, "gemm2");
     }

@@ -403,5 +403,11 @@ struct Gemm1SmallParams {
     uint8_t* hs;                // [A, I/32]
 };
 hipError_t launch_gemm1_small(const Gemm1SmallParams& p, hipStream_t s);
+// the same in bf16: h bf16 [A, I] in hq (byte strides for the weights)
+hipError_t launch_gemm1_small_bf16(const Gemm1SmallParams& p, hipStream_t s);
+// bf16 gemm2 (K split 4 inside the workgroup) with the combine folded in;
+// K = I a multiple of 256 from 512 to 1536
+bool gemm2_combine_bf16_supported(int64_t I);
+hipError_t launch_gemm2_combine_bf16(const Gemm2CombineParams& p, hipStream_t s);
 
 }  // namespace moe

@@ -334,3 +334,46 @@ def test_mxfp4_gemm1_per_slot_same_bits(fp4_weights, T):
     acc, _ = oracle_ffn_tokens(inp, oi, ow, toks, mx=oracle_quant_experts(w13, w2, shape.inter, used))
     got = bf16_to_f64(out[torch.from_numpy(toks).to(DEV)])
     assert rel_l2(got, acc) <= FP4_TOL and err_ratio(got, acc) <= FP4_ERR_RATIO
+
+
+@pytest.mark.parametrize("T", [1, 5, 16])
+def test_bf16_per_slot_and_fused_gemm2_same_bits(w235, T):
+    """bf16 gemm1 per slot without the align (family 7) and gemm2 with the
+    combine folded in (family 6), both with a 4-way K split, give the same
+    bits as the weight streams with that split followed by the separate
+    combine, for contiguous and transposed activations, packed w13 views and
+    the RMSNorm pre-pass; and match the oracle."""
+    sh = W.QWEN3_235B_BF16
+    inp = W.make_inputs(sh, T, seed=80 + T, device=DEV, weights=w235)
+    gpu, orc = route_both(inp)
+    gate, up = W.packed_views(inp["w13"], sh.inter)
+
+    def query(c):
+        return moe.moe_query_config(inp["x"], gate, up, inp["w2"], *gpu, force_config=c)
+    n = query(-1)["num_configs"]
+    kinds = {}
+    for c in range(n):
+        try:
+            q = query(c)
+        except moe.MoEError as err:
+            assert err.status == -6, err
+            continue
+        if q["gemm1_split_k"] == 4 and q["gemm2_split_k"] == 4:
+            kinds.setdefault((q["gemm1_kernel"], q["gemm2_kernel"]), []).append(c)
+    assert (1, 2) in kinds and (1, 6) in kinds and (7, 6) in kinds, kinds
+    ref_cfg = kinds[(1, 2)][0]
+    others = [c for key, cs in kinds.items() for c in cs if c != ref_cfg]
+    nw = torch.rand(sh.hidden, generator=torch.Generator(device=DEV).manual_seed(3), device=DEV)
+    xt = inp["x"].t().contiguous().t()
+    gc, uc = gate.contiguous(), up.contiguous()
+    for x, g_, u_, extra in ((inp["x"], gate, up, {}), (xt, gc, uc, {}), (inp["x"], gate, up, dict(norm_weight=nw))):
+        ref = moe.moe_fused_fwd(x, g_, u_, inp["w2"], *gpu, force_config=ref_cfg, **extra).clone()
+        for c in others:
+            got = moe.moe_fused_fwd(x, g_, u_, inp["w2"], *gpu, force_config=c, **extra)
+            assert torch.equal(got, ref), f"config {c}"
+    out = moe.moe_fused_fwd(inp["x"], gate, up, inp["w2"], *gpu, force_config=kinds[(7, 6)][0])
+    toks = sample_tokens(T, 4)
+    oi, ow = orc
+    acc, _ = oracle_ffn_tokens(inp, oi, ow, toks)
+    got = bf16_to_f64(out[torch.from_numpy(toks).to(DEV)])
+    assert rel_l2(got, acc) <= 1e-2
