@@ -803,17 +803,22 @@ namespace {
 // a few hundred waves on the chip.
 constexpr int kSmallMaxH = 8192;
 constexpr int kSmallChunk = 8;
+constexpr int kSmallBPW = 2;                    // measured: 2 beats 4 and 1 at T = 1-16
 
 // STEPS: 128-steps per wave, H / 512 (a compile-time count keeps the load
-// waits exact)
-template <int STEPS>
-__global__ __launch_bounds__(256) void gemm1_small_kernel(Gemm1SmallParams p) {
+// waits exact). BPW: MFMA blocks per wave (4, 2 or 1); the workgroup has
+// 4 x 4 / BPW waves, wave w taking K quarter w % 4 of blocks
+// (w / 4) BPW .. + BPW - 1. Every element's sum is the same for any BPW.
+template <int STEPS, int BPW>
+__global__ __launch_bounds__(256 * (4 / BPW)) void gemm1_small_kernel(Gemm1SmallParams p) {
+    constexpr int NT = 256 * (4 / BPW);
     __shared__ uint4 xcode[kSmallMaxH / 32];         // the row's e2m1 codes, 32 per entry
     __shared__ uint8_t xscale[kSmallMaxH / 32];
     __shared__ float red[4][4][4][64];
     const int tid = threadIdx.x;
     const int lane = lane_id();
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int qk = w & 3, b0 = (w >> 2) * BPW;
     const int r16 = lane & 15, kg = lane >> 4;
     const int ncb = p.I / 32;
     const int a = (int)(blockIdx.x / (uint32_t)ncb);
@@ -823,19 +828,20 @@ __global__ __launch_bounds__(256) void gemm1_small_kernel(Gemm1SmallParams p) {
     const int64_t e = (int64_t)p.ids[t * p.is_t + j * p.is_j] - p.e_off;
     if (e < 0 || e >= p.E) return;                   // the same for the whole workgroup
     const int kq = p.H / 4;                          // this wave's quarter of K
-    const int kbase = w * kq;
-    const uint8_t* wr[4];
-    const uint8_t* sr[4];
+    const int kbase = qk * kq;
+    const uint8_t* wr[BPW];
+    const uint8_t* sr[BPW];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
+    for (int bl = 0; bl < BPW; ++bl) {
+        const int b = b0 + bl;
         const int row = c0 + 16 * (b & 1) + r16;
-        wr[b] = b < 2 ? p.gate + e * p.g_e + (int64_t)row * p.g_r : p.up + e * p.u_e + (int64_t)row * p.u_r;
-        sr[b] = b < 2 ? p.gate_sc + e * p.gs_e + (int64_t)row * p.gs_r
-                      : p.up_sc + e * p.us_e + (int64_t)row * p.us_r;
+        wr[bl] = b < 2 ? p.gate + e * p.g_e + (int64_t)row * p.g_r : p.up + e * p.u_e + (int64_t)row * p.u_r;
+        sr[bl] = b < 2 ? p.gate_sc + e * p.gs_e + (int64_t)row * p.gs_r
+                       : p.up_sc + e * p.us_e + (int64_t)row * p.us_r;
     }
-    f32x4_t acc[4];
+    f32x4_t acc[BPW];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
+    for (int b = 0; b < BPW; ++b) {
         float z;
         __asm__("v_mov_b32 %0, 0" : "=v"(z));
         acc[b] = f32x4_t{z, z, z, z};
@@ -845,7 +851,8 @@ __global__ __launch_bounds__(256) void gemm1_small_kernel(Gemm1SmallParams p) {
     // weights so that its wait does not cover them
     const uint16_t* xr = p.x + t * p.xs_t;
     const bool xvec = p.xs_h == 1 && (((uintptr_t)xr) & 15u) == 0;
-    constexpr int kXPass = STEPS / 4;                // H = 2048 kXPass
+    constexpr int kXPass = (512 * STEPS + 8 * NT - 1) / (8 * NT);
+    constexpr bool kXTail = 8 * NT * kXPass != 512 * STEPS;
     auto quant8 = [&](const uint32_t (&v)[8], int h0) {
         uint32_t amax = 0;
 #pragma unroll
@@ -864,9 +871,10 @@ __global__ __launch_bounds__(256) void gemm1_small_kernel(Gemm1SmallParams p) {
     if (xvec) {
 #pragma unroll
         for (int q = 0; q < kXPass; ++q)
-            xv[q] = *reinterpret_cast<const i32x4_t*>(xr + 8 * tid + 2048 * q);
+            if (!kXTail || 8 * tid + 8 * NT * q < p.H)
+                xv[q] = *reinterpret_cast<const i32x4_t*>(xr + 8 * tid + 8 * NT * q);
     } else {
-        for (int h0 = 8 * tid; h0 < p.H; h0 += 8 * 256) {
+        for (int h0 = 8 * tid; h0 < p.H; h0 += 8 * NT) {
             uint32_t v[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) v[i] = xr[(int64_t)(h0 + i) * p.xs_h];
@@ -876,25 +884,25 @@ __global__ __launch_bounds__(256) void gemm1_small_kernel(Gemm1SmallParams p) {
     constexpr int steps = STEPS;
 #pragma unroll
     for (int u0 = 0; u0 < steps; u0 += kSmallChunk) {
-        i32x4_t wv[kSmallChunk][4];
+        i32x4_t wv[kSmallChunk][BPW];
 #pragma unroll
         for (int u = 0; u < kSmallChunk; ++u) {
             if (u0 + u < steps) {
                 const int k = kbase + 128 * (u0 + u) + 32 * kg;
 #pragma unroll
-                for (int b = 0; b < 4; ++b) wv[u][b] = *reinterpret_cast<const i32x4_t*>(wr[b] + k / 2);
+                for (int b = 0; b < BPW; ++b) wv[u][b] = *reinterpret_cast<const i32x4_t*>(wr[b] + k / 2);
             }
         }
         // scale byte 4u + kg of the row's window of 4 steps is this lane's
         // for step u; a window is one aligned 16-byte load (H % 2048 == 0;
         // a byte load per step would cost about as much issue time as a
         // weight load)
-        i32x4_t sw[kSmallChunk / 4][4];
+        i32x4_t sw[kSmallChunk / 4][BPW];
 #pragma unroll
         for (int v = 0; v < kSmallChunk / 4; ++v)
             if (u0 + 4 * v < steps)
 #pragma unroll
-                for (int b = 0; b < 4; ++b)
+                for (int b = 0; b < BPW; ++b)
                     sw[v][b] = *reinterpret_cast<const i32x4_t*>(sr[b] + kbase / 32 + 4 * (u0 + 4 * v));
         if (u0 == 0) {
             if (xvec) {
@@ -904,13 +912,14 @@ __global__ __launch_bounds__(256) void gemm1_small_kernel(Gemm1SmallParams p) {
                 for (int q = 0; q < kXPass; ++q) __asm__ volatile("" : "+v"(xv[q]));
 #pragma unroll
                 for (int q = 0; q < kXPass; ++q) {
+                    if (kXTail && 8 * tid + 8 * NT * q >= p.H) continue;
                     uint32_t v[8];
 #pragma unroll
                     for (int h = 0; h < 4; ++h) {
                         v[2 * h] = (uint32_t)xv[q][h] & 0xffffu;
                         v[2 * h + 1] = (uint32_t)xv[q][h] >> 16;
                     }
-                    quant8(v, 8 * tid + 2048 * q);
+                    quant8(v, 8 * tid + 8 * NT * q);
                 }
             }
             __syncthreads();
@@ -923,7 +932,7 @@ __global__ __launch_bounds__(256) void gemm1_small_kernel(Gemm1SmallParams p) {
                 const int asc = xscale[k / 32];
                 const i32x8_t a8 = {(int)fa.x, (int)fa.y, (int)fa.z, (int)fa.w, 0, 0, 0, 0};
 #pragma unroll
-                for (int b = 0; b < 4; ++b) {
+                for (int b = 0; b < BPW; ++b) {
                     const i32x8_t b8 = {wv[u][b][0], wv[u][b][1], wv[u][b][2], wv[u][b][3], 0, 0, 0, 0};
                     const int bsc = (int)((uint32_t)sw[u / 4][b][u % 4] >> (8 * kg));
                     acc[b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b8, a8, acc[b], 4, 4, 0, bsc, 0, asc);
@@ -932,10 +941,10 @@ __global__ __launch_bounds__(256) void gemm1_small_kernel(Gemm1SmallParams p) {
         }
     }
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
+    for (int b = 0; b < BPW; ++b) {
         __asm__ volatile("" : "+v"(acc[b]));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) red[w][b][i][lane] = acc[b][i];
+        for (int i = 0; i < 4; ++i) red[qk][b0 + b][i][lane] = acc[b][i];
     }
     __syncthreads();
     if (w != 0) return;
@@ -1174,11 +1183,12 @@ hipError_t launch_gemm1_small(const Gemm1SmallParams& p, hipStream_t s) {
     if (p.H % 2048 != 0 || p.H > kSmallMaxH || p.I % 32 != 0) return hipErrorInvalidValue;
     const int64_t grid = (int64_t)p.A * (p.I / 32);
     if (grid == 0) return hipSuccess;
+    const dim3 g((unsigned)grid), b(256 * (4 / kSmallBPW));
     switch (p.H / 512) {
-        case 4: hipLaunchKernelGGL(gemm1_small_kernel<4>, dim3((unsigned)grid), dim3(256), 0, s, p); break;
-        case 8: hipLaunchKernelGGL(gemm1_small_kernel<8>, dim3((unsigned)grid), dim3(256), 0, s, p); break;
-        case 12: hipLaunchKernelGGL(gemm1_small_kernel<12>, dim3((unsigned)grid), dim3(256), 0, s, p); break;
-        default: hipLaunchKernelGGL(gemm1_small_kernel<16>, dim3((unsigned)grid), dim3(256), 0, s, p); break;
+        case 4: hipLaunchKernelGGL((gemm1_small_kernel<4, kSmallBPW>), g, b, 0, s, p); break;
+        case 8: hipLaunchKernelGGL((gemm1_small_kernel<8, kSmallBPW>), g, b, 0, s, p); break;
+        case 12: hipLaunchKernelGGL((gemm1_small_kernel<12, kSmallBPW>), g, b, 0, s, p); break;
+        default: hipLaunchKernelGGL((gemm1_small_kernel<16, kSmallBPW>), g, b, 0, s, p); break;
     }
     return hipGetLastError();
 }
