@@ -547,14 +547,14 @@ hipError_t launch_one(const GemmParams& p, hipStream_t s) {
 // Tile shapes (rows x weight rows, waves): 0 = 256 x 256 x 8, 1 = 128 x 512 x
 // 8, 2 = 64 x 512 x 4, 3 = 32 x 512 x 4, 4 = 64 x 256 x 4 (bf16) or 32 x 256
 // x 4 (MXFP4), with four 128-byte stage buffers (three stages in flight)
-// where K allows it.
+// where K allows it, 5 = 128 x 256 x 8 (about 64 to 160 rows per expert).
 int gemm_tile_rows(int mode, int shape) {
-    static const int rows[5] = {256, 128, 64, 32, 64};
+    static const int rows[6] = {256, 128, 64, 32, 64, 128};
     return mode == 1 && shape == 4 ? 32 : rows[shape];
 }
 
 int gemm_tile_cols(int shape, int stage) {
-    const int bw = (shape == 0 || shape == 4) ? 256 : 512;
+    const int bw = (shape == 0 || shape == 4 || shape == 5) ? 256 : 512;
     return stage == 1 ? bw / 2 : bw;
 }
 
@@ -566,7 +566,7 @@ int gemm_tile_k_granule(int mode, int shape) {
 }
 
 // MXFP4 128 x 512 stages do not fit the LDS with their scales
-bool gemm_tile_supported(int mode, int shape) { return shape >= 0 && shape <= 4 && !(mode == 1 && shape == 1); }
+bool gemm_tile_supported(int mode, int shape) { return shape >= 0 && shape <= 5 && !(mode == 1 && shape == 1); }
 
 hipError_t launch_gemm_tile(int mode, int shape, int stage, const GemmParams& p, hipStream_t s) {
     if (!gemm_tile_supported(mode, shape) || p.N % gemm_tile_cols(shape, stage) != 0 ||
@@ -583,6 +583,7 @@ hipError_t launch_gemm_tile(int mode, int shape, int stage, const GemmParams& p,
             return stage == 1 ? launch_one<1, 1, 256, 256, 8>(p, s) : launch_one<1, 2, 256, 256, 8, 2, 2>(p, s);
         if (shape == 2) MOE_TILE(1, 64, 512, 4);
         if (shape == 3) MOE_TILE(1, 32, 512, 4);
+        if (shape == 5) MOE_TILE(1, 128, 256, 8);
         // four buffers need four 256-value stages per rotation
         if (p.K % (4 * 256) == 0) MOE_TILE4(1, 32, 256, 4);
         MOE_TILE(1, 32, 256, 4);
@@ -591,6 +592,7 @@ hipError_t launch_gemm_tile(int mode, int shape, int stage, const GemmParams& p,
     if (shape == 1) MOE_TILE(0, 128, 512, 8);
     if (shape == 2) MOE_TILE(0, 64, 512, 4);
     if (shape == 3) MOE_TILE(0, 32, 512, 4);
+    if (shape == 5) MOE_TILE(0, 128, 256, 8);
     MOE_TILE4(0, 64, 256, 4);
 #undef MOE_TILE
 #undef MOE_TILE4

@@ -182,6 +182,9 @@ const Cfg kConfigs[] = {
     {16, 1, 1, 4, 0, -1, 1, 1}, {16, 2, 1, 4, 0, -1, 1, 1}, {16, 4, 1, 4, 0, -1, 1, 1},
     // the same with gemm1 per slot (K split 4) and no align
     {16, 4, 1, 4, 0, -1, 1, 2},
+    // 128 x 256 tiles (about 64 to 160 rows per expert); gemm2 on them, on
+    // the MXFP4 multi-tile stream with 64-row blocks, or on 256 x 256 tiles
+    {128, 1, 1, 4, 6, -1}, {128, 1, 1, 4, 6, 31}, {128, 1, 1, 4, 6, 11},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 

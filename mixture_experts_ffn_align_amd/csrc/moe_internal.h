@@ -351,7 +351,7 @@ hipError_t launch_gemm(const GemmKernelId& id, const GemmParams& p, hipStream_t 
 
 // LDS-tiled grouped GEMM. Tile shapes (rows x weight rows per workgroup):
 // 0 = 256 x 256, 1 = 128 x 512 (bf16 only), 2 = 64 x 512, 3 = 32 x 512,
-// 4 = 64 x 256 (bf16) / 32 x 256 (MXFP4).
+// 4 = 64 x 256 (bf16) / 32 x 256 (MXFP4), 5 = 128 x 256.
 // Row blocks of gemm_tile_rows(mode, shape), gemm_tile_cols(shape, stage) output
 // columns per workgroup, K a multiple of gemm_tile_k_granule(mode, shape). Same
 // parameter block and epilogues as above.

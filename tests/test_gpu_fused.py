@@ -193,7 +193,7 @@ def test_tiled_and_streaming_gemms_same_bits_bf16(w235):
     gate, up = W.packed_views(inp["w13"], 1536)
     fam = _configs_by_family(lambda c: moe.moe_query_config(inp["x"], gate, up, inp["w2"], *gpu,
                                                             force_config=c))
-    assert len(fam[(3, 1, 1)]) == 5          # every tile shape
+    assert len(fam[(3, 1, 1)]) >= 6          # every tile shape (128 x 256 with two gemm2 choices)
     assert moe.moe_query_config(inp["x"], gate, up, inp["w2"], *gpu)["gemm1_kernel"] == 3
     out_s = _fused_bf16(inp, *gpu, force_config=fam[(1, 1, 1)][-1]).clone()
     for c in fam[(3, 1, 1)]:
@@ -218,7 +218,7 @@ def test_tiled_and_streaming_gemms_same_bits_mxfp4(fp4_weights, T):
                                     w2_scale=wsc, mode=moe.MODE_MXFP4, force_config=c)
 
     fam = _configs_by_family(query)
-    assert len(fam[(13, 1, 1)]) == 4          # every MXFP4 tile shape
+    assert len(fam[(13, 1, 1)]) >= 5          # every MXFP4 tile shape, and mixed gemm2 choices
     out_t = run(fam[(13, 1, 1)][0])
     for c in fam[(13, 1, 1)][1:] + fam[(11, 1, 1)]:
         assert torch.equal(run(c), out_t), f"config {c}"
