@@ -377,3 +377,33 @@ def test_bf16_per_slot_and_fused_gemm2_same_bits(w235, T):
     acc, _ = oracle_ffn_tokens(inp, oi, ow, toks)
     got = bf16_to_f64(out[torch.from_numpy(toks).to(DEV)])
     assert rel_l2(got, acc) <= 1e-2
+
+
+def test_few_token_kernels_reject_unsupported_shapes(w235):
+    """The per-slot gemm1 needs H a multiple of 2048 and the fused bf16 gemm2
+    I a multiple of 256 up to 1536; the configs that use them on the
+    Qwen3-235B shape, forced on the tiny layer (H=256, I=128), fail with
+    MOE_ERR_UNSUPPORTED, and the tiny layer's default never picks them."""
+    big = W.make_inputs(W.QWEN3_235B_BF16, 1, seed=9, device=DEV, weights=w235, routing="replay")
+    bg, bu = W.packed_views(big["w13"], 1536)
+    n = moe.moe_query_config(big["x"], bg, bu, big["w2"], big["topk_ids"], big["topk_weights"])["num_configs"]
+    few = []
+    for c in range(n):
+        try:
+            q = moe.moe_query_config(big["x"], bg, bu, big["w2"], big["topk_ids"], big["topk_weights"],
+                                     force_config=c)
+        except moe.MoEError:
+            continue
+        if q["gemm1_kernel"] == 7 or q["gemm2_kernel"] == 6:
+            few.append(c)
+    assert few
+    sh = W.TINY_BF16
+    inp = W.make_inputs(sh, 3, seed=9, device=DEV, routing="replay")
+    gate, up = W.packed_views(inp["w13"], sh.inter)
+    ids, w = inp["topk_ids"], inp["topk_weights"]
+    for c in few:
+        with pytest.raises(moe.MoEError) as ei:
+            moe.moe_fused_fwd(inp["x"], gate, up, inp["w2"], ids, w, force_config=c)
+        assert ei.value.status == -6
+    q = moe.moe_query_config(inp["x"], gate, up, inp["w2"], ids, w)
+    assert q["gemm1_kernel"] in (1, 3) and q["gemm2_kernel"] in (2, 4)
