@@ -785,10 +785,10 @@ __global__ __launch_bounds__(1024) void gemm2_combine_kernel(Gemm2CombineParams 
 namespace {
 
 // MXFP4 gemm1 for a few tokens, without the align. Workgroup (slot a, h
-// columns c0 .. c0 + 31): 4 waves take K = H in quarters, each chaining its
-// MFMAs over its quarter in ascending 128-steps from zero (weights first:
+// columns c0 .. c0 + 31): K = H is split in quarters, and each MFMA block
+// chains over its quarter in ascending 128-steps from zero (weights first:
 // gate rows c0 .. c0 + 31 in blocks 0, 1, up rows in blocks 2, 3); the
-// partial sums meet in LDS and are added in wave order ((p0 + p1) + p2) +
+// partial sums meet in LDS and are added in quarter order ((p0 + p1) + p2) +
 // p3, exactly as the register weight stream with a 4-way K split does. The
 // workgroup first quantises its token's activation row into LDS with the
 // quantisation kernel's arithmetic. So the h codes and scales are
@@ -798,9 +798,9 @@ namespace {
 //
 // With one to a few tokens the weight stream is all the traffic and each
 // wave has little else to do, so a wave issues the loads of up to 8 steps
-// (4 blocks x 16 bytes per lane and step, plus the scale bytes) before it
-// waits on any: 32 KB in flight per wave, which is what keeps HBM busy with
-// a few hundred waves on the chip.
+// (16 bytes per lane, step and block, plus one 16-byte scale window per 4
+// steps and block) before it waits on any: with two blocks per wave, 16 KB
+// in flight per wave.
 constexpr int kSmallMaxH = 8192;
 constexpr int kSmallChunk = 8;
 constexpr int kSmallBPW = 2;                    // measured: 2 beats 4 and 1 at T = 1-16
