@@ -683,10 +683,10 @@ namespace {
 // MXFP4 gemm2 and combine in one pass, for a few tokens: one workgroup per
 // token t and 16 output columns n0 .. n0 + 15, of W = min(ceil(k / S), 16)
 // waves. Wave w takes slots j = w, w + W, ... (S of them per round), issuing
-// the loads of a round before it waits on any; for a slot it multiplies the 16 w2 rows of
-// the slot's expert by the slot's h row with the same MFMA sequence as the
-// weight streams (weights as the first operand, K = 512 in four 128-steps
-// from zero) and leaves y rounded to bf16 in LDS. Then 16 lanes of wave 0
+// the loads of a round before it waits on any; for a slot it multiplies the
+// 16 w2 rows of the slot's expert by the slot's h row with the same MFMA
+// sequence as the weight streams (weights as the first operand, K = 512 in
+// four 128-steps from zero) and leaves y rounded to bf16 in LDS. Then 16 lanes of wave 0
 // add w_tj * y over j in slot order with fmaf, exactly as the separate
 // combine does; so the output is bit-identical to gemm2 followed by the
 // combine, without y in memory.
