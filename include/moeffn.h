@@ -178,6 +178,11 @@ int moe_quant_mxfp4(const moe_tensor_t *src, const moe_tensor_t *codes,
  * slot order from +0 with y widened exactly to fp32, then one round to bf16.
  * The tile configuration depends only on (mode, T, H, I, k) and the global
  * expert count, never on strides, so every layout runs the same arithmetic.
+ * For a few tokens a configuration may skip the align (gemm1 per slot, the
+ * expert read from topk_ids) and fold the combine into gemm2; the stages it
+ * skips then record nothing, and the results are bit-identical to the
+ * aligned path with the same K split. Such configurations never write
+ * y_rows: with y_rows the built-in choice falls back to the aligned path.
  */
 typedef struct {
     int32_t mode;
