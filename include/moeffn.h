@@ -180,8 +180,8 @@ int moe_quant_mxfp4(const moe_tensor_t *src, const moe_tensor_t *codes,
  * expert count, never on strides, so every layout runs the same arithmetic.
  * For a few tokens a configuration may skip the align (gemm1 per slot, the
  * expert read from topk_ids) and fold the combine into gemm2; the stages it
- * skips then record nothing, and the results are bit-identical to the
- * aligned path with the same K split. Such configurations never write
+ * skips are empty (their events are still recorded), and the results are
+ * bit-identical to the aligned path with the same K split. Such configurations never write
  * y_rows: with y_rows the built-in choice falls back to the aligned path.
  */
 typedef struct {
