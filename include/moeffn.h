@@ -74,7 +74,7 @@ typedef enum {
     MOE_ERR_DTYPE = -3,       /* wrong element type for this argument */
     MOE_ERR_LAYOUT = -4,      /* strides or alignment the kernels cannot honour */
     MOE_ERR_WORKSPACE = -5,   /* workspace NULL, misaligned or too small */
-    MOE_ERR_UNSUPPORTED = -6, /* sizes outside what this build handles */
+    MOE_ERR_UNSUPPORTED = -6, /* sizes outside what the library handles */
     MOE_ERR_HIP = -7,         /* a HIP launch failed */
     MOE_ERR_ARG = -8          /* any other invalid scalar argument */
 } moe_status_t;

@@ -431,7 +431,7 @@ int plan_fused(const moe_fused_args_t* a, Plan* pl) {
         if ((rc = check_shape(a->out, "out", {T, H}))) return rc;
     }
 
-    // sizes this build handles
+    // sizes the library handles
     if (E < 1 || E > 1024) return fail(MOE_ERR_UNSUPPORTED, "E = %lld outside [1, 1024]", (long long)E);
     if (E_cfg > (1 << 20)) return fail(MOE_ERR_UNSUPPORTED, "num_global_experts = %lld too large", (long long)E_cfg);
     if (k < 1 || k > 64) return fail(MOE_ERR_UNSUPPORTED, "k = %lld outside [1, 64]", (long long)k);
@@ -723,7 +723,7 @@ const char* moe_strerror(int status) {
         case MOE_ERR_DTYPE: return "wrong element type";
         case MOE_ERR_LAYOUT: return "unsupported strides or alignment";
         case MOE_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
-        case MOE_ERR_UNSUPPORTED: return "sizes outside what this build supports";
+        case MOE_ERR_UNSUPPORTED: return "sizes outside what the library supports";
         case MOE_ERR_HIP: return "HIP launch failed";
         case MOE_ERR_ARG: return "invalid argument";
         default: return "unknown status";
@@ -917,7 +917,7 @@ int moe_combine(const moe_tensor_t* y_rows, const moe_tensor_t* topk_ids, const 
     if ((rc = check_shape(*out, "out", {T, H}))) return rc;
     if (num_experts < 1) return fail(MOE_ERR_ARG, "num_experts = %d must be >= 1", num_experts);
     if (k < 1 || k > 64 || H < 4 || H % 4 != 0 || H > (1 << 24) || T > ((int64_t)1 << 24))
-        return fail(MOE_ERR_UNSUPPORTED, "k = %lld and H = %lld (a multiple of 4) outside what this build handles",
+        return fail(MOE_ERR_UNSUPPORTED, "k = %lld and H = %lld (a multiple of 4) outside what the library handles",
                     (long long)k, (long long)H);
     const moe_tensor_t& y = *y_rows;
     if (y.stride[2] != 1 || !aligned16(y.data) || (T > 1 && (y.stride[0] * 2) % 16 != 0) ||
