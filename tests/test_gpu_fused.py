@@ -407,3 +407,36 @@ def test_few_token_kernels_reject_unsupported_shapes(w235):
         assert ei.value.status == -6
     q = moe.moe_query_config(inp["x"], gate, up, inp["w2"], ids, w)
     assert q["gemm1_kernel"] in (1, 3) and q["gemm2_kernel"] in (2, 4)
+
+
+@pytest.mark.parametrize("k", [33, 40])
+def test_mxfp4_fused_gemm2_many_slots(k):
+    """More than 32 slots per token take the fused gemm2's multi-round
+    variant (16 waves, two slots each per round): bit-identical to gemm2 on
+    the multi-tile stream followed by the separate combine, with the same K
+    splits, including an invalid id and a zero weight."""
+    T, H, I, E = 5, 2048, 512, 48
+    g = torch.Generator(device=DEV).manual_seed(k)
+    w13 = (torch.randn(E, 2 * I, H, generator=g, device=DEV) * 0.02).to(torch.bfloat16)
+    w2 = (torch.randn(E, H, I, generator=g, device=DEV) * 0.02).to(torch.bfloat16)
+    gate, up = W.packed_views(w13, I)
+    (gq, gs), (uq, us), (wq, wsc) = moe.moe_quant_mxfp4(gate), moe.moe_quant_mxfp4(up), moe.moe_quant_mxfp4(w2)
+    x = torch.randn(T, H, generator=g, device=DEV).to(torch.bfloat16)
+    ids = torch.stack([torch.randperm(E, generator=g, device=DEV)[:k] for _ in range(T)]).to(torch.int32)
+    ids[1, 5] = -1
+    w = torch.rand(T, k, generator=g, device=DEV)
+    w[2, 7] = 0.0
+    kw = dict(gate_scale=gs, up_scale=us, w2_scale=wsc, mode=moe.MODE_MXFP4)
+    n = moe.moe_query_config(x, gq, uq, wq, ids, w, **kw)["num_configs"]
+    fused, plain = [], []
+    for c in range(n):
+        try:
+            q = moe.moe_query_config(x, gq, uq, wq, ids, w, force_config=c, **kw)
+        except moe.MoEError:
+            continue
+        if q["gemm1_kernel"] in (11, 17) and q["gemm1_split_k"] == 4 and q["gemm2_split_k"] == 1:
+            (fused if q["gemm2_kernel"] == 16 else plain).append(c)
+    assert fused and plain, (fused, plain)
+    ref = moe.moe_fused_fwd(x, gq, uq, wq, ids, w, force_config=plain[0], **kw).clone()
+    for c in fused:
+        assert torch.equal(moe.moe_fused_fwd(x, gq, uq, wq, ids, w, force_config=c, **kw), ref), f"config {c}"
