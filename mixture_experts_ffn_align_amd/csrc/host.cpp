@@ -525,9 +525,12 @@ int plan_fused(const moe_fused_args_t* a, Plan* pl) {
                         ci);
         if (H % 16 != 0 || T > (1 << 20))
             return fail(MOE_ERR_UNSUPPORTED, "config %d: fused gemm2 + combine needs H %% 16 == 0, T <= 2^20", ci);
-        if (pl->small1 && (H % 2048 != 0 || H > 8192 || T * k > (1 << 16)))
+        // MXFP4 per slot: H = 8192 (two full 8-step chunks per wave) disagreed
+        // with the weight stream in testing and is not offered
+        if (pl->small1 && (H % 2048 != 0 || H > (fp4 ? 6144 : 8192) || T * k > (1 << 16)))
             return fail(MOE_ERR_UNSUPPORTED,
-                        "config %d: gemm1 per slot needs H %% 2048 == 0, H <= 8192 and T*k <= 65536", ci);
+                        "config %d: gemm1 per slot needs H %% 2048 == 0, H <= %d and T*k <= 65536", ci,
+                        fp4 ? 6144 : 8192);
         if (y_out) return fail(MOE_ERR_UNSUPPORTED, "config %d: fused gemm2 + combine writes out, not y_rows", ci);
         pl->ks[1] = pl->ks[0];   // no second layout
     } else if ((rc = resolve(c2, 2, &pl->ks[1]))) {

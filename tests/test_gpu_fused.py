@@ -440,3 +440,78 @@ def test_mxfp4_fused_gemm2_many_slots(k):
     ref = moe.moe_fused_fwd(x, gq, uq, wq, ids, w, force_config=plain[0], **kw).clone()
     for c in fused:
         assert torch.equal(moe.moe_fused_fwd(x, gq, uq, wq, ids, w, force_config=c, **kw), ref), f"config {c}"
+
+
+def _few_token_same_bits(mode, H, I, E, k, T, seed):
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    w13 = (torch.randn(E, 2 * I, H, generator=g, device=DEV) * 0.02).to(torch.bfloat16)
+    w2 = (torch.randn(E, H, I, generator=g, device=DEV) * 0.02).to(torch.bfloat16)
+    gate, up = W.packed_views(w13, I)
+    kw = {}
+    if mode == moe.MODE_MXFP4:
+        (gate, gs), (up, us), (w2, wsc) = moe.moe_quant_mxfp4(gate), moe.moe_quant_mxfp4(up), moe.moe_quant_mxfp4(w2)
+        kw = dict(gate_scale=gs, up_scale=us, w2_scale=wsc, mode=mode)
+    x = torch.randn(T, H, generator=g, device=DEV).to(torch.bfloat16)
+    ids = torch.stack([torch.randperm(E, generator=g, device=DEV)[:k] for _ in range(T)]).to(torch.int32)
+    w = torch.rand(T, k, generator=g, device=DEV)
+    per_slot, fused_only, plain = (7, 6, 4) if mode == moe.MODE_BF16 else (17, 16, 1)
+    n = moe.moe_query_config(x, gate, up, w2, ids, w, **kw)["num_configs"]
+    want = {}
+    for c in range(n):
+        try:
+            q = moe.moe_query_config(x, gate, up, w2, ids, w, force_config=c, **kw)
+        except moe.MoEError:
+            continue
+        if q["gemm1_split_k"] == 4 and q["gemm2_split_k"] == plain:
+            want.setdefault((q["gemm1_kernel"], q["gemm2_kernel"]), []).append(c)
+    keys = sorted(want)
+    assert any(key[0] == per_slot for key in keys) and any(key[1] == fused_only for key in keys), keys
+    # the weight streams with the same split as reference where K allows
+    # that split; else the per-slot kernels against gemm1 on the stream
+    stream = [key for key in keys if key[0] != per_slot and key[1] != fused_only] or \
+        [key for key in keys if key[0] != per_slot]
+    assert stream, keys
+    ref = moe.moe_fused_fwd(x, gate, up, w2, ids, w, force_config=want[stream[0]][0], **kw).clone()
+    for key in keys:
+        for c in want[key]:
+            assert torch.equal(moe.moe_fused_fwd(x, gate, up, w2, ids, w, force_config=c, **kw), ref), (key, c)
+
+
+@pytest.mark.parametrize("H,I,k", [(2048, 512, 6), (6144, 1024, 10), (8192, 768, 3)])
+def test_bf16_few_token_kernels_other_shapes(H, I, k):
+    """The bf16 per-slot gemm1 and fused gemm2 at other row lengths, widths
+    and slot counts (every template instance of the row length): the same
+    bits as the weight streams with a 4-way K split and the separate
+    combine."""
+    _few_token_same_bits(moe.MODE_BF16, H, I, 24, k, 3, seed=H + k)
+
+
+@pytest.mark.parametrize("H,k", [(2048, 10), (6144, 7), (4096, 11)])
+def test_mxfp4_few_token_kernels_other_shapes(H, k):
+    """The MXFP4 per-slot gemm1 at other row lengths (every template instance
+    the library offers) and slot counts: the same bits as the weight stream
+    with a 4-way K split."""
+    _few_token_same_bits(moe.MODE_MXFP4, H, 512, 24, k, 3, seed=H + k)
+
+
+def test_mxfp4_per_slot_not_offered_at_h8192():
+    """MXFP4 gemm1 per slot with H = 8192 disagreed with the weight stream
+    in testing; the library rejects it (MOE_ERR_UNSUPPORTED)."""
+    H, I, E, k, T = 8192, 512, 16, 4, 2
+    g = torch.Generator(device=DEV).manual_seed(3)
+    w13 = (torch.randn(E, 2 * I, H, generator=g, device=DEV) * 0.02).to(torch.bfloat16)
+    w2 = (torch.randn(E, H, I, generator=g, device=DEV) * 0.02).to(torch.bfloat16)
+    gate, up = W.packed_views(w13, I)
+    (gq, gs), (uq, us), (wq, wsc) = moe.moe_quant_mxfp4(gate), moe.moe_quant_mxfp4(up), moe.moe_quant_mxfp4(w2)
+    x = torch.randn(T, H, generator=g, device=DEV).to(torch.bfloat16)
+    ids = torch.stack([torch.randperm(E, generator=g, device=DEV)[:k] for _ in range(T)]).to(torch.int32)
+    w = torch.rand(T, k, generator=g, device=DEV)
+    kw = dict(gate_scale=gs, up_scale=us, w2_scale=wsc, mode=moe.MODE_MXFP4)
+    n = moe.moe_query_config(x, gq, uq, wq, ids, w, **kw)["num_configs"]
+    for c in range(n):
+        try:
+            q = moe.moe_query_config(x, gq, uq, wq, ids, w, force_config=c, **kw)
+        except moe.MoEError as err:
+            assert err.status == -6
+            continue
+        assert q["gemm1_kernel"] != 17, c
