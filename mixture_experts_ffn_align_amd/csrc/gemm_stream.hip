@@ -239,8 +239,8 @@ void gemm_stream(GemmParams p) {
     // window once the weight stream has evicted it. Where the run fits
     // (K <= 4096), each wave loads its 64 rows' runs once, straight into
     // LDS, and the windows are read from there.
-    // (the host gives MXFP4 a 4-step ring only for a K share of 512, 1024,
-    // 2048 or 4096: the run of every row fits and lpr divides 64)
+    // (the host gives MXFP4 a 4-step ring only where the run of every row
+    // fits SC_ROW_MAX and lpr divides 64)
     const int sc_bpr = kw / 32;                          // scale bytes per row of the K share
     uint8_t* const sc_wave = sc_lds + w * 64 * SC_ROW_MAX;
     if constexpr (SC_LDS) {
@@ -659,16 +659,16 @@ GemmFn lookup(const GemmKernelId& id) {
 
 }  // namespace
 
-int gemm_ring_steps(int mode, int bm, int nb, int64_t k_per_wave) {
+int gemm_ring_steps(int mode, int bm, int nb, int wk, int64_t k_per_wave) {
     if (mode == 0 && nb == 2) return 8;
     if (bm >= 128) return 2;
     if (mode == 0) return 4;
     // a 4-step MXFP4 ring stages the share's weight scales in LDS: each row's
-    // run of k_per_wave / 32 bytes goes in 16-byte pieces, k_per_wave / 512
-    // lanes per row, and the wave's 64 lanes must cover whole rows (K share
-    // 512, 1024, 2048 or 4096)
+    // run of k_per_wave / 32 bytes must fit the 128 / wk bytes per row the
+    // kernel reserves, and goes in 16-byte pieces, k_per_wave / 512 lanes per
+    // row, so the wave's 64 lanes must cover whole rows
     const int64_t lanes_per_row = k_per_wave / 512;
-    return k_per_wave % 512 == 0 && k_per_wave <= 4096 && 64 % lanes_per_row == 0 ? 4 : 2;
+    return k_per_wave % 512 == 0 && k_per_wave / 32 <= 128 / wk && 64 % lanes_per_row == 0 ? 4 : 2;
 }
 
 int gemm_k_granule(const GemmKernelId& id) {
@@ -1184,16 +1184,15 @@ __global__ __launch_bounds__(1024) void gemm2_combine_bf16_kernel(Gemm2CombinePa
 }  // namespace
 
 hipError_t launch_gemm1_small(const Gemm1SmallParams& p, hipStream_t s) {
-    // H = 8192 (two full chunks per wave) disagreed with the weight stream in
-    // testing and is not offered
-    if (p.H % 2048 != 0 || p.H > 6144 || p.I % 32 != 0) return hipErrorInvalidValue;
+    if (p.H % 2048 != 0 || p.H > kSmallMaxH || p.I % 32 != 0) return hipErrorInvalidValue;
     const int64_t grid = (int64_t)p.A * (p.I / 32);
     if (grid == 0) return hipSuccess;
     const dim3 g((unsigned)grid), b(256 * (4 / kSmallBPW));
     switch (p.H / 512) {
         case 4: hipLaunchKernelGGL((gemm1_small_kernel<4, kSmallBPW>), g, b, 0, s, p); break;
         case 8: hipLaunchKernelGGL((gemm1_small_kernel<8, kSmallBPW>), g, b, 0, s, p); break;
-        default: hipLaunchKernelGGL((gemm1_small_kernel<12, kSmallBPW>), g, b, 0, s, p); break;
+        case 12: hipLaunchKernelGGL((gemm1_small_kernel<12, kSmallBPW>), g, b, 0, s, p); break;
+        default: hipLaunchKernelGGL((gemm1_small_kernel<16, kSmallBPW>), g, b, 0, s, p); break;
     }
     return hipGetLastError();
 }

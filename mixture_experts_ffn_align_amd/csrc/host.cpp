@@ -507,7 +507,7 @@ int plan_fused(const moe_fused_args_t* a, Plan* pl) {
         if (K % gran != 0)
             return fail(MOE_ERR_UNSUPPORTED, "config %d: gemm%d K = %lld must be a multiple of %d", ci, stage,
                         (long long)K, gran);
-        GemmKernelId id{md, stage, c.bm, w, gemm_ring_steps(a->mode, c.bm, c.nb, K / w), c.nb, ks->nt};
+        GemmKernelId id{md, stage, c.bm, w, gemm_ring_steps(a->mode, c.bm, c.nb, w, K / w), c.nb, ks->nt};
         if (ks->nt != 1 && K != 4 * 128)
             return fail(MOE_ERR_UNSUPPORTED, "config %d: multi-tile gemm2 needs K = 512", ci);
         if (!gemm_supported(id)) return fail(MOE_ERR_UNSUPPORTED, "config %d not built", ci);
@@ -525,12 +525,9 @@ int plan_fused(const moe_fused_args_t* a, Plan* pl) {
                         ci);
         if (H % 16 != 0 || T > (1 << 20))
             return fail(MOE_ERR_UNSUPPORTED, "config %d: fused gemm2 + combine needs H %% 16 == 0, T <= 2^20", ci);
-        // MXFP4 per slot: H = 8192 (two full 8-step chunks per wave) disagreed
-        // with the weight stream in testing and is not offered
-        if (pl->small1 && (H % 2048 != 0 || H > (fp4 ? 6144 : 8192) || T * k > (1 << 16)))
+        if (pl->small1 && (H % 2048 != 0 || H > 8192 || T * k > (1 << 16)))
             return fail(MOE_ERR_UNSUPPORTED,
-                        "config %d: gemm1 per slot needs H %% 2048 == 0, H <= %d and T*k <= 65536", ci,
-                        fp4 ? 6144 : 8192);
+                        "config %d: gemm1 per slot needs H %% 2048 == 0, H <= 8192 and T*k <= 65536", ci);
         if (y_out) return fail(MOE_ERR_UNSUPPORTED, "config %d: fused gemm2 + combine writes out, not y_rows", ci);
         pl->ks[1] = pl->ks[0];   // no second layout
     } else if ((rc = resolve(c2, 2, &pl->ks[1]))) {
@@ -1088,7 +1085,7 @@ int moe_fused_fwd(const moe_fused_args_t* args, void* ws, size_t ws_bytes, moe_s
         const KSpec& k = pl.ks[g];
         if (k.tile) return launch_gemm_tile(fp4 ? 1 : 0, k.tile - 1, g + 1, gp, s);
         GemmKernelId id{fp4 ? 1 : 0, g + 1, k.bm, k.wk,
-                        gemm_ring_steps(pl.mode, k.bm, k.nb, (g == 0 ? pl.H : pl.I) / k.wk), k.nb, k.nt};
+                        gemm_ring_steps(pl.mode, k.bm, k.nb, k.wk, (g == 0 ? pl.H : pl.I) / k.wk), k.nb, k.nt};
         return launch_gemm(id, gp, s);
     };
     // stage 2: gemm1 + SiLU(gate) * up

@@ -341,7 +341,7 @@ struct GemmKernelId {
     int nt = 1;  // MXFP4 gemm2 with K = 512: 256-column tiles per workgroup (1, 2, 4, 8)
 };
 // Ring depth for a wave's share of K.
-int gemm_ring_steps(int mode, int bm, int nb, int64_t k_per_wave);
+int gemm_ring_steps(int mode, int bm, int nb, int wk, int64_t k_per_wave);
 // Output columns one workgroup covers.
 int gemm_tile_n(const GemmKernelId& id);
 // Smallest unit of K a wave's share must be a multiple of.
