@@ -493,3 +493,33 @@ def test_mxfp4_few_token_kernels_other_shapes(H, k):
     (at H = 8192 this caught the stream's scale staging overflowing its LDS
     rows)."""
     _few_token_same_bits(moe.MODE_MXFP4, H, 512, 24, k, 3, seed=H + k)
+
+
+def test_mxfp4_long_rows_every_config_against_oracle():
+    """MXFP4 with H = 8192 (scale runs longer than a K split's LDS share):
+    every configuration the library accepts matches the oracle."""
+    import dataclasses
+    sh = dataclasses.replace(W.QWEN35_397B_TP2_FP4_512, name="mxfp4_h8192_i512_e16_k4", hidden=8192, experts=16,
+                             top_k=4, routed_experts=16, routed_k=4)
+    g = torch.Generator(device=DEV).manual_seed(3)
+    w13, w2 = W.draw_weights(sh, g, DEV)
+    (gq, gs), (uq, us), (wq, wsc) = quantise_weights_gpu(w13, w2, sh.inter)
+    T = 3
+    inp = W.make_inputs(sh, T, seed=4, device=DEV, weights=(w13, w2), routing="replay")
+    ids, w = inp["topk_ids"], inp["topk_weights"]
+    kw = dict(gate_scale=gs, up_scale=us, w2_scale=wsc, mode=moe.MODE_MXFP4)
+    oi, ow = np_(ids), np_(w)
+    toks = np.arange(T)
+    used = sorted({int(e) for e in oi.ravel()})
+    acc, _ = oracle_ffn_tokens(inp, oi, ow, toks, mx=oracle_quant_experts(w13, w2, sh.inter, used))
+    n = moe.moe_query_config(inp["x"], gq, uq, wq, ids, w, **kw)["num_configs"]
+    ran = 0
+    for c in range(n):
+        try:
+            moe.moe_query_config(inp["x"], gq, uq, wq, ids, w, force_config=c, **kw)
+        except moe.MoEError:
+            continue
+        got = bf16_to_f64(moe.moe_fused_fwd(inp["x"], gq, uq, wq, ids, w, force_config=c, **kw))
+        assert rel_l2(got, acc) <= FP4_TOL and err_ratio(got, acc) <= FP4_ERR_RATIO, c
+        ran += 1
+    assert ran >= 30
