@@ -91,6 +91,8 @@ def lib():
         L.orc_ffn_bwd.argtypes = [ctypes.POINTER(_FfnArgs), vp, i64, i64, vp, i64, vp, vp, vp, vp, i64,
                                   vp, vp, vp]
         L.orc_ffn_bwd.restype = i32
+        L.orc_route_exp.argtypes = [ctypes.c_double]
+        L.orc_route_exp.restype = ctypes.c_double
         L.orc_e2m1_value.argtypes = [i32]
         L.orc_e2m1_value.restype = ctypes.c_double
         L.orc_e8m0_value.argtypes = [i32]
@@ -113,10 +115,17 @@ def _ptr(a: Optional[np.ndarray]) -> Optional[int]:
 
 # ------------------------------------------------------------------ route
 
+def route_exp(d: float) -> float:
+    """The router's stated double-precision exp(d), d <= 0 (orc_route_exp)."""
+    return float(lib().orc_route_exp(float(d)))
+
+
 def route(logits: np.ndarray, k: int, renorm: bool = True, shared_id: int = -1,
           shared_w: float = 1.0) -> tuple[np.ndarray, np.ndarray]:
-    """Softmax over each row of ``logits`` (fp32 [T, E]), top-k with ties to the
-    lower index, optional renormalisation; plus an appended shared expert."""
+    """Top-k of the softmax over each row of ``logits`` (fp32 [T, E]): the k
+    largest logits with ties to the lower index, weights exp(l_j - l_max)
+    (the stated exp) over their slot-order sum (renorm) or over the sum over
+    all experts, rounded once to fp32; plus an appended shared expert."""
     assert logits.dtype == np.float32 and logits.ndim == 2
     T, E = logits.shape
     kt = k + (1 if shared_id >= 0 else 0)

@@ -8,7 +8,8 @@
  * slowly and in double precision.
  *
  * What is computed, and where it is defined:
- *   route  - softmax over the router logits, top-k, renormalise
+ *   route  - softmax over the router logits, top-k, renormalise, with the
+ *            weights defined through one stated double-precision exp
  *            (ROCm/aiter PR "TP2 MXFP4 fused-MoE configs for Qwen3.5-397B",
  *            Summary: the unfused 512/10 and shared-expert-fused 513/11
  *            routing conventions; the tiny workload spells out
@@ -195,11 +196,57 @@ static void orc_mxfp4_dequant_row(const uint8_t *codes, const uint8_t *scales, i
 /* --------------------------------------------------------------- route */
 
 /*
- * For each token: p = softmax(logits[t, :]) in double; the k largest p are
- * picked one after another (equal p: lower index first); with renorm the
- * picked p are divided by their sum (summed in slot order); the results are
- * rounded to fp32. With shared_id >= 0 the slot after the k routed ones gets
- * (shared_id, shared_w).
+ * exp(d) in double precision for d <= 0, the exponential the router weights
+ * are defined with. The pages fix no exponential, yet routing must match bit
+ * for bit, so the weights are defined through one stated sequence of IEEE
+ * double operations that any implementation can follow step by step:
+ *   d < -708 (or -inf): 0 (every such term is far below what an fp32 weight
+ *     can hold next to the leading term 1);
+ *   n = rint(d * RN(1/ln 2))                  (ties to even)
+ *   r = fma(-n, LN2_HI, d); r = fma(-n, LN2_LO, r)
+ *       with LN2_HI = RN(ln 2) and LN2_LO = RN(ln 2 - LN2_HI)
+ *   p = 1/13!; p = fma(p, r, 1/i!) for i = 12 down to 0
+ *       (Taylor coefficients 1/i!, each the double nearest to it)
+ *   result = p * 2^n                          (exact: n >= -1021)
+ * Cody-Waite reduction to |r| <= ln2/2 and the degree-13 Taylor polynomial
+ * leave a truncation error below 1e-17 relative; the whole sequence is
+ * within a few units in the last place of exp(d), which the tests check
+ * against math.exp and exact decimal arithmetic.
+ */
+double orc_route_exp(double d)
+{
+    static const double inv_ln2 = 0x1.71547652b82fep+0;
+    static const double ln2_hi = 0x1.62e42fefa39efp-1;
+    static const double ln2_lo = 0x1.abc9e3b39803fp-56;
+    if (!(d >= -708.0))
+        return 0.0;
+    double n = rint(d * inv_ln2);
+    double r = fma(-n, ln2_hi, d);
+    r = fma(-n, ln2_lo, r);
+    double fact = 1.0;
+    for (int i = 2; i <= 13; ++i)
+        fact *= (double)i;               /* 13! = 6227020800, exact */
+    double p = 1.0 / fact;
+    for (int i = 12; i >= 0; --i) {
+        fact /= (double)(i + 1);         /* i!, exact */
+        p = fma(p, r, 1.0 / fact);
+    }
+    return ldexp(p, (int)n);
+}
+
+/*
+ * For each token: the k largest logits, one after another, equal logits
+ * going to the lower expert index (softmax is strictly increasing, so these
+ * are the k largest softmax probabilities; selecting on the logits keeps
+ * rounding from creating ties). With m the first pick's logit and
+ * e_x = orc_route_exp(l_x - m) in double:
+ *   renorm: w_j = fp32(e_j / S), S = ((e_0 + e_1) + ...) + e_{k-1} over the
+ *           picks in slot order (the renormalised top-k softmax: the
+ *           partition function cancels);
+ *   else:   w_j = fp32(e_j / Z), Z = the sum of e_x over all experts in
+ *           ascending index order (the plain softmax probability).
+ * The double quotient is rounded once to fp32 (nearest, ties to even). With
+ * shared_id >= 0 the slot after the k routed ones gets (shared_id, shared_w).
  */
 int orc_route(const float *logits, int64_t T, int64_t E, int64_t ls_t, int64_t ls_e, int k,
               int renorm, int shared_id, float shared_w,
@@ -207,52 +254,47 @@ int orc_route(const float *logits, int64_t T, int64_t E, int64_t ls_t, int64_t l
 {
     if (k <= 0 || k > E)
         return ORC_EARG;
-    double *p = (double *)malloc(sizeof(double) * (size_t)E);
     char *taken = (char *)malloc((size_t)E);
-    double *pk = (double *)malloc(sizeof(double) * (size_t)k);
-    if (!p || !taken || !pk) {
-        free(p); free(taken); free(pk);
+    double *ek = (double *)malloc(sizeof(double) * (size_t)k);
+    if (!taken || !ek) {
+        free(taken); free(ek);
         return ORC_EARG;
     }
     for (int64_t t = 0; t < T; ++t) {
         const float *row = logits + t * ls_t;
-        double m = -INFINITY;
-        for (int64_t e = 0; e < E; ++e)
-            if ((double)row[e * ls_e] > m)
-                m = (double)row[e * ls_e];
-        double z = 0.0;
-        for (int64_t e = 0; e < E; ++e) {
-            p[e] = exp((double)row[e * ls_e] - m);
-            z += p[e];
-        }
-        for (int64_t e = 0; e < E; ++e)
-            p[e] /= z;
         memset(taken, 0, (size_t)E);
+        double m = 0.0;
         for (int j = 0; j < k; ++j) {
             int64_t best = -1;
             for (int64_t e = 0; e < E; ++e) {
                 if (taken[e])
                     continue;
-                if (best < 0 || p[e] > p[best])
+                if (best < 0 || row[e * ls_e] > row[best * ls_e])
                     best = e;
             }
             taken[best] = 1;
             ids[t * is_t + j * is_j] = (int32_t)best;
-            pk[j] = p[best];
+            if (j == 0)
+                m = (double)row[best * ls_e];
+            ek[j] = orc_route_exp((double)row[best * ls_e] - m);
         }
         double s = 0.0;
+        if (renorm) {
+            for (int j = 0; j < k; ++j)
+                s += ek[j];
+        } else {
+            for (int64_t e = 0; e < E; ++e)
+                s += orc_route_exp((double)row[e * ls_e] - m);
+        }
         for (int j = 0; j < k; ++j)
-            s += pk[j];
-        for (int j = 0; j < k; ++j)
-            w[t * ws_t + j * ws_j] = (float)(renorm ? pk[j] / s : pk[j]);
+            w[t * ws_t + j * ws_j] = (float)(ek[j] / s);
         if (shared_id >= 0) {
             ids[t * is_t + k * is_j] = shared_id;
             w[t * ws_t + k * ws_j] = shared_w;
         }
     }
-    free(p);
     free(taken);
-    free(pk);
+    free(ek);
     return ORC_OK;
 }
 
