@@ -52,6 +52,27 @@ def sample_tokens(T: int, n: int = 8, seed: int = 0) -> np.ndarray:
     return np.array(sorted(pick), dtype=np.int64)
 
 
+def tail_tokens(ids: np.ndarray, num_experts: int, n: int, seed: int = 0) -> np.ndarray:
+    """At least ``n`` tokens (all of them if T <= n) that include, for every
+    expert with assignments, the token of its last assignment in flat order
+    t*k + j. The align puts an expert's assignments in ascending flat order,
+    so that token sits in the expert's last (ragged, sentinel-padded) sorted
+    block whatever block_m is; the rest are the first, middle and last
+    tokens and seeded random ones."""
+    T, k = ids.shape
+    if T <= n:
+        return np.arange(T, dtype=np.int64)
+    flat = np.ascontiguousarray(ids).reshape(-1).astype(np.int64)
+    ok = (flat >= 0) & (flat < num_experts)
+    last = np.full(num_experts, -1, dtype=np.int64)
+    np.maximum.at(last, flat[ok], np.arange(flat.size, dtype=np.int64)[ok])
+    pick = set(int(a) // k for a in last[last >= 0]) | {0, T // 2, T - 1}
+    rng = np.random.default_rng(seed + T)
+    while len(pick) < n:
+        pick.add(int(rng.integers(0, T)))
+    return np.array(sorted(pick), dtype=np.int64)
+
+
 def route_both(inp: dict):
     """(gpu ids, gpu w) from the HIP router; (oracle ids, oracle w) from the oracle."""
     sh: W.MoEShape = inp["shape"]
@@ -67,8 +88,8 @@ def assert_routing_equal(g, o):
     oi, ow = o
     assert gi.shape == oi.shape
     assert (gi == oi).all(), "router ids differ from the oracle"
-    d = np.abs(gw.view(np.int32).astype(np.int64) - ow.view(np.int32).astype(np.int64))
-    assert d.max() <= 1, f"router weights differ by {d.max()} ulp"
+    bad = int((gw.view(np.int32) != ow.view(np.int32)).sum())
+    assert bad == 0, f"{bad} router weights differ from the oracle's bits"
 
 
 def quantise_weights_gpu(w13: torch.Tensor, w2: torch.Tensor, inter: int):

@@ -1,5 +1,5 @@
 """GPU parity of the single steps against the oracle, bit-exact:
-router ids (weights within 1 ulp), align, and MXFP4 quantisation."""
+router ids and weights, align, and MXFP4 quantisation."""
 import numpy as np
 import pytest
 import torch
@@ -29,8 +29,6 @@ def test_router_matches_oracle(shape, T, kind):
     inp = {"shape": shape, "logits": logits}
     gpu, orc = route_both(inp)
     assert_routing_equal(gpu, orc)
-    exact = (np_(gpu[1]) == orc[1]).mean()
-    assert exact > 0.999
 
 
 def test_router_strided_logits_and_outputs():
@@ -43,8 +41,8 @@ def test_router_strided_logits_and_outputs():
     oi, ow = oracle.route(np_(logits.contiguous()), 8)
     assert (np_(ids_all[:, 1, :]) == oi).all()
     assert (np_(ids_all[:, 0, :]) == -7).all() and (np_(ids_all[:, 2, :]) == -7).all()
-    d = np.abs(np_(w_all[:, 1, :]).view(np.int32).astype(np.int64) - ow.view(np.int32))
-    assert d.max() <= 1
+    assert (np_(w_all[:, 1, :]).view(np.int32) == ow.view(np.int32)).all()
+    assert np.isnan(np_(w_all[:, 0, :])).all() and np.isnan(np_(w_all[:, 2, :])).all()
 
 
 def test_router_without_renorm():
@@ -53,8 +51,21 @@ def test_router_without_renorm():
     gi, gw = moe.moe_topk_softmax(logits, 6, renorm=False)
     oi, ow = oracle.route(np_(logits), 6, renorm=False)
     assert (np_(gi) == oi).all()
-    d = np.abs(np_(gw).view(np.int32).astype(np.int64) - ow.view(np.int32))
-    assert d.max() <= 1
+    assert (np_(gw).view(np.int32) == ow.view(np.int32)).all()
+
+
+@pytest.mark.parametrize("E,k,renorm", [(512, 10, True), (512, 10, False), (1000, 32, True), (130, 3, False)])
+def test_router_bits_wide_logits(E, k, renorm):
+    """Bit-exact weights over logits of very different spreads (N(0,1) to
+    N(0,30), so many terms land near the exp cut-off), non-power-of-two E."""
+    g = torch.Generator(device=DEV).manual_seed(E + k)
+    T = 600
+    scale = torch.tensor([1.0, 5.0, 30.0], device=DEV).repeat(T // 3 + 1)[:T, None]
+    logits = torch.randn(T, E, generator=g, device=DEV) * scale
+    gi, gw = moe.moe_topk_softmax(logits, k, renorm=renorm)
+    oi, ow = oracle.route(np_(logits), k, renorm=renorm)
+    assert (np_(gi) == oi).all()
+    assert (np_(gw).view(np.int32) == ow.view(np.int32)).all()
 
 
 def _align_case(ids: torch.Tensor, E: int, bm: int):
