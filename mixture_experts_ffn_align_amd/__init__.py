@@ -162,13 +162,38 @@ def moe_query_config(x, gate, up, w2, topk_ids, topk_weights, out=None, **kw) ->
 _ws_cache: dict = {}
 
 
-def _workspace(nbytes: int, device) -> torch.Tensor:
-    key = (str(device),)
-    ws = _ws_cache.get(key)
+def _ws_get(cache: dict, key, nbytes: int, alloc):
+    """The cached buffer for ``key`` if it holds ``nbytes``, else a new one
+    from ``alloc`` that replaces it."""
+    ws = cache.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
-        _ws_cache[key] = ws
+        ws = alloc(max(nbytes, 256))
+        cache[key] = ws
     return ws
+
+
+def _workspace(nbytes: int, device, stream: int) -> torch.Tensor:
+    """The binding's default workspace for calls that pass none: one buffer
+    per (device, stream), since calls that share a workspace must be ordered
+    on one stream. A new buffer is marked as used on its stream
+    (record_stream), so when a larger one replaces it the caching allocator
+    waits for that stream's queued kernels before handing the memory out
+    again. During graph capture the caller must pass a workspace of its own:
+    a replayed graph would keep writing into a buffer this cache may drop."""
+    if torch.cuda.is_current_stream_capturing():
+        raise MoEError(-5, "pass workspace= explicitly when capturing a graph")
+    dev = torch.device(device)
+    if dev.index is None:
+        dev = torch.device(dev.type, torch.cuda.current_device())
+    st = int(stream)
+
+    def alloc(n):
+        ws = torch.empty(n, dtype=torch.uint8, device=dev)
+        use = torch.cuda.default_stream(dev) if st == 0 else torch.cuda.ExternalStream(st, device=dev)
+        if use.cuda_stream != torch.cuda.current_stream(dev).cuda_stream:
+            ws.record_stream(use)
+        return ws
+    return _ws_get(_ws_cache, (dev.type, dev.index, st), nbytes, alloc)
 
 
 def moe_fused_fwd(x: torch.Tensor, gate: torch.Tensor, up: torch.Tensor, w2: torch.Tensor,
@@ -198,10 +223,11 @@ def moe_fused_fwd(x: torch.Tensor, gate: torch.Tensor, up: torch.Tensor, w2: tor
                           num_global_experts, y_rows, norm_weight, norm_eps)
     n = ctypes.c_size_t(0)
     _abi.check(L.moe_fused_workspace_size(ctypes.byref(a), ctypes.byref(n)))
+    st = _stream(stream)
     if workspace is None:
-        workspace = _workspace(n.value, x.device)
+        workspace = _workspace(n.value, x.device, st)
     _abi.check(L.moe_fused_fwd(ctypes.byref(a), workspace.data_ptr() if workspace.numel() else 0,
-                               workspace.numel(), _stream(stream)))
+                               workspace.numel(), st))
     del keep
     return y_rows if y_rows is not None else out
 
@@ -265,10 +291,11 @@ def moe_fused_bwd(x, gate, up, w2, topk_ids, topk_weights, dout, *, dx=None, dga
                   expert_offset, num_global_experts, accumulate)
     n = ctypes.c_size_t(0)
     _abi.check(L.moe_fused_bwd_workspace_size(ctypes.byref(b), ctypes.byref(n)))
+    st = _stream(stream)
     if workspace is None:
-        workspace = _workspace(n.value, dev)
+        workspace = _workspace(n.value, dev, st)
     _abi.check(L.moe_fused_bwd(ctypes.byref(b), workspace.data_ptr() if workspace.numel() else 0,
-                               workspace.numel(), _stream(stream)))
+                               workspace.numel(), st))
     return dx, dgate, dup, dw2, dtopk_weights
 
 

@@ -283,3 +283,24 @@ def test_backward_packed_dw13_halves_accepted():
     assert size(dw13[:, :I], dw13[:, I:]) == 0
     assert size(dw13[:, I:], dw13[:, :I]) == 0
     assert _abi.STATUS[size(dw13[:, :I], dw13[:, I - 8:2 * I - 8])] == "MOE_ERR_LAYOUT"
+
+
+def test_binding_workspace_cache_is_per_device_and_stream():
+    """The binding's default workspace: one buffer per (device, stream) key,
+    reused while large enough, replaced when a call needs more; other keys
+    untouched (calls on different streams never share a buffer)."""
+    from mixture_experts_ffn_align_amd import _ws_get
+    cache, made = {}, []
+
+    def alloc(n):
+        made.append(n)
+        return torch.empty(n, dtype=torch.uint8)
+    a = _ws_get(cache, ("cuda", 0, 111), 1000, alloc)
+    b = _ws_get(cache, ("cuda", 0, 222), 1000, alloc)
+    assert a.data_ptr() != b.data_ptr()
+    assert _ws_get(cache, ("cuda", 0, 111), 900, alloc) is a
+    c = _ws_get(cache, ("cuda", 0, 111), 5000, alloc)
+    assert c is not a and c.numel() == 5000 and cache[("cuda", 0, 111)] is c
+    assert cache[("cuda", 0, 222)] is b
+    d = _ws_get(cache, ("cuda", 1, 111), 10, alloc)
+    assert d.numel() == 256 and made == [1000, 1000, 5000, 256]
