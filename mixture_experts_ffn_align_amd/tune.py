@@ -9,19 +9,27 @@ same workflow for this library:
 1. ``tune`` — for one layer shape and each token bucket T: draw the seeded
    synthetic inputs of that layer (workloads.py), route them, run every
    config index the library accepts for those sizes, gate each one's output
-   against the built-in choice (errRatio and rel-L2 bounds of the layer's
-   precision, finite values), time the survivors as one call captured in a
-   HIP graph and replayed back to back, and record the fastest in a CSV.
-   For an expert-parallel shard (``ep`` > 1: experts [0, E/ep), global ids,
-   per-slot rows out) only configs that split K like the unsharded call's
-   choice are candidates, so shard rows stay bit-identical to it.
+   against an independent reference of sampled tokens that the caller
+   supplies (the pages' tuner checks every tuned kernel against a reference
+   within errRatio 0.05, aiter PR, Details and Accuracy; here the rel-L2 and
+   errRatio bounds of the layer's precision, and finite values), time the
+   survivors as one call captured in a HIP graph and replayed back to back,
+   and record the fastest in a CSV. Configs that split K like the built-in
+   choice must also give its bits exactly (block_m and the kernel family
+   never change a sum). For an expert-parallel shard (``ep`` > 1: experts
+   [0, E/ep), global ids, per-slot rows out) only configs that split K like
+   the unsharded call's choice are candidates, so shard rows stay
+   bit-identical to it.
 2. ``write_inc`` — merge CSVs into ``csrc/tuned_configs.inc``, the static
    table compiled into libmoeffn.so; ``moe_fused_fwd`` looks up the exact
    (mode, H, I, E, E_local, k, bucket) there before its built-in rules.
 
+The reference comes from outside the library (the test suite's tuning driver
+passes the CPU oracle), so this module itself only times and compares.
+
 Usage (on a GPU, from the repository root):
-    python -m mixture_experts_ffn_align_amd.tune --layer qwen3_235b_bf16 \\
-        --buckets 1,2,4,...,32768 --out mixture_experts_ffn_align_amd/tuned/qwen3_235b_bf16.csv
+    python tests/tune_gated.py --layer qwen3_235b_bf16 --buckets 1,2,4,...,32768 \\
+        --out mixture_experts_ffn_align_amd/tuned/qwen3_235b_bf16.csv
     python -m mixture_experts_ffn_align_amd.tune --write-inc mixture_experts_ffn_align_amd/tuned/*.csv
 then rebuild (mixture_experts_ffn_align_amd/build.py).
 """
@@ -38,7 +46,7 @@ from typing import Optional
 HERE = os.path.dirname(os.path.abspath(__file__))
 INC = os.path.join(HERE, "csrc", "tuned_configs.inc")
 FIELDS = ["layer", "mode", "H", "I", "E", "E_local", "k", "bucket", "config", "us", "default_config",
-          "default_us", "candidates", "rejected", "rel_l2", "err_ratio"]
+          "default_us", "candidates", "rejected", "rel_l2", "err_ratio", "ref_tokens"]
 GATES = {"bf16": (1e-2, 0.05), "mxfp4": (2e-2, 0.05)}   # (rel-L2, errRatio) bounds
 
 
@@ -50,9 +58,10 @@ def _layers():
 
 
 def _metrics(got, ref, rtol: float = 1e-2):
-    """(rel-L2, errRatio, finite) of got against ref, both bf16 tensors."""
+    """(rel-L2, errRatio, finite) of got against ref (float64 tensors or
+    anything .double() accepts)."""
     import torch
-    g, r = got.double(), ref.double()
+    g, r = got.double(), torch.as_tensor(ref).double().to(got.device)
     finite = bool(torch.isfinite(g).all())
     rel = float((g - r).norm() / r.norm().clamp_min(1e-300))
     atol = rtol * float(r.pow(2).mean().sqrt())
@@ -90,11 +99,18 @@ def _graph_us(call, budget_ms: float = 40.0, rounds: int = 2) -> float:
     return us
 
 
-def tune(layer: str, buckets, ep: int = 1, seed: int = 0, log=print) -> list:
-    """Tune one layer shape over token buckets; returns CSV rows (dicts)."""
+def tune(layer: str, buckets, reference, ep: int = 1, seed: int = 0, log=print) -> list:
+    """Tune one layer shape over token buckets; returns CSV rows (dicts).
+
+    reference(T, x, ids, wts, weights) -> (toks, ref): the independent
+    expected output rows ``ref`` [len(toks), H] (float64) of tokens ``toks``
+    for this bucket's inputs, with the bf16 layer weights ``weights`` =
+    (w13, w2) and, for an expert-parallel shard, slots of experts outside
+    the shard dropped (ids set to -1). Candidates are gated on those rows."""
     import torch
     from . import workloads as W
-    from . import moe_fused_fwd, moe_query_config, moe_quant_mxfp4, moe_topk_softmax, MODE_BF16, MODE_MXFP4
+    from . import (moe_fused_fwd, moe_fused_workspace_size, moe_query_config, moe_quant_mxfp4, moe_topk_softmax,
+                   MODE_BF16, MODE_MXFP4)
     from . import MoEError
 
     sh = _layers()[layer]
@@ -111,7 +127,6 @@ def tune(layer: str, buckets, ep: int = 1, seed: int = 0, log=print) -> list:
     if fp4:
         (gq, gs), (uq, us_), (wq, ws_) = moe_quant_mxfp4(gate), moe_quant_mxfp4(up), moe_quant_mxfp4(w2)
         full_w = dict(gate=gq, up=uq, w2=wq, gate_scale=gs, up_scale=us_, w2_scale=ws_)
-        del w13, w2, gate, up
     else:
         full_w = dict(gate=gate, up=up, w2=w2)
     shard_w = {n: t[:es] for n, t in full_w.items()}
@@ -153,38 +168,62 @@ def tune(layer: str, buckets, ep: int = 1, seed: int = 0, log=print) -> list:
             cands.append(c)
 
         def run(c):
+            # each candidate gets its own workspace: its call is captured in
+            # a graph for timing
             if ep > 1:
                 y = torch.zeros((T, k, H), dtype=torch.bfloat16, device=dev)
                 a, kw = args(c, y=y)
                 kw.pop("out")
-                return lambda: moe_fused_fwd(*a, **kw)
-            out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-            a, kw = args(c, out=out)
+            else:
+                out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+                a, kw = args(c, out=out)
+            kw["workspace"] = torch.empty(moe_fused_workspace_size(*a, **kw), dtype=torch.uint8, device=dev)
             return lambda: moe_fused_fwd(*a, **kw)
 
-        ref = run(base["config_index"])().clone()
+        # the independent reference rows, and the candidates' rows of the
+        # same tokens (a shard's per-slot rows summed over its own slots)
+        ids_ref = ids
+        if ep > 1:
+            ids_ref = torch.where(ids < es, ids, torch.full_like(ids, -1))
+        toks, ref_rows = reference(T, x, ids_ref, wts, (w13, w2))
+        tsel = torch.as_tensor(toks, device=dev, dtype=torch.long)
+
+        def rows_of(res):
+            if ep > 1:
+                y = res[tsel].double()                              # [n, k, H]
+                wl = torch.where(ids_ref[tsel] >= 0, wts[tsel], torch.zeros_like(wts[tsel])).double()
+                return (wl[:, :, None] * y).sum(1)
+            return res[tsel]
+
+        def splits(c):
+            q = query(c)
+            return (q["gemm1_split_k"], q["gemm2_split_k"])
+        base_out = run(base["config_index"])().clone()
         timed, rejected = {}, []
         worst = (0.0, 0.0)
         for c in cands:
             call = run(c)
             got = call().clone()
-            rel, err, finite = _metrics(got, ref)
-            if not finite or rel > rel_max or err > err_max:
+            rel, err, finite = _metrics(rows_of(got), ref_rows)
+            same_split = splits(c) == splits(base["config_index"])
+            if not finite or rel > rel_max or err > err_max or (same_split and not torch.equal(got, base_out)):
                 rejected.append(c)
                 continue
             worst = (max(worst[0], rel), max(worst[1], err))
             timed[c] = _graph_us(call)
+        if not timed:
+            raise RuntimeError(f"{layer} T={T}: no config passed the reference gate (rejected {rejected})")
         best = min(timed, key=timed.get)
         row = {"layer": layer, "mode": mode, "H": H, "I": I, "E": E, "E_local": es, "k": k, "bucket": T,
                "config": best, "us": round(timed[best], 1), "default_config": base["config_index"],
                "default_us": round(timed.get(base["config_index"], float("nan")), 1),
                "candidates": len(cands), "rejected": " ".join(map(str, rejected)),
-               "rel_l2": f"{worst[0]:.2e}", "err_ratio": f"{worst[1]:.2e}"}
+               "rel_l2": f"{worst[0]:.2e}", "err_ratio": f"{worst[1]:.2e}", "ref_tokens": len(toks)}
         log(f"[tune] {layer} ep{ep} T={T}: config {best} {row['us']} us "
             f"(built-in {row['default_config']} {row['default_us']} us; {len(timed)} timed, "
             f"{len(rejected)} rejected)")
         rows.append(row)
-        del inp, ids, wts, x, ref
+        del inp, ids, wts, x, base_out
         torch.cuda.empty_cache()
     return rows
 
@@ -220,28 +259,32 @@ def write_inc(paths, inc: str = INC) -> int:
     return len(table)
 
 
-def main(argv: Optional[list] = None) -> int:
-    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+def add_tune_args(ap: argparse.ArgumentParser) -> None:
     ap.add_argument("--layer", choices=sorted(_layers()))
     ap.add_argument("--buckets", default=",".join(str(1 << i) for i in range(16)))
     ap.add_argument("--ep", type=int, default=1, help="expert-parallel shard 0 of this many")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--out", help="CSV to write")
-    ap.add_argument("--write-inc", nargs="*", metavar="CSV",
-                    help="merge these CSVs into csrc/tuned_configs.inc (no GPU needed)")
-    a = ap.parse_args(argv)
-    if a.write_inc is not None:
-        paths = sorted(p for pat in a.write_inc for p in glob.glob(pat))
-        n = write_inc(paths)
-        print(f"[tune] wrote {n} rows to {INC}")
-        return 0
-    if not a.layer or not a.out:
-        ap.error("--layer and --out are required for tuning")
+
+
+def run_cli(a, reference) -> int:
+    """Tune a.layer over a.buckets with ``reference`` as the gate; write a.out."""
     t0 = time.time()
-    rows = tune(a.layer, [int(t) for t in a.buckets.split(",")], ep=a.ep, seed=a.seed,
+    rows = tune(a.layer, [int(t) for t in a.buckets.split(",")], reference, ep=a.ep, seed=a.seed,
                 log=lambda s: print(s, flush=True))
     write_csv(rows, a.out)
     print(f"[tune] {len(rows)} buckets in {time.time() - t0:.0f} s -> {a.out}", flush=True)
+    return 0
+
+
+def main(argv: Optional[list] = None) -> int:
+    ap = argparse.ArgumentParser(description="merge tuned CSVs into the compiled-in table")
+    ap.add_argument("--write-inc", nargs="*", metavar="CSV", required=True,
+                    help="merge these CSVs into csrc/tuned_configs.inc (no GPU needed)")
+    a = ap.parse_args(argv)
+    paths = sorted(p for pat in a.write_inc for p in glob.glob(pat))
+    n = write_inc(paths)
+    print(f"[tune] wrote {n} rows to {INC}")
     return 0
 
 
