@@ -251,6 +251,26 @@ int moe_fused_workspace_size(const moe_fused_args_t *args, size_t *bytes);
  * its contents on entry do not matter. T = 0 returns MOE_OK with no launch. */
 int moe_fused_fwd(const moe_fused_args_t *args, void *ws, size_t ws_bytes, moe_stream_t stream);
 
+/* ------------------------------------------------------ no allocation --
+ * moe_fused_fwd_noalloc: moe_fused_fwd for callers that cannot allocate
+ * device memory or bring a workspace: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.
+ *   args, stream  exactly as for moe_fused_fwd (same checks, kernels and
+ *                 results, bit for bit); stream must belong to the current
+ *                 device.
+ * The workspace is the library's own device array of
+ * MOE_NOALLOC_SCRATCH_BYTES (64 MiB), which every GPU the library runs on
+ * holds from the first call until the process ends. The call allocates
+ * nothing and calls no allocating routine. A call whose
+ * moe_fused_workspace_size exceeds that size returns MOE_ERR_WORKSPACE
+ * before any launch (for the Qwen3-235B-shaped bf16 layer that is beyond
+ * about 600 tokens; the few-token configurations need a few KB). Every call
+ * on one GPU shares that GPU's array: calls that overlap there (other
+ * streams, other host threads) race, so callers order them.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int moe_fused_fwd_noalloc(const moe_fused_args_t *args, moe_stream_t stream);
+
 /* ----------------------------------------------------------- backward --
  * moe_fused_bwd: gradients of L = sum over t, n of dout[t, n] * out[t, n]
  * for the bf16 forward (Liger-Kernel PR #1377, Notes: the grad-enabled path

@@ -18,7 +18,8 @@ from ._abi import (DT_BF16, DT_E8M0, DT_F32, DT_FP4X2, DT_I32, MODE_BF16, MODE_M
                    MoEError)
 
 __all__ = ["moe_topk_softmax", "moe_align", "moe_align_capacity", "moe_quant_mxfp4",
-           "moe_fused_fwd", "moe_fused_workspace_size", "moe_query_config", "moe_combine",
+           "moe_fused_fwd", "moe_fused_fwd_noalloc", "moe_fused_workspace_size", "moe_query_config",
+           "moe_combine",
            "moe_rmsnorm", "moe_fused_bwd", "moe_fused_bwd_workspace_size", "MoEError",
            "MODE_BF16", "MODE_MXFP4", "STAGES", "library_path"]
 
@@ -228,6 +229,25 @@ def moe_fused_fwd(x: torch.Tensor, gate: torch.Tensor, up: torch.Tensor, w2: tor
         workspace = _workspace(n.value, x.device, st)
     _abi.check(L.moe_fused_fwd(ctypes.byref(a), workspace.data_ptr() if workspace.numel() else 0,
                                workspace.numel(), st))
+    del keep
+    return y_rows if y_rows is not None else out
+
+
+def moe_fused_fwd_noalloc(x: torch.Tensor, gate: torch.Tensor, up: torch.Tensor, w2: torch.Tensor,
+                          topk_ids: torch.Tensor, topk_weights: torch.Tensor, out: torch.Tensor, *,
+                          gate_scale=None, up_scale=None, w2_scale=None, mode: int = MODE_BF16,
+                          force_config: int = -1, expert_offset: int = 0, num_global_experts: int = 0,
+                          y_rows: Optional[torch.Tensor] = None, norm_weight: Optional[torch.Tensor] = None,
+                          norm_eps: float = 1e-6, stream=None) -> torch.Tensor:
+    """moe_fused_fwd on the library's built-in device scratch: no workspace and
+    no allocation, for callers that cannot allocate (out, or y_rows, must be
+    given). Calls that overlap on one GPU race on that scratch."""
+    L = _abi.load()
+    if out is None and y_rows is None:
+        raise ValueError("moe_fused_fwd_noalloc needs out (or y_rows): it allocates nothing")
+    a, keep = _fused_args(x, gate, up, w2, topk_ids, topk_weights, out, gate_scale, up_scale, w2_scale, mode,
+                          None, force_config, expert_offset, num_global_experts, y_rows, norm_weight, norm_eps)
+    _abi.check(L.moe_fused_fwd_noalloc(ctypes.byref(a), _stream(stream)))
     del keep
     return y_rows if y_rows is not None else out
 

@@ -57,6 +57,7 @@ class Config(ctypes.Structure):
 
 EXPORTS = ("moe_topk_softmax", "moe_align", "moe_align_capacity", "moe_align_workspace_size",
            "moe_quant_mxfp4", "moe_query_config", "moe_fused_workspace_size", "moe_fused_fwd",
+           "moe_fused_fwd_noalloc",
            "moe_combine", "moe_rmsnorm", "moe_fused_bwd_workspace_size", "moe_fused_bwd",
            "moe_strerror", "moe_last_error")
 
@@ -89,6 +90,7 @@ def load() -> ctypes.CDLL:
     L.moe_query_config.argtypes = [P(FusedArgs), P(Config)]
     L.moe_fused_workspace_size.argtypes = [P(FusedArgs), P(ctypes.c_size_t)]
     L.moe_fused_fwd.argtypes = [P(FusedArgs), vp, ctypes.c_size_t, vp]
+    L.moe_fused_fwd_noalloc.argtypes = [P(FusedArgs), vp]
     L.moe_combine.argtypes = [TD, TD, TD, i32, TD, vp]
     L.moe_rmsnorm.argtypes = [TD, TD, ctypes.c_float, TD, vp]
     L.moe_fused_bwd_workspace_size.argtypes = [P(BwdArgs), P(ctypes.c_size_t)]
@@ -97,7 +99,8 @@ def load() -> ctypes.CDLL:
     L.moe_strerror.restype = ctypes.c_char_p
     L.moe_last_error.restype = ctypes.c_char_p
     for name in ("moe_topk_softmax", "moe_align", "moe_align_workspace_size", "moe_quant_mxfp4",
-                 "moe_query_config", "moe_fused_workspace_size", "moe_fused_fwd", "moe_combine",
+                 "moe_query_config", "moe_fused_workspace_size", "moe_fused_fwd", "moe_fused_fwd_noalloc",
+                 "moe_combine",
                  "moe_rmsnorm", "moe_fused_bwd_workspace_size", "moe_fused_bwd"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L

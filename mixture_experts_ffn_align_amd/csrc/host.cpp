@@ -713,6 +713,10 @@ struct StageTimer {
 
 }  // namespace
 
+int moe::report_error(int status, const char* what, const char* detail) {
+    return fail(status, "%s: %s", what, detail);
+}
+
 extern "C" {
 
 const char* moe_strerror(int status) {

@@ -410,4 +410,8 @@ hipError_t launch_gemm1_small_bf16(const Gemm1SmallParams& p, hipStream_t s);
 bool gemm2_combine_bf16_supported(int64_t I);
 hipError_t launch_gemm2_combine_bf16(const Gemm2CombineParams& p, hipStream_t s);
 
+// Record "what: detail" as the calling thread's moe_last_error() text and
+// return status (for entry points outside the host planner's file).
+int report_error(int status, const char* what, const char* detail);
+
 }  // namespace moe
