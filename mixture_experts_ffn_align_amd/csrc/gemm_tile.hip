@@ -86,7 +86,6 @@ struct TileShape {
     // 32 consecutive row blocks (a few experts) share one weight tile at a
     // time on one XCD; a group never holds empty slots
     static constexpr int kGroupM = 32;
-    static constexpr int kGroupN = 1;
 };
 
 // 16-byte chunk position of chunk c in tile row r (rows of 64 or 128 bytes;
@@ -126,18 +125,40 @@ void gemm_tile(GemmParams p) {
     // ---- tile mapping
     constexpr int tile_cols = STAGE == 1 ? BW / 2 : BW;
     const int n_tiles = p.N / tile_cols;
-    const uint32_t Lg = xcd_remap(blockIdx.x, gridDim.x);
-    const uint32_t per_group = TS::kGroupM * TS::kGroupN;
-    const uint32_t m_groups = (uint32_t)(p.max_mblocks + TS::kGroupM - 1) / TS::kGroupM;
-    const uint32_t grp = Lg / per_group, rr = Lg % per_group;
-    const int mb = (int)((grp % m_groups) * TS::kGroupM + rr % TS::kGroupM);
-    const int nt = (int)((grp / m_groups) * TS::kGroupN + rr / TS::kGroupM);
-    if (nt >= n_tiles || mb >= p.max_mblocks) return;
+    // Workgroup b runs on XCD b % 8 (the dispatcher deals workgroups to the
+    // XCDs in turn) as that XCD's j-th workgroup, j = b / 8. The logical
+    // tiles, groups of kGroupM row blocks of one weight tile in order, are
+    // cut into 8 equal contiguous ranges, one per XCD: a group's weight tile
+    // then comes through one XCD's L2, neighbouring groups (which share the
+    // expert at their boundary) stay on the same XCD, and every XCD gets the
+    // same number of real tiles. The grid is sized by the sorted capacity;
+    // the count of real row blocks (the padded length the align wrote) is
+    // only known here, so workgroups past the real tiles leave at once.
     const int n_blocks = *p.n_padded / BM;
+    const uint32_t m_groups = (uint32_t)(n_blocks + TS::kGroupM - 1) / TS::kGroupM;
+    const uint32_t total = m_groups * (uint32_t)n_tiles * TS::kGroupM;
+    const uint32_t per_xcd = (total + 7u) / 8u;
+    const uint32_t xcd = blockIdx.x & 7u, j = blockIdx.x >> 3;
+    if (j >= per_xcd) return;
+    const uint32_t L = xcd * per_xcd + j;
+    if (L >= total) return;
+    const uint32_t grp = L / TS::kGroupM, rr = L % TS::kGroupM;
+    const int mb = (int)((grp % m_groups) * TS::kGroupM + rr);
+    const int nt = (int)(grp / m_groups);
     if (mb >= n_blocks) return;
     const int e = p.block_expert[mb];
     const int row0 = mb * BM;
     const int n0 = nt * tile_cols;
+    // Sentinel rows fill only the end of an expert's last block, so the
+    // wave's 16-row groups that hold an assignment are a prefix, found from
+    // each group's first row; the wave skips the fragment reads and MFMAs of
+    // the others (their accumulators stay 0 and the epilogue stores no
+    // padding row). A block without padding runs a copy of the pipeline with
+    // no such tests.
+    int nlive = 0;
+#pragma unroll
+    for (int mi = 0; mi < TS::kWMI; ++mi)
+        nlive += __builtin_amdgcn_readfirstlane(p.sorted[row0 + (wm * TS::kWMI + mi) * 16]) < p.A ? 1 : 0;
 
     // stage 1 gathers the token row t = a / k, stage 2 the h row of the flat
     // assignment a; a padding row re-reads row 0
@@ -240,28 +261,37 @@ void gemm_tile(GemmParams p) {
         i32x4_t a[WMI], b[8];
         uint32_t as[WMI], bs[8];
     };
-    auto read_frags = [&](const char* buf, int u, Frags& f) {
+    auto read_frags = [&](const char* buf, int u, Frags& f, auto full_c) {
+        constexpr bool FULL = decltype(full_c)::value;
         const int rd = r16 * kRowBytes + swz(r16, 4 * u + kg) * 16;
 #pragma unroll
         for (int mi = 0; mi < WMI; ++mi)
-            f.a[mi] = *reinterpret_cast<const i32x4_t*>(buf + (wm * WMI + mi) * 16 * kRowBytes + rd);
+            if (FULL || mi < nlive)
+                f.a[mi] = *reinterpret_cast<const i32x4_t*>(buf + (wm * WMI + mi) * 16 * kRowBytes + rd);
 #pragma unroll
         for (int ni = 0; ni < 8; ++ni)
             f.b[ni] = *reinterpret_cast<const i32x4_t*>(buf + (BM + b_rb(ni) * 16) * kRowBytes + rd);
         if constexpr (MODE == 1) {
-            const uint8_t* sb = reinterpret_cast<const uint8_t*>(buf + TS::kScOff + u * TS::kScPlane);
+            // a row's four scale bytes of the k-step form one dword: every
+            // lane of the row reads that dword (one address, a broadcast;
+            // byte reads of it by lanes kg = 0..3 would conflict) and shifts
+            // its own byte kg down, the byte the MFMA takes
+            const uint32_t* sb = reinterpret_cast<const uint32_t*>(buf + TS::kScOff + u * TS::kScPlane);
 #pragma unroll
-            for (int mi = 0; mi < WMI; ++mi) f.as[mi] = sb[((wm * WMI + mi) * 16 + r16) * kScStep + kg];
+            for (int mi = 0; mi < WMI; ++mi)
+                if (FULL || mi < nlive) f.as[mi] = sb[(wm * WMI + mi) * 16 + r16] >> (8 * kg);
 #pragma unroll
-            for (int ni = 0; ni < 8; ++ni) f.bs[ni] = sb[(BM + b_rb(ni) * 16 + r16) * kScStep + kg];
+            for (int ni = 0; ni < 8; ++ni) f.bs[ni] = sb[BM + b_rb(ni) * 16 + r16] >> (8 * kg);
         }
     };
     // weight fragment first: the accumulator then holds, in lane l, 4
     // consecutive output columns 4 (l / 16) .. +3 of row l % 16, so the
     // epilogues store 8 or 16 contiguous bytes per lane
-    auto mfma_frags = [&](const Frags& f) {
+    auto mfma_frags = [&](const Frags& f, auto full_c) {
+        constexpr bool FULL = decltype(full_c)::value;
 #pragma unroll
-        for (int mi = 0; mi < WMI; ++mi)
+        for (int mi = 0; mi < WMI; ++mi) {
+            if (!FULL && mi >= nlive) continue;
 #pragma unroll
             for (int ni = 0; ni < 8; ++ni) {
                 if constexpr (MODE == 0) {
@@ -275,141 +305,149 @@ void gemm_tile(GemmParams p) {
                                                                                    (int)f.bs[ni], 0, (int)f.as[mi]);
                 }
             }
-    };
-    auto compute = [&](const char* buf) {
-#pragma unroll
-        for (int u = 0; u < SUBS; ++u) {
-            Frags f;
-            read_frags(buf, u, f);
-            mfma_frags(f);
         }
     };
-    // stage s's loads have landed for every wave and every wave is done with
-    // stage s - 1: wait for this wave's loads up to stage s (the later
-    // stages stay in flight) and its LDS reads, then meet
-    auto publish = [&]() {
-        __builtin_amdgcn_sched_barrier(0);
-        wait_vm_lgkm<(TS::kNBuf - 2) * kPerStage>();
-        __builtin_amdgcn_s_barrier();
-        __asm__ volatile("" ::: "memory");
-        __builtin_amdgcn_sched_barrier(0);
-    };
-
-    // ---- pipeline over kNBuf rotating buffers: stage s in buffer s % kNBuf,
-    // stage s + kNBuf - 1 loading into the buffer stage s - 1 used
-    if constexpr (PP) {
-        // Two wave groups, one wave of each per SIMD, half a stage apart:
-        // while one group multiplies from registers, the other reads its next
-        // stage's fragments from LDS, so each SIMD's matrix core always has a
-        // wave with operands ready. Barriers B0, B1, ... separate phases;
-        // group 0 reads stage s in [B2s, B2s+1] and multiplies it in
-        // [B2s+1, B2s+2], group 1 reads it in [B2s+1, B2s+2] and multiplies in
-        // [B2s+2, B2s+3]. The loads of stage s + kNBuf - 1 go out at B2s from
-        // both groups into the buffer of stage s - 1, which both groups
-        // finished reading before B2s; every wave waits for its loads of
-        // stage s + 1 before B2s+2, the first barrier after which stage s + 1
-        // is read.
-        static_assert(NW == 8, "one wave of each group per SIMD");
-        const bool g1 = w >= NW / 2;
-        Frags f[SUBS];
-        auto bar = [&]() {
+    // the K loop, with every row group live (FULL) or with the tests
+    auto pipeline = [&](auto full_c) {
+        auto compute = [&](const char* buf) {
+#pragma unroll
+            for (int u = 0; u < SUBS; ++u) {
+                Frags f;
+                read_frags(buf, u, f, full_c);
+                mfma_frags(f, full_c);
+            }
+        };
+        // stage s's loads have landed for every wave and every wave is done with
+        // stage s - 1: wait for this wave's loads up to stage s (the later
+        // stages stay in flight) and its LDS reads, then meet
+        auto publish = [&]() {
             __builtin_amdgcn_sched_barrier(0);
+            wait_vm_lgkm<(TS::kNBuf - 2) * kPerStage>();
             __builtin_amdgcn_s_barrier();
             __asm__ volatile("" ::: "memory");
             __builtin_amdgcn_sched_barrier(0);
         };
-        auto read_stage = [&](const char* buf) {
+
+        // ---- pipeline over kNBuf rotating buffers: stage s in buffer s % kNBuf,
+        // stage s + kNBuf - 1 loading into the buffer stage s - 1 used
+        if constexpr (PP) {
+            // Two wave groups, one wave of each per SIMD, half a stage apart:
+            // while one group multiplies from registers, the other reads its next
+            // stage's fragments from LDS, so each SIMD's matrix core always has a
+            // wave with operands ready. Barriers B0, B1, ... separate phases;
+            // group 0 reads stage s in [B2s, B2s+1] and multiplies it in
+            // [B2s+1, B2s+2], group 1 reads it in [B2s+1, B2s+2] and multiplies in
+            // [B2s+2, B2s+3]. The loads of stage s + kNBuf - 1 go out at B2s from
+            // both groups into the buffer of stage s - 1, which both groups
+            // finished reading before B2s; every wave waits for its loads of
+            // stage s + 1 before B2s+2, the first barrier after which stage s + 1
+            // is read.
+            static_assert(NW == 8, "one wave of each group per SIMD");
+            const bool g1 = w >= NW / 2;
+            Frags f[SUBS];
+            auto bar = [&]() {
+                __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_s_barrier();
+                __asm__ volatile("" ::: "memory");
+                __builtin_amdgcn_sched_barrier(0);
+            };
+            auto read_stage = [&](const char* buf) {
 #pragma unroll
-            for (int u = 0; u < SUBS; ++u) read_frags(buf, u, f[u]);
-        };
-        auto mfma_stage = [&]() {
+                for (int u = 0; u < SUBS; ++u) read_frags(buf, u, f[u], full_c);
+            };
+            auto mfma_stage = [&]() {
 #pragma unroll
-            for (int u = 0; u < SUBS; ++u) mfma_frags(f[u]);
-        };
-        // group 0, stage s: read buffer rd, refill buffer wr (stage s - 1's)
-        auto g0 = [&](const char* rd, char* wr, int s) {
-            issue(wr, s + NBUF - 1);
-            read_stage(rd);
-            __builtin_amdgcn_sched_barrier(0);
-            wait_vm_lgkm<63>();
-            bar();
-            mfma_stage();
-            __builtin_amdgcn_sched_barrier(0);
+                for (int u = 0; u < SUBS; ++u) mfma_frags(f[u], full_c);
+            };
+            // group 0, stage s: read buffer rd, refill buffer wr (stage s - 1's)
+            auto g0 = [&](const char* rd, char* wr, int s) {
+                issue(wr, s + NBUF - 1);
+                read_stage(rd);
+                __builtin_amdgcn_sched_barrier(0);
+                wait_vm_lgkm<63>();
+                bar();
+                mfma_stage();
+                __builtin_amdgcn_sched_barrier(0);
+                wait_vm_lgkm<(NBUF - 2) * kPerStage>();
+                bar();
+            };
+            // group 1, stage s: read buffer b, then refill it with stage s + kNBuf
+            auto g1s = [&](char* b, int s) {
+                bar();
+                read_stage(b);
+                __builtin_amdgcn_sched_barrier(0);
+                wait_vm_lgkm<(NBUF - 2) * kPerStage>();
+                bar();
+                issue(b, s + NBUF);
+                mfma_stage();
+            };
+            issue(lds0, 0);
+            if constexpr (NBUF == 4) {
+                issue(lds1, 1);
+                issue(lds2, 2);
+            }
             wait_vm_lgkm<(NBUF - 2) * kPerStage>();
-            bar();
-        };
-        // group 1, stage s: read buffer b, then refill it with stage s + kNBuf
-        auto g1s = [&](char* b, int s) {
-            bar();
-            read_stage(b);
-            __builtin_amdgcn_sched_barrier(0);
-            wait_vm_lgkm<(NBUF - 2) * kPerStage>();
-            bar();
-            issue(b, s + NBUF);
-            mfma_stage();
-        };
-        issue(lds0, 0);
-        if constexpr (NBUF == 4) {
+            bar();   // B0
+            if (!g1) {
+                for (int s = 0; s < S; s += NBUF) {
+                    if constexpr (NBUF == 4) {
+                        g0(lds0, lds3, s);
+                        g0(lds1, lds0, s + 1);
+                        g0(lds2, lds1, s + 2);
+                        g0(lds3, lds2, s + 3);
+                    } else {
+                        g0(lds0, lds1, s);
+                        g0(lds1, lds0, s + 1);
+                    }
+                }
+            } else {
+                issue(NBUF == 4 ? lds3 : lds1, NBUF - 1);
+                for (int s = 0; s < S; s += NBUF) {
+                    if constexpr (NBUF == 4) {
+                        g1s(lds0, s);
+                        g1s(lds1, s + 1);
+                        g1s(lds2, s + 2);
+                        g1s(lds3, s + 3);
+                    } else {
+                        g1s(lds0, s);
+                        g1s(lds1, s + 1);
+                    }
+                }
+            }
+        } else if constexpr (NBUF == 4) {
+            issue(lds0, 0);
             issue(lds1, 1);
             issue(lds2, 2);
-        }
-        wait_vm_lgkm<(NBUF - 2) * kPerStage>();
-        bar();   // B0
-        if (!g1) {
-            for (int s = 0; s < S; s += NBUF) {
-                if constexpr (NBUF == 4) {
-                    g0(lds0, lds3, s);
-                    g0(lds1, lds0, s + 1);
-                    g0(lds2, lds1, s + 2);
-                    g0(lds3, lds2, s + 3);
-                } else {
-                    g0(lds0, lds1, s);
-                    g0(lds1, lds0, s + 1);
-                }
+            for (int s = 0; s < S; s += 4) {
+                publish();
+                issue(lds3, s + 3);
+                compute(lds0);
+                publish();
+                issue(lds0, s + 4);
+                compute(lds1);
+                publish();
+                issue(lds1, s + 5);
+                compute(lds2);
+                publish();
+                issue(lds2, s + 6);
+                compute(lds3);
             }
         } else {
-            issue(NBUF == 4 ? lds3 : lds1, NBUF - 1);
-            for (int s = 0; s < S; s += NBUF) {
-                if constexpr (NBUF == 4) {
-                    g1s(lds0, s);
-                    g1s(lds1, s + 1);
-                    g1s(lds2, s + 2);
-                    g1s(lds3, s + 3);
-                } else {
-                    g1s(lds0, s);
-                    g1s(lds1, s + 1);
-                }
+            issue(lds0, 0);
+            for (int s = 0; s < S; s += 2) {
+                publish();
+                issue(lds1, s + 1);
+                compute(lds0);
+                publish();
+                issue(lds0, s + 2);
+                compute(lds1);
             }
         }
-    } else if constexpr (NBUF == 4) {
-        issue(lds0, 0);
-        issue(lds1, 1);
-        issue(lds2, 2);
-        for (int s = 0; s < S; s += 4) {
-            publish();
-            issue(lds3, s + 3);
-            compute(lds0);
-            publish();
-            issue(lds0, s + 4);
-            compute(lds1);
-            publish();
-            issue(lds1, s + 5);
-            compute(lds2);
-            publish();
-            issue(lds2, s + 6);
-            compute(lds3);
-        }
-    } else {
-        issue(lds0, 0);
-        for (int s = 0; s < S; s += 2) {
-            publish();
-            issue(lds1, s + 1);
-            compute(lds0);
-            publish();
-            issue(lds0, s + 2);
-            compute(lds1);
-        }
-    }
+    };
+    if (nlive == WMI)
+        pipeline(std::integral_constant<bool, true>{});
+    else
+        pipeline(std::integral_constant<bool, false>{});
     // drain the loads past the end before the workgroup's LDS is released
     wait_vm_lgkm<0>();
 
@@ -534,8 +572,9 @@ hipError_t launch_one(const GemmParams& p, hipStream_t s) {
     using TS = TileShape<MODE, BM, BW, NW, SUBS, NBUF>;
     const int64_t n_tiles = p.N / (STAGE == 1 ? BW / 2 : BW);
     const int64_t m_groups = (p.max_mblocks + TS::kGroupM - 1) / TS::kGroupM;
-    const int64_t n_groups = (n_tiles + TS::kGroupN - 1) / TS::kGroupN;
-    const int64_t grid = m_groups * n_groups * TS::kGroupM * TS::kGroupN;
+    // a multiple of 8 workgroups, each XCD's share covering an eighth of
+    // the tiles the capacity allows
+    const int64_t grid = (m_groups * n_tiles + 7) / 8 * 8 * TS::kGroupM;
     if (grid == 0) return hipSuccess;
     hipLaunchKernelGGL((gemm_tile<MODE, STAGE, BM, BW, NW, SUBS, NBUF, PP>), dim3((unsigned)grid),
                        dim3(TS::kThreads), 0, s, p);
