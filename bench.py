@@ -247,6 +247,8 @@ def main():
     ap.add_argument("--bwd", default="",
                     help="comma-separated token counts: the backward of the bf16 Qwen3-235B-shaped layer "
                          "(fp32 weight gradients), one JSON line each")
+    ap.add_argument("--config", type=int, default=-1,
+                    help="with --mxfp4/--bf16: force this tile-config index (comparisons; -1 = the built-in choice)")
     ap.add_argument("--calls", type=int, default=0,
                     help="with --mxfp4/--bf16: only this many eager calls per bucket, no timing "
                          "(a short run for counter passes)")
@@ -269,7 +271,8 @@ def main():
         log("[bench] copied 1 GiB three times")
         return
     if args.mxfp4:
-        for line in mxfp4_lines([int(t) for t in args.mxfp4.split(",")], args.routing, dev, args.calls):
+        for line in mxfp4_lines([int(t) for t in args.mxfp4.split(",")], args.routing, dev, args.calls,
+                                force=args.config):
             print(json.dumps(line), flush=True)
         return
     if args.norm:
@@ -282,7 +285,7 @@ def main():
         ep_buckets([int(t) for t in args.bf16.split(",")], args.ep, dev)
         return
     if args.bf16:
-        for line in bf16_lines([int(t) for t in args.bf16.split(",")], dev, args.calls):
+        for line in bf16_lines([int(t) for t in args.bf16.split(",")], dev, args.calls, force=args.config):
             print(json.dumps(line), flush=True)
         return
     headline(args, dev)
@@ -567,7 +570,7 @@ def layout_pair(timer, a, b, outs, keys=("strided_us", "contiguous_us"), rounds=
             "bit_identical": True}
 
 
-def bf16_lines(buckets, dev, calls=0):
+def bf16_lines(buckets, dev, calls=0, force=-1):
     """bf16 Qwen3-235B-shaped layer: per token bucket, the fused forward on
     router ids computed beforehand, gate/up as packed w13 views."""
     import torch
@@ -587,10 +590,11 @@ def bf16_lines(buckets, dev, calls=0):
         inp = W.make_inputs(sh, T, seed=T, device=dev, weights=(w13, w2))
         ids, wts = moe.moe_topk_softmax(inp["logits"], k)
         out = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
-        ws = torch.empty(moe.moe_fused_workspace_size(inp["x"], gate, up, w2, ids, wts), dtype=torch.uint8,
+        fk = dict(force_config=force)
+        ws = torch.empty(moe.moe_fused_workspace_size(inp["x"], gate, up, w2, ids, wts, **fk), dtype=torch.uint8,
                          device=dev)
-        cfg = moe.moe_query_config(inp["x"], gate, up, w2, ids, wts)
-        call = lambda: moe.moe_fused_fwd(inp["x"], gate, up, w2, ids, wts, out=out, workspace=ws)
+        cfg = moe.moe_query_config(inp["x"], gate, up, w2, ids, wts, **fk)
+        call = lambda: moe.moe_fused_fwd(inp["x"], gate, up, w2, ids, wts, out=out, workspace=ws, **fk)
         if calls:
             for _ in range(calls):
                 call()
@@ -616,7 +620,7 @@ def bf16_lines(buckets, dev, calls=0):
     return lines
 
 
-def mxfp4_lines(buckets, routing, dev, calls=0, timer=None):
+def mxfp4_lines(buckets, routing, dev, calls=0, timer=None, force=-1):
     """MXFP4 TP2 shard (H=4096, I=512; 512 experts top-10, or 513 with the
     shared expert): per token bucket, the fused forward (align + activation
     quantisation, gemm1 + SiLU*up with h quantised, gemm2, combine) on router
@@ -646,7 +650,7 @@ def mxfp4_lines(buckets, routing, dev, calls=0, timer=None):
         logits = torch.randn(T, sh.routed_experts, generator=gx, device=dev)
         ids, wts = moe.moe_topk_softmax(logits, sh.routed_k, shared_id=sh.shared_expert, shared_w=1.0)
         out = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
-        kw = dict(gate_scale=gs, up_scale=us, w2_scale=wsc, mode=moe.MODE_MXFP4)
+        kw = dict(gate_scale=gs, up_scale=us, w2_scale=wsc, mode=moe.MODE_MXFP4, force_config=force)
         ws = torch.empty(moe.moe_fused_workspace_size(x, gq, uq, wq, ids, wts, **kw), dtype=torch.uint8, device=dev)
         cfg = moe.moe_query_config(x, gq, uq, wq, ids, wts, **kw)
         call = lambda: moe.moe_fused_fwd(x, gq, uq, wq, ids, wts, out=out, workspace=ws, **kw)

@@ -233,7 +233,10 @@ typedef struct {
                               MXFP4 mode */
     int32_t gemm2_kernel;  /* kernel family of gemm2: gemm1's plus one, or 6 / 16: gemm2 with the
                               combine folded in (few tokens; bf16 with I a multiple of 256 from 512
-                              to 1536 and K split 4, MXFP4 with I = 512; bit-identical results) */
+                              to 1536 and K split 4, MXFP4 with I = 512; bit-identical results),
+                              or 18: MXFP4 gemm2 with K = 512 keeping each block's h rows in
+                              registers and walking 128-column weight tiles (many tokens;
+                              bit-identical results; y rows below 4 GB, else the LDS tile) */
     int32_t gemm1_split_k; /* waves splitting K inside a workgroup */
     int32_t gemm2_split_k;
     int32_t config_index;  /* index into the library's config list */

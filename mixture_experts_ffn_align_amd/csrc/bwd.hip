@@ -290,8 +290,8 @@ __global__ __launch_bounds__(256) void bwd_gemm_kernel(BwdGemmParams p) {
                         v[3] = __uint_as_float(o.y & 0xffff0000u) + v[3];
                     }
                     *reinterpret_cast<uint2*>(row + nb * 16) =
-                        make_uint2(f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16),
-                                   f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16));
+                        make_uint2(bf16x2_bits(v[0], v[1]),
+                                   bf16x2_bits(v[2], v[3]));
                 }
             }
         }

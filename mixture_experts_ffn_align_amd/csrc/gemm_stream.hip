@@ -581,8 +581,8 @@ void gemm_stream_nt(GemmParams p) {
             for (int nb = 0; nb < NB; ++nb) {
                 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
                 const u32x2_t pk = {
-                    f32_to_bf16_bits(acc[mi][nb][0]) | ((uint32_t)f32_to_bf16_bits(acc[mi][nb][1]) << 16),
-                    f32_to_bf16_bits(acc[mi][nb][2]) | ((uint32_t)f32_to_bf16_bits(acc[mi][nb][3]) << 16)};
+                    bf16x2_bits(acc[mi][nb][0], acc[mi][nb][1]),
+                    bf16x2_bits(acc[mi][nb][2], acc[mi][nb][3])};
                 __builtin_nontemporal_store(pk, reinterpret_cast<u32x2_t*>(yr + nb * 16));
             }
         }

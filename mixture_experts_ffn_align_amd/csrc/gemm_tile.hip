@@ -134,7 +134,7 @@ void gemm_tile(GemmParams p) {
     // same number of real tiles. The grid is sized by the sorted capacity;
     // the count of real row blocks (the padded length the align wrote) is
     // only known here, so workgroups past the real tiles leave at once.
-    const int n_blocks = *p.n_padded / BM;
+    const int n_blocks = __builtin_amdgcn_readfirstlane(*p.n_padded) / BM;
     const uint32_t m_groups = (uint32_t)(n_blocks + TS::kGroupM - 1) / TS::kGroupM;
     const uint32_t total = m_groups * (uint32_t)n_tiles * TS::kGroupM;
     const uint32_t per_xcd = (total + 7u) / 8u;
@@ -146,7 +146,7 @@ void gemm_tile(GemmParams p) {
     const int mb = (int)((grp % m_groups) * TS::kGroupM + rr);
     const int nt = (int)(grp / m_groups);
     if (mb >= n_blocks) return;
-    const int e = p.block_expert[mb];
+    const int e = __builtin_amdgcn_readfirstlane(p.block_expert[mb]);
     const int row0 = mb * BM;
     const int n0 = nt * tile_cols;
     // Sentinel rows fill only the end of an expert's last block, so the
@@ -494,10 +494,11 @@ void gemm_tile(GemmParams p) {
             [&](int mi, char* prow) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    uint32_t v[4];
+                    float v[4];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) v[i] = f32_to_bf16_bits(silu_mul(acc[mi][j][i], acc[mi][4 + j][i]));
-                    *reinterpret_cast<uint2*>(prow + (j * 16 + kg * 4) * 2) = uint2{v[0] | (v[1] << 16), v[2] | (v[3] << 16)};
+                    for (int i = 0; i < 4; ++i) v[i] = silu_mul(acc[mi][j][i], acc[mi][4 + j][i]);
+                    *reinterpret_cast<uint2*>(prow + (j * 16 + kg * 4) * 2) =
+                        uint2{bf16x2_bits(v[0], v[1]), bf16x2_bits(v[2], v[3])};
                 }
             },
             std::integral_constant<int, 128>{},
@@ -549,8 +550,8 @@ void gemm_tile(GemmParams p) {
 #pragma unroll
                 for (int ni = 0; ni < 8; ++ni) {
                     const uint2 pk = {
-                        f32_to_bf16_bits(acc[mi][ni][0]) | ((uint32_t)f32_to_bf16_bits(acc[mi][ni][1]) << 16),
-                        f32_to_bf16_bits(acc[mi][ni][2]) | ((uint32_t)f32_to_bf16_bits(acc[mi][ni][3]) << 16)};
+                        bf16x2_bits(acc[mi][ni][0], acc[mi][ni][1]),
+                        bf16x2_bits(acc[mi][ni][2], acc[mi][ni][3])};
                     *reinterpret_cast<uint2*>(prow + (ni * 16 + kg * 4) * 2) = pk;
                 }
             },
@@ -588,11 +589,14 @@ hipError_t launch_one(const GemmParams& p, hipStream_t s) {
 // x 4 (MXFP4), with four 128-byte stage buffers (three stages in flight)
 // where K allows it, 5 = 128 x 256 x 8 (about 64 to 160 rows per expert).
 int gemm_tile_rows(int mode, int shape) {
-    static const int rows[6] = {256, 128, 64, 32, 64, 128};
+    static const int rows[8] = {256, 128, 64, 32, 64, 128, 256, 128};
     return mode == 1 && shape == 4 ? 32 : rows[shape];
 }
 
+// Output columns one tile covers (shapes 6 and 7: gemm2 only, 128 columns
+// per step of their column walk; as gemm1 they accept no N)
 int gemm_tile_cols(int shape, int stage) {
+    if (shape >= 6) return stage == 2 ? 128 : (1 << 30);
     const int bw = (shape == 0 || shape == 4 || shape == 5) ? 256 : 512;
     return stage == 1 ? bw / 2 : bw;
 }
@@ -604,8 +608,12 @@ int gemm_tile_k_granule(int mode, int shape) {
     return shape == 4 ? 4 * 64 : 2 * 64;
 }
 
-// MXFP4 128 x 512 stages do not fit the LDS with their scales
-bool gemm_tile_supported(int mode, int shape) { return shape >= 0 && shape <= 5 && !(mode == 1 && shape == 1); }
+// MXFP4 128 x 512 stages do not fit the LDS with their scales; shapes 6 and
+// 7 are MXFP4 only
+bool gemm_tile_supported(int mode, int shape) {
+    if (shape == 6 || shape == 7) return mode == 1;
+    return shape >= 0 && shape <= 5 && !(mode == 1 && shape == 1);
+}
 
 hipError_t launch_gemm_tile(int mode, int shape, int stage, const GemmParams& p, hipStream_t s) {
     if (!gemm_tile_supported(mode, shape) || p.N % gemm_tile_cols(shape, stage) != 0 ||
@@ -615,6 +623,10 @@ hipError_t launch_gemm_tile(int mode, int shape, int stage, const GemmParams& p,
     return stage == 1 ? launch_one<MD, 1, BM, BW, NW>(p, s) : launch_one<MD, 2, BM, BW, NW>(p, s)
 #define MOE_TILE4(MD, BM, BW, NW) \
     return stage == 1 ? launch_one<MD, 1, BM, BW, NW, 2, 4>(p, s) : launch_one<MD, 2, BM, BW, NW, 2, 4>(p, s)
+    if (shape == 6 || shape == 7) {
+        if (mode != 1 || stage != 2) return hipErrorInvalidValue;
+        return launch_gemm2_rows(shape == 6 ? 256 : 128, p, s);
+    }
     if (mode == 1) {
         // gemm2 (K = I) runs faster with two 128-byte stages; gemm1 keeps
         // four 64-byte ones

@@ -185,6 +185,13 @@ const Cfg kConfigs[] = {
     // 128 x 256 tiles (about 64 to 160 rows per expert); gemm2 on them, on
     // the MXFP4 multi-tile stream with 64-row blocks, or on 256 x 256 tiles
     {128, 1, 1, 4, 6, -1}, {128, 1, 1, 4, 6, 31}, {128, 1, 1, 4, 6, 11},
+    // MXFP4 with K = 512 in gemm2: gemm1 on 256 x 256 or 128 x 256 tiles,
+    // gemm2 with its h rows in registers walking 128-column weight tiles
+    // (entries 43 and 44 name that gemm2 kernel; as gemm1 they cannot run)
+    {256, 1, 1, 4, 1, 43}, {128, 1, 1, 4, 6, 44},
+    {256, 1, 1, 4, 7, -1}, {128, 1, 1, 4, 8, -1},
+    // the same with the other block size for gemm2 (a second padded layout)
+    {256, 1, 1, 4, 1, 44}, {128, 1, 1, 4, 6, 43},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -260,6 +267,8 @@ int heuristic_config(int mode, int64_t T, int64_t H, int64_t I, int64_t E, int64
     } else {
         if (rows >= 128.0) c = tile_config(1, 0, H, I);
         else if (rows >= 64.0) c = tile_config(1, 2, H, I);
+        // with K = 512 in gemm2 (I = 512), its h rows stay in registers
+        if (c == tile_config(1, 0, H, I) && c >= 0 && I == 512) c = 41;
     }
     if (c >= 0) return c;
     // MXFP4 with I = 512: gemm2 on the multi-tile weight stream (one align)
@@ -481,7 +490,7 @@ int plan_fused(const moe_fused_args_t* a, Plan* pl) {
     }
     if (ci >= kNumConfigs) return fail(MOE_ERR_ARG, "force_config %d out of range", ci);
     const Cfg c1 = kConfigs[ci];
-    const Cfg c2 = c1.g2 >= 0 ? kConfigs[c1.g2] : c1;
+    Cfg c2 = c1.g2 >= 0 ? kConfigs[c1.g2] : c1;
     const int md = fp4 ? 1 : 0;
     // resolve and check one GEMM's kernel; the split of K is a preference:
     // halve it until every wave's share of K is a whole number of pipelined
@@ -498,6 +507,9 @@ int plan_fused(const moe_fused_args_t* a, Plan* pl) {
             if (K % gran != 0 || N % gemm_tile_cols(shape, stage) != 0)
                 return fail(MOE_ERR_UNSUPPORTED, "config %d: gemm%d needs K %% %d == 0 and N %% %d == 0", ci, stage,
                             gran, gemm_tile_cols(shape, stage));
+            if (shape >= 6 && (stage != 2 || !gemm2_rows_supported(K, N, T * k, y_out ? y_rows_stride(a->y_rows) : H)))
+                return fail(MOE_ERR_UNSUPPORTED,
+                            "config %d: the register-resident gemm2 needs K = 512 and y rows below 4 GB", ci);
             return MOE_OK;
         }
         int w = ks->wk;
@@ -523,15 +535,22 @@ int plan_fused(const moe_fused_args_t* a, Plan* pl) {
             return fail(MOE_ERR_UNSUPPORTED,
                         "config %d: fused gemm2 + combine needs I = 512 (MXFP4) or I in {512, 768, ..., 1536} (bf16)",
                         ci);
-        if (H % 16 != 0 || T > (1 << 20))
-            return fail(MOE_ERR_UNSUPPORTED, "config %d: fused gemm2 + combine needs H %% 16 == 0, T <= 2^20", ci);
+        // one workgroup of up to 1024 threads per (token, 16 columns); a
+        // launch holds fewer than 2^32 threads
+        if (H % 16 != 0 || T * (H / 16) * 1024 >= ((int64_t)1 << 32))
+            return fail(MOE_ERR_UNSUPPORTED,
+                        "config %d: fused gemm2 + combine needs H %% 16 == 0 and T * H / 16 < 2^22", ci);
         if (pl->small1 && (H % 2048 != 0 || H > 8192 || T * k > (1 << 16)))
             return fail(MOE_ERR_UNSUPPORTED,
                         "config %d: gemm1 per slot needs H %% 2048 == 0, H <= 8192 and T*k <= 65536", ci);
         if (y_out) return fail(MOE_ERR_UNSUPPORTED, "config %d: fused gemm2 + combine writes out, not y_rows", ci);
         pl->ks[1] = pl->ks[0];   // no second layout
     } else if ((rc = resolve(c2, 2, &pl->ks[1]))) {
-        return rc;
+        // a chosen (not forced) register-resident gemm2 whose y rows would
+        // span 4 GB or more: the LDS tile with the same block rows instead
+        if (a->force_config >= 0 || c2.tile < 7) return rc;
+        c2 = kConfigs[c2.bm == 256 ? 11 : 38];
+        if ((rc = resolve(c2, 2, &pl->ks[1]))) return rc;
     }
 
     pl->mode = a->mode;
@@ -964,7 +983,7 @@ int moe_query_config(const moe_fused_args_t* args, moe_config_t* cfg) {
     cfg->block_m2 = pl.ks[1].bm;
     const int base = args->mode == MOE_MODE_MXFP4 ? 10 : 0;
     cfg->gemm1_kernel = pl.small1 ? base + 7 : base + (pl.ks[0].tile ? 2 : 0) + 1;
-    cfg->gemm2_kernel = pl.fuse ? base + 6 : base + (pl.ks[1].tile ? 2 : 0) + 2;
+    cfg->gemm2_kernel = pl.fuse ? base + 6 : (pl.ks[1].tile >= 7 ? base + 8 : base + (pl.ks[1].tile ? 2 : 0) + 2);
     cfg->gemm1_split_k = pl.small1 ? 4 : (pl.ks[0].tile ? 1 : pl.ks[0].wk);
     cfg->gemm2_split_k = pl.fuse ? (base ? 1 : 4) : (pl.ks[1].tile ? 1 : pl.ks[1].wk);
     cfg->config_index = pl.cfg_index;

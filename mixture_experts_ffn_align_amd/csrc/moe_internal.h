@@ -19,13 +19,19 @@ constexpr int kWave = 64;
 
 // ---------------------------------------------------------- bf16 helpers
 
-// fp32 -> bf16 bits, round to nearest even (NaN kept quiet).
-__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return (uint16_t)((u >> 16) | 0x40u);
-    uint32_t r = u + 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(r >> 16);
+// Two fp32 -> two bf16 (low half = a), round to nearest even, with the
+// chip's packed conversion (v_cvt_pk_bf16_f32; fp32 denormals are kept, the
+// kernels' float mode): one instruction per pair, where a rounding written
+// out in integer arithmetic took about six per value and bound the y
+// epilogues. The bits equal the integer rounding for every finite value.
+__device__ __forceinline__ uint32_t bf16x2_bits(float a, float b) {
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
 }
+
+// fp32 -> bf16 bits, round to nearest even.
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) { return (uint16_t)bf16x2_bits(f, 0.0f); }
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
     return __uint_as_float((uint32_t)b << 16);
@@ -355,6 +361,12 @@ hipError_t launch_gemm(const GemmKernelId& id, const GemmParams& p, hipStream_t 
 // Row blocks of gemm_tile_rows(mode, shape), gemm_tile_cols(shape, stage) output
 // columns per workgroup, K a multiple of gemm_tile_k_granule(mode, shape). Same
 // parameter block and epilogues as above.
+// Shapes 6 and 7 (MXFP4 gemm2 with K = 512 only): a workgroup keeps 256 or
+// 128 h rows in registers and walks the output columns in 128-wide weight
+// tiles (gemm2_rows.hip); y stored with 32-bit buffer offsets, so the y rows
+// must span less than 4 GB.
+bool gemm2_rows_supported(int64_t K, int64_t N, int64_t A, int64_t out_row);
+hipError_t launch_gemm2_rows(int bm, const GemmParams& p, hipStream_t s);
 int gemm_tile_rows(int mode, int shape);
 int gemm_tile_cols(int shape, int stage);
 int gemm_tile_k_granule(int mode, int shape);

@@ -304,3 +304,31 @@ def test_binding_workspace_cache_is_per_device_and_stream():
     assert cache[("cuda", 0, 222)] is b
     d = _ws_get(cache, ("cuda", 1, 111), 10, alloc)
     assert d.numel() == 256 and made == [1000, 1000, 5000, 256]
+
+
+def test_mxfp4_register_gemm2_falls_back_past_4gb_of_y():
+    """An MXFP4 layer's built-in choice at many tokens keeps h rows in
+    registers for gemm2 (family 18); where the y rows would span 4 GB or more
+    (the kernel addresses them with 32-bit buffer offsets) the planner takes
+    the LDS tile with the same block rows instead, and a forced config that
+    cannot run fails before any launch."""
+    def q(T, **kw):
+        H, I, E, k = 4096, 512, 256, 10     # a layer outside the tuned table: the built-in rules
+        def view(shape, dtype, row=16):
+            n = len(shape)
+            st = [row] * (n - 1) + [1]
+            return torch.empty(1 + sum((s - 1) * t for s, t in zip(shape, st)) + 64, dtype=dtype).as_strided(shape, st)
+        x = view((T, H), torch.bfloat16)
+        g = view((E, I, H // 2), torch.uint8)
+        w2 = view((E, H, I // 2), torch.uint8)
+        sc = dict(gate_scale=view((E, I, H // 32), torch.uint8), up_scale=view((E, I, H // 32), torch.uint8),
+                  w2_scale=view((E, H, I // 32), torch.uint8), mode=moe.MODE_MXFP4)
+        ids, w = view((T, k), torch.int32, 1), view((T, k), torch.float32, 1)
+        out = torch.empty(T * H + 64, dtype=torch.bfloat16).as_strided((T, H), (H, 1))
+        return moe.moe_query_config(x, g, g, w2, ids, w, out=out, **sc, **kw)
+    assert q(32768)["gemm2_kernel"] == 18
+    big = q(60000)
+    assert big["gemm2_kernel"] == 14 and big["block_m2"] == big["block_m"]
+    with pytest.raises(moe.MoEError) as ei:
+        q(60000, force_config=41)
+    assert ei.value.status == -6

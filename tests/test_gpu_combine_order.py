@@ -150,15 +150,17 @@ def test_mxfp4_combine_order(fp4_513, T):
     assert (want == out).all(), f"{int((want != out).sum())} elements differ from the stated order"
 
 
-def test_combine_entry_point_order_with_skipped_slots():
+@pytest.mark.parametrize("lo,hi", [(-20, 21), (-140, -120)])
+def test_combine_entry_point_order_with_skipped_slots(lo, hi):
     """moe_combine on strided rows with invalid ids, zero and negative
     weights, and magnitudes spread over 2^-20 .. 2^20 (so the fp32 sums
-    round often): the emulation of the stated order, bit for bit."""
+    round often), or down where products and sums are fp32 and bf16
+    subnormals: the emulation of the stated order, bit for bit."""
     T, k, H, E = 37, 12, 512, 64
     g = torch.Generator(device=DEV).manual_seed(5)
-    ybuf = torch.randn(T, k + 2, H, generator=g, device=DEV)
-    ybuf *= torch.exp2(torch.randint(-20, 21, (T, k + 2, 1), generator=g, device=DEV).float())
-    y = ybuf.to(torch.bfloat16)[:, 1:k + 1, :]
+    ybuf = torch.randn(T, k + 2, H, generator=g, device=DEV, dtype=torch.float64)
+    ybuf *= torch.exp2(torch.randint(lo, hi, (T, k + 2, 1), generator=g, device=DEV).double())
+    y = ybuf.to(torch.bfloat16)[:, 1:k + 1, :]   # rounded from fp64 (keeps bf16 subnormals)
     ids = torch.randint(-3, E + 3, (T, k), generator=g, device=DEV, dtype=torch.int32)
     w = torch.randn(T, k, generator=g, device=DEV)
     w[0, 0] = 0.0
