@@ -570,7 +570,11 @@ int plan_fused(const moe_fused_args_t* a, Plan* pl) {
     const bool x_direct = a->x.stride[1] == 1 && aligned16(a->x.data) &&
                           (T <= 1 || (a->x.stride[0] * 2) % 16 == 0);
     pl->norm = norm;
-    pl->pack_x = !fp4 && !x_direct && !norm;
+    // bf16 rows with a non-unit last-dim stride are laid out into the
+    // workspace for the GEMMs that stage whole 16-byte row chunks (one pass,
+    // coalesced along the stride-1 dimension); gemm1 per slot reads x
+    // through both strides itself
+    pl->pack_x = !fp4 && !x_direct && !norm && !pl->small1;
     {
         // the tiled kernels address every operand row with a 32-bit offset
         const int64_t eb = fp4 ? 1 : 2;
