@@ -734,6 +734,290 @@ struct StageTimer {
     }
 };
 
+// Calls whose tokens exceed what one launch sequence can address (tiled
+// operand offsets of 2^31 bytes, thread counts, T*k) run in chunks of this
+// many tokens. Tokens are independent and every chunk takes the whole
+// call's configuration (the bucket of the first chunk is the whole call's:
+// buckets stop at 32768), so the result is what one launch would give.
+constexpr int64_t kChunkT = 32768;
+
+// The call restricted to tokens [t0, t0 + n): the per-token tensors' views
+// (x, ids, weights, and out or y_rows) start at row t0 and hold n rows.
+moe_fused_args_t token_slice(const moe_fused_args_t& a, int64_t t0, int64_t n) {
+    moe_fused_args_t c = a;
+    auto cut = [&](moe_tensor_t& t, int eb) {
+        if (t.data) t.data = (char*)t.data + t0 * t.stride[0] * eb;
+        t.size[0] = n;
+    };
+    cut(c.x, 2);
+    cut(c.topk_ids, 4);
+    cut(c.topk_weights, 4);
+    if (c.y_rows.data)
+        cut(c.y_rows, 2);
+    else
+        cut(c.out, 2);
+    return c;
+}
+
+// plan_fused, or, when the whole call is too large for one launch sequence
+// and the configuration is the built-in choice, the plan of one chunk of
+// kChunkT tokens (*chunk = kChunkT; 0 when the call runs whole).
+int plan_auto(const moe_fused_args_t* a, Plan* pl, int64_t* chunk) {
+    *chunk = 0;
+    const int rc = plan_fused(a, pl);
+    if (rc != MOE_ERR_UNSUPPORTED || a->force_config >= 0 || a->x.size[0] <= kChunkT) return rc;
+    const std::string why = g_last_error;
+    const moe_fused_args_t c = token_slice(*a, 0, kChunkT);
+    if (plan_fused(&c, pl) != MOE_OK) {
+        g_last_error = why;
+        return rc;
+    }
+    *chunk = kChunkT;
+    return MOE_OK;
+}
+
+// The launches of one planned fused call: align, (prepare), gemm1 + act,
+// gemm2, combine. The plan has been checked; base is the workspace.
+int run_fused(const moe_fused_args_t& a, const Plan& pl, char* base, hipStream_t s) {
+    const StageTimer tm{a.stage_events, s};
+    const bool fp4 = pl.mode == MOE_MODE_MXFP4;
+    int32_t *sorted[2], *bexp[2], *npad[2];
+    for (int g = 0; g < 2; ++g) {
+        sorted[g] = (int32_t*)(base + pl.off_sorted[g]);
+        bexp[g] = (int32_t*)(base + pl.off_bexp[g]);
+        npad[g] = (int32_t*)(base + pl.off_npad[g]);
+    }
+    hipError_t e;
+
+    // MXFP4 activation quantisation: its own launch in stage 1, or folded
+    // into the single-workgroup align launch of stage 0
+    QuantParams qp{};
+    if (fp4) {
+        qp.src = (const uint16_t*)a.x.data;
+        qp.E = 1;
+        qp.R = pl.T;
+        qp.K = pl.H;
+        qp.ss_r = a.x.stride[0];
+        qp.ss_k = a.x.stride[1];
+        qp.codes = (uint8_t*)(base + pl.off_x);
+        qp.cs_r = pl.H / 2;
+        qp.scales = (uint8_t*)(base + pl.off_xs);
+        qp.xs_r = pl.H / 32;
+    }
+    const bool quant_in_align = fp4 && !pl.norm && align_single_launch(pl.A, (int32_t)pl.E);
+
+    // stage 0: align; when the two GEMMs use different block sizes, the same
+    // pass writes the second padded layout too
+    tm.begin(0);
+    if (!pl.small1) {
+        AlignParams ap{};
+        ap.ids = (const int32_t*)a.topk_ids.data;
+        ap.is_t = a.topk_ids.stride[0];
+        ap.is_j = a.topk_ids.stride[1];
+        ap.T = (int32_t)pl.T;
+        ap.k = (int32_t)pl.k;
+        ap.A = (int32_t)pl.A;
+        ap.E = (int32_t)pl.E;
+        ap.e_off = pl.e_off;
+        ap.bm = pl.ks[0].bm;
+        ap.cap = (int32_t)pl.cap[0];
+        ap.sorted = sorted[0];
+        ap.block_expert = bexp[0];
+        ap.n_padded = npad[0];
+        ap.counts = (int32_t*)(base + pl.off_counts);
+        if (pl.two_aligns) {
+            ap.bm2 = pl.ks[1].bm;
+            ap.cap2 = (int32_t)pl.cap[1];
+            ap.sorted2 = sorted[1];
+            ap.block_expert2 = bexp[1];
+            ap.n_padded2 = npad[1];
+        }
+        e = quant_in_align ? launch_align_with_quant(ap, qp, s) : launch_align(ap, s);
+        if (e != hipSuccess) return hip_fail(e, "align");
+    }
+    tm.end(0);
+
+    // stage 1: prepare the activation operand
+    tm.begin(1);
+    const void* a_op = a.x.data;
+    int64_t a_row = a.x.stride[0];
+    if (pl.norm) {
+        NormParams np{};
+        norm_params(&np, a.x, a.norm_weight, a.norm_eps);
+        np.out = (uint16_t*)(base + pl.off_xn);
+        np.os_t = pl.H;
+        np.os_h = 1;
+        if ((e = launch_rmsnorm(np, s)) != hipSuccess) return hip_fail(e, "rmsnorm");
+        a_op = base + pl.off_xn;
+        a_row = pl.H;
+        qp.src = (const uint16_t*)(base + pl.off_xn);
+        qp.ss_r = pl.H;
+        qp.ss_k = 1;
+    }
+    if (fp4 && !pl.small1) {
+        if (!quant_in_align && (e = launch_quant_mxfp4(qp, s)) != hipSuccess) return hip_fail(e, "quant x");
+        a_op = base + pl.off_x;
+        a_row = pl.H / 2;
+    } else if (pl.pack_x) {
+        PackParams pp{};
+        pp.src = (const uint16_t*)a.x.data;
+        pp.s_t = a.x.stride[0];
+        pp.s_h = a.x.stride[1];
+        pp.dst = (uint16_t*)(base + pl.off_x);
+        pp.T = pl.T;
+        pp.H = pl.H;
+        if ((e = launch_pack_bf16(pp, s)) != hipSuccess) return hip_fail(e, "pack x");
+        a_op = base + pl.off_x;
+        a_row = pl.H;
+    }
+    tm.end(1);
+
+    // launch one GEMM with its resolved kernel
+    auto launch = [&](int g, const GemmParams& gp) -> hipError_t {
+        const KSpec& k = pl.ks[g];
+        if (k.tile) return launch_gemm_tile(fp4 ? 1 : 0, k.tile - 1, g + 1, gp, s);
+        GemmKernelId id{fp4 ? 1 : 0, g + 1, k.bm, k.wk,
+                        gemm_ring_steps(pl.mode, k.bm, k.nb, k.wk, (g == 0 ? pl.H : pl.I) / k.wk), k.nb, k.nt};
+        return launch_gemm(id, gp, s);
+    };
+    // stage 2: gemm1 + SiLU(gate) * up
+    tm.begin(2);
+    if (pl.small1) {
+        // per slot, from the bf16 activation (or its normalised rows)
+        Gemm1SmallParams sp{};
+        sp.x = pl.norm ? (const uint16_t*)(base + pl.off_xn) : (const uint16_t*)a.x.data;
+        sp.xs_t = pl.norm ? pl.H : a.x.stride[0];
+        sp.xs_h = pl.norm ? 1 : (pl.H > 1 ? a.x.stride[1] : 1);
+        sp.gate = (const uint8_t*)a.gate.data;
+        sp.up = (const uint8_t*)a.up.data;
+        sp.g_e = a.gate.stride[0];
+        sp.g_r = a.gate.stride[1];
+        sp.u_e = a.up.stride[0];
+        sp.u_r = a.up.stride[1];
+        sp.gate_sc = (const uint8_t*)a.gate_scale.data;
+        sp.up_sc = (const uint8_t*)a.up_scale.data;
+        sp.gs_e = a.gate_scale.stride[0];
+        sp.gs_r = a.gate_scale.stride[1];
+        sp.us_e = a.up_scale.stride[0];
+        sp.us_r = a.up_scale.stride[1];
+        sp.ids = (const int32_t*)a.topk_ids.data;
+        sp.is_t = a.topk_ids.stride[0];
+        sp.is_j = a.topk_ids.stride[1];
+        sp.e_off = pl.e_off;
+        sp.E = (int32_t)pl.E;
+        sp.k = (int32_t)pl.k;
+        sp.A = (int32_t)pl.A;
+        sp.H = (int32_t)pl.H;
+        sp.I = (int32_t)pl.I;
+        sp.hq = (uint8_t*)(base + pl.off_h);
+        sp.hs = (uint8_t*)(base + pl.off_hs);
+        if (!fp4) {
+            // bf16 weights: byte strides
+            sp.g_e *= 2;
+            sp.g_r *= 2;
+            sp.u_e *= 2;
+            sp.u_r *= 2;
+        }
+        if ((e = fp4 ? launch_gemm1_small(sp, s) : launch_gemm1_small_bf16(sp, s)) != hipSuccess)
+            return hip_fail(e, "gemm1");
+    }
+    GemmParams g1{};
+    g1.sorted = sorted[0];
+    g1.block_expert = bexp[0];
+    g1.n_padded = npad[0];
+    g1.A = (int32_t)pl.A;
+    g1.k = (int32_t)pl.k;
+    g1.E = (int32_t)pl.E;
+    g1.a = a_op;
+    g1.a_row = a_row;
+    g1.a_sc = fp4 ? (const uint8_t*)(base + pl.off_xs) : nullptr;
+    g1.a_sc_row = pl.H / 32;
+    g1.b0 = a.gate.data;
+    g1.b1 = a.up.data;
+    g1.b0_e = a.gate.stride[0];
+    g1.b0_r = a.gate.stride[1];
+    g1.b1_e = a.up.stride[0];
+    g1.b1_r = a.up.stride[1];
+    if (fp4) {
+        g1.b0_sc = (const uint8_t*)a.gate_scale.data;
+        g1.b1_sc = (const uint8_t*)a.up_scale.data;
+        g1.b0sc_e = a.gate_scale.stride[0];
+        g1.b0sc_r = a.gate_scale.stride[1];
+        g1.b1sc_e = a.up_scale.stride[0];
+        g1.b1sc_r = a.up_scale.stride[1];
+    }
+    g1.K = (int32_t)pl.H;
+    g1.N = (int32_t)pl.I;
+    g1.out = base + pl.off_h;
+    g1.out_sc = fp4 ? (uint8_t*)(base + pl.off_hs) : nullptr;
+    g1.n_tile_groups = 2;
+    g1.max_mblocks = (int32_t)(pl.cap[0] / pl.ks[0].bm);
+    if (!pl.small1 && (e = launch(0, g1)) != hipSuccess) return hip_fail(e, "gemm1");
+    tm.end(2);
+
+    // the combine's arguments (the separate combine, or folded into gemm2)
+    CombineParams cp{};
+    cp.y = reinterpret_cast<const uint16_t*>(base + pl.off_y);
+    cp.ys_t = pl.k * pl.H;
+    cp.ys_j = pl.H;
+    cp.e_off = pl.e_off;
+    cp.ids = (const int32_t*)a.topk_ids.data;
+    cp.is_t = a.topk_ids.stride[0];
+    cp.is_j = a.topk_ids.stride[1];
+    cp.w = (const float*)a.topk_weights.data;
+    cp.ws_t = a.topk_weights.stride[0];
+    cp.ws_j = a.topk_weights.stride[1];
+    cp.out = (uint16_t*)a.out.data;
+    cp.os_t = a.out.stride[0];
+    cp.os_h = a.out.stride[1];
+    cp.T = (int32_t)pl.T;
+    cp.k = (int32_t)pl.k;
+    cp.E = (int32_t)pl.E;
+    cp.H = (int32_t)pl.H;
+
+    // stage 3: gemm2
+    tm.begin(3);
+    GemmParams g2{};
+    g2.sorted = sorted[1];
+    g2.block_expert = bexp[1];
+    g2.n_padded = npad[1];
+    g2.A = (int32_t)pl.A;
+    g2.k = (int32_t)pl.k;
+    g2.E = (int32_t)pl.E;
+    g2.a = base + pl.off_h;
+    g2.a_row = fp4 ? pl.I / 2 : pl.I;
+    g2.a_sc = fp4 ? (const uint8_t*)(base + pl.off_hs) : nullptr;
+    g2.a_sc_row = pl.I / 32;
+    g2.b0 = a.w2.data;
+    g2.b0_e = a.w2.stride[0];
+    g2.b0_r = a.w2.stride[1];
+    if (fp4) {
+        g2.b0_sc = (const uint8_t*)a.w2_scale.data;
+        g2.b0sc_e = a.w2_scale.stride[0];
+        g2.b0sc_r = a.w2_scale.stride[1];
+    }
+    g2.K = (int32_t)pl.I;
+    g2.N = (int32_t)pl.H;
+    g2.out = pl.y_out ? a.y_rows.data : (void*)(base + pl.off_y);
+    g2.out_row = pl.y_row;
+    g2.n_tile_groups = 2;
+    g2.max_mblocks = (int32_t)(pl.cap[1] / pl.ks[1].bm);
+    if (pl.fuse) {
+        const Gemm2CombineParams gc{g2, cp};
+        if ((e = fp4 ? launch_gemm2_combine(gc, s) : launch_gemm2_combine_bf16(gc, s)) != hipSuccess)
+            return hip_fail(e, "gemm2");
+    } else if ((e = launch(1, g2)) != hipSuccess) {
+        return hip_fail(e, "gemm2");
+    }
+    tm.end(3);
+
+    // stage 4: combine (the caller combines y_rows itself; fused into gemm2)
+    tm.begin(4);
+    if (!pl.y_out && !pl.fuse && (e = launch_combine(cp, s)) != hipSuccess) return hip_fail(e, "combine");
+    tm.end(4);
+    return ok();
+}
+
 }  // namespace
 
 int moe::report_error(int status, const char* what, const char* detail) {
@@ -980,7 +1264,8 @@ int moe_combine(const moe_tensor_t* y_rows, const moe_tensor_t* topk_ids, const 
 int moe_query_config(const moe_fused_args_t* args, moe_config_t* cfg) {
     if (!cfg) return fail(MOE_ERR_NULL, "cfg is NULL");
     Plan pl;
-    int rc = plan_fused(args, &pl);
+    int64_t chunk = 0;
+    int rc = plan_auto(args, &pl, &chunk);
     if (rc) return rc;
     cfg->bucket = bucket_of(pl.T);
     cfg->block_m = pl.ks[0].bm;
@@ -998,7 +1283,8 @@ int moe_query_config(const moe_fused_args_t* args, moe_config_t* cfg) {
 int moe_fused_workspace_size(const moe_fused_args_t* args, size_t* bytes) {
     if (!bytes) return fail(MOE_ERR_NULL, "bytes is NULL");
     Plan pl;
-    int rc = plan_fused(args, &pl);
+    int64_t chunk = 0;
+    int rc = plan_auto(args, &pl, &chunk);
     if (rc) return rc;
     *bytes = pl.total;
     return ok();
@@ -1006,250 +1292,30 @@ int moe_fused_workspace_size(const moe_fused_args_t* args, size_t* bytes) {
 
 int moe_fused_fwd(const moe_fused_args_t* args, void* ws, size_t ws_bytes, moe_stream_t stream) {
     Plan pl;
-    int rc = plan_fused(args, &pl);
+    int64_t chunk = 0;
+    int rc = plan_auto(args, &pl, &chunk);
     if (rc) return rc;
-    if (pl.T == 0) return ok();
+    if (args->x.size[0] == 0) return ok();
     if (!ws || ((uintptr_t)ws & 255u) || ws_bytes < pl.total)
         return fail(MOE_ERR_WORKSPACE, "fused forward needs %zu bytes of 256-byte aligned workspace", pl.total);
-    const moe_fused_args_t& a = *args;
     hipStream_t s = (hipStream_t)stream;
     char* base = (char*)ws;
-    const StageTimer tm{a.stage_events, s};
-    const bool fp4 = pl.mode == MOE_MODE_MXFP4;
-    int32_t *sorted[2], *bexp[2], *npad[2];
-    for (int g = 0; g < 2; ++g) {
-        sorted[g] = (int32_t*)(base + pl.off_sorted[g]);
-        bexp[g] = (int32_t*)(base + pl.off_bexp[g]);
-        npad[g] = (int32_t*)(base + pl.off_npad[g]);
+    if (!chunk) return run_fused(*args, pl, base, s);
+    // token chunks, each with the configuration of the first (the whole
+    // call's bucket); both chunk shapes are planned before any launch
+    const int64_t T = args->x.size[0], tail = T % chunk;
+    Plan pl_tail;
+    if (tail) {
+        moe_fused_args_t c = token_slice(*args, T - tail, tail);
+        c.force_config = pl.cfg_index;
+        if ((rc = plan_fused(&c, &pl_tail))) return rc;
     }
-    hipError_t e;
-
-    // MXFP4 activation quantisation: its own launch in stage 1, or folded
-    // into the single-workgroup align launch of stage 0
-    QuantParams qp{};
-    if (fp4) {
-        qp.src = (const uint16_t*)a.x.data;
-        qp.E = 1;
-        qp.R = pl.T;
-        qp.K = pl.H;
-        qp.ss_r = a.x.stride[0];
-        qp.ss_k = a.x.stride[1];
-        qp.codes = (uint8_t*)(base + pl.off_x);
-        qp.cs_r = pl.H / 2;
-        qp.scales = (uint8_t*)(base + pl.off_xs);
-        qp.xs_r = pl.H / 32;
+    for (int64_t t0 = 0; t0 < T; t0 += chunk) {
+        const int64_t n = std::min(chunk, T - t0);
+        moe_fused_args_t c = token_slice(*args, t0, n);
+        c.force_config = pl.cfg_index;
+        if ((rc = run_fused(c, n == chunk ? pl : pl_tail, base, s))) return rc;
     }
-    const bool quant_in_align = fp4 && !pl.norm && align_single_launch(pl.A, (int32_t)pl.E);
-
-    // stage 0: align; when the two GEMMs use different block sizes, the same
-    // pass writes the second padded layout too
-    tm.begin(0);
-    if (!pl.small1) {
-        AlignParams ap{};
-        ap.ids = (const int32_t*)a.topk_ids.data;
-        ap.is_t = a.topk_ids.stride[0];
-        ap.is_j = a.topk_ids.stride[1];
-        ap.T = (int32_t)pl.T;
-        ap.k = (int32_t)pl.k;
-        ap.A = (int32_t)pl.A;
-        ap.E = (int32_t)pl.E;
-        ap.e_off = pl.e_off;
-        ap.bm = pl.ks[0].bm;
-        ap.cap = (int32_t)pl.cap[0];
-        ap.sorted = sorted[0];
-        ap.block_expert = bexp[0];
-        ap.n_padded = npad[0];
-        ap.counts = (int32_t*)(base + pl.off_counts);
-        if (pl.two_aligns) {
-            ap.bm2 = pl.ks[1].bm;
-            ap.cap2 = (int32_t)pl.cap[1];
-            ap.sorted2 = sorted[1];
-            ap.block_expert2 = bexp[1];
-            ap.n_padded2 = npad[1];
-        }
-        e = quant_in_align ? launch_align_with_quant(ap, qp, s) : launch_align(ap, s);
-        if (e != hipSuccess) return hip_fail(e, "align");
-    }
-    tm.end(0);
-
-    // stage 1: prepare the activation operand
-    tm.begin(1);
-    const void* a_op = a.x.data;
-    int64_t a_row = a.x.stride[0];
-    if (pl.norm) {
-        NormParams np{};
-        norm_params(&np, a.x, a.norm_weight, a.norm_eps);
-        np.out = (uint16_t*)(base + pl.off_xn);
-        np.os_t = pl.H;
-        np.os_h = 1;
-        if ((e = launch_rmsnorm(np, s)) != hipSuccess) return hip_fail(e, "rmsnorm");
-        a_op = base + pl.off_xn;
-        a_row = pl.H;
-        qp.src = (const uint16_t*)(base + pl.off_xn);
-        qp.ss_r = pl.H;
-        qp.ss_k = 1;
-    }
-    if (fp4 && !pl.small1) {
-        if (!quant_in_align && (e = launch_quant_mxfp4(qp, s)) != hipSuccess) return hip_fail(e, "quant x");
-        a_op = base + pl.off_x;
-        a_row = pl.H / 2;
-    } else if (pl.pack_x) {
-        PackParams pp{};
-        pp.src = (const uint16_t*)a.x.data;
-        pp.s_t = a.x.stride[0];
-        pp.s_h = a.x.stride[1];
-        pp.dst = (uint16_t*)(base + pl.off_x);
-        pp.T = pl.T;
-        pp.H = pl.H;
-        if ((e = launch_pack_bf16(pp, s)) != hipSuccess) return hip_fail(e, "pack x");
-        a_op = base + pl.off_x;
-        a_row = pl.H;
-    }
-    tm.end(1);
-
-    // launch one GEMM with its resolved kernel
-    auto launch = [&](int g, const GemmParams& gp) -> hipError_t {
-        const KSpec& k = pl.ks[g];
-        if (k.tile) return launch_gemm_tile(fp4 ? 1 : 0, k.tile - 1, g + 1, gp, s);
-        GemmKernelId id{fp4 ? 1 : 0, g + 1, k.bm, k.wk,
-                        gemm_ring_steps(pl.mode, k.bm, k.nb, k.wk, (g == 0 ? pl.H : pl.I) / k.wk), k.nb, k.nt};
-        return launch_gemm(id, gp, s);
-    };
-    // stage 2: gemm1 + SiLU(gate) * up
-    tm.begin(2);
-    if (pl.small1) {
-        // per slot, from the bf16 activation (or its normalised rows)
-        Gemm1SmallParams sp{};
-        sp.x = pl.norm ? (const uint16_t*)(base + pl.off_xn) : (const uint16_t*)a.x.data;
-        sp.xs_t = pl.norm ? pl.H : a.x.stride[0];
-        sp.xs_h = pl.norm ? 1 : (pl.H > 1 ? a.x.stride[1] : 1);
-        sp.gate = (const uint8_t*)a.gate.data;
-        sp.up = (const uint8_t*)a.up.data;
-        sp.g_e = a.gate.stride[0];
-        sp.g_r = a.gate.stride[1];
-        sp.u_e = a.up.stride[0];
-        sp.u_r = a.up.stride[1];
-        sp.gate_sc = (const uint8_t*)a.gate_scale.data;
-        sp.up_sc = (const uint8_t*)a.up_scale.data;
-        sp.gs_e = a.gate_scale.stride[0];
-        sp.gs_r = a.gate_scale.stride[1];
-        sp.us_e = a.up_scale.stride[0];
-        sp.us_r = a.up_scale.stride[1];
-        sp.ids = (const int32_t*)a.topk_ids.data;
-        sp.is_t = a.topk_ids.stride[0];
-        sp.is_j = a.topk_ids.stride[1];
-        sp.e_off = pl.e_off;
-        sp.E = (int32_t)pl.E;
-        sp.k = (int32_t)pl.k;
-        sp.A = (int32_t)pl.A;
-        sp.H = (int32_t)pl.H;
-        sp.I = (int32_t)pl.I;
-        sp.hq = (uint8_t*)(base + pl.off_h);
-        sp.hs = (uint8_t*)(base + pl.off_hs);
-        if (!fp4) {
-            // bf16 weights: byte strides
-            sp.g_e *= 2;
-            sp.g_r *= 2;
-            sp.u_e *= 2;
-            sp.u_r *= 2;
-        }
-        if ((e = fp4 ? launch_gemm1_small(sp, s) : launch_gemm1_small_bf16(sp, s)) != hipSuccess)
-            return hip_fail(e, "gemm1");
-    }
-    GemmParams g1{};
-    g1.sorted = sorted[0];
-    g1.block_expert = bexp[0];
-    g1.n_padded = npad[0];
-    g1.A = (int32_t)pl.A;
-    g1.k = (int32_t)pl.k;
-    g1.E = (int32_t)pl.E;
-    g1.a = a_op;
-    g1.a_row = a_row;
-    g1.a_sc = fp4 ? (const uint8_t*)(base + pl.off_xs) : nullptr;
-    g1.a_sc_row = pl.H / 32;
-    g1.b0 = a.gate.data;
-    g1.b1 = a.up.data;
-    g1.b0_e = a.gate.stride[0];
-    g1.b0_r = a.gate.stride[1];
-    g1.b1_e = a.up.stride[0];
-    g1.b1_r = a.up.stride[1];
-    if (fp4) {
-        g1.b0_sc = (const uint8_t*)a.gate_scale.data;
-        g1.b1_sc = (const uint8_t*)a.up_scale.data;
-        g1.b0sc_e = a.gate_scale.stride[0];
-        g1.b0sc_r = a.gate_scale.stride[1];
-        g1.b1sc_e = a.up_scale.stride[0];
-        g1.b1sc_r = a.up_scale.stride[1];
-    }
-    g1.K = (int32_t)pl.H;
-    g1.N = (int32_t)pl.I;
-    g1.out = base + pl.off_h;
-    g1.out_sc = fp4 ? (uint8_t*)(base + pl.off_hs) : nullptr;
-    g1.n_tile_groups = 2;
-    g1.max_mblocks = (int32_t)(pl.cap[0] / pl.ks[0].bm);
-    if (!pl.small1 && (e = launch(0, g1)) != hipSuccess) return hip_fail(e, "gemm1");
-    tm.end(2);
-
-    // the combine's arguments (the separate combine, or folded into gemm2)
-    CombineParams cp{};
-    cp.y = reinterpret_cast<const uint16_t*>(base + pl.off_y);
-    cp.ys_t = pl.k * pl.H;
-    cp.ys_j = pl.H;
-    cp.e_off = pl.e_off;
-    cp.ids = (const int32_t*)a.topk_ids.data;
-    cp.is_t = a.topk_ids.stride[0];
-    cp.is_j = a.topk_ids.stride[1];
-    cp.w = (const float*)a.topk_weights.data;
-    cp.ws_t = a.topk_weights.stride[0];
-    cp.ws_j = a.topk_weights.stride[1];
-    cp.out = (uint16_t*)a.out.data;
-    cp.os_t = a.out.stride[0];
-    cp.os_h = a.out.stride[1];
-    cp.T = (int32_t)pl.T;
-    cp.k = (int32_t)pl.k;
-    cp.E = (int32_t)pl.E;
-    cp.H = (int32_t)pl.H;
-
-    // stage 3: gemm2
-    tm.begin(3);
-    GemmParams g2{};
-    g2.sorted = sorted[1];
-    g2.block_expert = bexp[1];
-    g2.n_padded = npad[1];
-    g2.A = (int32_t)pl.A;
-    g2.k = (int32_t)pl.k;
-    g2.E = (int32_t)pl.E;
-    g2.a = base + pl.off_h;
-    g2.a_row = fp4 ? pl.I / 2 : pl.I;
-    g2.a_sc = fp4 ? (const uint8_t*)(base + pl.off_hs) : nullptr;
-    g2.a_sc_row = pl.I / 32;
-    g2.b0 = a.w2.data;
-    g2.b0_e = a.w2.stride[0];
-    g2.b0_r = a.w2.stride[1];
-    if (fp4) {
-        g2.b0_sc = (const uint8_t*)a.w2_scale.data;
-        g2.b0sc_e = a.w2_scale.stride[0];
-        g2.b0sc_r = a.w2_scale.stride[1];
-    }
-    g2.K = (int32_t)pl.I;
-    g2.N = (int32_t)pl.H;
-    g2.out = pl.y_out ? a.y_rows.data : (void*)(base + pl.off_y);
-    g2.out_row = pl.y_row;
-    g2.n_tile_groups = 2;
-    g2.max_mblocks = (int32_t)(pl.cap[1] / pl.ks[1].bm);
-    if (pl.fuse) {
-        const Gemm2CombineParams gc{g2, cp};
-        if ((e = fp4 ? launch_gemm2_combine(gc, s) : launch_gemm2_combine_bf16(gc, s)) != hipSuccess)
-            return hip_fail(e, "gemm2");
-    } else if ((e = launch(1, g2)) != hipSuccess) {
-        return hip_fail(e, "gemm2");
-    }
-    tm.end(3);
-
-    // stage 4: combine (the caller combines y_rows itself; fused into gemm2)
-    tm.begin(4);
-    if (!pl.y_out && !pl.fuse && (e = launch_combine(cp, s)) != hipSuccess) return hip_fail(e, "combine");
-    tm.end(4);
     return ok();
 }
 

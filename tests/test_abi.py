@@ -332,3 +332,31 @@ def test_mxfp4_register_gemm2_falls_back_past_4gb_of_y():
     with pytest.raises(moe.MoEError) as ei:
         q(60000, force_config=41)
     assert ei.value.status == -6
+
+
+def test_oversized_calls_run_in_token_chunks():
+    """A bf16 Qwen3-235B-shaped call with 90000 tokens (its tiled gemm2
+    operands would pass 2^31 bytes) is planned as chunks of 32768 tokens:
+    accepted, with the workspace and configuration of one full chunk; a
+    forced configuration that cannot take the whole call still fails."""
+    def args(T, **kw):
+        H, I, E, k = 4096, 1536, 128, 8
+        def view(shape, dtype, row=16):
+            n = len(shape)
+            st = [row] * (n - 1) + [1]
+            return torch.empty(1 + sum((s - 1) * t for s, t in zip(shape, st)) + 64, dtype=dtype).as_strided(shape, st)
+        x = view((T, H), torch.bfloat16)
+        g = view((E, I, H), torch.bfloat16)
+        w2 = view((E, H, I), torch.bfloat16)
+        ids, w = view((T, k), torch.int32, 1), view((T, k), torch.float32, 1)
+        out = torch.empty(T * H + 64, dtype=torch.bfloat16).as_strided((T, H), (H, 1))
+        return (x, g, g, w2, ids, w), dict(out=out, **kw)
+    a, kw = args(90000)
+    big = moe.moe_query_config(*a, **kw)
+    a1, kw1 = args(32768)
+    one = moe.moe_query_config(*a1, **kw1)
+    assert big == one and big["bucket"] == 32768
+    assert moe.moe_fused_workspace_size(*a, **kw) == moe.moe_fused_workspace_size(*a1, **kw1)
+    with pytest.raises(moe.MoEError) as ei:
+        moe.moe_query_config(*a, force_config=big["config_index"], **kw)
+    assert ei.value.status == -6

@@ -537,3 +537,22 @@ def test_mxfp4_long_rows_every_config_against_oracle():
         assert rel_l2(got, acc) <= FP4_TOL and err_ratio(got, acc) <= FP4_ERR_RATIO, c
         ran += 1
     assert ran >= 30
+
+
+def test_bf16_oversized_call_in_token_chunks(w235):
+    """90000 tokens on the bf16 Qwen3-235B-shaped layer run as chunks of
+    32768 tokens with the whole call's configuration: every chunk's rows
+    equal a call on those rows alone (bit for bit), and sampled tokens,
+    including the experts' ragged tail blocks, match the oracle."""
+    sh = W.QWEN3_235B_BF16
+    T = 90000
+    inp = W.make_inputs(sh, T, seed=11, device=DEV, routing="replay", weights=w235)
+    gate, up = W.packed_views(inp["w13"], sh.inter)
+    ids, w = inp["topk_ids"], inp["topk_weights"]
+    q = moe.moe_query_config(inp["x"], gate, up, inp["w2"], ids, w)
+    out = moe.moe_fused_fwd(inp["x"], gate, up, inp["w2"], ids, w).clone()
+    for t0, n in ((32768, 32768), (65536, T - 65536)):
+        part = moe.moe_fused_fwd(inp["x"][t0:t0 + n], gate, up, inp["w2"], ids[t0:t0 + n], w[t0:t0 + n],
+                                 force_config=q["config_index"])
+        assert torch.equal(part, out[t0:t0 + n]), t0
+    _check_bf16(inp, out, np_(ids), np_(w), tail_tokens(np_(ids), sh.experts, 256))
