@@ -140,7 +140,7 @@ __device__ int block_exclusive_scan(int* v, int n, int* wave_tot) {
 // A from an earlier pass; the scatter overwrites the real ones.)
 template <int NT>
 __device__ void layout_experts(const AlignParams& p, int bm, int32_t* block_expert, int32_t* n_padded,
-                               const int* tot, int* off, int* scratch) {
+                               int32_t* expert_block, const int* tot, int* off, int* scratch) {
     const int E = p.E;
     for (int e = threadIdx.x; e < E; e += NT) off[e] = (tot[e] + bm - 1) / bm * bm;
     __syncthreads();
@@ -157,6 +157,10 @@ __device__ void layout_experts(const AlignParams& p, int bm, int32_t* block_expe
         }
         block_expert[b] = lo;
     }
+    if (expert_block) {
+        for (int e = threadIdx.x; e < E; e += NT) expert_block[e] = off[e] / bm;
+        if (threadIdx.x == 0) expert_block[E] = nblk;
+    }
     if (threadIdx.x == 0) *n_padded = npad;
 }
 
@@ -170,8 +174,9 @@ __device__ __forceinline__ void fill_sentinels(const AlignParams& p, int i0, int
 // both layouts (the second only when asked for)
 template <int NT>
 __device__ void layout_both(const AlignParams& p, const int* tot, int* off, int* off2, int* scratch) {
-    layout_experts<NT>(p, p.bm, p.block_expert, p.n_padded, tot, off, scratch);
-    if (p.sorted2) layout_experts<NT>(p, p.bm2, p.block_expert2, p.n_padded2, tot, off2, scratch);
+    layout_experts<NT>(p, p.bm, p.block_expert, p.n_padded, p.expert_block, tot, off, scratch);
+    if (p.sorted2)
+        layout_experts<NT>(p, p.bm2, p.block_expert2, p.n_padded2, p.expert_block2, tot, off2, scratch);
 }
 
 // Whole align in one workgroup.

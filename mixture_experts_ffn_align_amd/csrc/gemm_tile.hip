@@ -83,9 +83,6 @@ struct TileShape {
     static constexpr int kScOff = kRows * kRowBytes;
     static constexpr int kScPlane = kScLoads * kThreads * kScStep;   // one k-step's scales
     static constexpr int kBuf = kScOff + SUBS * kScPlane;
-    // 32 consecutive row blocks (a few experts) share one weight tile at a
-    // time on one XCD; a group never holds empty slots
-    static constexpr int kGroupM = 32;
 };
 
 // 16-byte chunk position of chunk c in tile row r (rows of 64 or 128 bytes;
@@ -125,28 +122,32 @@ void gemm_tile(GemmParams p) {
     // ---- tile mapping
     constexpr int tile_cols = STAGE == 1 ? BW / 2 : BW;
     const int n_tiles = p.N / tile_cols;
-    // Workgroup b runs on XCD b % 8 (the dispatcher deals workgroups to the
-    // XCDs in turn) as that XCD's j-th workgroup, j = b / 8. The logical
-    // tiles, groups of kGroupM row blocks of one weight tile in order, are
-    // cut into 8 equal contiguous ranges, one per XCD: a group's weight tile
-    // then comes through one XCD's L2, neighbouring groups (which share the
-    // expert at their boundary) stay on the same XCD, and every XCD gets the
-    // same number of real tiles. The grid is sized by the sorted capacity;
-    // the count of real row blocks (the padded length the align wrote) is
+    // Logical tiles in expert-major order: for each expert, its weight tiles
+    // in turn, and for each weight tile the expert's row blocks, so the row
+    // blocks that share a weight tile run together and the weight tiles that
+    // share those row blocks run next to them. Workgroup b runs on XCD b % 8
+    // (the dispatcher deals workgroups to the XCDs in turn) as that XCD's
+    // j-th, j = b / 8; the logical tiles are cut into 8 equal contiguous
+    // ranges, one per XCD, so an expert's tiles share one L2 and every XCD
+    // gets the same number of real tiles. The grid is sized by the sorted
+    // capacity; the real block count (the padded length the align wrote) is
     // only known here, so workgroups past the real tiles leave at once.
     const int n_blocks = __builtin_amdgcn_readfirstlane(*p.n_padded) / BM;
-    const uint32_t m_groups = (uint32_t)(n_blocks + TS::kGroupM - 1) / TS::kGroupM;
-    const uint32_t total = m_groups * (uint32_t)n_tiles * TS::kGroupM;
+    const uint32_t total = (uint32_t)n_blocks * (uint32_t)n_tiles;
     const uint32_t per_xcd = (total + 7u) / 8u;
     const uint32_t xcd = blockIdx.x & 7u, j = blockIdx.x >> 3;
     if (j >= per_xcd) return;
     const uint32_t L = xcd * per_xcd + j;
     if (L >= total) return;
-    const uint32_t grp = L / TS::kGroupM, rr = L % TS::kGroupM;
-    const int mb = (int)((grp % m_groups) * TS::kGroupM + rr);
-    const int nt = (int)(grp / m_groups);
-    if (mb >= n_blocks) return;
-    const int e = __builtin_amdgcn_readfirstlane(p.block_expert[mb]);
+    // expert e owns blocks [b0, b0 + nb) and logical tiles
+    // [b0 * n_tiles, (b0 + nb) * n_tiles), so block L / n_tiles is one of its
+    const int eo = __builtin_amdgcn_readfirstlane(p.block_expert[L / (uint32_t)n_tiles]);
+    const int b0 = __builtin_amdgcn_readfirstlane(p.expert_block[eo]);
+    const int nb = __builtin_amdgcn_readfirstlane(p.expert_block[eo + 1]) - b0;
+    const uint32_t r = L - (uint32_t)b0 * (uint32_t)n_tiles;
+    const int nt = (int)(r / (uint32_t)nb);
+    const int mb = b0 + (int)(r % (uint32_t)nb);
+    const int e = eo;
     const int row0 = mb * BM;
     const int n0 = nt * tile_cols;
     // Sentinel rows fill only the end of an expert's last block, so the
@@ -572,10 +573,9 @@ template <int MODE, int STAGE, int BM, int BW, int NW, int SUBS = (MODE == 0 || 
 hipError_t launch_one(const GemmParams& p, hipStream_t s) {
     using TS = TileShape<MODE, BM, BW, NW, SUBS, NBUF>;
     const int64_t n_tiles = p.N / (STAGE == 1 ? BW / 2 : BW);
-    const int64_t m_groups = (p.max_mblocks + TS::kGroupM - 1) / TS::kGroupM;
     // a multiple of 8 workgroups, each XCD's share covering an eighth of
     // the tiles the capacity allows
-    const int64_t grid = (m_groups * n_tiles + 7) / 8 * 8 * TS::kGroupM;
+    const int64_t grid = ((int64_t)p.max_mblocks * n_tiles + 7) / 8 * 8;
     if (grid == 0) return hipSuccess;
     hipLaunchKernelGGL((gemm_tile<MODE, STAGE, BM, BW, NW, SUBS, NBUF, PP>), dim3((unsigned)grid),
                        dim3(TS::kThreads), 0, s, p);

@@ -340,7 +340,8 @@ struct Plan {
     bool fuse;             // gemm2 and the combine in one kernel (no y, no second layout)
     bool small1;           // gemm1 per slot, without the align (implies fuse)
     // workspace offsets
-    size_t off_counts, off_sorted[2], off_bexp[2], off_npad[2], off_x, off_xs, off_xn, off_h, off_hs, off_y, total;
+    size_t off_counts, off_sorted[2], off_bexp[2], off_npad[2], off_eblk[2], off_x, off_xs, off_xn, off_h, off_hs, off_y,
+        total;
 };
 
 int kstep(int mode) { return mode == MOE_MODE_MXFP4 ? 128 : 32; }
@@ -599,11 +600,13 @@ int plan_fused(const moe_fused_args_t* a, Plan* pl) {
             pl->off_sorted[1] = pl->off_sorted[0];
             pl->off_bexp[1] = pl->off_bexp[0];
             pl->off_npad[1] = pl->off_npad[0];
+            pl->off_eblk[1] = pl->off_eblk[0];
             break;
         }
         pl->off_sorted[g] = take((size_t)pl->cap[g] * 4);
         pl->off_bexp[g] = take((size_t)(pl->cap[g] / pl->ks[g].bm) * 4);
         pl->off_npad[g] = take(4);
+        pl->off_eblk[g] = take((size_t)(E + 1) * 4);
     }
     pl->off_x = pl->off_xs = pl->off_xn = 0;
     if (norm) pl->off_xn = take((size_t)T * (size_t)H * 2);   // normalised rows, bf16
@@ -781,11 +784,12 @@ int plan_auto(const moe_fused_args_t* a, Plan* pl, int64_t* chunk) {
 int run_fused(const moe_fused_args_t& a, const Plan& pl, char* base, hipStream_t s) {
     const StageTimer tm{a.stage_events, s};
     const bool fp4 = pl.mode == MOE_MODE_MXFP4;
-    int32_t *sorted[2], *bexp[2], *npad[2];
+    int32_t *sorted[2], *bexp[2], *npad[2], *eblk[2];
     for (int g = 0; g < 2; ++g) {
         sorted[g] = (int32_t*)(base + pl.off_sorted[g]);
         bexp[g] = (int32_t*)(base + pl.off_bexp[g]);
         npad[g] = (int32_t*)(base + pl.off_npad[g]);
+        eblk[g] = (int32_t*)(base + pl.off_eblk[g]);
     }
     hipError_t e;
 
@@ -825,12 +829,14 @@ int run_fused(const moe_fused_args_t& a, const Plan& pl, char* base, hipStream_t
         ap.block_expert = bexp[0];
         ap.n_padded = npad[0];
         ap.counts = (int32_t*)(base + pl.off_counts);
+        ap.expert_block = eblk[0];
         if (pl.two_aligns) {
             ap.bm2 = pl.ks[1].bm;
             ap.cap2 = (int32_t)pl.cap[1];
             ap.sorted2 = sorted[1];
             ap.block_expert2 = bexp[1];
             ap.n_padded2 = npad[1];
+            ap.expert_block2 = eblk[1];
         }
         e = quant_in_align ? launch_align_with_quant(ap, qp, s) : launch_align(ap, s);
         if (e != hipSuccess) return hip_fail(e, "align");
@@ -952,6 +958,7 @@ int run_fused(const moe_fused_args_t& a, const Plan& pl, char* base, hipStream_t
     g1.out_sc = fp4 ? (uint8_t*)(base + pl.off_hs) : nullptr;
     g1.n_tile_groups = 2;
     g1.max_mblocks = (int32_t)(pl.cap[0] / pl.ks[0].bm);
+    g1.expert_block = eblk[0];
     if (!pl.small1 && (e = launch(0, g1)) != hipSuccess) return hip_fail(e, "gemm1");
     tm.end(2);
 
@@ -1002,6 +1009,7 @@ int run_fused(const moe_fused_args_t& a, const Plan& pl, char* base, hipStream_t
     g2.out_row = pl.y_row;
     g2.n_tile_groups = 2;
     g2.max_mblocks = (int32_t)(pl.cap[1] / pl.ks[1].bm);
+    g2.expert_block = eblk[1];
     if (pl.fuse) {
         const Gemm2CombineParams gc{g2, cp};
         if ((e = fp4 ? launch_gemm2_combine(gc, s) : launch_gemm2_combine_bf16(gc, s)) != hipSuccess)

@@ -145,6 +145,10 @@ struct AlignParams {
     int32_t* sorted2;
     int32_t* block_expert2;
     int32_t* n_padded2;
+    // optional [E + 1]: first sorted block of each expert (entry E: the
+    // block count), per layout (null: not written)
+    int32_t* expert_block;
+    int32_t* expert_block2;
 };
 // Scratch bytes the multi-block path needs for A assignments over E experts.
 size_t align_scratch_bytes(int64_t A, int32_t E);
@@ -335,6 +339,7 @@ struct GemmParams {
     uint8_t* out_sc;        // stage 1 MXFP4: h scales [A, I/32]
     int32_t n_tile_groups;  // tiles along N are walked in groups of this size
     int32_t max_mblocks;
+    const int32_t* expert_block;   // [E + 1] first sorted block of each expert (LDS-tiled kernels)
 };
 
 struct GemmKernelId {
