@@ -37,17 +37,19 @@
 // stored non-temporally.
 //
 // LDS layout. Rows are stored row-major, the 16-byte chunk c of tile row r at
-// chunk position c ^ g(r): g(r) = r / 4 (mod 4) for 64-byte rows and
-// (r / 2) ^ 4 (r % 2) (mod 8) for 128-byte rows (r mod 16). An MFMA fragment
-// (lane l: row l % 16, chunk l / 16 of its k-step) then reads 16 distinct
-// 16-byte bank groups in every 16 lanes; the loads choose which chunk each
-// lane fetches so that the lane order of the LDS write is the swizzled
-// order.
+// chunk position c ^ g(r): g(r) = (r / 2) ^ (r / 8) (mod 4) for 64-byte rows
+// and (r / 2) ^ 4 (r % 2) (mod 8) for 128-byte rows (r mod 16). An MFMA
+// fragment (lane l: row l % 16, chunk l / 16 of its k-step) then reads 8
+// distinct 16-byte bank groups of a 128-byte bank row in every 8 lanes and
+// 16 distinct ones of a 256-byte row in every 16 lanes, so a 16-byte LDS read
+// is conflict-free whether the LDS serves 8 or 16 lanes per pass; the loads
+// choose which chunk each lane fetches so that the lane order of the LDS
+// write is the swizzled order.
 //
-// Consecutive workgroups are kept on one XCD and walk 32 consecutive row
-// blocks of one weight tile, so the row blocks of an expert stream its weight
-// tile through that XCD's L2 together (the token rows, a few MB, are re-read
-// once per weight tile from the L2 / MALL).
+// Workgroups walk the tiles in expert-major order (see the tile mapping in
+// the kernel), cut into one contiguous range per XCD, so the row blocks of an
+// expert stream its weight tiles through one XCD's L2 together (the token
+// rows, a few MB, are re-read once per weight tile from the L2 / MALL).
 #include <type_traits>
 
 #include "moe_internal.h"
@@ -89,7 +91,7 @@ struct TileShape {
 // see the LDS layout above)
 template <int CPR>
 __device__ __forceinline__ int swz_t(int r, int c) {
-    if (CPR == 4) return (c ^ (r >> 2)) & 3;
+    if (CPR == 4) return (c ^ (r >> 1) ^ (r >> 3)) & 3;
     return (c ^ ((r >> 1) ^ ((r & 1) << 2))) & 7;
 }
 
