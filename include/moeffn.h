@@ -104,7 +104,15 @@ typedef void *moe_stream_t;
  *   ids      [T, k (+1 if shared)] int32 out, any strides.
  *   weights  [T, k (+1)] float32 out, any strides.
  * Picks the k largest logits, ties to the lower expert index, slots in that
- * order. Weights are computed in double precision and rounded once to fp32.
+ * order. Weight w_j = fp32(e_j / S), rounded once, with e_j = exp(l_j - l_max)
+ * in double precision and S the sum of the picked e_j in slot order
+ * (renorm) or of all E of them in ascending expert order (plain softmax).
+ * The exponential is a stated sequence, so the weights are reproducible bit
+ * for bit: n = rint(d * 0x1.71547652b82fep+0) (1/ln2 rounded to double),
+ * r = fma(-n, 0x1.62e42fefa39efp-1, d), then r = fma(-n,
+ * 0x1.abc9e3b39803fp-56, r) (ln2 split in two doubles), e^r by its degree-13
+ * Taylor polynomial in Horner form with fma (coefficients the doubles
+ * nearest 1/i!), times 2^n; 0 for d below -708.
  * T = 0 is a no-op.
  */
 int moe_topk_softmax(const moe_tensor_t *logits, int32_t k, int32_t renorm, int32_t shared_id,
