@@ -568,8 +568,8 @@ void gemm_tile(GemmParams p) {
 }
 
 // Stages of 128 bytes per row (8 rows x 128 bytes per load, two buffers),
-// except MXFP4 with 256-row blocks: 64 bytes (four buffers; the e2m1 k-step
-// is four times deeper, so a stage is already long)
+// except MXFP4 with 128- or 256-row blocks: 64 bytes (four buffers; the e2m1
+// k-step is four times deeper, so a stage is already long)
 template <int MODE, int STAGE, int BM, int BW, int NW, int SUBS = (MODE == 0 || BM <= 64 ? 2 : 1),
           int NBUF = 4 / SUBS, bool PP = (NW == 8 && MODE == 0)>
 hipError_t launch_one(const GemmParams& p, hipStream_t s) {
@@ -589,17 +589,19 @@ hipError_t launch_one(const GemmParams& p, hipStream_t s) {
 // Tile shapes (rows x weight rows, waves): 0 = 256 x 256 x 8, 1 = 128 x 512 x
 // 8, 2 = 64 x 512 x 4, 3 = 32 x 512 x 4, 4 = 64 x 256 x 4 (bf16) or 32 x 256
 // x 4 (MXFP4), with four 128-byte stage buffers (three stages in flight)
-// where K allows it, 5 = 128 x 256 x 8 (about 64 to 160 rows per expert).
+// where K allows it, 5 = 128 x 256 x 8 (about 64 to 160 rows per expert),
+// 6 and 7 = the register-resident MXFP4 gemm2 (256 or 128 rows), 8 = MXFP4
+// 256 x 256 x 8 with 128-byte gemm1 stages.
 int gemm_tile_rows(int mode, int shape) {
-    static const int rows[8] = {256, 128, 64, 32, 64, 128, 256, 128};
+    static const int rows[9] = {256, 128, 64, 32, 64, 128, 256, 128, 256};
     return mode == 1 && shape == 4 ? 32 : rows[shape];
 }
 
 // Output columns one tile covers (shapes 6 and 7: gemm2 only, 128 columns
 // per step of their column walk; as gemm1 they accept no N)
 int gemm_tile_cols(int shape, int stage) {
-    if (shape >= 6) return stage == 2 ? 128 : (1 << 30);
-    const int bw = (shape == 0 || shape == 4 || shape == 5) ? 256 : 512;
+    if (shape == 6 || shape == 7) return stage == 2 ? 128 : (1 << 30);
+    const int bw = (shape == 0 || shape == 4 || shape == 5 || shape == 8) ? 256 : 512;
     return stage == 1 ? bw / 2 : bw;
 }
 
@@ -610,10 +612,10 @@ int gemm_tile_k_granule(int mode, int shape) {
     return shape == 4 ? 4 * 64 : 2 * 64;
 }
 
-// MXFP4 128 x 512 stages do not fit the LDS with their scales; shapes 6 and
-// 7 are MXFP4 only
+// MXFP4 128 x 512 stages do not fit the LDS with their scales; shapes 6, 7
+// and 8 are MXFP4 only
 bool gemm_tile_supported(int mode, int shape) {
-    if (shape == 6 || shape == 7) return mode == 1;
+    if (shape == 6 || shape == 7 || shape == 8) return mode == 1;
     return shape >= 0 && shape <= 5 && !(mode == 1 && shape == 1);
 }
 
@@ -630,10 +632,16 @@ hipError_t launch_gemm_tile(int mode, int shape, int stage, const GemmParams& p,
         return launch_gemm2_rows(shape == 6 ? 256 : 128, p, s);
     }
     if (mode == 1) {
-        // gemm2 (K = I) runs faster with two 128-byte stages; gemm1 keeps
-        // four 64-byte ones
+        // 256 x 256: gemm2 (K = I) runs faster with two 128-byte stages;
+        // gemm1 keeps four 64-byte ones (shape 0) or takes two 128-byte ones
+        // too (shape 8): a load then reads whole 128-byte lines (8 rows x 128
+        // bytes), which the L2 serves about twice as fast as the half lines
+        // of 64-byte stages, but only one stage is in flight. Which wins
+        // depends on the bucket.
         if (shape == 0)
             return stage == 1 ? launch_one<1, 1, 256, 256, 8>(p, s) : launch_one<1, 2, 256, 256, 8, 2, 2>(p, s);
+        if (shape == 8)
+            return stage == 1 ? launch_one<1, 1, 256, 256, 8, 2, 2>(p, s) : launch_one<1, 2, 256, 256, 8, 2, 2>(p, s);
         if (shape == 2) MOE_TILE(1, 64, 512, 4);
         if (shape == 3) MOE_TILE(1, 32, 512, 4);
         if (shape == 5) MOE_TILE(1, 128, 256, 8);

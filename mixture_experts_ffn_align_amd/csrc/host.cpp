@@ -192,6 +192,9 @@ const Cfg kConfigs[] = {
     {256, 1, 1, 4, 7, -1}, {128, 1, 1, 4, 8, -1},
     // the same with the other block size for gemm2 (a second padded layout)
     {256, 1, 1, 4, 1, 44}, {128, 1, 1, 4, 6, 43},
+    // MXFP4 256 x 256 with 128-byte gemm1 stages; gemm2 on its own tile, or
+    // register-resident with 256 or 128 rows
+    {256, 1, 1, 4, 9, -1}, {256, 1, 1, 4, 9, 43}, {256, 1, 1, 4, 9, 44},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -508,7 +511,7 @@ int plan_fused(const moe_fused_args_t* a, Plan* pl) {
             if (K % gran != 0 || N % gemm_tile_cols(shape, stage) != 0)
                 return fail(MOE_ERR_UNSUPPORTED, "config %d: gemm%d needs K %% %d == 0 and N %% %d == 0", ci, stage,
                             gran, gemm_tile_cols(shape, stage));
-            if (shape >= 6 && (stage != 2 || !gemm2_rows_supported(K, N, T * k, y_out ? y_rows_stride(a->y_rows) : H)))
+            if ((shape == 6 || shape == 7) && (stage != 2 || !gemm2_rows_supported(K, N, T * k, y_out ? y_rows_stride(a->y_rows) : H)))
                 return fail(MOE_ERR_UNSUPPORTED,
                             "config %d: the register-resident gemm2 needs K = 512 and y rows below 4 GB", ci);
             return MOE_OK;
@@ -549,7 +552,7 @@ int plan_fused(const moe_fused_args_t* a, Plan* pl) {
     } else if ((rc = resolve(c2, 2, &pl->ks[1]))) {
         // a chosen (not forced) register-resident gemm2 whose y rows would
         // span 4 GB or more: the LDS tile with the same block rows instead
-        if (a->force_config >= 0 || c2.tile < 7) return rc;
+        if (a->force_config >= 0 || !(c2.tile == 7 || c2.tile == 8)) return rc;
         c2 = kConfigs[c2.bm == 256 ? 11 : 38];
         if ((rc = resolve(c2, 2, &pl->ks[1]))) return rc;
     }
@@ -1280,7 +1283,9 @@ int moe_query_config(const moe_fused_args_t* args, moe_config_t* cfg) {
     cfg->block_m2 = pl.ks[1].bm;
     const int base = args->mode == MOE_MODE_MXFP4 ? 10 : 0;
     cfg->gemm1_kernel = pl.small1 ? base + 7 : base + (pl.ks[0].tile ? 2 : 0) + 1;
-    cfg->gemm2_kernel = pl.fuse ? base + 6 : (pl.ks[1].tile >= 7 ? base + 8 : base + (pl.ks[1].tile ? 2 : 0) + 2);
+    cfg->gemm2_kernel =
+        pl.fuse ? base + 6
+                : (pl.ks[1].tile == 7 || pl.ks[1].tile == 8 ? base + 8 : base + (pl.ks[1].tile ? 2 : 0) + 2);
     cfg->gemm1_split_k = pl.small1 ? 4 : (pl.ks[0].tile ? 1 : pl.ks[0].wk);
     cfg->gemm2_split_k = pl.fuse ? (base ? 1 : 4) : (pl.ks[1].tile ? 1 : pl.ks[1].wk);
     cfg->config_index = pl.cfg_index;
