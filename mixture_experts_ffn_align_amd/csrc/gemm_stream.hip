@@ -819,6 +819,8 @@ __global__ __launch_bounds__(256 * (4 / BPW)) void gemm1_small_kernel(Gemm1Small
     __shared__ uint4 xcode[kSmallMaxH / 32];         // the row's e2m1 codes, 32 per entry
     __shared__ uint8_t xscale[kSmallMaxH / 32];
     __shared__ float red[4][4][4][64];
+    static_assert(sizeof(red) >= kSmallMaxH * 2, "the reduction buffer holds a bf16 row");
+    __shared__ float rsc;                            // the row's RMSNorm scale
     const int tid = threadIdx.x;
     const int lane = lane_id();
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -871,18 +873,25 @@ __global__ __launch_bounds__(256 * (4 / BPW)) void gemm1_small_kernel(Gemm1Small
         reinterpret_cast<uint32_t*>(xcode)[h0 / 8] = word;
         if ((tid & 3) == 0) xscale[h0 / 32] = (uint8_t)(xs + 127);
     };
+    // the row's chunks (8 values) h0 = 8 tid + 8 NT q into registers; with
+    // the RMSNorm folded in, also their norm weights
     i32x4_t xv[kXPass];
-    if (xvec) {
+    float nwv[kXPass][8];
 #pragma unroll
-        for (int q = 0; q < kXPass; ++q)
-            if (!kXTail || 8 * tid + 8 * NT * q < p.H)
-                xv[q] = *reinterpret_cast<const i32x4_t*>(xr + 8 * tid + 8 * NT * q);
-    } else {
-        for (int h0 = 8 * tid; h0 < p.H; h0 += 8 * NT) {
-            uint32_t v[8];
+    for (int q = 0; q < kXPass; ++q) {
+        const int h0 = 8 * tid + 8 * NT * q;
+        if (kXTail && h0 >= p.H) continue;
+        if (xvec) {
+            xv[q] = *reinterpret_cast<const i32x4_t*>(xr + h0);
+        } else {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) v[i] = xr[(int64_t)(h0 + i) * p.xs_h];
-            quant8(v, h0);
+            for (int i = 0; i < 4; ++i)
+                xv[q][i] = (int)((uint32_t)xr[(int64_t)(h0 + 2 * i) * p.xs_h] |
+                                 ((uint32_t)xr[(int64_t)(h0 + 2 * i + 1) * p.xs_h] << 16));
+        }
+        if (p.nw) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) nwv[q][i] = norm_weight_at(p.nw, p.nw_f32 != 0, p.nws, h0 + i);
         }
     }
     constexpr int steps = STEPS;
@@ -909,22 +918,46 @@ __global__ __launch_bounds__(256 * (4 / BPW)) void gemm1_small_kernel(Gemm1Small
                 for (int b = 0; b < BPW; ++b)
                     sw[v][b] = *reinterpret_cast<const i32x4_t*>(sr[b] + kbase / 32 + 4 * (u0 + 4 * v));
         if (u0 == 0) {
-            if (xvec) {
-                // keep the row's arithmetic behind the weight loads
-                __builtin_amdgcn_sched_barrier(0);
+            // keep the row's arithmetic behind the weight loads
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int q = 0; q < kXPass; ++q) __asm__ volatile("" : "+v"(xv[q]));
+            for (int q = 0; q < kXPass; ++q) __asm__ volatile("" : "+v"(xv[q]));
+            float r = 1.f;
+            if (p.nw) {
+                // RMSNorm folded in, in the norm kernels' order: the raw row
+                // goes to LDS (the reduction buffer, unused until the end),
+                // wave 0 sums its squares, and every thread scales its chunks
+                uint4* xrow = reinterpret_cast<uint4*>(&red[0][0][0][0]);
 #pragma unroll
                 for (int q = 0; q < kXPass; ++q) {
                     if (kXTail && 8 * tid + 8 * NT * q >= p.H) continue;
-                    uint32_t v[8];
-#pragma unroll
-                    for (int h = 0; h < 4; ++h) {
-                        v[2 * h] = (uint32_t)xv[q][h] & 0xffffu;
-                        v[2 * h + 1] = (uint32_t)xv[q][h] >> 16;
-                    }
-                    quant8(v, 8 * tid + 8 * NT * q);
+                    xrow[tid + NT * q] = make_uint4((uint32_t)xv[q][0], (uint32_t)xv[q][1], (uint32_t)xv[q][2],
+                                                    (uint32_t)xv[q][3]);
                 }
+                __syncthreads();
+                if (w == 0) {
+                    const float ss = row_sumsq_chunks(xrow, p.H / 8);
+                    if (lane == 0) rsc = rms_scale(ss, p.H, p.eps);
+                }
+                __syncthreads();
+                r = rsc;
+            }
+#pragma unroll
+            for (int q = 0; q < kXPass; ++q) {
+                if (kXTail && 8 * tid + 8 * NT * q >= p.H) continue;
+                uint32_t v[8];
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    const uint32_t u = (uint32_t)xv[q][h];
+                    if (p.nw) {
+                        v[2 * h] = f32_to_bf16_bits((bf16_lo(u) * r) * nwv[q][2 * h]);
+                        v[2 * h + 1] = f32_to_bf16_bits((bf16_hi(u) * r) * nwv[q][2 * h + 1]);
+                    } else {
+                        v[2 * h] = u & 0xffffu;
+                        v[2 * h + 1] = u >> 16;
+                    }
+                }
+                quant8(v, 8 * tid + 8 * NT * q);
             }
             __syncthreads();
         }
@@ -1002,6 +1035,7 @@ template <int NCH>
 __global__ __launch_bounds__(256) void gemm1_small_bf16_kernel(Gemm1SmallParams p) {
     __shared__ i32x4_t xs[kSmallMaxH / 8];           // the token row, 8 bf16 per entry
     __shared__ float red[4][2][4][64];
+    __shared__ float rsc;                            // the row's RMSNorm scale
     const int tid = threadIdx.x;
     const int lane = lane_id();
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1034,6 +1068,14 @@ __global__ __launch_bounds__(256) void gemm1_small_bf16_kernel(Gemm1SmallParams 
 #pragma unroll
         for (int q = 0; q < XP; ++q) xv[q] = *reinterpret_cast<const i32x4_t*>(xr + 8 * tid + 2048 * q);
     }
+    // RMSNorm folded in: the weights of this thread's chunks
+    float nwv[XP][8];
+    if (p.nw) {
+#pragma unroll
+        for (int q = 0; q < XP; ++q)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) nwv[q][i] = norm_weight_at(p.nw, p.nw_f32 != 0, p.nws, 8 * tid + 2048 * q + i);
+    }
     i32x4_t wv[2][8][2];
     auto load_chunk = [&](int buf, int c) {
 #pragma unroll
@@ -1061,6 +1103,30 @@ __global__ __launch_bounds__(256) void gemm1_small_bf16_kernel(Gemm1SmallParams 
         }
     }
     __syncthreads();
+    if (p.nw) {
+        // the row normalised in place, in the norm kernels' order: the sum of
+        // squares by wave 0, then each thread its own chunks
+        if (w == 0) {
+            const float ss = row_sumsq_chunks(reinterpret_cast<const uint4*>(xs), p.H / 8);
+            if (lane == 0) rsc = rms_scale(ss, p.H, p.eps);
+        }
+        __syncthreads();
+        const float r = rsc;
+#pragma unroll
+        for (int q = 0; q < XP; ++q) {
+            const int c = tid + 256 * q;
+            const i32x4_t v = xs[c];
+            i32x4_t o;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t u = (uint32_t)v[i];
+                o[i] = (int)((uint32_t)f32_to_bf16_bits((bf16_lo(u) * r) * nwv[q][2 * i]) |
+                             ((uint32_t)f32_to_bf16_bits((bf16_hi(u) * r) * nwv[q][2 * i + 1]) << 16));
+            }
+            xs[c] = o;
+        }
+        __syncthreads();
+    }
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
         if (c + 1 < NCH) load_chunk((c + 1) & 1, c + 1);

@@ -342,6 +342,7 @@ struct Plan {
     bool norm;             // RMSNorm pre-pass into the xn segment
     bool fuse;             // gemm2 and the combine in one kernel (no y, no second layout)
     bool small1;           // gemm1 per slot, without the align (implies fuse)
+    bool norm_fold;        // the per-slot gemm1 normalises its token rows itself (no RMSNorm launch)
     // workspace offsets
     size_t off_counts, off_sorted[2], off_bexp[2], off_npad[2], off_eblk[2], off_x, off_xs, off_xn, off_h, off_hs, off_y,
         total;
@@ -574,6 +575,11 @@ int plan_fused(const moe_fused_args_t* a, Plan* pl) {
     const bool x_direct = a->x.stride[1] == 1 && aligned16(a->x.data) &&
                           (T <= 1 || (a->x.stride[0] * 2) % 16 == 0);
     pl->norm = norm;
+    // Each per-slot gemm1 workgroup normalising its own token row saves the
+    // RMSNorm launch (measured: 8-9 us of norm cost down to 3-5 us at T = 1
+    // and 4) but repeats the row's reduction once per workgroup, which loses
+    // from about 16 tokens (MXFP4 T = 16: 15 against 8 us). Same bits either way.
+    pl->norm_fold = norm && pl->small1 && T <= 8;
     // bf16 rows with a non-unit last-dim stride are laid out into the
     // workspace for the GEMMs that stage whole 16-byte row chunks (one pass,
     // coalesced along the stride-1 dimension); gemm1 per slot reads x
@@ -612,7 +618,8 @@ int plan_fused(const moe_fused_args_t* a, Plan* pl) {
         pl->off_eblk[g] = take((size_t)(E + 1) * 4);
     }
     pl->off_x = pl->off_xs = pl->off_xn = 0;
-    if (norm) pl->off_xn = take((size_t)T * (size_t)H * 2);   // normalised rows, bf16
+    // normalised rows, bf16 (unless the per-slot gemm1 normalises in LDS)
+    if (norm && !pl->norm_fold) pl->off_xn = take((size_t)T * (size_t)H * 2);
     if (fp4) {
         pl->off_x = take((size_t)T * (size_t)(H / 2));
         pl->off_xs = take((size_t)T * (size_t)(H / 32));
@@ -850,7 +857,7 @@ int run_fused(const moe_fused_args_t& a, const Plan& pl, char* base, hipStream_t
     tm.begin(1);
     const void* a_op = a.x.data;
     int64_t a_row = a.x.stride[0];
-    if (pl.norm) {
+    if (pl.norm && !pl.norm_fold) {
         NormParams np{};
         norm_params(&np, a.x, a.norm_weight, a.norm_eps);
         np.out = (uint16_t*)(base + pl.off_xn);
@@ -894,9 +901,18 @@ int run_fused(const moe_fused_args_t& a, const Plan& pl, char* base, hipStream_t
     if (pl.small1) {
         // per slot, from the bf16 activation (or its normalised rows)
         Gemm1SmallParams sp{};
-        sp.x = pl.norm ? (const uint16_t*)(base + pl.off_xn) : (const uint16_t*)a.x.data;
-        sp.xs_t = pl.norm ? pl.H : a.x.stride[0];
-        sp.xs_h = pl.norm ? 1 : (pl.H > 1 ? a.x.stride[1] : 1);
+        sp.x = pl.norm && !pl.norm_fold ? (const uint16_t*)(base + pl.off_xn) : (const uint16_t*)a.x.data;
+        sp.xs_t = pl.norm && !pl.norm_fold ? pl.H : a.x.stride[0];
+        sp.xs_h = pl.norm && !pl.norm_fold ? 1 : (pl.H > 1 ? a.x.stride[1] : 1);
+        if (pl.norm_fold) {
+            // the RMSNorm is folded into this gemm1 (same order, same bits)
+            NormParams np{};
+            norm_params(&np, a.x, a.norm_weight, a.norm_eps);
+            sp.nw = np.w;
+            sp.nws = np.ws;
+            sp.nw_f32 = np.w_f32;
+            sp.eps = np.eps;
+        }
         sp.gate = (const uint8_t*)a.gate.data;
         sp.up = (const uint8_t*)a.up.data;
         sp.g_e = a.gate.stride[0];

@@ -106,6 +106,49 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
     return l == 0 ? 0ull : (~0ull >> (64 - l));
 }
 
+// ------------------------------------------------------------- RMSNorm
+//
+// One summation order for every kernel that normalises a row (the norm
+// kernels and the few-token gemm1 that folds the norm in): chunk c holds
+// elements 8c .. 8c+7; lane q of one wave chains fmaf over the chunks
+// c = q, q + 64, ... in ascending order, element by element; the 64 partials
+// meet in a wave64 xor butterfly (distance 32, 16, ..., 1). The scale is
+// then r = 1 / sqrt(ss / H + eps) and the output bf16((x * r) * w).
+
+__device__ __forceinline__ float rms_scale(float ss, int64_t H, float eps) {
+    return 1.0f / __builtin_sqrtf(ss / (float)H + eps);
+}
+
+// the two bf16 values of a 32-bit word, element order (low half first)
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+// Sum of squares of a bf16 row staged as nc 16-byte chunks (LDS), in the
+// order above; call from one whole wave; every lane gets the sum.
+__device__ __forceinline__ float row_sumsq_chunks(const uint4* row, int nc) {
+    const int q = lane_id();
+    float acc = 0.f;
+    for (int c = q; c < nc; c += 64) {
+        const uint4 v = row[c];
+        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float lo = bf16_lo(u[i]), hi = bf16_hi(u[i]);
+            acc = __builtin_fmaf(lo, lo, acc);
+            acc = __builtin_fmaf(hi, hi, acc);
+        }
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) acc = acc + __shfl_xor(acc, m, 64);
+    return acc;
+}
+
+// Element h of the norm weight ([H], bf16 or fp32, element stride ws).
+__device__ __forceinline__ float norm_weight_at(const void* w, bool f32, int64_t ws, int64_t h) {
+    return f32 ? reinterpret_cast<const float*>(w)[h * ws]
+               : bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(w)[h * ws]);
+}
+
 // Workgroup index remapped so that consecutive logical tiles land on the same
 // XCD: the hardware deals workgroups round-robin over the 8 XCDs, so block b
 // runs on XCD b % 8. Logical index = (b % 8) * (G / 8) + b / 8 for the part of
@@ -418,6 +461,13 @@ struct Gemm1SmallParams {
     int32_t E, k, A, H, I;
     uint8_t* hq;                // [A, I/2]
     uint8_t* hs;                // [A, I/32]
+    // RMSNorm folded in (nw null: off): the token row is normalised in LDS
+    // in the norm kernels' order before it is used, bit-identical to the
+    // separate pass
+    const void* nw;             // [H] bf16, or fp32 when nw_f32
+    int64_t nws;                // element stride of nw
+    int32_t nw_f32;
+    float eps;
 };
 hipError_t launch_gemm1_small(const Gemm1SmallParams& p, hipStream_t s);
 // the same in bf16: h bf16 [A, I] in hq (byte strides for the weights)

@@ -15,13 +15,8 @@
 namespace moe {
 namespace {
 
-__device__ __forceinline__ float rms_scale(float ss, int64_t H, float eps) {
-    return 1.0f / __builtin_sqrtf(ss / (float)H + eps);
-}
-
 __device__ __forceinline__ float norm_weight(const NormParams& p, int64_t h) {
-    return p.w_f32 ? reinterpret_cast<const float*>(p.w)[h * p.ws]
-                   : bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(p.w)[h * p.ws]);
+    return norm_weight_at(p.w, p.w_f32 != 0, p.ws, h);
 }
 
 // The 8 values of chunk c of row xr.

@@ -335,8 +335,13 @@ def test_mxfp4_gemm1_per_slot_same_bits(fp4_weights, T):
     small = fam[(17, 4, 1)]
     stream = fam[(11, 4, 1)]
     nw = torch.rand(shape.hidden, generator=torch.Generator(device=DEV).manual_seed(2), device=DEV)
+    # a bf16 norm weight with element stride 3 (the per-slot gemm1 folds the
+    # norm in; the stream configs run the separate pass)
+    nwb = torch.rand(3 * shape.hidden, generator=torch.Generator(device=DEV).manual_seed(4),
+                     device=DEV).to(torch.bfloat16)[::3]
     xt = inp["x"].t().contiguous().t()
-    for x, extra in ((inp["x"], {}), (xt, {}), (inp["x"], dict(norm_weight=nw))):
+    for x, extra in ((inp["x"], {}), (xt, {}), (inp["x"], dict(norm_weight=nw)),
+                     (xt, dict(norm_weight=nwb, norm_eps=1e-3))):
         ref = moe.moe_fused_fwd(x, gq, uq, wq, *gpu, force_config=stream[0], **extra, **kw).clone()
         for c in small + stream[1:]:
             got = moe.moe_fused_fwd(x, gq, uq, wq, *gpu, force_config=c, **extra, **kw)
@@ -378,9 +383,12 @@ def test_bf16_per_slot_and_fused_gemm2_same_bits(w235, T):
     ref_cfg = kinds[(1, 2)][0]
     others = [c for key, cs in kinds.items() for c in cs if c != ref_cfg]
     nw = torch.rand(sh.hidden, generator=torch.Generator(device=DEV).manual_seed(3), device=DEV)
+    nwb = torch.rand(3 * sh.hidden, generator=torch.Generator(device=DEV).manual_seed(5),
+                     device=DEV).to(torch.bfloat16)[::3]
     xt = inp["x"].t().contiguous().t()
     gc, uc = gate.contiguous(), up.contiguous()
-    for x, g_, u_, extra in ((inp["x"], gate, up, {}), (xt, gc, uc, {}), (inp["x"], gate, up, dict(norm_weight=nw))):
+    for x, g_, u_, extra in ((inp["x"], gate, up, {}), (xt, gc, uc, {}), (inp["x"], gate, up, dict(norm_weight=nw)),
+                             (xt, gate, up, dict(norm_weight=nwb, norm_eps=1e-3))):
         ref = moe.moe_fused_fwd(x, g_, u_, inp["w2"], *gpu, force_config=ref_cfg, **extra).clone()
         for c in others:
             got = moe.moe_fused_fwd(x, g_, u_, inp["w2"], *gpu, force_config=c, **extra)
@@ -485,10 +493,16 @@ def _few_token_same_bits(mode, H, I, E, k, T, seed):
     stream = [key for key in keys if key[0] != per_slot and key[1] != fused_only] or \
         [key for key in keys if key[0] != per_slot]
     assert stream, keys
-    ref = moe.moe_fused_fwd(x, gate, up, w2, ids, w, force_config=want[stream[0]][0], **kw).clone()
-    for key in keys:
-        for c in want[key]:
-            assert torch.equal(moe.moe_fused_fwd(x, gate, up, w2, ids, w, force_config=c, **kw), ref), (key, c)
+    # also with the RMSNorm, which the per-slot gemm1 folds in (the others
+    # run the separate pass): an fp32 weight, or a bf16 one with stride 2
+    nw = torch.rand(2 * H, generator=g, device=DEV)
+    nw = nw[:H] if seed % 2 else nw.to(torch.bfloat16)[::2]
+    for extra in ({}, dict(norm_weight=nw)):
+        ref = moe.moe_fused_fwd(x, gate, up, w2, ids, w, force_config=want[stream[0]][0], **extra, **kw).clone()
+        for key in keys:
+            for c in want[key]:
+                got = moe.moe_fused_fwd(x, gate, up, w2, ids, w, force_config=c, **extra, **kw)
+                assert torch.equal(got, ref), (key, c, bool(extra))
 
 
 @pytest.mark.parametrize("H,I,k", [(2048, 512, 6), (6144, 1024, 10), (8192, 768, 3)])
