@@ -591,9 +591,10 @@ hipError_t launch_one(const GemmParams& p, hipStream_t s) {
 // x 4 (MXFP4), with four 128-byte stage buffers (three stages in flight)
 // where K allows it, 5 = 128 x 256 x 8 (about 64 to 160 rows per expert),
 // 6 and 7 = the register-resident MXFP4 gemm2 (256 or 128 rows), 8 = MXFP4
-// 256 x 256 x 8 with 128-byte gemm1 stages.
+// 256 x 256 x 8 with 128-byte gemm1 stages, 9 = MXFP4 128 x 256 x 8 with
+// 128-byte stages.
 int gemm_tile_rows(int mode, int shape) {
-    static const int rows[9] = {256, 128, 64, 32, 64, 128, 256, 128, 256};
+    static const int rows[10] = {256, 128, 64, 32, 64, 128, 256, 128, 256, 128};
     return mode == 1 && shape == 4 ? 32 : rows[shape];
 }
 
@@ -601,7 +602,7 @@ int gemm_tile_rows(int mode, int shape) {
 // per step of their column walk; as gemm1 they accept no N)
 int gemm_tile_cols(int shape, int stage) {
     if (shape == 6 || shape == 7) return stage == 2 ? 128 : (1 << 30);
-    const int bw = (shape == 0 || shape == 4 || shape == 5 || shape == 8) ? 256 : 512;
+    const int bw = (shape == 0 || shape == 4 || shape == 5 || shape == 8 || shape == 9) ? 256 : 512;
     return stage == 1 ? bw / 2 : bw;
 }
 
@@ -612,10 +613,10 @@ int gemm_tile_k_granule(int mode, int shape) {
     return shape == 4 ? 4 * 64 : 2 * 64;
 }
 
-// MXFP4 128 x 512 stages do not fit the LDS with their scales; shapes 6, 7
-// and 8 are MXFP4 only
+// MXFP4 128 x 512 stages do not fit the LDS with their scales; shapes 6 to
+// 9 are MXFP4 only
 bool gemm_tile_supported(int mode, int shape) {
-    if (shape == 6 || shape == 7 || shape == 8) return mode == 1;
+    if (shape >= 6 && shape <= 9) return mode == 1;
     return shape >= 0 && shape <= 5 && !(mode == 1 && shape == 1);
 }
 
@@ -627,6 +628,9 @@ hipError_t launch_gemm_tile(int mode, int shape, int stage, const GemmParams& p,
     return stage == 1 ? launch_one<MD, 1, BM, BW, NW>(p, s) : launch_one<MD, 2, BM, BW, NW>(p, s)
 #define MOE_TILE4(MD, BM, BW, NW) \
     return stage == 1 ? launch_one<MD, 1, BM, BW, NW, 2, 4>(p, s) : launch_one<MD, 2, BM, BW, NW, 2, 4>(p, s)
+#define MOE_TILE_S(MD, BM, BW, NW, SUBS, NBUF)                                      \
+    return stage == 1 ? launch_one<MD, 1, BM, BW, NW, SUBS, NBUF>(p, s) \
+                      : launch_one<MD, 2, BM, BW, NW, SUBS, NBUF>(p, s)
     if (shape == 6 || shape == 7) {
         if (mode != 1 || stage != 2) return hipErrorInvalidValue;
         return launch_gemm2_rows(shape == 6 ? 256 : 128, p, s);
@@ -642,6 +646,9 @@ hipError_t launch_gemm_tile(int mode, int shape, int stage, const GemmParams& p,
             return stage == 1 ? launch_one<1, 1, 256, 256, 8>(p, s) : launch_one<1, 2, 256, 256, 8, 2, 2>(p, s);
         if (shape == 8)
             return stage == 1 ? launch_one<1, 1, 256, 256, 8, 2, 2>(p, s) : launch_one<1, 2, 256, 256, 8, 2, 2>(p, s);
+        // 128 x 256 with two 128-byte stages (shape 9; shape 5 has four
+        // 64-byte ones)
+        if (shape == 9) MOE_TILE_S(1, 128, 256, 8, 2, 2);
         if (shape == 2) MOE_TILE(1, 64, 512, 4);
         if (shape == 3) MOE_TILE(1, 32, 512, 4);
         if (shape == 5) MOE_TILE(1, 128, 256, 8);
@@ -657,6 +664,7 @@ hipError_t launch_gemm_tile(int mode, int shape, int stage, const GemmParams& p,
     MOE_TILE4(0, 64, 256, 4);
 #undef MOE_TILE
 #undef MOE_TILE4
+#undef MOE_TILE_S
 }
 
 }  // namespace moe

@@ -195,6 +195,9 @@ const Cfg kConfigs[] = {
     // MXFP4 256 x 256 with 128-byte gemm1 stages; gemm2 on its own tile, or
     // register-resident with 256 or 128 rows
     {256, 1, 1, 4, 9, -1}, {256, 1, 1, 4, 9, 43}, {256, 1, 1, 4, 9, 44},
+    // MXFP4 128 x 256 with 128-byte stages; gemm2 on its own tile, or
+    // register-resident with 128 or 256 rows
+    {128, 1, 1, 4, 10, -1}, {128, 1, 1, 4, 10, 44}, {128, 1, 1, 4, 10, 43},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
