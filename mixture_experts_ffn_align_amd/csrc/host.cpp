@@ -198,6 +198,10 @@ const Cfg kConfigs[] = {
     // MXFP4 128 x 256 with 128-byte stages; gemm2 on its own tile, or
     // register-resident with 128 or 256 rows
     {128, 1, 1, 4, 10, -1}, {128, 1, 1, 4, 10, 44}, {128, 1, 1, 4, 10, 43},
+    // mid T (about 20 to 60 rows per expert): gemm1 on 64 x 512 tiles or on
+    // the weight stream, gemm2 register-resident with 128-row blocks (its
+    // own padded layout)
+    {64, 1, 1, 4, 3, 44}, {32, 1, 1, 4, 0, 44}, {64, 1, 1, 4, 0, 44}, {16, 1, 1, 4, 0, 44},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
