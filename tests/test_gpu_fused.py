@@ -570,3 +570,34 @@ def test_bf16_oversized_call_in_token_chunks(w235):
                                  force_config=q["config_index"])
         assert torch.equal(part, out[t0:t0 + n]), t0
     _check_bf16(inp, out, np_(ids), np_(w), tail_tokens(np_(ids), sh.experts, 256))
+
+
+def test_mxfp4_beyond_largest_bucket(fp4_weights):
+    """70000 tokens on the 512/10 MXFP4 shard, past the largest bucket (the
+    32768 bucket's configuration, 5.7 GB of per-slot rows written through
+    64-bit offsets, the multi-launch align at 700000 assignments): slices of
+    the tokens run alone give the same rows bit for bit, and sampled tokens,
+    including the experts' ragged tail blocks, match the oracle."""
+    shape = W.QWEN35_397B_TP2_FP4_512
+    w13, w2, ((gq, gs), (uq, us), (wq, wsc)) = fp4_weights(shape)
+    T = 70000
+    inp = W.make_inputs(shape, T, seed=13, device=DEV, weights=(w13, w2))
+    gpu, orc = route_both(inp)
+    assert_routing_equal(gpu, orc)
+    kw = dict(gate_scale=gs, up_scale=us, w2_scale=wsc, mode=moe.MODE_MXFP4)
+    q = moe.moe_query_config(inp["x"], gq, uq, wq, *gpu, **kw)
+    out = moe.moe_fused_fwd(inp["x"], gq, uq, wq, *gpu, **kw).clone()
+    ids, w = gpu
+    for t0, n in ((32768, 32768), (65536, T - 65536)):
+        part = moe.moe_fused_fwd(inp["x"][t0:t0 + n], gq, uq, wq, ids[t0:t0 + n], w[t0:t0 + n],
+                                 force_config=q["config_index"], **kw)
+        assert torch.equal(part, out[t0:t0 + n]), t0
+    oi, ow = orc
+    toks = tail_tokens(oi, shape.experts, 128)
+    mx = fp4_weights.oracle_codes(shape, sorted({int(e) for e in oi[toks].ravel()}))
+    acc, _ = oracle_ffn_tokens(inp, oi, ow, toks, mx=mx)
+    got = bf16_to_f64(out[torch.from_numpy(toks).to(DEV)])
+    r, er = rel_l2(got, acc), err_ratio(got, acc)
+    print(f"T={T} {len(toks)} tokens rel_l2={r:.3e} err_ratio={er:.3e}")
+    assert np.isfinite(got).all()
+    assert r <= FP4_TOL and er <= FP4_ERR_RATIO
