@@ -238,13 +238,18 @@ typedef struct {
     int32_t gemm1_kernel;  /* kernel family of gemm1: 1 bf16 weight-streaming, 3 bf16 LDS-tiled,
                               7 bf16 per slot without the align (few tokens; K split 4,
                               bit-identical to 1 with that split); 11, 13 and 17 the same three in
-                              MXFP4 mode */
+                              MXFP4 mode; 19 MXFP4 weight-streaming as a persistent kernel (one
+                              workgroup per compute unit walking its row-block x column-tile items
+                              with the weight loads running on from one item into the next;
+                              bit-identical to 11) */
     int32_t gemm2_kernel;  /* kernel family of gemm2: gemm1's plus one, or 6 / 16: gemm2 with the
                               combine folded in (few tokens; bf16 with I a multiple of 256 from 512
                               to 1536 and K split 4, MXFP4 with I = 512; bit-identical results),
                               or 18: MXFP4 gemm2 with K = 512 keeping each block's h rows in
                               registers and walking 128-column weight tiles (many tokens;
-                              bit-identical results; y rows below 4 GB, else the LDS tile) */
+                              bit-identical results; y rows below 4 GB, else the LDS tile), or 20:
+                              MXFP4 gemm2 with K = 512 as a persistent weight stream (see 19;
+                              bit-identical results) */
     int32_t gemm1_split_k; /* waves splitting K inside a workgroup */
     int32_t gemm2_split_k;
     int32_t config_index;  /* index into the library's config list */

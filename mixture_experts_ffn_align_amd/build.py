@@ -21,7 +21,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["route.hip", "align.hip", "quant.hip", "norm.hip", "gemm_stream.hip", "gemm_tile.hip", "combine.hip",
-           "bwd.hip", "noalloc.hip", "gemm2_rows.hip", "host.cpp"]
+           "bwd.hip", "noalloc.hip", "gemm2_rows.hip", "gemm_persist.hip", "host.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

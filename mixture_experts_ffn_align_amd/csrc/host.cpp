@@ -15,6 +15,7 @@
 #include <cstring>
 #include <string>
 
+#include "gemm_persist.h"
 #include "moe_internal.h"
 #include "moeffn.h"
 
@@ -159,6 +160,8 @@ struct Cfg {
     int nt2 = 1;  // MXFP4 gemm2 on the stream with K = 512: 256-column tiles per workgroup
     int fuse = 0; // 1: gemm2 and the combine in one kernel, per token (few tokens; MXFP4 K = 512, bf16
                   // K split 4); 2: besides, gemm1 per slot without the align (expert from the ids)
+    int persist = 0;  // MXFP4 gemm1 on the persistent weight stream with this many waves (4 or 8)
+    int persist2 = 0; // 1: MXFP4 gemm2 (K = 512) on the persistent weight stream
 };
 const Cfg kConfigs[] = {
     {16, 4, 4, 4, 0, -1}, {32, 4, 4, 4, 0, -1}, {64, 2, 2, 4, 0, -1},
@@ -202,6 +205,14 @@ const Cfg kConfigs[] = {
     // the weight stream, gemm2 register-resident with 128-row blocks (its
     // own padded layout)
     {64, 1, 1, 4, 3, 44}, {32, 1, 1, 4, 0, 44}, {64, 1, 1, 4, 0, 44}, {16, 1, 1, 4, 0, 44},
+    // MXFP4 gemm1 as a persistent weight stream (one workgroup per compute
+    // unit, 4 or 8 waves), gemm2 on the multi-tile stream or register-resident
+    {16, 1, 1, 4, 0, -1, 4, 0, 4}, {16, 1, 1, 4, 0, -1, 8, 0, 4}, {32, 1, 1, 4, 0, -1, 8, 0, 4},
+    {16, 1, 1, 4, 0, -1, 4, 0, 8}, {16, 1, 1, 4, 0, -1, 8, 0, 8}, {32, 1, 1, 4, 0, -1, 8, 0, 8},
+    {32, 1, 1, 4, 0, 44, 1, 0, 4}, {32, 1, 1, 4, 0, 44, 1, 0, 8},
+    // both GEMMs on persistent weight streams (gemm2 with K = 512), or gemm2 only
+    {16, 1, 1, 4, 0, -1, 1, 0, 4, 1}, {32, 1, 1, 4, 0, -1, 1, 0, 4, 1}, {16, 1, 1, 4, 0, -1, 1, 0, 8, 1},
+    {32, 1, 1, 4, 0, -1, 1, 0, 8, 1}, {16, 1, 1, 4, 0, -1, 1, 0, 0, 1}, {32, 1, 1, 4, 0, -1, 1, 0, 0, 1},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -331,8 +342,9 @@ int default_config(int mode, int64_t T, int64_t H, int64_t I, int64_t E, int64_t
 // blocks per wave (register stream), or an LDS tile shape.
 struct KSpec {
     int bm, wk, nb;
-    int tile;    // 0: register weight stream; 1 + shape: LDS-tiled
-    int nt = 1;  // register stream: column tiles per workgroup
+    int tile;         // 0: register weight stream; 1 + shape: LDS-tiled
+    int nt = 1;       // register stream: column tiles per workgroup
+    int persist = 0;  // MXFP4 gemm1: the persistent weight stream with this many waves
 };
 
 struct Plan {
@@ -522,6 +534,35 @@ int plan_fused(const moe_fused_args_t* a, Plan* pl) {
             if ((shape == 6 || shape == 7) && (stage != 2 || !gemm2_rows_supported(K, N, T * k, y_out ? y_rows_stride(a->y_rows) : H)))
                 return fail(MOE_ERR_UNSUPPORTED,
                             "config %d: the register-resident gemm2 needs K = 512 and y rows below 4 GB", ci);
+            return MOE_OK;
+        }
+        if (stage == 2 && c.persist2) {
+            int dev = 0, cus = 256;
+            if (hipGetDevice(&dev) != hipSuccess ||
+                hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+                cus = 256;
+            const int64_t items = align_capacity(T * k, E, c.bm) / c.bm * (N / 256);
+            if (md != 1 || !gemm2_persist_supported(c.bm, K, N) || items > (int64_t)cus * 256)
+                return fail(MOE_ERR_UNSUPPORTED,
+                            "config %d: the persistent gemm2 needs MXFP4, K = 512, N %% 256 == 0 and at most 256 "
+                            "items per compute unit", ci);
+            ks->wk = 1;
+            ks->persist = 1;
+            return MOE_OK;
+        }
+        if (stage == 1 && c.persist) {
+            // one workgroup per compute unit, at most 256 items each
+            int dev = 0, cus = 256;
+            if (hipGetDevice(&dev) != hipSuccess ||
+                hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+                cus = 256;
+            const int64_t items = align_capacity(T * k, E, c.bm) / c.bm * (N / (32 * c.persist));
+            if (md != 1 || !gemm1_persist_supported(c.bm, c.persist, K, N) || items > (int64_t)cus * 256)
+                return fail(MOE_ERR_UNSUPPORTED,
+                            "config %d: the persistent gemm1 needs MXFP4, K in {2048, 4096, 8192}, N %% %d == 0 "
+                            "and at most 256 items per compute unit", ci, 32 * c.persist);
+            ks->wk = 1;
+            ks->persist = c.persist;
             return MOE_OK;
         }
         int w = ks->wk;
@@ -899,6 +940,7 @@ int run_fused(const moe_fused_args_t& a, const Plan& pl, char* base, hipStream_t
     auto launch = [&](int g, const GemmParams& gp) -> hipError_t {
         const KSpec& k = pl.ks[g];
         if (k.tile) return launch_gemm_tile(fp4 ? 1 : 0, k.tile - 1, g + 1, gp, s);
+        if (k.persist) return g == 0 ? launch_gemm1_persist(k.bm, k.persist, gp, s) : launch_gemm2_persist(k.bm, gp, s);
         GemmKernelId id{fp4 ? 1 : 0, g + 1, k.bm, k.wk,
                         gemm_ring_steps(pl.mode, k.bm, k.nb, k.wk, (g == 0 ? pl.H : pl.I) / k.wk), k.nb, k.nt};
         return launch_gemm(id, gp, s);
@@ -1305,10 +1347,12 @@ int moe_query_config(const moe_fused_args_t* args, moe_config_t* cfg) {
     cfg->block_m = pl.ks[0].bm;
     cfg->block_m2 = pl.ks[1].bm;
     const int base = args->mode == MOE_MODE_MXFP4 ? 10 : 0;
-    cfg->gemm1_kernel = pl.small1 ? base + 7 : base + (pl.ks[0].tile ? 2 : 0) + 1;
+    cfg->gemm1_kernel = pl.small1 ? base + 7 : (pl.ks[0].persist ? base + 9 : base + (pl.ks[0].tile ? 2 : 0) + 1);
     cfg->gemm2_kernel =
         pl.fuse ? base + 6
-                : (pl.ks[1].tile == 7 || pl.ks[1].tile == 8 ? base + 8 : base + (pl.ks[1].tile ? 2 : 0) + 2);
+                : (pl.ks[1].persist ? base + 10
+                                    : (pl.ks[1].tile == 7 || pl.ks[1].tile == 8 ? base + 8
+                                                                                : base + (pl.ks[1].tile ? 2 : 0) + 2));
     cfg->gemm1_split_k = pl.small1 ? 4 : (pl.ks[0].tile ? 1 : pl.ks[0].wk);
     cfg->gemm2_split_k = pl.fuse ? (base ? 1 : 4) : (pl.ks[1].tile ? 1 : pl.ks[1].wk);
     cfg->config_index = pl.cfg_index;

@@ -233,8 +233,9 @@ def test_tiled_and_streaming_gemms_same_bits_mxfp4(fp4_weights, T):
 
     fam = _configs_by_family(query)
     assert len(fam[(13, 1, 1)]) >= 5          # every MXFP4 tile shape, and mixed gemm2 choices
+    assert len(fam[(19, 1, 1)]) >= 8          # the persistent gemm1 with 4 and 8 waves
     out_t = run(fam[(13, 1, 1)][0])
-    for c in fam[(13, 1, 1)][1:] + fam[(11, 1, 1)]:
+    for c in fam[(13, 1, 1)][1:] + fam[(11, 1, 1)] + fam[(19, 1, 1)]:
         assert torch.equal(run(c), out_t), f"config {c}"
     toks = sample_tokens(T, 4)
     oi, ow = orc
@@ -521,6 +522,44 @@ def test_mxfp4_few_token_kernels_other_shapes(H, k):
     (at H = 8192 this caught the stream's scale staging overflowing its LDS
     rows)."""
     _few_token_same_bits(moe.MODE_MXFP4, H, 512, 24, k, 3, seed=H + k)
+
+
+@pytest.mark.parametrize("T", [1, 5, 333, 4099, 9000])
+def test_mxfp4_persistent_streams(fp4_weights, T):
+    """The persistent weight streams (gemm1, gemm2 with K = 512, or both: one
+    workgroup per compute unit walking its items, the weight ring running on
+    across them) against the per-item weight stream: bit-identical h and y,
+    so identical outputs, from fewer items than compute units (T = 1, 5) to
+    more than a hundred items per workgroup (T = 9000); sampled tokens (the
+    experts' tail blocks from T = 4099 on) against the oracle."""
+    shape = W.QWEN35_397B_TP2_FP4_512 if T % 2 else W.QWEN35_397B_TP2_FP4_513
+    w13, w2, ((gq, gs), (uq, us), (wq, wsc)) = fp4_weights(shape)
+    inp = W.make_inputs(shape, T, seed=T + 11, device=DEV, weights=(w13, w2))
+    gpu, orc = route_both(inp)
+    kw = dict(gate_scale=gs, up_scale=us, w2_scale=wsc, mode=moe.MODE_MXFP4)
+    n = moe.moe_query_config(inp["x"], gq, uq, wq, *gpu, **kw)["num_configs"]
+    pers, plain = [], []
+    for c in range(n):
+        try:
+            q = moe.moe_query_config(inp["x"], gq, uq, wq, *gpu, force_config=c, **kw)
+        except moe.MoEError as err:
+            assert err.status == -6, err
+            continue
+        if q["gemm1_split_k"] != 1 or q["gemm2_split_k"] != 1:
+            continue
+        (pers if q["gemm1_kernel"] == 19 or q["gemm2_kernel"] == 20 else plain).append(c)
+    # 16-row blocks of gemm2 exceed 256 items per compute unit from about 6000 tokens
+    assert len(pers) >= (14 if T < 6000 else 10)
+    out_r = moe.moe_fused_fwd(inp["x"], gq, uq, wq, *gpu, force_config=plain[0], **kw).clone()
+    for c in pers:
+        out_p = moe.moe_fused_fwd(inp["x"], gq, uq, wq, *gpu, force_config=c, **kw)
+        assert torch.equal(out_p, out_r), f"config {c}"
+    oi, ow = orc
+    toks = tail_tokens(oi, shape.experts, 64) if T >= 4096 else sample_tokens(T, 4)
+    used = sorted({int(e) for e in oi[toks].ravel()})
+    acc, _ = oracle_ffn_tokens(inp, oi, ow, toks, mx=fp4_weights.oracle_codes(shape, used))
+    got = bf16_to_f64(out_r[torch.from_numpy(toks).to(DEV)])
+    assert rel_l2(got, acc) <= FP4_TOL and err_ratio(got, acc) <= FP4_ERR_RATIO
 
 
 def test_mxfp4_long_rows_every_config_against_oracle():
