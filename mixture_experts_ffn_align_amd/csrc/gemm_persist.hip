@@ -43,10 +43,13 @@
 namespace moe {
 namespace {
 
-// bytes of weight scales per row the LDS runs hold (K / 32 at most)
-template <int NW>
+// bytes of weight scales per row the LDS runs hold (K / 32 at most): K up
+// to 8192 with four waves and blocks of 16 or 32 rows, else 4096 (the
+// token-row buffers of 64-row blocks, or the runs of eight waves, take the
+// rest of the 160 KB)
+template <int NW, int BM>
 constexpr int persist_scb() {
-    return NW == 4 ? 256 : 128;
+    return NW == 4 && BM <= 32 ? 256 : 128;
 }
 constexpr int kPersistItems = 256;   // items per workgroup at most (the host checks)
 
@@ -59,9 +62,20 @@ struct PItem {
     const char* a[MB];       // token row r16 of each 16-row group (padding: row 0)
     const uint8_t* as[MB];   // its scale row
     int row[MB];             // flat assignment index of that row (>= A: padding)
+    int e;                   // expert
     int n0;                  // the wave's first h column
     int s0;                  // first step (the dummy after the last item re-reads the last round)
 };
+
+// Keeps a value of the accumulator chain where it is: in AGPRs with four
+// waves (one per SIMD: room for both register files), in VGPRs with eight.
+template <int NW>
+__device__ __forceinline__ void pin_acc(f32x4_t& v) {
+    if constexpr (NW == 4)
+        __asm__ volatile("" : "+a"(v));
+    else
+        __asm__ volatile("" : "+v"(v));
+}
 
 template <int BM, int NW, int R>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
@@ -70,7 +84,7 @@ void gemm1_persist(GemmParams p) {
     constexpr int STEPS = 4 * R;                // 128 k per step, R ring rounds per item
     constexpr int FR = 4 * MB;                  // 1 KB token-row fragments per round: (mi, u)
     constexpr int AR = (FR + NW - 1) / NW;      // fragments one wave stages per round
-    constexpr int SCB = persist_scb<NW>();
+    constexpr int SCB = persist_scb<NW, BM>();
     static_assert(R % 2 == 0 && STEPS * 4 <= SCB, "scale runs must fit their LDS rows");
     __shared__ __attribute__((aligned(16))) uint8_t a_lds[2 * FR * 1024];
     __shared__ __attribute__((aligned(16))) uint8_t sc_lds[2 * NW * 64 * SCB];
@@ -85,19 +99,22 @@ void gemm1_persist(GemmParams p) {
     int it = (int)blockIdx.x;
     if (it >= n_items) return;
 
-    // weight rows and scale-run row of an item (no loads)
-    auto set_weights = [&](PItem<MB>& I, int item, int e) {
-        const int nt = item % n_tiles;
-        I.n0 = nt * (32 * NW) + w * 32;
+    // an item's first h column and its expert's scales (wave-uniform)
+    auto set_item = [&](PItem<MB>& I, int item, int e) {
+        I.e = e;
+        I.n0 = (item % n_tiles) * (32 * NW) + w * 32;
+        I.scg = p.b0_sc + (int64_t)e * p.b0sc_e;
+        I.scu = p.b1_sc + (int64_t)e * p.b1sc_e;
+    };
+    // this lane's weight rows (needed from the item's first refill on)
+    auto set_weights = [&](PItem<MB>& I) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             const bool up = nb >= 2;
             const int wrow = I.n0 + (nb & 1) * 16 + r16;
-            I.b[nb] = reinterpret_cast<const char*>(up ? p.b1 : p.b0) + (int64_t)e * (up ? p.b1_e : p.b0_e) +
+            I.b[nb] = reinterpret_cast<const char*>(up ? p.b1 : p.b0) + (int64_t)I.e * (up ? p.b1_e : p.b0_e) +
                       (int64_t)wrow * (up ? p.b1_r : p.b0_r);
         }
-        I.scg = p.b0_sc + (int64_t)e * p.b0sc_e;
-        I.scu = p.b1_sc + (int64_t)e * p.b1sc_e;
     };
     // staging load i of an item's scale runs: rows i * 64 / R .. of the wave
     // (row nb * 16 + rr: column block nb, row rr), R lanes of 16 bytes per row
@@ -136,7 +153,8 @@ void gemm1_persist(GemmParams p) {
     __syncthreads();
 
     PItem<MB> cur;
-    set_weights(cur, it, e_tab[0]);
+    set_item(cur, it, e_tab[0]);
+    set_weights(cur);
     load_rows(cur, it);
     set_rows(cur);
     cur.s0 = 0;
@@ -166,11 +184,16 @@ void gemm1_persist(GemmParams p) {
         for (int i = 0; i < AR; ++i) {
             int f = w + NW * i;
             f = f < FR ? f : FR - 1;
-            const int mi = f >> 2, u = f & 3;
-            const char* src = a[0];
+            const char* src;
+            if constexpr (NW == 4) {
+                src = a[i];                    // f = w + 4i: row group i, step w
+            } else {
+                const int mi = f >> 2;
+                src = a[0];
 #pragma unroll
-            for (int m = 1; m < MB; ++m) src = m == mi ? a[m] : src;
-            areg[i] = *reinterpret_cast<const i32x4_t*>(src + (int64_t)(st0 + u) * 64 + kg * 16);
+                for (int m = 1; m < MB; ++m) src = m == mi ? a[m] : src;
+            }
+            areg[i] = *reinterpret_cast<const i32x4_t*>(src + (int64_t)(st0 + (f & 3)) * 64 + kg * 16);
         }
     };
     auto store_A = [&](int buf) {
@@ -240,13 +263,13 @@ void gemm1_persist(GemmParams p) {
                     a8, b8, acc[mi][nb], 4, 4, 0, (int)(asc[mi] >> (8 * u)), 0, (int)(bsc[nb] >> (8 * u)));
             }
         }
-        // pinned here: the rounds are straight-line code, and the compiler
-        // would otherwise sink every MFMA to the epilogue and keep all their
-        // operands alive until then
+        // pinned here (in AGPRs, where the MFMAs accumulate): the rounds are
+        // straight-line code, and the compiler would otherwise sink every
+        // MFMA to the epilogue and keep all their operands alive until then
 #pragma unroll
         for (int mi = 0; mi < MB; ++mi)
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) __asm__ volatile("" : "+v"(acc[mi][nb]));
+            for (int nb = 0; nb < NB; ++nb) pin_acc<NW>(acc[mi][nb]);
     };
     // LDS-only workgroup barrier: waits for this wave's LDS accesses, not for
     // the weight loads in flight
@@ -277,7 +300,7 @@ void gemm1_persist(GemmParams p) {
         const bool has_n = it_n < n_items;
         const int it_x = has_n ? it_n : it;
         PItem<MB> nxt;
-        set_weights(nxt, it_x, e_tab[has_n ? j + 1 : j]);
+        set_item(nxt, it_x, e_tab[has_n ? j + 1 : j]);
         nxt.s0 = has_n ? 0 : STEPS - 4;
         const uint8_t* run_cur = sc_buf(j & 1);
         uint8_t* run_nxt = sc_buf((j + 1) & 1);
@@ -290,6 +313,7 @@ void gemm1_persist(GemmParams p) {
             const int st0 = last ? nxt.s0 : 4 * (r + 1);
             if (last) {
                 set_rows(nxt);
+                set_weights(nxt);
                 load_A(nxt.a, st0);
             } else {
                 load_A(cur.a, st0);
@@ -329,7 +353,7 @@ void gemm1_persist(GemmParams p) {
 #pragma unroll
         for (int mi = 0; mi < MB; ++mi)
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) __asm__ volatile("" : "+v"(acc[mi][nb]));
+            for (int nb = 0; nb < NB; ++nb) pin_acc<NW>(acc[mi][nb]);
         const int n0 = cur.n0;
 #pragma unroll
         for (int mi = 0; mi < MB; ++mi) {
@@ -481,14 +505,17 @@ void gemm2_persist(GemmParams p) {
     };
 
     // ---- prologue: item 0's operands, the next item's sorted entries
+    // (the next item's sorted entries go out before the ring: on this path
+    // into the loop, as on the loop's own, the weight loads are the newest,
+    // so the loop's wait for the entries leaves the ring in flight)
     int rows_c[MB], rows_n[MB];
     load_rows(rows_c, it);
+    load_rows(rows_n, n_mine > 1 ? it + G : it);
     int e_c = e_tab[0];
 #pragma unroll
     for (int u = 0; u < U; ++u) load_B(u, e_c, it);
     load_A(rows_c);
     load_bs(e_c, it);
-    load_rows(rows_n, n_mine > 1 ? it + G : it);
     store_A(0);
     store_bs(0);
     lds_barrier();
@@ -525,7 +552,7 @@ void gemm2_persist(GemmParams p) {
 #pragma unroll
             for (int mi = 0; mi < MB; ++mi)
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb) __asm__ volatile("" : "+v"(acc[mi][nb]));
+                for (int nb = 0; nb < NB; ++nb) __asm__ volatile("" : "+a"(acc[mi][nb]));
             __builtin_amdgcn_sched_barrier(0);
             load_B(u, e_n, it_n);
             __builtin_amdgcn_sched_barrier(0);
@@ -604,32 +631,33 @@ hipError_t launch_one(const GemmParams& p, hipStream_t s) {
 }  // namespace
 
 bool gemm1_persist_supported(int bm, int nw, int64_t K, int64_t N) {
-    if (!(bm == 16 || bm == 32) || !(nw == 4 || nw == 8)) return false;
-    const bool k_ok = K == 2048 || K == 4096 || (nw == 4 && K == 8192);
+    if (!(bm == 16 || bm == 32 || (bm == 64 && nw == 4)) || !(nw == 4 || nw == 8)) return false;
+    const bool k_ok = K == 2048 || K == 4096 || (nw == 4 && bm <= 32 && K == 8192);
     return k_ok && N % (32 * nw) == 0;
 }
 
 template <int BM, int NW>
 hipError_t launch_r(const GemmParams& p, hipStream_t s) {
     if (p.K == 2048) return launch_one<BM, NW, 4>(p, s);
-    if constexpr (NW == 4) {
+    if constexpr (NW == 4 && BM <= 32) {
         if (p.K == 8192) return launch_one<BM, NW, 16>(p, s);
     }
     return launch_one<BM, NW, 8>(p, s);
 }
 
 bool gemm2_persist_supported(int bm, int64_t K, int64_t N) {
-    return (bm == 16 || bm == 32) && K == 512 && N % 256 == 0;
+    return (bm == 16 || bm == 32 || bm == 64) && K == 512 && N % 256 == 0;
 }
 
 hipError_t launch_gemm2_persist(int bm, const GemmParams& p, hipStream_t s) {
     if (!gemm2_persist_supported(bm, p.K, p.N)) return hipErrorInvalidValue;
-    return bm == 16 ? launch_g2<16>(p, s) : launch_g2<32>(p, s);
+    return bm == 16 ? launch_g2<16>(p, s) : (bm == 32 ? launch_g2<32>(p, s) : launch_g2<64>(p, s));
 }
 
 hipError_t launch_gemm1_persist(int bm, int nw, const GemmParams& p, hipStream_t s) {
     if (!gemm1_persist_supported(bm, nw, p.K, p.N)) return hipErrorInvalidValue;
     if (bm == 16) return nw == 4 ? launch_r<16, 4>(p, s) : launch_r<16, 8>(p, s);
+    if (bm == 64) return launch_r<64, 4>(p, s);
     return nw == 4 ? launch_r<32, 4>(p, s) : launch_r<32, 8>(p, s);
 }
 

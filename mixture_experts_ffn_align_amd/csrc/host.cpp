@@ -213,6 +213,8 @@ const Cfg kConfigs[] = {
     // both GEMMs on persistent weight streams (gemm2 with K = 512), or gemm2 only
     {16, 1, 1, 4, 0, -1, 1, 0, 4, 1}, {32, 1, 1, 4, 0, -1, 1, 0, 4, 1}, {16, 1, 1, 4, 0, -1, 1, 0, 8, 1},
     {32, 1, 1, 4, 0, -1, 1, 0, 8, 1}, {16, 1, 1, 4, 0, -1, 1, 0, 0, 1}, {32, 1, 1, 4, 0, -1, 1, 0, 0, 1},
+    // the same with 64-row blocks (about 40 to 60 rows per expert)
+    {64, 1, 1, 4, 0, -1, 1, 0, 4, 1}, {64, 1, 1, 4, 0, -1, 1, 0, 0, 1}, {64, 1, 1, 4, 0, 44, 1, 0, 4},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
