@@ -560,8 +560,7 @@ void gemm2_persist(GemmParams p) {
         // y rows by flat assignment (bf16, RNE). A lane holds columns 4 kg ..
         // +3 of column block nb for row r16; through the wave's LDS patch the
         // 16 rows leave as whole 128-byte lines, 8 lanes of 16 bytes per row
-        // (stores of 32-byte pieces per column block cost gemm2 a fifth of
-        // its time: the load counter is shared with the stores, in order).
+        // (about 5% faster than storing each column block's 32-byte pieces).
         const int c0 = col0(it);
         uint8_t* yp = y_lds + w * (MB * 16 * YP);
 #pragma unroll
