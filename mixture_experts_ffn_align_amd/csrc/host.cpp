@@ -270,7 +270,31 @@ int tile_config(int md, int shape, int64_t H, int64_t I) {
 // grid would leave half the CUs idle. Tiles never split K, so the tile shape
 // keeps the sums bit-identical to the unsharded call, and the register
 // stream's K split is chosen from E alone.
-int heuristic_config(int mode, int64_t T, int64_t H, int64_t I, int64_t E, int64_t E_local, int64_t k) {
+// Compute units of the current device (256 if it cannot be asked).
+int device_cus() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        return 256;
+    return cus;
+}
+
+// Whether a config's persistent weight streams (if any) can run this call:
+// MXFP4, the kernels' K and N, and at most 256 items per compute unit.
+bool persist_fits(const Cfg& c, int md, int64_t A, int64_t E, int64_t H, int64_t I) {
+    if (!c.persist && !c.persist2) return true;
+    if (md != 1) return false;
+    const int64_t cap = (int64_t)device_cus() * 256;
+    if (c.persist && (!gemm1_persist_supported(c.bm, c.persist, H, I) ||
+                      align_capacity(A, E, c.bm) / c.bm * (I / (32 * c.persist)) > cap))
+        return false;
+    if (c.persist2 && (!gemm2_persist_supported(c.bm, I, H) || align_capacity(A, E, c.bm) / c.bm * (H / 256) > cap))
+        return false;
+    return true;
+}
+
+int heuristic_config(int mode, int64_t T, int64_t H, int64_t I, int64_t E, int64_t E_local, int64_t k,
+                     bool persist = true) {
     const int64_t bucket = bucket_of(T);
     const double rows = (double)bucket * (double)k / (double)E;   // expected rows per expert
     const double busy = rows + 3.0 * __builtin_sqrt(rows);          // typical maximum
@@ -294,6 +318,16 @@ int heuristic_config(int mode, int64_t T, int64_t H, int64_t I, int64_t E, int64
         if (c == tile_config(1, 0, H, I) && c >= 0 && I == 512) c = 41;
     }
     if (c >= 0) return c;
+    // MXFP4 with I = 512 from half a row to 64 rows per expert: both GEMMs
+    // on the persistent weight streams, blocks of 16, 32 or 64 rows by the
+    // expected rows per expert (the tuner's choice for the TP2 shard)
+    if (persist && md == 1 && I == 4 * 128 && rows >= 0.5 && rows < 64.0) {
+        const int want = rows < 16.0 ? 16 : (rows < 32.0 ? 32 : 64);
+        for (c = 0; c < kNumConfigs; ++c)
+            if (kConfigs[c].bm == want && kConfigs[c].persist == 4 && kConfigs[c].persist2 == 1 &&
+                persist_fits(kConfigs[c], md, bucket * k, E_local, H, I))
+                return c;
+    }
     // MXFP4 with I = 512: gemm2 on the multi-tile weight stream (one align)
     // from 2 tokens up to about 32 rows per expert
     if (md == 1 && I == 4 * 128 && rows > 0.025 && rows < 32.0) {
@@ -513,6 +547,10 @@ int plan_fused(const moe_fused_args_t* a, Plan* pl) {
         ci = default_config(a->mode, T, H, I, E_cfg, E, k);
         // a tuned gemm2 fused with the combine cannot write per-slot rows
         if (y_out && ci < kNumConfigs && kConfigs[ci].fuse) ci = heuristic_config(a->mode, T, H, I, E_cfg, E, k);
+        // a persistent stream that cannot run here (too many items for this
+        // device's compute units): the per-item streams instead
+        if (ci < kNumConfigs && !persist_fits(kConfigs[ci], fp4 ? 1 : 0, T * k, E, H, I))
+            ci = heuristic_config(a->mode, T, H, I, E_cfg, E, k, false);
     }
     if (ci >= kNumConfigs) return fail(MOE_ERR_ARG, "force_config %d out of range", ci);
     const Cfg c1 = kConfigs[ci];
@@ -539,12 +577,8 @@ int plan_fused(const moe_fused_args_t* a, Plan* pl) {
             return MOE_OK;
         }
         if (stage == 2 && c.persist2) {
-            int dev = 0, cus = 256;
-            if (hipGetDevice(&dev) != hipSuccess ||
-                hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-                cus = 256;
-            const int64_t items = align_capacity(T * k, E, c.bm) / c.bm * (N / 256);
-            if (md != 1 || !gemm2_persist_supported(c.bm, K, N) || items > (int64_t)cus * 256)
+            if (md != 1 || !gemm2_persist_supported(c.bm, K, N) ||
+                align_capacity(T * k, E, c.bm) / c.bm * (N / 256) > (int64_t)device_cus() * 256)
                 return fail(MOE_ERR_UNSUPPORTED,
                             "config %d: the persistent gemm2 needs MXFP4, K = 512, N %% 256 == 0 and at most 256 "
                             "items per compute unit", ci);
@@ -554,12 +588,8 @@ int plan_fused(const moe_fused_args_t* a, Plan* pl) {
         }
         if (stage == 1 && c.persist) {
             // one workgroup per compute unit, at most 256 items each
-            int dev = 0, cus = 256;
-            if (hipGetDevice(&dev) != hipSuccess ||
-                hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-                cus = 256;
-            const int64_t items = align_capacity(T * k, E, c.bm) / c.bm * (N / (32 * c.persist));
-            if (md != 1 || !gemm1_persist_supported(c.bm, c.persist, K, N) || items > (int64_t)cus * 256)
+            if (md != 1 || !gemm1_persist_supported(c.bm, c.persist, K, N) ||
+                align_capacity(T * k, E, c.bm) / c.bm * (N / (32 * c.persist)) > (int64_t)device_cus() * 256)
                 return fail(MOE_ERR_UNSUPPORTED,
                             "config %d: the persistent gemm1 needs MXFP4, K in {2048, 4096, 8192}, N %% %d == 0 "
                             "and at most 256 items per compute unit", ci, 32 * c.persist);

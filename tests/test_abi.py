@@ -306,6 +306,51 @@ def test_binding_workspace_cache_is_per_device_and_stream():
     assert d.numel() == 256 and made == [1000, 1000, 5000, 256]
 
 
+def _strided_query(T, H, I, E, k, mode, **kw):
+    """moe_query_config on views of small buffers (shapes only; no launch)."""
+    def view(shape, dtype, row=16):
+        st = [row] * (len(shape) - 1) + [1]
+        return torch.empty(1 + sum((s - 1) * t for s, t in zip(shape, st)) + 64, dtype=dtype).as_strided(shape, st)
+    x = view((T, H), torch.bfloat16)
+    ids, w = view((T, k), torch.int32, 1), view((T, k), torch.float32, 1)
+    if mode == moe.MODE_MXFP4:
+        g, w2 = view((E, I, H // 2), torch.uint8), view((E, H, I // 2), torch.uint8)
+        kw.update(gate_scale=view((E, I, H // 32), torch.uint8), up_scale=view((E, I, H // 32), torch.uint8),
+                  w2_scale=view((E, H, I // 32), torch.uint8))
+    else:
+        g, w2 = view((E, I, H), torch.bfloat16), view((E, H, I), torch.bfloat16)
+    return moe.moe_query_config(x, g, g, w2, ids, w, mode=mode, **kw)
+
+
+def test_rules_take_persistent_streams_where_they_fit():
+    """For an MXFP4 layer outside the tuned table (I = 512), the built-in
+    rules run both GEMMs on the persistent weight streams from half a row to
+    64 rows per expert, with 16-, 32- or 64-row blocks by the expected rows;
+    not at fewer rows, not on tiles' ground, never in bf16 (forcing one there
+    fails before any launch), nor where a workgroup per compute unit would
+    get more than 256 items (forced there, it fails before any launch; the
+    rules then fall back to the per-item streams)."""
+    fp4 = moe.MODE_MXFP4
+
+    def q(T, E=256, k=10, **kw):
+        return _strided_query(T, 4096, 512, E, k, fp4, **kw)
+    for T, bm in ((64, 16), (512, 32), (1024, 64)):
+        c = q(T)
+        assert (c["gemm1_kernel"], c["gemm2_kernel"], c["block_m"]) == (19, 20, bm), (T, c)
+    assert q(8)["gemm1_kernel"] != 19 and q(4096)["gemm1_kernel"] != 19
+    pers = q(64)["config_index"]
+    bf = _strided_query(64, 4096, 512, 256, 10, moe.MODE_BF16)
+    assert bf["gemm1_kernel"] != 19 and bf["gemm2_kernel"] != 20
+    with pytest.raises(moe.MoEError) as ei:
+        _strided_query(64, 4096, 512, 256, 10, moe.MODE_BF16, force_config=pers)
+    assert ei.value.status == -6
+    # 32768 tokens, top-32 of 1024 experts in 16-row blocks: over a million
+    # gemm2 items, far more than 256 per compute unit
+    with pytest.raises(moe.MoEError) as ei:
+        q(32768, E=1024, k=32, force_config=pers)
+    assert ei.value.status == -6
+
+
 def test_mxfp4_register_gemm2_falls_back_past_4gb_of_y():
     """An MXFP4 layer's built-in choice at many tokens keeps h rows in
     registers for gemm2 (family 18); where the y rows would span 4 GB or more
