@@ -28,7 +28,7 @@
 //    first half of an item, two 1 KB loads per round that each read whole
 //    runs (R lanes of 16 bytes per row: a load that took 16 bytes of each of
 //    64 rows asked for four times the cache lines per byte and cost a tenth
-//    of the kernel's time), written to this wave's half of a double-buffered
+//    of the kernel's time), written to this wave's part of a double-buffered
 //    LDS area (each wave reads only its own rows' runs, so no barrier guards
 //    them);
 //  * the token-row fragments of the next round (one round = 4 steps of 128
