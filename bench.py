@@ -815,7 +815,8 @@ def bwd_lines(tokens, dev):
 def norm_lines(tokens, dev):
     """RMSNorm of H=4096 bf16 rows (weight fp32 uniform [0, 1), eps 1e-6):
     moe_rmsnorm on a contiguous and on a transposed x, and the bf16
-    Qwen3-235B-shaped fused forward with and without norm_weight. Cold-timed."""
+    Qwen3-235B-shaped fused forward with and without norm_weight, on a
+    contiguous and on a transposed x. Cold-timed."""
     import torch
     import mixture_experts_ffn_align_amd as moe
     from mixture_experts_ffn_align_amd import workloads as W
@@ -835,13 +836,16 @@ def norm_lines(tokens, dev):
         xn = torch.empty_like(x)
         ids, wts = moe.moe_topk_softmax(inp["logits"], k)
         out = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
-        ws = torch.empty(moe.moe_fused_workspace_size(x, gate, up, w2, ids, wts, norm_weight=nw),
+        ws = torch.empty(moe.moe_fused_workspace_size(xt, gate, up, w2, ids, wts, norm_weight=nw),
                          dtype=torch.uint8, device=dev)
         (us_rows, _, _), _ = timer.both(lambda: moe.moe_rmsnorm(x, nw, 1e-6, out=xn))
         (us_cols, _, _), _ = timer.both(lambda: moe.moe_rmsnorm(xt, nw, 1e-6, out=xn))
         (us_f, _, _), _ = timer.both(lambda: moe.moe_fused_fwd(x, gate, up, w2, ids, wts, out=out, workspace=ws))
         (us_fn, _, _), _ = timer.both(lambda: moe.moe_fused_fwd(x, gate, up, w2, ids, wts, out=out, workspace=ws,
                                                                 norm_weight=nw, norm_eps=1e-6))
+        (us_ft, _, _), _ = timer.both(lambda: moe.moe_fused_fwd(xt, gate, up, w2, ids, wts, out=out, workspace=ws))
+        (us_fnt, _, _), _ = timer.both(lambda: moe.moe_fused_fwd(xt, gate, up, w2, ids, wts, out=out, workspace=ws,
+                                                                 norm_weight=nw, norm_eps=1e-6))
         byts = T * H * 2 * 2 + H * 4
         print(json.dumps({
             "workload": f"RMSNorm of [T, {H}] bf16 rows, fp32 weight; {sh.name} fused forward with it",
@@ -851,6 +855,7 @@ def norm_lines(tokens, dev):
             "rmsnorm_transposed_x_us": round(us_cols, 2),
             "rmsnorm_transposed_x_gbs": round(byts / (us_cols * 1e-6) / 1e9, 1),
             "fused_us": round(us_f, 1), "fused_with_norm_us": round(us_fn, 1),
+            "fused_transposed_x_us": round(us_ft, 1), "fused_with_norm_transposed_x_us": round(us_fnt, 1),
             "timing": "cold: L2 and MALL flushed before each graph-replayed call",
         }), flush=True)
         del inp, x, xt, xn, ids, wts, out, ws

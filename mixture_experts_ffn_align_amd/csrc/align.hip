@@ -12,7 +12,7 @@
 // pass also writes the order padded to the second block size (an element's
 // place there is its place in the first layout, shifted by the difference of
 // its expert's two padded offsets).
-#include "moe_internal.h"
+#include "prep.h"
 
 namespace moe {
 namespace {
@@ -220,22 +220,22 @@ __device__ void align_fused_body(const AlignParams& p) {
 
 __global__ __launch_bounds__(kFusedThreads) void align_fused(AlignParams p) { align_fused_body(p); }
 
-// Workgroup 0 aligns; workgroups 1.. quantise the activation to MXFP4, one
-// thread per group of 32 values (neither depends on the other).
-__global__ __launch_bounds__(kFusedThreads) void align_fused_quant(AlignParams p, QuantParams q) {
+// Workgroup 0 aligns; workgroups 1.. prepare the activation operand
+// (neither depends on the other).
+template <int KIND>
+__global__ __launch_bounds__(kFusedThreads) void align_fused_prep(AlignParams p, PrepParams q) {
     if (blockIdx.x == 0) {
         align_fused_body(p);
         return;
     }
-    const int64_t g = (int64_t)(blockIdx.x - 1) * kFusedThreads + threadIdx.x;
-    if (g < q.E * q.R * (q.K / 32)) quant_group_mxfp4(q, g);
+    prep_block<KIND, 0, kFusedThreads>(q, (int64_t)blockIdx.x - 1);
 }
 
-// Multi-block phase 1: counts[b][e] for chunk b.
-__global__ __launch_bounds__(kThreads) void align_count(AlignParams p) {
+// Multi-block phase 1: counts[b][e] for chunk b (b < nchunks).
+__device__ void align_count_body(const AlignParams& p, int nchunks) {
     extern __shared__ int lds[];
     const int E = p.E;
-    fill_sentinels(p, blockIdx.x * kThreads + threadIdx.x, gridDim.x * kThreads);
+    fill_sentinels(p, blockIdx.x * kThreads + threadIdx.x, nchunks * kThreads);
     for (int i = threadIdx.x; i < E; i += kThreads) lds[i] = 0;
     __syncthreads();
     const int w = threadIdx.x >> 6;
@@ -245,6 +245,25 @@ __global__ __launch_bounds__(kThreads) void align_count(AlignParams p) {
     wave_count(eid, lds, hi - lo);
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += kThreads) p.counts[(int64_t)blockIdx.x * E + e] = lds[e];
+}
+
+__global__ __launch_bounds__(kThreads) void align_count(AlignParams p) { align_count_body(p, gridDim.x); }
+
+// Workgroups past the nchunks counting ones prepare the activation operand.
+template <int KIND>
+__global__ __launch_bounds__(kThreads) void align_count_prep(AlignParams p, PrepParams q, int nchunks) {
+    if ((int)blockIdx.x < nchunks) {
+        align_count_body(p, nchunks);
+        return;
+    }
+    prep_block<KIND, 0, kThreads>(q, (int64_t)blockIdx.x - nchunks);
+}
+
+// The row-layout RMSNorm (and the quantisation of the normalised rows) on
+// its own: four rows per workgroup.
+template <int NCL>
+__global__ __launch_bounds__(256) void prep_kernel(PrepParams q) {
+    prep_block<kPrepNormRows, NCL, 256>(q, blockIdx.x);
 }
 
 // Multi-block phase 2: per-expert prefix over chunks, padded offsets.
@@ -331,35 +350,60 @@ bool use_fused(int A, int E) {
 
 bool align_single_launch(int64_t A, int32_t E) { return use_fused((int)A, E); }
 
-hipError_t launch_align_with_quant(const AlignParams& p, const QuantParams& q, hipStream_t s) {
-    if (!use_fused(p.A, p.E)) return hipErrorInvalidValue;
-    const int64_t groups = q.E * q.R * (q.K / 32);
-    const size_t lds = sizeof(int) * ((size_t)kFusedWaves * p.E + 3 * p.E + kFusedWaves + 1);
-    const int64_t grid = 1 + (groups + kFusedThreads - 1) / kFusedThreads;
-    hipLaunchKernelGGL(align_fused_quant, dim3((unsigned)grid), dim3(kFusedThreads), lds, s, p, q);
-    return hipGetLastError();
-}
-
 size_t align_scratch_bytes(int64_t A, int32_t E) {
     if (use_fused((int)A, E)) return 0;
     const int64_t nchunks = (A + kChunk - 1) / kChunk;
     return (size_t)(nchunks + 2) * (size_t)E * sizeof(int32_t);
 }
 
-hipError_t launch_align(const AlignParams& p, hipStream_t s) {
+hipError_t launch_align_prep(const AlignParams& p, int kind, const PrepParams& prep, hipStream_t s) {
     const int E = p.E;
     if (use_fused(p.A, E)) {
         const size_t lds = sizeof(int) * ((size_t)kFusedWaves * E + 3 * E + kFusedWaves + 1);
-        hipLaunchKernelGGL(align_fused, dim3(1), dim3(kFusedThreads), lds, s, p);
+        const PrepParams& q = prep;
+        const dim3 grid((unsigned)(1 + prep_blocks(kind, q, kFusedThreads)));
+        switch (kind) {
+        case 0: hipLaunchKernelGGL(align_fused, dim3(1), dim3(kFusedThreads), lds, s, p); break;
+        case kPrepQuant: hipLaunchKernelGGL(align_fused_prep<kPrepQuant>, grid, dim3(kFusedThreads), lds, s, p, q); break;
+        case kPrepPack: hipLaunchKernelGGL(align_fused_prep<kPrepPack>, grid, dim3(kFusedThreads), lds, s, p, q); break;
+        case kPrepNormRows:
+            hipLaunchKernelGGL(align_fused_prep<kPrepNormRows>, grid, dim3(kFusedThreads), lds, s, p, q);
+            break;
+        default: return hipErrorInvalidValue;
+        }
         return hipGetLastError();
     }
     const int nchunks = (p.A + kChunk - 1) / kChunk;
     const size_t lds_c = sizeof(int) * (size_t)E;
-    hipLaunchKernelGGL(align_count, dim3(nchunks), dim3(kThreads), lds_c, s, p);
+    const PrepParams& q = prep;
+    const dim3 grid((unsigned)(nchunks + prep_blocks(kind, q, kThreads)));
+    switch (kind) {
+    case 0: hipLaunchKernelGGL(align_count, dim3(nchunks), dim3(kThreads), lds_c, s, p); break;
+    case kPrepQuant: hipLaunchKernelGGL(align_count_prep<kPrepQuant>, grid, dim3(kThreads), lds_c, s, p, q, nchunks); break;
+    case kPrepPack: hipLaunchKernelGGL(align_count_prep<kPrepPack>, grid, dim3(kThreads), lds_c, s, p, q, nchunks); break;
+    case kPrepNormRows:
+        hipLaunchKernelGGL(align_count_prep<kPrepNormRows>, grid, dim3(kThreads), lds_c, s, p, q, nchunks);
+        break;
+    default: return hipErrorInvalidValue;
+    }
     const size_t lds_s = sizeof(int) * (3 * (size_t)E + kWaves + 1);
     hipLaunchKernelGGL(align_scan, dim3(1), dim3(kThreads), lds_s, s, p, nchunks);
     const size_t lds_x = sizeof(int) * ((size_t)kWaves + 2) * E;
     hipLaunchKernelGGL(align_scatter, dim3(nchunks), dim3(kThreads), lds_x, s, p, nchunks);
+    return hipGetLastError();
+}
+
+hipError_t launch_align(const AlignParams& p, hipStream_t s) { return launch_align_prep(p, 0, PrepParams{}, s); }
+
+hipError_t launch_prep_norm_rows(const PrepParams& q, hipStream_t s) {
+    if (q.n.T == 0) return hipSuccess;
+    const dim3 grid((unsigned)prep_blocks(kPrepNormRows, q, 256));
+    if (q.n.H <= 512 * 8)
+        hipLaunchKernelGGL(prep_kernel<8>, grid, dim3(256), 0, s, q);
+    else if (q.n.H <= 512 * 16)
+        hipLaunchKernelGGL(prep_kernel<16>, grid, dim3(256), 0, s, q);
+    else
+        hipLaunchKernelGGL(prep_kernel<0>, grid, dim3(256), 0, s, q);
     return hipGetLastError();
 }
 

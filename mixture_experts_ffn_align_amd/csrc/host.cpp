@@ -17,6 +17,7 @@
 
 #include "gemm_persist.h"
 #include "moe_internal.h"
+#include "prep.h"
 #include "moeffn.h"
 
 using namespace moe;
@@ -398,8 +399,9 @@ struct Plan {
     bool fuse;             // gemm2 and the combine in one kernel (no y, no second layout)
     bool small1;           // gemm1 per slot, without the align (implies fuse)
     bool norm_fold;        // the per-slot gemm1 normalises its token rows itself (no RMSNorm launch)
+    bool norm_via_pack;    // a strided x is re-laid out (in the align launch), then normalised by rows
     // workspace offsets
-    size_t off_counts, off_sorted[2], off_bexp[2], off_npad[2], off_eblk[2], off_x, off_xs, off_xn, off_h, off_hs, off_y,
+    size_t off_counts, off_sorted[2], off_bexp[2], off_npad[2], off_eblk[2], off_x, off_xs, off_xn, off_xp, off_h, off_hs, off_y,
         total;
 };
 
@@ -665,6 +667,11 @@ int plan_fused(const moe_fused_args_t* a, Plan* pl) {
     // coalesced along the stride-1 dimension); gemm1 per slot reads x
     // through both strides itself
     pl->pack_x = !fp4 && !x_direct && !norm && !pl->small1;
+    // With the RMSNorm on the aligned path, x with a non-unit last-dim
+    // stride is re-laid out by the align launch's spare workgroups and then
+    // normalised by rows (a launch of its own: it needs the whole row); the
+    // column-layout norm would leave few workgroups each reading 64 rows
+    pl->norm_via_pack = norm && !pl->norm_fold && !pl->small1 && H > 1 && a->x.stride[1] != 1;
     {
         // the tiled kernels address every operand row with a 32-bit offset
         const int64_t eb = fp4 ? 1 : 2;
@@ -697,9 +704,10 @@ int plan_fused(const moe_fused_args_t* a, Plan* pl) {
         pl->off_npad[g] = take(4);
         pl->off_eblk[g] = take((size_t)(E + 1) * 4);
     }
-    pl->off_x = pl->off_xs = pl->off_xn = 0;
+    pl->off_x = pl->off_xs = pl->off_xn = pl->off_xp = 0;
     // normalised rows, bf16 (unless the per-slot gemm1 normalises in LDS)
     if (norm && !pl->norm_fold) pl->off_xn = take((size_t)T * (size_t)H * 2);
+    if (pl->norm_via_pack) pl->off_xp = take((size_t)T * (size_t)H * 2);
     if (fp4) {
         pl->off_x = take((size_t)T * (size_t)(H / 2));
         pl->off_xs = take((size_t)T * (size_t)(H / 32));
@@ -883,25 +891,76 @@ int run_fused(const moe_fused_args_t& a, const Plan& pl, char* base, hipStream_t
     }
     hipError_t e;
 
-    // MXFP4 activation quantisation: its own launch in stage 1, or folded
-    // into the single-workgroup align launch of stage 0
-    QuantParams qp{};
+    // The activation operand of gemm1 is prepared by the spare workgroups of
+    // the align launch (its first launch when the align takes three): the
+    // RMSNorm (then, in MXFP4 mode, the quantisation of the normalised rows),
+    // the MXFP4 quantisation, or the bf16 re-layout of a strided x. The
+    // per-slot gemm1 (no align) reads x itself, folding the norm in.
+    PrepParams pr{};
+    int prep = 0;
+    const void* a_op = a.x.data;
+    int64_t a_row = a.x.stride[0];
     if (fp4) {
-        qp.src = (const uint16_t*)a.x.data;
-        qp.E = 1;
-        qp.R = pl.T;
-        qp.K = pl.H;
-        qp.ss_r = a.x.stride[0];
-        qp.ss_k = a.x.stride[1];
-        qp.codes = (uint8_t*)(base + pl.off_x);
-        qp.cs_r = pl.H / 2;
-        qp.scales = (uint8_t*)(base + pl.off_xs);
-        qp.xs_r = pl.H / 32;
+        pr.q.src = (const uint16_t*)a.x.data;
+        pr.q.E = 1;
+        pr.q.R = pl.T;
+        pr.q.K = pl.H;
+        pr.q.ss_r = a.x.stride[0];
+        pr.q.ss_k = a.x.stride[1];
+        pr.q.codes = (uint8_t*)(base + pl.off_x);
+        pr.q.cs_r = pl.H / 2;
+        pr.q.scales = (uint8_t*)(base + pl.off_xs);
+        pr.q.xs_r = pl.H / 32;
     }
-    const bool quant_in_align = fp4 && !pl.norm && align_single_launch(pl.A, (int32_t)pl.E);
+    if (!pl.small1) {
+        if (pl.norm) {
+            norm_params(&pr.n, a.x, a.norm_weight, a.norm_eps);
+            pr.n.out = (uint16_t*)(base + pl.off_xn);
+            pr.n.os_t = pl.H;
+            pr.n.os_h = 1;
+            prep = kPrepNormRows;
+            if (pl.norm_via_pack) {
+                // the align launch re-lays x out; the norm follows in stage 1
+                prep = kPrepPack;
+                pr.pk.src = (const uint16_t*)a.x.data;
+                pr.pk.s_t = a.x.stride[0];
+                pr.pk.s_h = a.x.stride[1];
+                pr.pk.dst = (uint16_t*)(base + pl.off_xp);
+                pr.pk.T = pl.T;
+                pr.pk.H = pl.H;
+                pr.n.x = pr.pk.dst;
+                pr.n.xs_t = pl.H;
+                pr.n.xs_h = 1;
+            }
+            a_op = base + pl.off_xn;
+            a_row = pl.H;
+            if (fp4) {
+                pr.quant_after = 1;
+                pr.q.src = (const uint16_t*)(base + pl.off_xn);
+                pr.q.ss_r = pl.H;
+                pr.q.ss_k = 1;
+            }
+        } else if (fp4) {
+            prep = kPrepQuant;
+        } else if (pl.pack_x) {
+            prep = kPrepPack;
+            pr.pk.src = (const uint16_t*)a.x.data;
+            pr.pk.s_t = a.x.stride[0];
+            pr.pk.s_h = a.x.stride[1];
+            pr.pk.dst = (uint16_t*)(base + pl.off_x);
+            pr.pk.T = pl.T;
+            pr.pk.H = pl.H;
+            a_op = base + pl.off_x;
+            a_row = pl.H;
+        }
+        if (fp4) {
+            a_op = base + pl.off_x;
+            a_row = pl.H / 2;
+        }
+    }
 
-    // stage 0: align; when the two GEMMs use different block sizes, the same
-    // pass writes the second padded layout too
+    // stage 0: align (with the preparation); when the two GEMMs use
+    // different block sizes, the same pass writes the second padded layout
     tm.begin(0);
     if (!pl.small1) {
         AlignParams ap{};
@@ -928,43 +987,21 @@ int run_fused(const moe_fused_args_t& a, const Plan& pl, char* base, hipStream_t
             ap.n_padded2 = npad[1];
             ap.expert_block2 = eblk[1];
         }
-        e = quant_in_align ? launch_align_with_quant(ap, qp, s) : launch_align(ap, s);
-        if (e != hipSuccess) return hip_fail(e, "align");
+        if ((e = launch_align_prep(ap, prep, pr, s)) != hipSuccess) return hip_fail(e, "align");
     }
     tm.end(0);
-
-    // stage 1: prepare the activation operand
+    // stage 1: the RMSNorm (and MXFP4 quantisation) of a re-laid-out x, and
+    // the RMSNorm of a per-slot gemm1 call that does not fold it in (there is
+    // no align launch), have launches of their own
     tm.begin(1);
-    const void* a_op = a.x.data;
-    int64_t a_row = a.x.stride[0];
-    if (pl.norm && !pl.norm_fold) {
+    if (pl.norm_via_pack && (e = launch_prep_norm_rows(pr, s)) != hipSuccess) return hip_fail(e, "rmsnorm");
+    if (pl.small1 && pl.norm && !pl.norm_fold) {
         NormParams np{};
         norm_params(&np, a.x, a.norm_weight, a.norm_eps);
         np.out = (uint16_t*)(base + pl.off_xn);
         np.os_t = pl.H;
         np.os_h = 1;
         if ((e = launch_rmsnorm(np, s)) != hipSuccess) return hip_fail(e, "rmsnorm");
-        a_op = base + pl.off_xn;
-        a_row = pl.H;
-        qp.src = (const uint16_t*)(base + pl.off_xn);
-        qp.ss_r = pl.H;
-        qp.ss_k = 1;
-    }
-    if (fp4 && !pl.small1) {
-        if (!quant_in_align && (e = launch_quant_mxfp4(qp, s)) != hipSuccess) return hip_fail(e, "quant x");
-        a_op = base + pl.off_x;
-        a_row = pl.H / 2;
-    } else if (pl.pack_x) {
-        PackParams pp{};
-        pp.src = (const uint16_t*)a.x.data;
-        pp.s_t = a.x.stride[0];
-        pp.s_h = a.x.stride[1];
-        pp.dst = (uint16_t*)(base + pl.off_x);
-        pp.T = pl.T;
-        pp.H = pl.H;
-        if ((e = launch_pack_bf16(pp, s)) != hipSuccess) return hip_fail(e, "pack x");
-        a_op = base + pl.off_x;
-        a_row = pl.H;
     }
     tm.end(1);
 

@@ -196,12 +196,17 @@ struct AlignParams {
 // Scratch bytes the multi-block path needs for A assignments over E experts.
 size_t align_scratch_bytes(int64_t A, int32_t E);
 hipError_t launch_align(const AlignParams& p, hipStream_t s);
-// The align in one workgroup (A and E small enough) with the MXFP4
-// quantisation q of the activation in the other workgroups of the same
-// launch; false if the align needs several launches (nothing launched).
+// Whether the align runs in one workgroup (A and E small enough) and one
+// launch.
 bool align_single_launch(int64_t A, int32_t E);
-struct QuantParams;
-hipError_t launch_align_with_quant(const AlignParams& p, const QuantParams& q, hipStream_t s);
+// The align with the activation preparation of kind (prep.h; 0: none) run by
+// the spare workgroups of its first launch.
+struct PrepParams;
+hipError_t launch_align_prep(const AlignParams& p, int kind, const PrepParams& prep, hipStream_t s);
+// The row-layout RMSNorm of prep.n (unit last-dim stride), then, with
+// prep.quant_after, the MXFP4 quantisation prep.q of the normalised rows, as
+// a launch of its own.
+hipError_t launch_prep_norm_rows(const PrepParams& prep, hipStream_t s);
 
 struct QuantParams {
     const uint16_t* src;

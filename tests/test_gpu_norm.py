@@ -8,7 +8,13 @@
   with a padded stride and a base that is not 16-byte aligned, a strided out;
 * the fused forward with ``norm_weight`` equals the fused forward on
   ``moe_rmsnorm``'s output bit for bit, in bf16 and MXFP4, with contiguous
-  and transposed x, and matches the oracle (RMSNorm, then the FFN).
+  and transposed x, and matches the oracle (RMSNorm, then the FFN). The
+  sizes reach both align paths, which run the norm in the spare workgroups
+  of the one-workgroup align launch (T = 5, 512 bf16; T = 64 MXFP4) or of
+  the first of its three launches (T = 4099 bf16; T = 2048 MXFP4), and the
+  per-slot gemm1 without the align (T = 16 MXFP4). A transposed x is re-laid
+  out first and then normalised by rows (``moe_rmsnorm`` into a contiguous
+  out, and the fused forward); a strided out takes the column kernel.
 """
 import numpy as np
 import pytest
@@ -51,8 +57,8 @@ def test_rmsnorm_matches_oracle(T, f32):
     assert d.max() <= 1 and np.mean(d == 0) >= 0.999
 
 
-def test_rmsnorm_layouts_same_bits():
-    T, H = 333, 4096
+@pytest.mark.parametrize("T,H", [(1, 4096), (333, 4096), (4099, 4096), (77, 8192)])
+def test_rmsnorm_layouts_same_bits(T, H):
     g = torch.Generator(device=DEV).manual_seed(4)
     x = torch.randn(T, H, generator=g, device=DEV).to(torch.bfloat16)
     w = _weight(H, False, 1)
@@ -77,7 +83,7 @@ def w235():
     return W.draw_weights(W.QWEN3_235B_BF16, g, DEV)
 
 
-@pytest.mark.parametrize("T", [5, 512])
+@pytest.mark.parametrize("T", [5, 512, 4099])
 def test_fused_bf16_with_norm(w235, T):
     sh = W.QWEN3_235B_BF16
     inp = W.make_inputs(sh, T, seed=300 + T, device=DEV, weights=w235)
@@ -102,7 +108,7 @@ def test_fused_bf16_with_norm(w235, T):
     assert r <= 1e-2
 
 
-@pytest.mark.parametrize("T", [64, 2048])
+@pytest.mark.parametrize("T", [16, 64, 2048])
 def test_fused_mxfp4_with_norm(T):
     sh = W.QWEN35_397B_TP2_FP4_512
     g = torch.Generator(device=DEV).manual_seed(31)
@@ -116,6 +122,9 @@ def test_fused_mxfp4_with_norm(T):
     xn = moe.moe_rmsnorm(inp["x"], nw, EPS)
     ref = moe.moe_fused_fwd(xn, gq, uq, wq, ids, wts, **kw)
     assert np.array_equal(np_bits(out), np_bits(ref))
+    xt = inp["x"].t().contiguous().t()
+    out_t = moe.moe_fused_fwd(xt, gq, uq, wq, ids, wts, norm_weight=nw, norm_eps=EPS, **kw)
+    assert np.array_equal(np_bits(out_t), np_bits(out))
     toks = sample_tokens(T, 4)
     used = sorted({int(e) for e in oi[toks].ravel()})
     mx = oracle_quant_experts(w13, w2, sh.inter, used)
