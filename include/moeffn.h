@@ -176,8 +176,11 @@ int moe_quant_mxfp4(const moe_tensor_t *src, const moe_tensor_t *codes,
  *   stage_events NULL, or 2*MOE_NUM_STAGES hipEvent_t handles created by the
  *               caller; event 2s is recorded before stage s and 2s+1 after
  *               it, on the call's stream; NULL entries are skipped. Stages:
- *               0 align, 1 prepare (RMSNorm, activation quantise or
- *               re-layout; may be empty), 2 gemm1 + act, 3 gemm2, 4 combine.
+ *               0 align (its launch also prepares the activation: RMSNorm,
+ *               MXFP4 quantisation or the re-layout of a strided x), 1
+ *               prepare (the RMSNorm of a re-laid-out x, or of the rows of a
+ *               per-slot gemm1 that does not fold it in; usually empty),
+ *               2 gemm1 + act, 3 gemm2, 4 combine.
  *   force_config  -1 for the built-in choice, else an index into the
  *               library's config list (tests of tile invariance).
  * Numerics: fp32 accumulation; h rounded to bf16 (bf16 mode) or quantised to
