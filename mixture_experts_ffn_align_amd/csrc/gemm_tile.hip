@@ -76,7 +76,7 @@ struct TileShape {
     static constexpr int kWN = BW / 128;                   // waves along weight rows
     static constexpr int kWM = NW / kWN;                   // waves along rows
     static constexpr int kWMI = BM / (16 * kWM);           // row blocks per wave
-    static_assert(kWM * kWN == NW && kWMI * 16 * kWM == BM && kWMI >= 1 && kWMI <= 4, "wave grid");
+    static_assert(kWM * kWN == NW && kWMI * 16 * kWM == BM && kWMI >= 1 && kWMI <= 5, "wave grid");
     static constexpr int kRows = BM + BW;
     static constexpr int kLoads = kRows / (kRowsPerLoad * NW);   // 1 KB loads per wave per stage
     static_assert(kLoads * kRowsPerLoad * NW == kRows, "whole loads");
@@ -592,9 +592,11 @@ hipError_t launch_one(const GemmParams& p, hipStream_t s) {
 // where K allows it, 5 = 128 x 256 x 8 (about 64 to 160 rows per expert),
 // 6 and 7 = the register-resident MXFP4 gemm2 (256 or 128 rows), 8 = MXFP4
 // 256 x 256 x 8 with 128-byte gemm1 stages, 9 = MXFP4 128 x 256 x 8 with
-// 128-byte stages.
+// 128-byte stages, 10 = bf16 320 x 256 x 8 (experts of up to 320 rows in
+// one block: a weight tile is staged once for them, where 256-row blocks
+// stage it twice for an expert of 257 to 320 rows).
 int gemm_tile_rows(int mode, int shape) {
-    static const int rows[10] = {256, 128, 64, 32, 64, 128, 256, 128, 256, 128};
+    static const int rows[11] = {256, 128, 64, 32, 64, 128, 256, 128, 256, 128, 320};
     return mode == 1 && shape == 4 ? 32 : rows[shape];
 }
 
@@ -602,7 +604,7 @@ int gemm_tile_rows(int mode, int shape) {
 // per step of their column walk; as gemm1 they accept no N)
 int gemm_tile_cols(int shape, int stage) {
     if (shape == 6 || shape == 7) return stage == 2 ? 128 : (1 << 30);
-    const int bw = (shape == 0 || shape == 4 || shape == 5 || shape == 8 || shape == 9) ? 256 : 512;
+    const int bw = (shape == 0 || shape == 4 || shape == 5 || shape == 8 || shape == 9 || shape == 10) ? 256 : 512;
     return stage == 1 ? bw / 2 : bw;
 }
 
@@ -614,9 +616,10 @@ int gemm_tile_k_granule(int mode, int shape) {
 }
 
 // MXFP4 128 x 512 stages do not fit the LDS with their scales; shapes 6 to
-// 9 are MXFP4 only
+// 9 are MXFP4 only, shape 10 bf16 only
 bool gemm_tile_supported(int mode, int shape) {
     if (shape >= 6 && shape <= 9) return mode == 1;
+    if (shape == 10) return mode == 0;
     return shape >= 0 && shape <= 5 && !(mode == 1 && shape == 1);
 }
 
@@ -661,6 +664,12 @@ hipError_t launch_gemm_tile(int mode, int shape, int stage, const GemmParams& p,
     if (shape == 2) MOE_TILE(0, 64, 512, 4);
     if (shape == 3) MOE_TILE(0, 32, 512, 4);
     if (shape == 5) MOE_TILE(0, 128, 256, 8);
+    // 320 rows: the two-group schedule holds two k-steps of fragments on top
+    // of the 160 accumulator registers, more than a wave's 256 at two waves
+    // per SIMD, so this shape runs the one-barrier pipeline
+    if (shape == 10)
+        return stage == 1 ? launch_one<0, 1, 320, 256, 8, 2, 2, false>(p, s)
+                          : launch_one<0, 2, 320, 256, 8, 2, 2, false>(p, s);
     MOE_TILE4(0, 64, 256, 4);
 #undef MOE_TILE
 #undef MOE_TILE4

@@ -216,6 +216,9 @@ const Cfg kConfigs[] = {
     {32, 1, 1, 4, 0, -1, 1, 0, 8, 1}, {16, 1, 1, 4, 0, -1, 1, 0, 0, 1}, {32, 1, 1, 4, 0, -1, 1, 0, 0, 1},
     // the same with 64-row blocks (about 40 to 60 rows per expert)
     {64, 1, 1, 4, 0, -1, 1, 0, 4, 1}, {64, 1, 1, 4, 0, -1, 1, 0, 0, 1}, {64, 1, 1, 4, 0, 44, 1, 0, 4},
+    // bf16 320 x 256 tiles (about 200 to 320 rows per expert: one block
+    // each); gemm2 on them or on 256 x 256 tiles (a second padded layout)
+    {320, 1, 1, 4, 11, -1}, {320, 1, 1, 4, 11, 11},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -257,8 +260,9 @@ int tile_config(int md, int shape, int64_t H, int64_t I) {
 // (Qwen3-235B-shaped bf16 and the TP2 MXFP4 shard):
 //  * enough rows per expert: LDS-tiled GEMMs (bf16: 64 x 256 tiles with
 //    three stages in flight from 0.1 expected rows per expert, 128 x 512 from
-//    64, 256 x 256 from 128; MXFP4: 64 x 512 from 64 rows, 256 x 256 from
-//    128);
+//    64, 256 x 256 from 128, 320 x 256 where the typical busiest expert has
+//    257 to 320 rows, so one block holds it; MXFP4: 64 x 512 from 64 rows,
+//    256 x 256 from 128);
 //  * otherwise the register weight stream, whose block rows cover the
 //    typical busiest expert of the bucket in one block (each expert's
 //    weights stream from HBM once) and whose K split grows only while the
@@ -304,13 +308,14 @@ int heuristic_config(int mode, int64_t T, int64_t H, int64_t I, int64_t E, int64
     int c = -1;
     if (md == 0) {
         int shape = -1;
-        if (rows >= 128.0) shape = 0;
+        if (rows >= 128.0) shape = busy > 256.0 && busy <= 320.0 ? 10 : 0;
         else if (rows >= 64.0) shape = 1;
         else if (rows >= 0.1) shape = 4;
         const int64_t grid1 = std::min<int64_t>(bucket * k, E_local) * (int64_t)std::ceil(rows / 128.0) *
                               (I / gemm_tile_cols(1, 1));
         if (shape == 1 && grid1 < 128 && tile_config(0, 0, H, I) >= 0) shape = 0;
         if (shape >= 0) c = tile_config(0, shape, H, I);
+        if (c < 0 && shape == 10) c = tile_config(0, 0, H, I);
         if (c < 0 && shape >= 0 && shape != 4) c = tile_config(0, 4, H, I);
     } else {
         if (rows >= 128.0) c = tile_config(1, 0, H, I);

@@ -44,7 +44,7 @@ def _bits(t):
     return np_bits(t.contiguous())
 
 
-@pytest.mark.parametrize("T,kind", [(1, "uniform"), (7, "zipf"), (512, "uniform"), (4099, "zipf")])
+@pytest.mark.parametrize("T,kind", [(1, "uniform"), (7, "zipf"), (512, "uniform"), (4096, "uniform"), (4099, "zipf")])
 def test_bf16_ep8_rows_combine_to_unsharded(w235, T, kind):
     sh = W.QWEN3_235B_BF16
     inp = W.make_inputs(sh, T, seed=50 + T, device=DEV, weights=w235, logits_kind=kind)
