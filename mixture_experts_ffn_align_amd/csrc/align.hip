@@ -12,6 +12,11 @@
 // pass also writes the order padded to the second block size (an element's
 // place there is its place in the first layout, shifted by the difference of
 // its expert's two padded offsets).
+//
+// The workgroups the sort leaves idle (all but one in the single-workgroup
+// launch; those past the counting ones in the first of the three launches)
+// prepare gemm1's activation operand meanwhile (prep.h): the MXFP4
+// quantisation, the bf16 re-layout of a strided x, or the RMSNorm by rows.
 #include "prep.h"
 
 namespace moe {
@@ -348,19 +353,16 @@ bool use_fused(int A, int E) {
 
 }  // namespace
 
-bool align_single_launch(int64_t A, int32_t E) { return use_fused((int)A, E); }
-
 size_t align_scratch_bytes(int64_t A, int32_t E) {
     if (use_fused((int)A, E)) return 0;
     const int64_t nchunks = (A + kChunk - 1) / kChunk;
     return (size_t)(nchunks + 2) * (size_t)E * sizeof(int32_t);
 }
 
-hipError_t launch_align_prep(const AlignParams& p, int kind, const PrepParams& prep, hipStream_t s) {
+hipError_t launch_align_prep(const AlignParams& p, int kind, const PrepParams& q, hipStream_t s) {
     const int E = p.E;
     if (use_fused(p.A, E)) {
         const size_t lds = sizeof(int) * ((size_t)kFusedWaves * E + 3 * E + kFusedWaves + 1);
-        const PrepParams& q = prep;
         const dim3 grid((unsigned)(1 + prep_blocks(kind, q, kFusedThreads)));
         switch (kind) {
         case 0: hipLaunchKernelGGL(align_fused, dim3(1), dim3(kFusedThreads), lds, s, p); break;
@@ -375,7 +377,6 @@ hipError_t launch_align_prep(const AlignParams& p, int kind, const PrepParams& p
     }
     const int nchunks = (p.A + kChunk - 1) / kChunk;
     const size_t lds_c = sizeof(int) * (size_t)E;
-    const PrepParams& q = prep;
     const dim3 grid((unsigned)(nchunks + prep_blocks(kind, q, kThreads)));
     switch (kind) {
     case 0: hipLaunchKernelGGL(align_count, dim3(nchunks), dim3(kThreads), lds_c, s, p); break;

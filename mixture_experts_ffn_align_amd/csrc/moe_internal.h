@@ -196,9 +196,6 @@ struct AlignParams {
 // Scratch bytes the multi-block path needs for A assignments over E experts.
 size_t align_scratch_bytes(int64_t A, int32_t E);
 hipError_t launch_align(const AlignParams& p, hipStream_t s);
-// Whether the align runs in one workgroup (A and E small enough) and one
-// launch.
-bool align_single_launch(int64_t A, int32_t E);
 // The align with the activation preparation of kind (prep.h; 0: none) run by
 // the spare workgroups of its first launch.
 struct PrepParams;
