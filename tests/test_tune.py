@@ -81,3 +81,25 @@ def test_shard_rows_split_k_like_the_unsharded_call():
         s = _query(mode, H, I, E, E_local, k, bucket)
         u = _query(mode, H, I, E, E, k, bucket)
         assert (s["gemm1_split_k"], s["gemm2_split_k"]) == (u["gemm1_split_k"], u["gemm2_split_k"])
+
+
+def test_rules_take_the_320_row_tile_where_one_block_holds_the_busiest_expert():
+    """Outside the table (here E = 256 experts, not a tuned layer) the bf16
+    rules take 320-row tiles where the typical busiest expert has 257 to 320
+    rows (expected rows r with r + 3 sqrt(r) in that range), so one block
+    holds every expert, and 256-row tiles on either side."""
+    H, I, E, k = 4096, 1536, 256, 8
+
+    def rows(T):
+        return T * k / E
+
+    def busy(T):
+        r = rows(T)
+        return r + 3 * r ** 0.5
+
+    for T in (4096, 8192, 16384, 32768):
+        q = _query(moe.MODE_BF16, H, I, E, E, k, T)
+        want = 320 if rows(T) >= 128 and 256 < busy(T) <= 320 else 256
+        assert q["block_m"] == want, (T, rows(T), busy(T), q)
+    # T = 8192: 256 rows per expert at E = 256, the case the rule is for
+    assert _query(moe.MODE_BF16, H, I, E, E, k, 8192)["block_m"] == 320
