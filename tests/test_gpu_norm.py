@@ -135,3 +135,37 @@ def test_fused_mxfp4_with_norm(T):
     r, er = rel_l2(got, acc), err_ratio(got, acc)
     print(f"T={T} rel_l2={r:.3e} err_ratio={er:.3e}")
     assert r <= 2e-2 and er <= 0.05
+
+
+@pytest.mark.parametrize("mode,H,I,E,k,T", [(moe.MODE_BF16, 6144, 512, 16, 4, 37),
+                                           (moe.MODE_BF16, 2048, 1024, 8, 6, 3001),
+                                           (moe.MODE_MXFP4, 2048, 512, 32, 4, 300),
+                                           (moe.MODE_MXFP4, 6144, 512, 16, 10, 1700)])
+def test_fused_with_norm_other_row_lengths(mode, H, I, E, k, T):
+    """The activation preparation in the align launch at other row lengths
+    (one-workgroup and three-launch align): the fused forward with
+    ``norm_weight`` equals ``moe_rmsnorm`` then the plain call bit for bit,
+    for a contiguous and a transposed x, and a transposed x without the norm
+    (the re-layout) equals the contiguous call."""
+    fp4 = mode == moe.MODE_MXFP4
+    sh = W.MoEShape(f"t_h{H}_i{I}_e{E}_k{k}", H, I, E, k, "mxfp4" if fp4 else "bf16", E, k)
+    g = torch.Generator(device=DEV).manual_seed(H + T)
+    w13, w2 = W.draw_weights(sh, g, DEV)
+    inp = W.make_inputs(sh, T, seed=T, device=DEV, weights=(w13, w2))
+    (ids, wts), _ = route_both(inp)
+    if fp4:
+        (gate, gs), (up, us), (dn, ds) = quantise_weights_gpu(w13, w2, I)
+        kw = dict(gate_scale=gs, up_scale=us, w2_scale=ds, mode=moe.MODE_MXFP4)
+    else:
+        gate, up = W.packed_views(w13, I)
+        dn, kw = w2, {}
+    nw = _weight(H, T % 2 == 0, T)
+    x = inp["x"]
+    xt = x.t().contiguous().t()
+    xn = moe.moe_rmsnorm(x, nw, EPS)
+    ref_n = moe.moe_fused_fwd(xn, gate, up, dn, ids, wts, **kw).clone()
+    for xx in (x, xt):
+        out = moe.moe_fused_fwd(xx, gate, up, dn, ids, wts, norm_weight=nw, norm_eps=EPS, **kw)
+        assert np.array_equal(np_bits(out), np_bits(ref_n))
+    ref = moe.moe_fused_fwd(x, gate, up, dn, ids, wts, **kw).clone()
+    assert np.array_equal(np_bits(moe.moe_fused_fwd(xt, gate, up, dn, ids, wts, **kw)), np_bits(ref))
